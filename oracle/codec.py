@@ -1,0 +1,288 @@
+"""Quantize-on-write in fp64: norm, rotation, Lloyd-Max codes, QJL residual sketch,
+bit packing and the 16-token page layout.
+
+Sources
+  "Closing - The Three-Step Summary", Steps 1-3 and the two-line recipe: rotate, then
+    quantize each coordinate with the Gaussian Lloyd-Max codebook scaled by
+    1/sqrt(d); at b <= 2 bits quantize with b-1 bits and add a 1-bit QJL sketch of
+    the residual; at b >= 3 bits quantize with b bits and skip the sketch.
+  "What the Paper Doesn't Tell You", Finding 2 (the same split by bit width) and
+    Finding 3 (the 5.12x ratio at 3 bits for 128-coordinate blocks, which closes
+    only with one 16-bit norm per block).
+  "Where This Fits in the Inference Stack", section on Blackwell FP4: codes are
+    integer indices dequantized by table lookup.
+  "Why the KV Cache Exists", section on PagedAttention: fixed-size pages allocated
+    on demand.
+
+Readings adopted where the pages are silent (each is listed in the design notes):
+  * the vector norm n = ||x||_2 is stored as fp16 (round to nearest even); the
+    direction u = x / n is formed with the unrounded n; a zero vector has n = 0
+    and u = 0;
+  * the stored codebook levels are the Lloyd-Max levels for N(0,1) rounded to fp16
+    (the 1/sqrt(d) factor is applied in arithmetic), and the decision thresholds are
+    the exact midpoints of those stored levels;
+  * the code of coordinate i is the number of thresholds t_j with y'_i >= t_j, where
+    y' = sqrt(d) * R u is the rotated unit vector in N(0,1) units rounded to fp32
+    (ties go to the upper cell);
+  * prod mode: r = y - yhat in the rotated unit-vector domain (y = R u,
+    yhat_i = level[code_i] / sqrt(d)); gamma = ||r|| stored as fp16; the sketch bit
+    z_j = [(S r)_j >= 0] for the m = d rows of a Gaussian matrix S;
+  * packing: code i of a vector occupies bits [b*i, b*i + b) of a little-endian bit
+    stream; sketch bit j is bit j of the sketch stream.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import lloyd_max, rotation
+
+MSE = 0
+PROD = 1
+PAGE_TOKENS = 16
+SUPPORTED_BITS = (1, 2, 3, 4, 8)
+
+
+def mse_bits(bits: int, mode: int) -> int:
+    """Bits of the Lloyd-Max index: b for MSE mode, b - 1 for prod mode."""
+    return bits - 1 if mode == PROD else bits
+
+
+def fp16_round(x) -> np.ndarray:
+    """Round fp64 values to the nearest fp16 (ties to even), returned as fp64."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def fp16_bits(x) -> np.ndarray:
+    """The IEEE binary16 bit patterns of fp64 values after rounding."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+@dataclass
+class Codebook:
+    head_dim: int
+    bits: int
+    mode: int
+    mse_bits: int
+    levels16: np.ndarray  # 2**mse_bits stored levels (fp16 values, N(0,1) units), ascending
+    thresholds: np.ndarray  # 2**mse_bits - 1 midpoints (N(0,1) units), exact in fp32
+    sign_words: np.ndarray  # head_dim/32 uint32
+    S: np.ndarray | None  # (m, head_dim) projection, fp32 values held in fp64
+
+    @property
+    def signs(self) -> np.ndarray:
+        return rotation.sign_vector(self.sign_words, self.head_dim)
+
+    @property
+    def R(self) -> np.ndarray:
+        return rotation.rotation_matrix(self.sign_words, self.head_dim)
+
+    @property
+    def m(self) -> int:
+        return 0 if self.S is None else self.S.shape[0]
+
+
+def make_codebook(head_dim: int, bits: int, mode: int, sign_words, S=None) -> Codebook:
+    if bits not in SUPPORTED_BITS:
+        raise ValueError("bits must be one of 1, 2, 3, 4, 8")
+    if mode == PROD and bits < 2:
+        raise ValueError("prod mode needs at least 2 bits (1 Lloyd-Max bit + 1 sketch bit)")
+    b = mse_bits(bits, mode)
+    lv = fp16_round(lloyd_max.levels(b))
+    th = lloyd_max.thresholds_of(lv)
+    assert np.all(th.astype(np.float32).astype(np.float64) == th)
+    proj = None
+    if mode == PROD:
+        if S is None:
+            raise ValueError("prod mode needs the projection matrix S")
+        proj = np.asarray(S, dtype=np.float32).astype(np.float64)
+    return Codebook(head_dim, bits, mode, b, lv, th, np.asarray(sign_words, dtype=np.uint32), proj)
+
+
+@dataclass
+class Encoded:
+    codes: np.ndarray  # (N, d) int64 Lloyd-Max indices
+    norm16: np.ndarray  # (N,) fp64 holding fp16 values
+    norm: np.ndarray  # (N,) unrounded fp64 norms (for parity diagnostics)
+    y: np.ndarray  # (N, d) rotated unit vectors R u (N(0,1/d) units)
+    gamma16: np.ndarray | None = None  # (N,) fp16-valued residual norms
+    gamma: np.ndarray | None = None
+    qjl: np.ndarray | None = None  # (N, m) bool sketch bits
+    Sr: np.ndarray | None = None  # (N, m) fp64 projections of the residual
+
+
+def encode(x, cb: Codebook) -> Encoded:
+    """Quantize rows of x (N, d) with codebook cb (one KV tensor of one layer)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = cb.head_dim
+    n = np.sqrt(np.sum(x * x, axis=1))
+    safe = np.where(n > 0, n, 1.0)
+    u = np.where(n[:, None] > 0, x / safe[:, None], 0.0)
+    y = rotation.rotate(u, cb.sign_words)
+    y32 = (y * math.sqrt(d)).astype(np.float32).astype(np.float64)
+    codes = np.searchsorted(cb.thresholds, y32, side="right").astype(np.int64)
+    enc = Encoded(codes=codes, norm16=fp16_round(n), norm=n, y=y)
+    if cb.mode == PROD:
+        yhat = cb.levels16[codes] / math.sqrt(d)
+        r = y - yhat
+        g = np.sqrt(np.sum(r * r, axis=1))
+        Sr = r @ cb.S.T
+        enc.gamma, enc.gamma16, enc.Sr, enc.qjl = g, fp16_round(g), Sr, Sr >= 0.0
+    return enc
+
+
+def code_boundary_distance(enc: Encoded, cb: Codebook) -> np.ndarray:
+    """Distance of each y_i (N(0,1/d) units) to the nearest decision threshold t_j / sqrt(d)."""
+    t = cb.thresholds / math.sqrt(cb.head_dim)
+    return np.min(np.abs(enc.y[..., None] - t[None, None, :]), axis=-1)
+
+
+def dequantize_rotated(codes, norm16, cb: Codebook, gamma16=None, qjl=None) -> np.ndarray:
+    """n * (yhat + [prod] gamma * sqrt(pi/2)/m * S^T (2z - 1)) in the rotated domain (N, d)."""
+    d = cb.head_dim
+    yh = cb.levels16[np.asarray(codes)] / math.sqrt(d)
+    if cb.mode == PROD:
+        pm = 2.0 * np.asarray(qjl, dtype=np.float64) - 1.0
+        yh = yh + (np.asarray(gamma16)[:, None] * math.sqrt(math.pi / 2.0) / cb.m) * (pm @ cb.S)
+    return np.asarray(norm16)[:, None] * yh
+
+
+def dequantize(codes, norm16, cb: Codebook, gamma16=None, qjl=None) -> np.ndarray:
+    """Reconstructed vectors in the original domain: R^T applied to the rotated reconstruction."""
+    return rotation.unrotate(dequantize_rotated(codes, norm16, cb, gamma16, qjl), cb.sign_words)
+
+
+# ---------------------------------------------------------------------------------------------
+# Bit packing
+# ---------------------------------------------------------------------------------------------
+
+
+def pack_codes(codes, b: int) -> np.ndarray:
+    """(N, d) codes of b bits -> (N, d*b/8) bytes, code i at bits [b*i, b*i+b) little-endian."""
+    c = np.asarray(codes, dtype=np.int64)
+    N, d = c.shape
+    bits = ((c[:, :, None] >> np.arange(b)[None, None, :]) & 1).astype(np.uint8).reshape(N, d * b)
+    return np.packbits(bits, axis=1, bitorder="little")
+
+
+def unpack_codes(data, b: int, d: int) -> np.ndarray:
+    bits = np.unpackbits(np.asarray(data, dtype=np.uint8), axis=1, bitorder="little")[:, : d * b]
+    bits = bits.reshape(-1, d, b).astype(np.int64)
+    return np.sum(bits << np.arange(b)[None, None, :], axis=2)
+
+
+def pack_bits(z) -> np.ndarray:
+    """(N, m) booleans -> (N, m/8) bytes, bit j at bit j%8 of byte j/8."""
+    return np.packbits(np.asarray(z, dtype=np.uint8), axis=1, bitorder="little")
+
+
+def unpack_bits(data, m: int) -> np.ndarray:
+    return np.unpackbits(np.asarray(data, dtype=np.uint8), axis=1, bitorder="little")[:, :m].astype(bool)
+
+
+# ---------------------------------------------------------------------------------------------
+# Page layout
+# ---------------------------------------------------------------------------------------------
+
+
+def _align16(x: int) -> int:
+    return (x + 15) // 16 * 16
+
+
+def page_layout(num_kv_heads: int, head_dim: int, k_bits: int, k_mode: int, v_bits: int, v_mode: int) -> dict:
+    """Byte offsets of the sub-arrays of one 16-token page of one layer.
+
+    A page holds 16 token slots for every KV head of the layer, in this order,
+    each sub-array starting on a 16-byte boundary:
+      K codes  [head][slot][d*bK/8]        natural bit stream per vector
+      K norms  [head][slot] fp16
+      K sketch [head][slot][m/8]            (prod mode only)
+      K gamma  [head][slot] fp16            (prod mode only)
+      V codes  [head][d/8][slot][bV]        the vector's bit stream cut into d/8
+                                            pieces of bV bytes (8 coordinates each),
+                                            stored piece-major then slot
+      V norms  [head][slot] fp16
+      V sketch, V gamma                     (prod mode only, as for K)
+    bK, bV are the Lloyd-Max index widths (bits, or bits - 1 in prod mode) and the
+    sketch has m = d bits.
+    """
+    H, d, T = num_kv_heads, head_dim, PAGE_TOKENS
+    off = 0
+    L = {"H": H, "d": d}
+    for name, bits, mode in (("k", k_bits, k_mode), ("v", v_bits, v_mode)):
+        b = mse_bits(bits, mode)
+        L[name + "_b"] = b
+        L[name + "_mode"] = mode
+        L[name + "_codes"] = off
+        off = _align16(off + H * T * d * b // 8)
+        L[name + "_norms"] = off
+        off = _align16(off + H * T * 2)
+        if mode == PROD:
+            L[name + "_qjl"] = off
+            off = _align16(off + H * T * d // 8)
+            L[name + "_gamma"] = off
+            off = _align16(off + H * T * 2)
+    L["page_bytes"] = off
+    return L
+
+
+def _code_byte_index(L: dict, which: str, page, slot, head):
+    """Byte offsets (from pool start, as (n_rec, nbytes) array) of each record's code stream."""
+    d, b, pb = L["d"], L[which + "_b"], L["page_bytes"]
+    page = np.asarray(page, dtype=np.int64)[:, None]
+    slot = np.asarray(slot, dtype=np.int64)[:, None]
+    head = np.asarray(head, dtype=np.int64)[:, None]
+    base = page * pb + L[which + "_codes"]
+    if which == "k":
+        nb = d * b // 8
+        return base + (head * PAGE_TOKENS + slot) * nb + np.arange(nb)[None, :]
+    # V: piece j of b bytes (coordinates 8j..8j+7) at [head][j][slot]
+    j = np.arange(d // 8)
+    within = np.arange(b)
+    # shape (n_rec, d/8, b): piece j, byte within piece -> the vector's stream bytes j*b .. j*b+b-1
+    idx = ((head[:, :, None] * (d // 8) + j[None, :, None]) * PAGE_TOKENS + slot[:, :, None]) * b + within[None, None, :]
+    return base + idx.reshape(idx.shape[0], -1)
+
+
+def _scalar_index(L: dict, key: str, page, slot, head, nbytes: int):
+    page = np.asarray(page, dtype=np.int64)[:, None]
+    slot = np.asarray(slot, dtype=np.int64)[:, None]
+    head = np.asarray(head, dtype=np.int64)[:, None]
+    return page * L["page_bytes"] + L[key] + (head * PAGE_TOKENS + slot) * nbytes + np.arange(nbytes)[None, :]
+
+
+def write_records(pool: np.ndarray, L: dict, which: str, slots, head, enc: Encoded) -> None:
+    """Store encoded vectors of tensor ``which`` ('k' or 'v') for one head at global slots.
+
+    ``pool`` is the flat uint8 page pool; slot s lives in page s // 16 at offset s % 16.
+    Negative slots are skipped.
+    """
+    slots = np.asarray(slots, dtype=np.int64)
+    keep = slots >= 0
+    slots = slots[keep]
+    page, slot = slots // PAGE_TOKENS, slots % PAGE_TOKENS
+    head = np.broadcast_to(np.asarray(head, dtype=np.int64), slots.shape)
+    b = L[which + "_b"]
+    pool[_code_byte_index(L, which, page, slot, head)] = pack_codes(enc.codes[keep], b)
+    pool[_scalar_index(L, which + "_norms", page, slot, head, 2)] = fp16_bits(enc.norm16[keep]).view(np.uint8).reshape(-1, 2)
+    if L[which + "_mode"] == PROD:
+        pool[_scalar_index(L, which + "_qjl", page, slot, head, L["d"] // 8)] = pack_bits(enc.qjl[keep])
+        pool[_scalar_index(L, which + "_gamma", page, slot, head, 2)] = fp16_bits(enc.gamma16[keep]).view(np.uint8).reshape(-1, 2)
+
+
+def read_records(pool: np.ndarray, L: dict, which: str, page, slot, head) -> dict:
+    """Codes, norms (and sketch, gamma in prod mode) of records at (page, slot, head)."""
+    page = np.asarray(page, dtype=np.int64)
+    slot = np.asarray(slot, dtype=np.int64)
+    head = np.broadcast_to(np.asarray(head, dtype=np.int64), page.shape)
+    d, b = L["d"], L[which + "_b"]
+    out = {"codes": unpack_codes(pool[_code_byte_index(L, which, page, slot, head)], b, d)}
+    nb = pool[_scalar_index(L, which + "_norms", page, slot, head, 2)]
+    out["norm16"] = np.ascontiguousarray(nb).view(np.float16).reshape(-1).astype(np.float64)
+    if L[which + "_mode"] == PROD:
+        out["qjl"] = unpack_bits(pool[_scalar_index(L, which + "_qjl", page, slot, head, d // 8)], d)
+        gb = pool[_scalar_index(L, which + "_gamma", page, slot, head, 2)]
+        out["gamma16"] = np.ascontiguousarray(gb).view(np.float16).reshape(-1).astype(np.float64)
+    return out

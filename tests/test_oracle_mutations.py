@@ -1,0 +1,151 @@
+"""Plant plausible mistakes in the CPU oracle and check that a pin catches each one.
+
+Every mutant is applied with monkeypatch for the duration of one test only; the
+oracle's files are never modified. A mutant that no pin rejects would mean the
+pins leave that part of the oracle unchecked.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention, codec, lloyd_max, rotation
+from tests import pins
+
+
+def _caught(*checks):
+    failures = 0
+    for chk in checks:
+        try:
+            chk()
+        except AssertionError:
+            failures += 1
+    return failures
+
+
+def test_mutant_thresholds_not_midpoints(monkeypatch):
+    orig = lloyd_max.thresholds_of
+    monkeypatch.setattr(lloyd_max, "thresholds_of", lambda c: orig(c) + 0.05 * (np.asarray(c)[1:] - np.asarray(c)[:-1]))
+    assert _caught(pins.check_max_1960_table, pins.check_centroid_condition_by_quadrature)
+
+
+def test_mutant_levels_off_by_one_percent(monkeypatch):
+    orig = lloyd_max.positive_levels
+    monkeypatch.setattr(lloyd_max, "positive_levels", lambda b, **kw: 1.01 * orig(b, **kw))
+    assert _caught(pins.check_max_1960_table, pins.check_one_bit_closed_form)
+
+
+def test_mutant_rotation_normalised_by_d(monkeypatch):
+    monkeypatch.setattr(rotation, "rotation_matrix",
+                        lambda sw, d: rotation.hadamard(d) * rotation.sign_vector(sw, d)[None, :] / d)
+    assert _caught(pins.check_rotation_orthogonal)
+
+
+def test_mutant_signs_after_hadamard(monkeypatch):
+    monkeypatch.setattr(rotation, "rotation_matrix",
+                        lambda sw, d: rotation.sign_vector(sw, d)[:, None] * rotation.hadamard(d) / math.sqrt(d))
+    assert _caught(pins.check_rotation_first_column, pins.check_fast_transform_agrees)
+
+
+def test_mutant_sign_bits_msb_first(monkeypatch):
+    def msb_first(sw, d):
+        w = np.asarray(sw, dtype=np.uint32)
+        i = np.arange(d)
+        bit = (w[i // 32] >> (31 - i % 32).astype(np.uint32)) & np.uint32(1)
+        return np.where(bit == 1, -1.0, 1.0)
+
+    monkeypatch.setattr(rotation, "sign_vector", msb_first)
+    assert _caught(pins.check_sign_bits)
+
+
+def test_mutant_ties_go_down(monkeypatch):
+    orig = codec.encode
+
+    def ties_down(x, cb):
+        e = orig(x, cb)
+        y32 = (e.y * math.sqrt(cb.head_dim)).astype(np.float32).astype(np.float64)
+        e.codes = e.codes - np.isin(y32, cb.thresholds)
+        return e
+
+    monkeypatch.setattr(codec, "encode", ties_down)
+    assert _caught(pins.check_zero_vector)
+
+
+def test_mutant_big_endian_packing(monkeypatch):
+    def big_endian(codes, b):
+        c = np.asarray(codes, dtype=np.int64)
+        N, d = c.shape
+        bits = ((c[:, :, None] >> np.arange(b)[None, None, :]) & 1).astype(np.uint8).reshape(N, d * b)
+        return np.packbits(bits, axis=1, bitorder="big")
+
+    monkeypatch.setattr(codec, "pack_codes", big_endian)
+    assert _caught(pins.check_packing_by_hand)
+
+
+def test_mutant_wrong_qjl_constant(monkeypatch):
+    orig = codec.dequantize_rotated
+
+    def wrong_const(codes, norm16, cb, gamma16=None, qjl=None):
+        g = None if gamma16 is None else np.asarray(gamma16) * (2.0 / math.pi)  # sqrt(2/pi) instead of sqrt(pi/2)
+        return orig(codes, norm16, cb, g, qjl)
+
+    monkeypatch.setattr(codec, "dequantize_rotated", wrong_const)
+    assert _caught(pins.check_qjl_unbiased)
+
+
+def test_mutant_dequantize_ignores_norm(monkeypatch):
+    orig = codec.dequantize_rotated
+    monkeypatch.setattr(codec, "dequantize_rotated",
+                        lambda codes, norm16, cb, gamma16=None, qjl=None: orig(codes, np.ones_like(norm16), cb, gamma16, qjl))
+    assert _caught(pins.check_inner_product_bias)
+
+
+def test_mutant_gqa_head_mapping_modulo(monkeypatch):
+    orig = attention.decode_attention
+
+    def modulo_mapping(pool, L, cb_k, cb_v, q, page_table, seq_lens, scale, heads=None):
+        q = np.asarray(q, dtype=np.float64)
+        B, Hq, d = q.shape
+        Hkv = L["H"]
+        G = Hq // Hkv
+        sigma = np.array([(h % Hkv) * G + h // Hkv for h in range(Hq)])
+        q2 = np.empty_like(q)
+        q2[:, sigma] = q
+        return orig(pool, L, cb_k, cb_v, q2, page_table, seq_lens, scale)[:, sigma]
+
+    monkeypatch.setattr(attention, "decode_attention", modulo_mapping)
+    assert _caught(pins.check_attention_vs_torch_sdpa)
+
+
+def test_mutant_scale_dropped(monkeypatch):
+    orig = attention.decode_attention
+    monkeypatch.setattr(attention, "decode_attention",
+                        lambda pool, L, cb_k, cb_v, q, pt, sl, scale, heads=None: orig(pool, L, cb_k, cb_v, q, pt, sl, 1.0, heads))
+    assert _caught(pins.check_attention_vs_torch_sdpa)
+
+
+def test_mutant_v_layout_slot_major(monkeypatch):
+    orig = codec._code_byte_index
+
+    def slot_major(L, which, page, slot, head):
+        if which == "v":
+            L2 = dict(L)
+            L2["k_codes"], L2["k_b"] = L["v_codes"], L["v_b"]
+            return orig(L2, "k", page, slot, head)
+        return orig(L, which, page, slot, head)
+
+    monkeypatch.setattr(codec, "_code_byte_index", slot_major)
+    assert _caught(pins.check_layout_positions)
+
+
+@pytest.mark.parametrize("scale", [0.5, 2.0])
+def test_mutant_norm_scaled(monkeypatch, scale):
+    orig = codec.encode
+
+    def scaled(x, cb):
+        e = orig(x, cb)
+        e.norm16 = codec.fp16_round(e.norm16 * scale)
+        return e
+
+    monkeypatch.setattr(codec, "encode", scaled)
+    assert _caught(pins.check_vector_mse)
