@@ -1,0 +1,191 @@
+/*
+ * tq.h - C ABI of the TurboQuant KV-cache library for MI355X (gfx950).
+ *
+ * The library does three things, each named after the step of the method it runs:
+ *   tq_build_codebook   builds the per-layer, per-tensor codebook blob: Gaussian Lloyd-Max levels
+ *                       and thresholds, the rotation's random sign vector and (prod mode) the QJL
+ *                       projection ("Closing - The Three-Step Summary", Step 2 and "The One-Slide
+ *                       Version"; "Why the KV Cache Exists", "Prefix Caching": the rotation is
+ *                       fixed per model load).
+ *   tq_quantize_kv      quantize-on-write of K and V vectors into 16-token pages: norm, random
+ *                       signs, Walsh-Hadamard transform, Lloyd-Max index, bit packing, and for
+ *                       prod mode the 1-bit QJL sketch of the residual ("Closing - The Three-Step
+ *                       Summary", Steps 1-3; "Where This Fits in the Inference Stack", "Production
+ *                       Deployment: Tensor Parallelism": quantize on the owning GPU before the
+ *                       write to HBM).
+ *   tq_decode_attention GQA decode attention that reads the packed pages and dequantizes inside
+ *                       the kernel ("Where This Fits in the Inference Stack", "TensorRT-LLM: Why
+ *                       Integration Is a Kernel Problem"), with scores and value sums formed in the
+ *                       rotated domain and one inverse rotation per output ("Closing - The
+ *                       Three-Step Summary", Step 1: the rotation keeps inner products).
+ *
+ * Conventions for every call:
+ *   - Returns TQ_OK (0) or a negative TQ_E* status; never aborts, never allocates device memory.
+ *   - Argument checks happen on the host, synchronously, before anything is launched; a failed
+ *     check launches nothing and leaves every buffer untouched.
+ *   - "device" pointers are caller-owned GPU memory (for instance PyTorch tensors); "host"
+ *     pointers are caller-owned CPU memory. The library keeps no pointer after a call returns.
+ *   - Kernels run asynchronously on `stream` (a hipStream_t passed as void*; NULL = the null
+ *     stream). A launch error reported by the HIP runtime returns TQ_EHIP.
+ *   - The library holds no global state; calls on different streams may run concurrently as long
+ *     as they do not write the same bytes.
+ *   - NaN or infinite inputs give unspecified (but in-bounds) results.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------------------------- */
+#define TQ_OK 0
+#define TQ_EINVAL (-1)   /* null pointer, unsupported shape, bit width or mode, bad blob */
+#define TQ_ENOSPC (-2)   /* a caller buffer is smaller than required */
+#define TQ_ENOTSUP (-3)  /* a valid combination this build does not implement */
+#define TQ_EHIP (-4)     /* the HIP runtime reported an error */
+
+/* ---- modes and dtypes ------------------------------------------------------------------ */
+#define TQ_MSE 0   /* b-bit Lloyd-Max index ("b >= 3: rotate, quantize with b bits") */
+#define TQ_PROD 1  /* (b-1)-bit Lloyd-Max index + 1-bit QJL residual sketch ("b <= 2") */
+
+#define TQ_F32 0
+#define TQ_BF16 1
+#define TQ_F16 2
+
+#define TQ_PAGE_TOKENS 16
+#define TQ_CODEBOOK_MAGIC 0x42435154u /* "TQCB" little-endian */
+#define TQ_CODEBOOK_VERSION 1u
+
+/* One layer's cache layout. head_dim is 64 or 128; bits is 1, 2, 3, 4 or 8 in MSE mode and
+ * 2, 3 or 4 in prod mode; page_tokens must be 16. */
+typedef struct tq_layout {
+  int32_t head_dim;
+  int32_t num_kv_heads;
+  int32_t page_tokens;
+  int32_t k_bits;
+  int32_t k_mode;
+  int32_t v_bits;
+  int32_t v_mode;
+} tq_layout;
+
+/* Byte offsets of the sub-arrays inside one page, and the page size. A page holds 16 token slots
+ * of every KV head of one layer; every sub-array starts on a 16-byte boundary:
+ *   k_codes [head][slot][head_dim*bK/8]   natural little-endian bit stream, code i at bits b*i..
+ *   k_norms [head][slot] fp16             vector norm
+ *   k_qjl   [head][slot][head_dim/8]      sketch bit j = [(S r)_j >= 0]          (prod mode)
+ *   k_gamma [head][slot] fp16             residual norm                          (prod mode)
+ *   v_codes [head][head_dim/8][slot][bV]  the bit stream cut into pieces of bV bytes
+ *                                         (8 coordinates each), piece-major
+ *   v_norms, v_qjl, v_gamma               as for K (the V code pieces are the only difference)
+ * bK, bV are the Lloyd-Max index widths (bits, or bits-1 in prod mode). Offsets of absent
+ * sub-arrays are 0. Token t of sequence b is stored at global slot
+ * page_table[b][t/16]*16 + t%16, i.e. page slot/16, offset slot%16. */
+typedef struct tq_page_offsets {
+  uint64_t k_codes, k_norms, k_qjl, k_gamma;
+  uint64_t v_codes, v_norms, v_qjl, v_gamma;
+  uint64_t page_bytes;
+} tq_page_offsets;
+
+/* Codebook blob header (little-endian). The blob is `total_bytes` long and holds, at the given
+ * byte offsets from its start:
+ *   levels      n_levels fp16: the Lloyd-Max levels for N(0,1) with 2^mse_bits levels, rounded
+ *               to fp16, ascending (the 1/sqrt(head_dim) scale is applied in arithmetic)
+ *   thresholds  n_levels-1 fp32: exact midpoints of consecutive stored levels
+ *   signs       head_dim/32 uint32: bit i of word i/32 set = coordinate i negated before the
+ *               Walsh-Hadamard transform
+ *   proj        qjl_rows*head_dim fp32, row-major: the QJL projection S (prod mode only)
+ * The host builds it once per model load; the caller copies it to device memory and passes the
+ * device copy to tq_quantize_kv / tq_decode_attention. */
+typedef struct tq_codebook_header {
+  uint32_t magic;
+  uint32_t version;
+  int32_t head_dim;
+  int32_t bits;
+  int32_t mode;
+  int32_t mse_bits;
+  int32_t n_levels;
+  int32_t qjl_rows;
+  uint32_t levels_off;
+  uint32_t thresholds_off;
+  uint32_t signs_off;
+  uint32_t proj_off;
+  uint32_t total_bytes;
+  uint32_t reserved[3];
+} tq_codebook_header;
+
+/* Human-readable text of a status code (static storage). */
+const char *tq_strerror(int status);
+
+/* Size in bytes of the codebook blob for (head_dim, bits, mode). Host only.
+ * Errors: TQ_EINVAL for a null `out` or an unsupported combination. */
+int tq_codebook_bytes(int head_dim, int bits, int mode, size_t *out);
+
+/* Build a codebook blob in caller-owned host memory `blob` of `blob_bytes` bytes. Host only,
+ * synchronous, deterministic. The Lloyd-Max levels are solved in fp64 (Gaussian centroid and
+ * midpoint conditions, "Closing - The Three-Step Summary", Step 2).
+ *   sign_words  host, head_dim/32 uint32: the rotation's random signs (drawn by the caller once per
+ *               model load, "Why the KV Cache Exists", "Prefix Caching")
+ *   qjl_proj    host, head_dim*head_dim fp32 row-major iid N(0,1) projection S; required in prod
+ *               mode, ignored (may be NULL) in MSE mode ("Closing - The Three-Step Summary",
+ *               Step 3: the 1-bit QJL sketch)
+ * Errors: TQ_EINVAL (null pointers, unsupported combination), TQ_ENOSPC (blob too small). */
+int tq_build_codebook(int head_dim, int bits, int mode, const uint32_t *sign_words,
+                      const float *qjl_proj, void *blob, size_t blob_bytes);
+
+/* Page layout of one layer. Host only. Errors: TQ_EINVAL for an invalid layout or null pointer. */
+int tq_page_layout(const tq_layout *layout, tq_page_offsets *out);
+
+/* Quantize n_tok tokens of K and V into the page pool ("Closing - The Three-Step Summary",
+ * Steps 1-3; "Where This Fits in the Inference Stack", tensor-parallel section: per-vector
+ * state only, nothing crosses a vector boundary).
+ *   pages       device, num_pages * page_bytes bytes: the layer's page pool (written)
+ *   k, v        device, element (t, h, i) at [t*k_stride_tok + h*head_dim + i] of dtype `dtype`
+ *               (TQ_F32, TQ_BF16 or TQ_F16)
+ *   slots       device int64 [n_tok]: global slot of each token; a slot < 0 or >= num_pages*16 is
+ *               skipped. Two tokens of one call must not share a slot.
+ *   k_cb, v_cb  device copies of blobs built for (head_dim, k_bits, k_mode) and (head_dim, v_bits,
+ *               v_mode)
+ * Each vector's record (codes, norm, and in prod mode sketch and residual norm) is written in full;
+ * no other byte of the pool is touched. n_tok = 0 launches nothing.
+ * Errors: TQ_EINVAL (layout, dtype, strides, null pointers), TQ_ENOTSUP, TQ_EHIP. */
+int tq_quantize_kv(const tq_layout *layout, void *pages, int64_t num_pages, const void *k,
+                   const void *v, int dtype, int64_t n_tok, int64_t k_stride_tok,
+                   int64_t v_stride_tok, const int64_t *slots, const void *k_cb, const void *v_cb,
+                   void *stream);
+
+/* Workspace bytes needed by tq_decode_attention for these arguments (same `pages_per_split`
+ * rule; 0 = automatic choice for the current device). Host only. */
+int tq_decode_workspace_bytes(const tq_layout *layout, int batch, int num_q_heads,
+                              int max_pages_per_seq, int pages_per_split, size_t *out);
+
+/* Decode attention for one new query per sequence over the packed cache ("Why the KV Cache
+ * Exists", "The KV Cache Solution": each step reads every cached K/V of the sequence).
+ *   q           device [batch][num_q_heads][head_dim] of q_dtype
+ *   page_table  device int32 [batch][max_pages_per_seq]: physical page of each 16-token block
+ *   seq_lens    device int32 [batch]: cached tokens per sequence (clamped to
+ *               max_pages_per_seq*16); 0 gives a zero output row. Page-table entries < 0 or
+ *               >= num_pages inside a sequence are treated as empty pages.
+ *   pages_per_split  pages handled by one work-group before the split results are merged
+ *               (0 = automatic). The result does not depend on it beyond fp32 rounding.
+ *   workspace   device scratch of at least tq_decode_workspace_bytes(...) bytes
+ *   out         device fp32 [batch][num_q_heads][head_dim]
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads) (grouped-query attention, "Why the
+ * KV Cache Exists", "What's in the KV Cache"); out = sum_t softmax_t(softmax_scale * q.khat_t)
+ * vhat_t over the sequence's tokens, with khat, vhat the dequantized vectors.
+ * Errors: TQ_EINVAL, TQ_ENOSPC (workspace), TQ_ENOTSUP, TQ_EHIP. */
+int tq_decode_attention(const tq_layout *layout, const void *pages, int64_t num_pages,
+                        const void *q, int q_dtype, int batch, int num_q_heads,
+                        const int32_t *page_table, int max_pages_per_seq, const int32_t *seq_lens,
+                        float softmax_scale, int pages_per_split, const void *k_cb,
+                        const void *v_cb, void *workspace, size_t workspace_bytes, float *out,
+                        void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

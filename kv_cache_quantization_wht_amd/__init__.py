@@ -1,0 +1,208 @@
+"""Python binding of the TurboQuant KV-cache library (``libtq.so``, C ABI in ``include/tq.h``).
+
+Argument marshalling only: every step of the method runs in the library's HIP kernels (or, for
+``build_codebook``, in its host code). PyTorch supplies device memory and streams. Function names
+follow the C ABI without the ``tq_`` prefix. The library must have been built
+(``python -m kv_cache_quantization_wht_amd.build``); nothing here falls back to another
+implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+MSE = 0
+PROD = 1
+F32, BF16, F16 = 0, 1, 2
+PAGE_TOKENS = 16
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+_LIB = None
+
+C_SYMBOLS = (
+    "tq_strerror", "tq_codebook_bytes", "tq_build_codebook", "tq_page_layout", "tq_quantize_kv",
+    "tq_decode_workspace_bytes", "tq_decode_attention",
+)
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("head_dim", "num_kv_heads", "page_tokens", "k_bits", "k_mode", "v_bits", "v_mode")]
+
+
+class _Offsets(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in
+                ("k_codes", "k_norms", "k_qjl", "k_gamma", "v_codes", "v_norms", "v_qjl", "v_gamma", "page_bytes")]
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib().tq_strerror(status).decode()} ({status})")
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m kv_cache_quantization_wht_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        lib.tq_strerror.restype = ctypes.c_char_p
+        lib.tq_strerror.argtypes = [i32]
+        lib.tq_codebook_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+        lib.tq_build_codebook.argtypes = [i32, i32, i32, vp, vp, vp, sz]
+        lib.tq_page_layout.argtypes = [ctypes.POINTER(_Layout), ctypes.POINTER(_Offsets)]
+        lib.tq_quantize_kv.argtypes = [ctypes.POINTER(_Layout), vp, i64, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp]
+        lib.tq_decode_workspace_bytes.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32, i32, ctypes.POINTER(sz)]
+        lib.tq_decode_attention.argtypes = [ctypes.POINTER(_Layout), vp, i64, vp, i32, i32, i32, vp, i32, vp,
+                                            ctypes.c_float, i32, vp, vp, vp, sz, vp, vp]
+        for name in C_SYMBOLS:
+            getattr(lib, name).restype = ctypes.c_char_p if name == "tq_strerror" else ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise TQError(status, where)
+
+
+@dataclass(frozen=True)
+class Layout:
+    head_dim: int
+    num_kv_heads: int
+    k_bits: int
+    k_mode: int
+    v_bits: int
+    v_mode: int
+    page_tokens: int = PAGE_TOKENS
+
+    def c(self) -> _Layout:
+        return _Layout(self.head_dim, self.num_kv_heads, self.page_tokens, self.k_bits, self.k_mode,
+                       self.v_bits, self.v_mode)
+
+
+def strerror(status: int) -> str:
+    return _lib().tq_strerror(status).decode()
+
+
+def codebook_bytes(head_dim: int, bits: int, mode: int) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib().tq_codebook_bytes(head_dim, bits, mode, ctypes.byref(out)), "tq_codebook_bytes")
+    return out.value
+
+
+def build_codebook(head_dim: int, bits: int, mode: int, sign_words, qjl_proj=None) -> np.ndarray:
+    """Host codebook blob (uint8). ``sign_words``: head_dim/32 uint32; ``qjl_proj``: d x d fp32 (prod)."""
+    sw = np.ascontiguousarray(sign_words, dtype=np.uint32)
+    pj = None if qjl_proj is None else np.ascontiguousarray(qjl_proj, dtype=np.float32)
+    n = codebook_bytes(head_dim, bits, mode)
+    blob = np.zeros(n, dtype=np.uint8)
+    _check(_lib().tq_build_codebook(head_dim, bits, mode, sw.ctypes.data,
+                                    None if pj is None else pj.ctypes.data, blob.ctypes.data, n),
+           "tq_build_codebook")
+    return blob
+
+
+def page_layout(layout: Layout) -> dict:
+    o = _Offsets()
+    _check(_lib().tq_page_layout(ctypes.byref(layout.c()), ctypes.byref(o)), "tq_page_layout")
+    return {n: int(getattr(o, n)) for n, _ in _Offsets._fields_}
+
+
+def _stream(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+_DT = {}
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if not _DT:
+        _DT.update({torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16})
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _need(t, what, dtype=None, cuda=True):
+    if cuda and not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+
+
+def quantize_kv(layout: Layout, pages, k, v, slots, k_cb, v_cb, stream=None) -> None:
+    """Quantize K, V [n_tok, num_kv_heads, head_dim] into ``pages`` at global ``slots`` (int64)."""
+    import torch
+
+    _need(pages, "pages", torch.uint8)
+    _need(slots, "slots", torch.int64)
+    _need(k, "k")
+    _need(v, "v")
+    if k.dtype != v.dtype:
+        raise TypeError("k and v must share a dtype")
+    if k.dim() != 3 or v.dim() != 3 or k.shape[1:] != (layout.num_kv_heads, layout.head_dim) or v.shape != k.shape:
+        raise ValueError("k, v must be [n_tok, num_kv_heads, head_dim]")
+    if k.stride(2) != 1 or k.stride(1) != layout.head_dim or v.stride(2) != 1 or v.stride(1) != layout.head_dim:
+        raise ValueError("k, v rows must be contiguous per token")
+    if not slots.is_contiguous() or slots.numel() != k.shape[0]:
+        raise ValueError("slots must be a contiguous int64 vector with one entry per token")
+    page_bytes = page_layout(layout)["page_bytes"]
+    num_pages = pages.numel() // page_bytes
+    _check(_lib().tq_quantize_kv(ctypes.byref(layout.c()), pages.data_ptr(), num_pages, k.data_ptr(), v.data_ptr(),
+                                 _dtype_code(k), k.shape[0], k.stride(0), v.stride(0), slots.data_ptr(),
+                                 k_cb.data_ptr(), v_cb.data_ptr(), _stream(stream)), "tq_quantize_kv")
+
+
+def decode_workspace_bytes(layout: Layout, batch: int, num_q_heads: int, max_pages_per_seq: int,
+                           pages_per_split: int = 0) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib().tq_decode_workspace_bytes(ctypes.byref(layout.c()), batch, num_q_heads, max_pages_per_seq,
+                                            pages_per_split, ctypes.byref(out)), "tq_decode_workspace_bytes")
+    return out.value
+
+
+def decode_attention(layout: Layout, pages, q, page_table, seq_lens, softmax_scale, k_cb, v_cb,
+                     workspace=None, out=None, pages_per_split: int = 0, stream=None):
+    """Decode attention for q [batch, num_q_heads, head_dim]; returns fp32 out of the same shape."""
+    import torch
+
+    _need(pages, "pages", torch.uint8)
+    _need(q, "q")
+    _need(page_table, "page_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    if q.dim() != 3 or q.shape[2] != layout.head_dim or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [batch, num_q_heads, head_dim] tensor")
+    B, Hq, _ = q.shape
+    if page_table.dim() != 2 or page_table.shape[0] != B or not page_table.is_contiguous():
+        raise ValueError("page_table must be a contiguous [batch, max_pages_per_seq] int32 tensor")
+    if seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must hold one int32 per sequence")
+    maxp = page_table.shape[1]
+    need = decode_workspace_bytes(layout, B, Hq, maxp, pages_per_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(B, Hq, layout.head_dim, dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32)
+    if out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor shaped like q")
+    page_bytes = page_layout(layout)["page_bytes"]
+    num_pages = pages.numel() // page_bytes
+    _check(_lib().tq_decode_attention(ctypes.byref(layout.c()), pages.data_ptr(), num_pages, q.data_ptr(),
+                                      _dtype_code(q), B, Hq, page_table.data_ptr(), maxp, seq_lens.data_ptr(),
+                                      float(softmax_scale), pages_per_split, k_cb.data_ptr(), v_cb.data_ptr(),
+                                      workspace.data_ptr(), workspace.numel(), out.data_ptr(), _stream(stream)),
+           "tq_decode_attention")
+    return out

@@ -1,0 +1,388 @@
+// Host side of the C ABI: argument checks, the Gaussian Lloyd-Max solver that builds codebook blobs,
+// the page layout, the decode workspace plan, and dispatch to the HIP launchers.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "tq_internal.h"
+
+namespace {
+
+constexpr int kPageTokens = TQ_PAGE_TOKENS;
+
+bool valid_head_dim(int d) { return d == 64 || d == 128; }
+
+// Bits accepted per mode: MSE 1,2,3,4,8; prod 2,3,4 (a 1..3-bit Lloyd-Max index plus one sketch bit).
+bool valid_bits(int bits, int mode) {
+  if (mode == TQ_MSE) return bits == 1 || bits == 2 || bits == 3 || bits == 4 || bits == 8;
+  if (mode == TQ_PROD) return bits == 2 || bits == 3 || bits == 4;
+  return false;
+}
+
+int index_bits(int bits, int mode) { return mode == TQ_PROD ? bits - 1 : bits; }
+
+size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
+
+// ------------------------------------------------------------------------------------------
+// Gaussian Lloyd-Max levels (fp64). The positive half p_0 < ... < p_{K-1} of a symmetric
+// 2K-level quantizer satisfies, with cell edges e_0 = 0, e_k = (p_{k-1} + p_k)/2, e_K = inf:
+//     p_k * (Q(e_k) - Q(e_{k+1})) = phi(e_k) - phi(e_{k+1})          (conditional mean)
+// where Q is the Gaussian upper tail. Lloyd sweeps from equiprobable cells get close; damped
+// Newton with a tridiagonal Jacobian finishes the solve.
+// ------------------------------------------------------------------------------------------
+const double kInvSqrt2Pi = 0.39894228040143267794;
+
+double gauss_pdf(double x) { return std::isinf(x) ? 0.0 : kInvSqrt2Pi * std::exp(-0.5 * x * x); }
+double gauss_upper(double x) { return 0.5 * std::erfc(x / std::sqrt(2.0)); }
+
+// x >= 0 with Q(x) = target (target in (0, 0.5]) by bisection.
+double gauss_upper_inverse(double target) {
+  double lo = 0.0, hi = 40.0;
+  for (int it = 0; it < 200; ++it) {
+    double mid = 0.5 * (lo + hi);
+    if (gauss_upper(mid) > target) lo = mid; else hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+void cell_edges(const std::vector<double> &p, std::vector<double> &e) {
+  size_t K = p.size();
+  e.assign(K + 1, 0.0);
+  for (size_t k = 1; k < K; ++k) e[k] = 0.5 * (p[k - 1] + p[k]);
+  e[K] = INFINITY;
+}
+
+void lloyd_sweep(std::vector<double> &p) {
+  std::vector<double> e;
+  cell_edges(p, e);
+  for (size_t k = 0; k < p.size(); ++k)
+    p[k] = (gauss_pdf(e[k]) - gauss_pdf(e[k + 1])) / (gauss_upper(e[k]) - gauss_upper(e[k + 1]));
+}
+
+std::vector<double> positive_levels(int index_bits_) {
+  const int L = 1 << index_bits_;
+  const int K = L / 2;
+  std::vector<double> p(K);
+  for (int k = 0; k < K; ++k) p[k] = gauss_upper_inverse(0.5 - (k + 0.5) / L);
+  for (int it = 0; it < 100; ++it) lloyd_sweep(p);
+  std::vector<double> e, F(K), lo(K), di(K), up(K), step(K), cp(K), dp(K);
+  for (int it = 0; it < 200; ++it) {
+    cell_edges(p, e);
+    for (int k = 0; k < K; ++k) {
+      double mass = gauss_upper(e[k]) - gauss_upper(e[k + 1]);
+      F[k] = p[k] * mass - (gauss_pdf(e[k]) - gauss_pdf(e[k + 1]));
+      di[k] = mass;
+      lo[k] = up[k] = 0.0;
+      if (k >= 1) {
+        double g = (e[k] - p[k]) * gauss_pdf(e[k]);
+        di[k] += 0.5 * g;
+        lo[k] = 0.5 * g;
+      }
+      if (k <= K - 2) {
+        double g = (p[k] - e[k + 1]) * gauss_pdf(e[k + 1]);
+        di[k] += 0.5 * g;
+        up[k] = 0.5 * g;
+      }
+    }
+    // Thomas algorithm for J * step = -F
+    cp[0] = up[0] / di[0];
+    dp[0] = -F[0] / di[0];
+    for (int k = 1; k < K; ++k) {
+      double den = di[k] - lo[k] * cp[k - 1];
+      cp[k] = up[k] / den;
+      dp[k] = (-F[k] - lo[k] * dp[k - 1]) / den;
+    }
+    step[K - 1] = dp[K - 1];
+    for (int k = K - 2; k >= 0; --k) step[k] = dp[k] - cp[k] * step[k + 1];
+    double lam = 1.0;
+    std::vector<double> cand(K);
+    for (int tries = 0; tries < 60; ++tries) {
+      bool ok = true;
+      for (int k = 0; k < K; ++k) cand[k] = p[k] + lam * step[k];
+      if (cand[0] <= 0) ok = false;
+      for (int k = 1; k < K && ok; ++k) ok = cand[k] > cand[k - 1];
+      if (ok) break;
+      lam *= 0.5;
+    }
+    double rel = 0.0;
+    for (int k = 0; k < K; ++k) rel = std::max(rel, std::fabs(lam * step[k]) / std::max(1.0, std::fabs(cand[k])));
+    p = cand;
+    if (rel < 1e-15) break;
+  }
+  lloyd_sweep(p);
+  return p;
+}
+
+// Round to IEEE binary16, ties to even (current rounding mode is assumed round-to-nearest).
+uint16_t to_half_bits(double x) {
+  uint16_t sign = std::signbit(x) ? 0x8000 : 0;
+  double a = std::fabs(x);
+  if (std::isnan(x)) return 0x7E00;
+  if (a >= 65520.0) return sign | 0x7C00;
+  int e;
+  std::frexp(a, &e);  // a = m * 2^e, m in [0.5, 1)
+  int E = e - 1;      // a in [2^E, 2^(E+1))
+  if (a == 0.0) return sign;
+  if (E >= -14) {
+    double r = std::nearbyint(std::ldexp(a, 10 - E));  // [1024, 2048]
+    if (r >= 2048.0) { r = 1024.0; E += 1; }
+    if (E > 15) return sign | 0x7C00;
+    return sign | (uint16_t)(((E + 15) << 10) | ((int)r - 1024));
+  }
+  double r = std::nearbyint(std::ldexp(a, 24));  // subnormal count of 2^-24
+  return sign | (uint16_t)r;
+}
+
+double half_bits_to_double(uint16_t h) {
+  int s = h >> 15, E = (h >> 10) & 31, M = h & 1023;
+  double v;
+  if (E == 0) v = std::ldexp((double)M, -24);
+  else if (E == 31) v = M ? NAN : INFINITY;
+  else v = std::ldexp(1024.0 + M, E - 25);
+  return s ? -v : v;
+}
+
+struct BlobPlan {
+  int n_levels, rows;
+  uint32_t levels_off, thresholds_off, signs_off, proj_off, total;
+};
+
+BlobPlan plan_blob(int head_dim, int bits, int mode) {
+  BlobPlan b{};
+  b.n_levels = 1 << index_bits(bits, mode);
+  b.rows = mode == TQ_PROD ? head_dim : 0;
+  size_t off = sizeof(tq_codebook_header);
+  b.levels_off = (uint32_t)off;
+  off = align16(off + 2 * (size_t)b.n_levels);
+  b.thresholds_off = (uint32_t)off;
+  off = align16(off + 4 * (size_t)(b.n_levels - 1));
+  b.signs_off = (uint32_t)off;
+  off = align16(off + 4 * (size_t)(head_dim / 32));
+  b.proj_off = 0;
+  if (b.rows) {
+    b.proj_off = (uint32_t)off;
+    off = align16(off + 4 * (size_t)b.rows * head_dim);
+  }
+  b.total = (uint32_t)off;
+  return b;
+}
+
+bool valid_layout(const tq_layout *L) {
+  return L && valid_head_dim(L->head_dim) && L->num_kv_heads >= 1 && L->num_kv_heads <= 4096 &&
+         L->page_tokens == kPageTokens && valid_bits(L->k_bits, L->k_mode) &&
+         valid_bits(L->v_bits, L->v_mode);
+}
+
+}  // namespace
+
+namespace tq {
+
+int make_geom(const tq_layout *L, PageGeom *g) {
+  if (!valid_layout(L) || !g) return TQ_EINVAL;
+  const int64_t H = L->num_kv_heads, d = L->head_dim, T = kPageTokens;
+  int64_t off = 0;
+  auto section = [&](int bits, int mode, int64_t *codes, int64_t *norms, int64_t *qjl, int64_t *gamma,
+                     int *b_out) {
+    int b = index_bits(bits, mode);
+    *b_out = b;
+    *codes = off;
+    off = (int64_t)align16(off + H * T * d * b / 8);
+    *norms = off;
+    off = (int64_t)align16(off + H * T * 2);
+    *qjl = *gamma = 0;
+    if (mode == TQ_PROD) {
+      *qjl = off;
+      off = (int64_t)align16(off + H * T * d / 8);
+      *gamma = off;
+      off = (int64_t)align16(off + H * T * 2);
+    }
+  };
+  section(L->k_bits, L->k_mode, &g->k_codes, &g->k_norms, &g->k_qjl, &g->k_gamma, &g->k_mse_bits);
+  section(L->v_bits, L->v_mode, &g->v_codes, &g->v_norms, &g->v_qjl, &g->v_gamma, &g->v_mse_bits);
+  g->page_bytes = off;
+  g->head_dim = (int)d;
+  g->num_kv_heads = (int)H;
+  g->k_mode = L->k_mode;
+  g->v_mode = L->v_mode;
+  return TQ_OK;
+}
+
+int plan_decode(const PageGeom &g, int batch, int num_q_heads, int max_pages_per_seq,
+                int pages_per_split, DecodeWs *ws) {
+  if (batch < 0 || num_q_heads < 1 || max_pages_per_seq < 1 || pages_per_split < 0) return TQ_EINVAL;
+  if (num_q_heads % g.num_kv_heads) return TQ_EINVAL;
+  int pps = pages_per_split;
+  if (pps == 0) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+      int v = 0;
+      if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    // aim for about 8 one-wave work-groups per compute unit
+    int64_t units = (int64_t)std::max(batch, 1) * g.num_kv_heads;
+    int64_t want_splits = std::max<int64_t>(1, (8LL * cus + units - 1) / units);
+    pps = (int)std::max<int64_t>(2, (max_pages_per_seq + want_splits - 1) / want_splits);
+    pps = std::max(2, std::min(pps, 64));
+  }
+  pps = (pps + 1) & ~1;  // whole page pairs
+  ws->pages_per_split = pps;
+  ws->n_splits = (max_pages_per_seq + pps - 1) / pps;
+  const size_t B = (size_t)std::max(batch, 0), Hq = (size_t)num_q_heads, d = (size_t)g.head_dim;
+  const size_t S = (size_t)ws->n_splits;
+  size_t off = 0;
+  ws->qrot_off = off;
+  off = align16(off + 4 * B * Hq * d);
+  ws->qsk_off = off;
+  if (g.k_mode == TQ_PROD) off = align16(off + 4 * B * Hq * d);
+  ws->qscale_off = off;
+  off = align16(off + 4 * B * Hq * 2);
+  ws->part_o_off = off;
+  off = align16(off + 4 * B * Hq * S * d);
+  ws->part_ml_off = off;
+  off = align16(off + 4 * B * Hq * S * 2);
+  ws->total = off;
+  return TQ_OK;
+}
+
+}  // namespace tq
+
+extern "C" {
+
+const char *tq_strerror(int status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_EINVAL: return "invalid argument";
+    case TQ_ENOSPC: return "buffer too small";
+    case TQ_ENOTSUP: return "combination not supported";
+    case TQ_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int tq_codebook_bytes(int head_dim, int bits, int mode, size_t *out) {
+  if (!out || !valid_head_dim(head_dim) || !valid_bits(bits, mode)) return TQ_EINVAL;
+  *out = plan_blob(head_dim, bits, mode).total;
+  return TQ_OK;
+}
+
+int tq_build_codebook(int head_dim, int bits, int mode, const uint32_t *sign_words,
+                      const float *qjl_proj, void *blob, size_t blob_bytes) {
+  if (!valid_head_dim(head_dim) || !valid_bits(bits, mode) || !sign_words || !blob) return TQ_EINVAL;
+  if (mode == TQ_PROD && !qjl_proj) return TQ_EINVAL;
+  BlobPlan P = plan_blob(head_dim, bits, mode);
+  if (blob_bytes < P.total) return TQ_ENOSPC;
+  unsigned char *base = (unsigned char *)blob;
+  std::memset(base, 0, P.total);
+  tq_codebook_header h{};
+  h.magic = TQ_CODEBOOK_MAGIC;
+  h.version = TQ_CODEBOOK_VERSION;
+  h.head_dim = head_dim;
+  h.bits = bits;
+  h.mode = mode;
+  h.mse_bits = index_bits(bits, mode);
+  h.n_levels = P.n_levels;
+  h.qjl_rows = P.rows;
+  h.levels_off = P.levels_off;
+  h.thresholds_off = P.thresholds_off;
+  h.signs_off = P.signs_off;
+  h.proj_off = P.proj_off;
+  h.total_bytes = P.total;
+  std::memcpy(base, &h, sizeof(h));
+
+  std::vector<double> pos = positive_levels(h.mse_bits);
+  const int K = P.n_levels / 2;
+  std::vector<uint16_t> lv(P.n_levels);
+  for (int k = 0; k < K; ++k) {
+    uint16_t hb = to_half_bits(pos[k]);
+    lv[K + k] = hb;
+    lv[K - 1 - k] = (uint16_t)(hb | 0x8000);
+  }
+  std::memcpy(base + P.levels_off, lv.data(), 2 * lv.size());
+  std::vector<float> th(P.n_levels - 1);
+  for (int j = 0; j + 1 < P.n_levels; ++j)
+    th[j] = (float)(0.5 * (half_bits_to_double(lv[j]) + half_bits_to_double(lv[j + 1])));
+  std::memcpy(base + P.thresholds_off, th.data(), 4 * th.size());
+  std::memcpy(base + P.signs_off, sign_words, 4 * (size_t)(head_dim / 32));
+  if (P.rows) std::memcpy(base + P.proj_off, qjl_proj, 4 * (size_t)P.rows * head_dim);
+  return TQ_OK;
+}
+
+int tq_page_layout(const tq_layout *layout, tq_page_offsets *out) {
+  if (!out) return TQ_EINVAL;
+  tq::PageGeom g;
+  int st = tq::make_geom(layout, &g);
+  if (st) return st;
+  out->k_codes = g.k_codes;
+  out->k_norms = g.k_norms;
+  out->k_qjl = g.k_qjl;
+  out->k_gamma = g.k_gamma;
+  out->v_codes = g.v_codes;
+  out->v_norms = g.v_norms;
+  out->v_qjl = g.v_qjl;
+  out->v_gamma = g.v_gamma;
+  out->page_bytes = g.page_bytes;
+  return TQ_OK;
+}
+
+int tq_quantize_kv(const tq_layout *layout, void *pages, int64_t num_pages, const void *k,
+                   const void *v, int dtype, int64_t n_tok, int64_t k_stride_tok,
+                   int64_t v_stride_tok, const int64_t *slots, const void *k_cb, const void *v_cb,
+                   void *stream) {
+  tq::PageGeom g;
+  int st = tq::make_geom(layout, &g);
+  if (st) return st;
+  if (dtype != TQ_F32 && dtype != TQ_BF16 && dtype != TQ_F16) return TQ_EINVAL;
+  if (n_tok < 0 || num_pages < 0) return TQ_EINVAL;
+  if (n_tok == 0) return TQ_OK;
+  if (!pages || !k || !v || !slots || !k_cb || !v_cb) return TQ_EINVAL;
+  if (((uintptr_t)pages | (uintptr_t)k_cb | (uintptr_t)v_cb) & 15) return TQ_EINVAL;
+  const int64_t row = (int64_t)g.num_kv_heads * g.head_dim;
+  if (k_stride_tok < row || v_stride_tok < row) return TQ_EINVAL;
+  if (n_tok > ((int64_t)1 << 40)) return TQ_EINVAL;
+  return tq::launch_quantize(g, pages, num_pages, k, v, dtype, n_tok, k_stride_tok, v_stride_tok,
+                             slots, k_cb, v_cb, (hipStream_t)stream);
+}
+
+int tq_decode_workspace_bytes(const tq_layout *layout, int batch, int num_q_heads,
+                              int max_pages_per_seq, int pages_per_split, size_t *out) {
+  if (!out) return TQ_EINVAL;
+  tq::PageGeom g;
+  int st = tq::make_geom(layout, &g);
+  if (st) return st;
+  tq::DecodeWs ws;
+  st = tq::plan_decode(g, batch, num_q_heads, max_pages_per_seq, pages_per_split, &ws);
+  if (st) return st;
+  *out = ws.total;
+  return TQ_OK;
+}
+
+int tq_decode_attention(const tq_layout *layout, const void *pages, int64_t num_pages,
+                        const void *q, int q_dtype, int batch, int num_q_heads,
+                        const int32_t *page_table, int max_pages_per_seq, const int32_t *seq_lens,
+                        float softmax_scale, int pages_per_split, const void *k_cb,
+                        const void *v_cb, void *workspace, size_t workspace_bytes, float *out,
+                        void *stream) {
+  tq::PageGeom g;
+  int st = tq::make_geom(layout, &g);
+  if (st) return st;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return TQ_EINVAL;
+  if (batch < 0 || num_q_heads < 1 || num_q_heads % g.num_kv_heads) return TQ_EINVAL;
+  if (num_q_heads / g.num_kv_heads > 16) return TQ_ENOTSUP;  // one MFMA column block of query heads
+  if (g.v_mode == TQ_PROD) return TQ_ENOTSUP;
+  if (max_pages_per_seq < 1 || num_pages < 1 || !std::isfinite(softmax_scale)) return TQ_EINVAL;
+  if (batch == 0) return TQ_OK;
+  if (!pages || !q || !page_table || !seq_lens || !k_cb || !v_cb || !workspace || !out) return TQ_EINVAL;
+  if (((uintptr_t)pages | (uintptr_t)k_cb | (uintptr_t)v_cb | (uintptr_t)workspace) & 15) return TQ_EINVAL;
+  tq::DecodeWs ws;
+  st = tq::plan_decode(g, batch, num_q_heads, max_pages_per_seq, pages_per_split, &ws);
+  if (st) return st;
+  if (workspace_bytes < ws.total) return TQ_ENOSPC;
+  return tq::launch_decode(g, ws, pages, num_pages, q, q_dtype, batch, num_q_heads, page_table,
+                           max_pages_per_seq, seq_lens, softmax_scale, k_cb, v_cb, workspace, out,
+                           (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+"""Helpers for GPU-vs-oracle parity tests: drive the library on the GPU, read its packed pool back to the
+host, and compare with the CPU oracle under the stated tolerance rules.
+
+Tolerances
+  codes   bit-exact, except where the oracle's rotated value y = R u lies within 1e-6 (N(0,1/d) units)
+          of a decision threshold t_j / sqrt(d); such flips must be one level apart and are counted.
+  sketch  bit-exact, except |(S r)_j| <= 1e-6; every sketch bit of a vector with an allowed code flip is
+          excluded (its residual differs) and counted separately.
+  norms   fp16 bit-exact, except within d * 2^-24 relative of an fp16 rounding midpoint (the fp32
+          sum-of-squares error bound), where one ulp is allowed and counted; gamma likewise, excluding
+          vectors with a code flip.
+  attention  max over (b, h) of ||o_gpu - o_ref||_inf / ||o_ref||_inf <= 2e-3 with o_ref from the
+          oracle run on the GPU's own packed pool.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import kvsynth
+from oracle import attention, codec
+
+CODE_BAND = 1e-6
+SKETCH_BAND = 1e-6
+ATTN_TOL = 2e-3
+
+
+def fp16_midpoint_rel_distance(x):
+    """Relative distance of each fp64 value to the nearest fp16 rounding midpoint."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    h = x.astype(np.float16)
+    up = np.nextafter(h, np.float16(np.inf)).astype(np.float64)
+    dn = np.nextafter(h, np.float16(0)).astype(np.float64)
+    hf = h.astype(np.float64)
+    d = np.minimum(np.abs(x - 0.5 * (hf + up)), np.abs(x - 0.5 * (hf + dn)))
+    return np.where(x > 0, d / np.where(x > 0, x, 1.0), np.inf)
+
+
+def ulp_diff16(a, b):
+    ia = np.asarray(a, dtype=np.float64).astype(np.float16).view(np.int16).astype(np.int64)
+    ib = np.asarray(b, dtype=np.float64).astype(np.float16).view(np.int16).astype(np.int64)
+    return np.abs(ia - ib)
+
+
+class Report(dict):
+    def __repr__(self):
+        return " ".join(f"{k}={v}" for k, v in self.items())
+
+
+def compare_records(got: dict, enc: codec.Encoded, cb: codec.Codebook, rep: Report, tag: str):
+    """Compare records read back from the GPU pool with the oracle's encoding; fills counters in rep."""
+    d = cb.head_dim
+    mism = got["codes"] != enc.codes
+    dist = codec.code_boundary_distance(enc, cb)
+    bad = mism & ~((dist <= CODE_BAND) & (np.abs(got["codes"] - enc.codes) == 1))
+    assert not bad.any(), f"{tag}: {int(bad.sum())} code mismatches outside the 1e-6 band; first at {np.argwhere(bad)[:5]}"
+    rep[tag + "_codes"] = int(enc.codes.size)
+    rep[tag + "_code_flips"] = int(mism.sum())
+    flipped = mism.any(axis=1)
+
+    band = d * 2.0 ** -24
+    nd = ulp_diff16(got["norm16"], enc.norm16)
+    near = fp16_midpoint_rel_distance(enc.norm) <= band
+    badn = (nd > 1) | ((nd == 1) & ~near)
+    assert not badn.any(), f"{tag}: norm mismatch at {np.argwhere(badn)[:5].ravel()}"
+    rep[tag + "_norm_ulp"] = int((nd == 1).sum())
+
+    if cb.mode == codec.PROD:
+        z_m = got["qjl"] != enc.qjl
+        allowed = (np.abs(enc.Sr) <= SKETCH_BAND) | flipped[:, None]
+        badz = z_m & ~allowed
+        assert not badz.any(), f"{tag}: sketch mismatches outside the band: {int(badz.sum())}"
+        rep[tag + "_sketch_bits"] = int(enc.qjl.size)
+        rep[tag + "_sketch_flips_near0"] = int((z_m & ~flipped[:, None]).sum())
+        rep[tag + "_sketch_excluded_vectors"] = int(flipped.sum())
+        gd = ulp_diff16(got["gamma16"], enc.gamma16)
+        gnear = fp16_midpoint_rel_distance(enc.gamma) <= band
+        badg = ((gd > 1) | ((gd == 1) & ~gnear)) & ~flipped
+        assert not badg.any(), f"{tag}: gamma mismatch at {np.argwhere(badg)[:5].ravel()}"
+        rep[tag + "_gamma_ulp"] = int(((gd == 1) & ~flipped).sum())
+
+
+def device_codebook(head_dim, bits, mode, seed, device="cuda"):
+    """Library codebook blob (host numpy) and its device copy, plus the oracle codebook."""
+    import torch
+    import kv_cache_quantization_wht_amd as tq
+
+    sw = kvsynth.rotation_signs(seed, head_dim)
+    S = kvsynth.qjl_projection(seed, head_dim) if mode == codec.PROD else None
+    blob = tq.build_codebook(head_dim, bits, mode, sw, S)
+    return torch.from_numpy(blob).to(device), codec.make_codebook(head_dim, bits, mode, sw, S)
+
+
+def attention_error(out_gpu, out_ref):
+    return attention.relative_error(np.asarray(out_gpu, dtype=np.float64), out_ref)
+
+
+def seeded_kv(n_tok, H, d, seed, recipe="lognormal", dtype="bf16"):
+    """K/V test tensors: log-normal channel scales, a few zero and huge vectors."""
+    import torch
+
+    g = torch.Generator().manual_seed(seed)
+    k = torch.randn(n_tok, H, d, generator=g) * torch.exp(torch.randn(H, d, generator=g))
+    v = torch.randn(n_tok, H, d, generator=g)
+    if recipe == "lognormal":
+        if n_tok > 5:
+            k[3] = 0.0
+            v[4] = 0.0
+            k[5] *= 300.0
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    return k.to(dt), v.to(dt)
+
+
+def make_layout(H, d, kb, km, vb, vm):
+    import kv_cache_quantization_wht_amd as tq
+
+    return tq.Layout(d, H, kb, km, vb, vm), codec.page_layout(H, d, kb, km, vb, vm)
+
+
+def encode_all(x, cb):
+    """Oracle encoding of every (token, head) vector of x [n_tok, H, d]."""
+    xs = np.asarray(x, dtype=np.float64)
+    n_tok, H, d = xs.shape
+    return [codec.encode(xs[:, h], cb) for h in range(H)]
+
+
+def gpu_quantize_into_pool(layout, Lo, pool_bytes, k, v, slots, kcb_dev, vcb_dev, fill=0xA5):
+    import torch
+    import kv_cache_quantization_wht_amd as tq
+
+    pages = torch.full((pool_bytes,), fill, dtype=torch.uint8, device="cuda")
+    tq.quantize_kv(layout, pages, k.cuda(), v.cuda(), torch.as_tensor(slots, dtype=torch.int64).cuda(), kcb_dev, vcb_dev)
+    torch.cuda.synchronize()
+    return pages
+
+
+def written_mask(Lo, num_pages, slots, H):
+    """Boolean mask of every pool byte that a record of a valid slot owns."""
+    pb = Lo["page_bytes"]
+    mask = np.zeros(num_pages * pb, dtype=bool)
+    slots = np.asarray(slots)
+    slots = slots[(slots >= 0) & (slots < num_pages * 16)]
+    page, off = slots // 16, slots % 16
+    for h in range(H):
+        for which in ("k", "v"):
+            hh = np.full(slots.shape, h)
+            mask[codec._code_byte_index(Lo, which, page, off, hh).ravel()] = True
+            mask[codec._scalar_index(Lo, which + "_norms", page, off, hh, 2).ravel()] = True
+            if Lo[which + "_mode"] == codec.PROD:
+                mask[codec._scalar_index(Lo, which + "_qjl", page, off, hh, Lo["d"] // 8).ravel()] = True
+                mask[codec._scalar_index(Lo, which + "_gamma", page, off, hh, 2).ravel()] = True
+    return mask
