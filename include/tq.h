@@ -144,7 +144,7 @@ int tq_page_layout(const tq_layout *layout, tq_page_offsets *out);
  * state only, nothing crosses a vector boundary).
  *   pages       device, num_pages * page_bytes bytes: the layer's page pool (written)
  *   k, v        device, element (t, h, i) at [t*k_stride_tok + h*head_dim + i] of dtype `dtype`
- *               (TQ_F32, TQ_BF16 or TQ_F16)
+ *               (TQ_F32, TQ_BF16 or TQ_F16); 16-byte aligned, token strides a multiple of 8
  *   slots       device int64 [n_tok]: global slot of each token; a slot < 0 or >= num_pages*16 is
  *               skipped. Two tokens of one call must not share a slot.
  *   k_cb, v_cb  device copies of blobs built for (head_dim, k_bits, k_mode) and (head_dim, v_bits,
@@ -169,9 +169,11 @@ int tq_decode_workspace_bytes(const tq_layout *layout, int batch, int num_q_head
  *   seq_lens    device int32 [batch]: cached tokens per sequence (clamped to
  *               max_pages_per_seq*16); 0 gives a zero output row. Page-table entries < 0 or
  *               >= num_pages inside a sequence are treated as empty pages.
+ *   softmax_scale    >= 0 (usually 1/sqrt(head_dim))
  *   pages_per_split  pages handled by one work-group before the split results are merged
  *               (0 = automatic). The result does not depend on it beyond fp32 rounding.
- *   workspace   device scratch of at least tq_decode_workspace_bytes(...) bytes
+ *   workspace   device scratch of at least tq_decode_workspace_bytes(...) bytes (no initial
+ *               contents needed). Calls that share a workspace must not overlap in time.
  *   out         device fp32 [batch][num_q_heads][head_dim]
  * Query head h reads KV head h / (num_q_heads / num_kv_heads) (grouped-query attention, "Why the
  * KV Cache Exists", "What's in the KV Cache"); out = sum_t softmax_t(softmax_scale * q.khat_t)

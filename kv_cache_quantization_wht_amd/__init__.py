@@ -192,7 +192,7 @@ def decode_attention(layout: Layout, pages, q, page_table, seq_lens, softmax_sca
     maxp = page_table.shape[1]
     need = decode_workspace_bytes(layout, B, Hq, maxp, pages_per_split)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty(B, Hq, layout.head_dim, dtype=torch.float32, device=q.device)
     _need(out, "out", torch.float32)

@@ -180,6 +180,11 @@ bool valid_layout(const tq_layout *L) {
 
 namespace tq {
 
+BlobOffsets blob_offsets(int head_dim, int bits, int mode) {
+  BlobPlan P = plan_blob(head_dim, bits, mode);
+  return BlobOffsets{P.levels_off, P.thresholds_off, P.signs_off, P.proj_off, P.rows};
+}
+
 int make_geom(const tq_layout *L, PageGeom *g) {
   if (!valid_layout(L) || !g) return TQ_EINVAL;
   const int64_t H = L->num_kv_heads, d = L->head_dim, T = kPageTokens;
@@ -207,6 +212,8 @@ int make_geom(const tq_layout *L, PageGeom *g) {
   g->num_kv_heads = (int)H;
   g->k_mode = L->k_mode;
   g->v_mode = L->v_mode;
+  g->kcb = blob_offsets(L->head_dim, L->k_bits, L->k_mode);
+  g->vcb = blob_offsets(L->head_dim, L->v_bits, L->v_mode);
   return TQ_OK;
 }
 
@@ -221,24 +228,23 @@ int plan_decode(const PageGeom &g, int batch, int num_q_heads, int max_pages_per
       int v = 0;
       if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     }
-    // aim for about 8 one-wave work-groups per compute unit
+    // about one 8-wave work-group per compute unit over all (sequence, KV head) pairs
     int64_t units = (int64_t)std::max(batch, 1) * g.num_kv_heads;
-    int64_t want_splits = std::max<int64_t>(1, (8LL * cus + units - 1) / units);
+    int64_t want_splits = std::max<int64_t>(1, (cus + units - 1) / units);
     pps = (int)std::max<int64_t>(2, (max_pages_per_seq + want_splits - 1) / want_splits);
-    pps = std::max(2, std::min(pps, 64));
   }
   pps = (pps + 1) & ~1;  // whole page pairs
+  if (pps > kDecodePidCap) pps = kDecodePidCap;
+  if ((max_pages_per_seq + pps - 1) / pps > kDecodeMaxSplits) {
+    pps = (max_pages_per_seq + kDecodeMaxSplits - 1) / kDecodeMaxSplits;
+    pps = (pps + 1) & ~1;
+    if (pps > kDecodePidCap) return TQ_EINVAL;
+  }
   ws->pages_per_split = pps;
   ws->n_splits = (max_pages_per_seq + pps - 1) / pps;
   const size_t B = (size_t)std::max(batch, 0), Hq = (size_t)num_q_heads, d = (size_t)g.head_dim;
   const size_t S = (size_t)ws->n_splits;
   size_t off = 0;
-  ws->qrot_off = off;
-  off = align16(off + 4 * B * Hq * d);
-  ws->qsk_off = off;
-  if (g.k_mode == TQ_PROD) off = align16(off + 4 * B * Hq * d);
-  ws->qscale_off = off;
-  off = align16(off + 4 * B * Hq * 2);
   ws->part_o_off = off;
   off = align16(off + 4 * B * Hq * S * d);
   ws->part_ml_off = off;
@@ -341,6 +347,8 @@ int tq_quantize_kv(const tq_layout *layout, void *pages, int64_t num_pages, cons
   if (((uintptr_t)pages | (uintptr_t)k_cb | (uintptr_t)v_cb) & 15) return TQ_EINVAL;
   const int64_t row = (int64_t)g.num_kv_heads * g.head_dim;
   if (k_stride_tok < row || v_stride_tok < row) return TQ_EINVAL;
+  if ((k_stride_tok | v_stride_tok) & 7) return TQ_EINVAL;             // 8-element rows stay 16-byte aligned
+  if (((uintptr_t)k | (uintptr_t)v) & 15) return TQ_EINVAL;
   if (n_tok > ((int64_t)1 << 40)) return TQ_EINVAL;
   return tq::launch_quantize(g, pages, num_pages, k, v, dtype, n_tok, k_stride_tok, v_stride_tok,
                              slots, k_cb, v_cb, (hipStream_t)stream);
@@ -372,7 +380,7 @@ int tq_decode_attention(const tq_layout *layout, const void *pages, int64_t num_
   if (batch < 0 || num_q_heads < 1 || num_q_heads % g.num_kv_heads) return TQ_EINVAL;
   if (num_q_heads / g.num_kv_heads > 16) return TQ_ENOTSUP;  // one MFMA column block of query heads
   if (g.v_mode == TQ_PROD) return TQ_ENOTSUP;
-  if (max_pages_per_seq < 1 || num_pages < 1 || !std::isfinite(softmax_scale)) return TQ_EINVAL;
+  if (max_pages_per_seq < 1 || num_pages < 1 || !std::isfinite(softmax_scale) || softmax_scale < 0.f) return TQ_EINVAL;
   if (batch == 0) return TQ_OK;
   if (!pages || !q || !page_table || !seq_lens || !k_cb || !v_cb || !workspace || !out) return TQ_EINVAL;
   if (((uintptr_t)pages | (uintptr_t)k_cb | (uintptr_t)v_cb | (uintptr_t)workspace) & 15) return TQ_EINVAL;

@@ -1,21 +1,23 @@
-// Decode attention over the packed cache ("Where This Fits in the Inference Stack", "TensorRT-LLM: Why
-// Integration Is a Kernel Problem": dequantize in registers while the K/V tiles stream in; "Why the KV
-// Cache Exists", "The KV Cache Solution": one new query per sequence attends over every cached token).
+// Decode attention over the packed cache, one kernel launch ("Where This Fits in the Inference Stack",
+// "TensorRT-LLM: Why Integration Is a Kernel Problem": dequantize in registers while the K/V tiles stream
+// in; "Why the KV Cache Exists", "The KV Cache Solution": the new query attends over every cached token).
 //
-// Three kernels on the caller's stream:
-//   prologue  per (batch, query head): q_rot = R q = H (s * q) / sqrt(d), stored scaled by 1/sqrt(d)
-//             (the stored levels are in N(0,1) units); for a sketched K also q_s = S q_rot * sqrt(pi/2)/m.
-//             A power-of-two range factor per head makes the fp16 hi/lo split below exact to 2^-22.
-//   split     one wavefront per (batch, KV head, run of pages). For each pair of 16-token pages:
-//               scores  S^T[16 tokens, 16 cols] = Khat[16, d] * Q[d, 16] on MFMA 16x16x32 f16, where the
-//                       K operand holds the fp16 levels looked up from the codes and Q holds the G query
-//                       heads of this KV head as fp16 hi + lo parts (two MFMAs per 32 coordinates);
-//               softmax running max / sum per head (base-2 exponent);
-//               values  O[16 rows, d] += P'[rows, 32 tokens] * Vhat[32 tokens, d], P' = p * ||v|| split
-//                       into fp16 hi + lo rows, Vhat the fp16 V levels.
-//             Writes the run's (max, sum, O) partial. Everything stays in the rotated domain.
-//   combine   per (batch, query head): log-sum-exp merge of the partials, then one inverse rotation
-//             R_V^T (Walsh-Hadamard butterflies in LDS) and the fp32 output.
+// Grid (splits, KV heads, batch); a work-group of WAVES wavefronts owns one run of pages of one
+// (sequence, KV head) and all G = Hq/Hkv query heads that share it, so every K/V byte is read once.
+//   1. Query rotation: q_rot = R q = H (s * q) / sqrt(d) for the G heads, in LDS (Walsh-Hadamard
+//      butterflies); stored divided once more by sqrt(d) because the stored levels are in N(0,1) units.
+//      For a sketched K also q_s = S q_rot * sqrt(pi/2) / m. A power-of-two factor per head brings each
+//      into [128, 256) so that an fp16 hi + lo split carries ~22 bits.
+//   2. Each wavefront walks page pairs (32 tokens), loading the next pair while it computes this one:
+//        scores  S^T[16 tok, 16 col] = Khat[16, d] Q[d, 16] on MFMA 16x16x32 f16: the K operand holds fp16
+//                levels looked up from the codes (v_perm byte tables for 4-bit codes), the Q operand the
+//                hi and lo parts of the G rotated queries (two MFMAs per 32 coordinates);
+//        softmax running max per head (base-2), sums kept per lane;
+//        values  O[rows, d] += P'[rows, 32 tok] Vhat[32 tok, d] with P' = p * ||v|| as fp16 hi + lo and
+//                Vhat the fp16 V levels (v_perm table for 2-bit codes).
+//   3. The wavefronts merge in LDS (fixed-order tree). With one run per (sequence, KV head) the work-group
+//      applies R_V^T once per output (butterflies in LDS) and writes fp32 out; with several runs it writes
+//      its (max, sum, O) partial and a second, small kernel merges the runs and finishes the rows.
 #include <hip/hip_runtime.h>
 
 #include "tq_common.h"
@@ -25,6 +27,9 @@ namespace tq {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWaves = 8;
+constexpr int kMlCap = 2048;   // split partials merged by one combine work-group
+constexpr int kPidCap = 4096;  // page ids of one run held in LDS
 
 struct DecodeArgs {
   const unsigned char *pages;
@@ -39,17 +44,11 @@ struct DecodeArgs {
   const int32_t *seq_lens;
   float scale_log2;
   const unsigned char *kcb, *vcb;
-  float *qrot, *qsk, *qscale, *part_o, *part_ml;
+  BlobOffsets ko, vo;  // section offsets inside the K and V codebook blobs
+  float *part_o, *part_ml;
   int n_splits, pps;
   float *out;
 };
-
-__device__ __forceinline__ int clamp_len(const DecodeArgs &a, int b) {
-  int L = a.seq_lens[b];
-  L = L < 0 ? 0 : L;
-  int cap = a.max_pages * TQ_PAGE_TOKENS;
-  return L > cap ? cap : L;
-}
 
 // Largest power of two sigma with max|x| * sigma < 256 (1 if x is all zero).
 __device__ __forceinline__ float range_factor(float maxabs) {
@@ -59,58 +58,12 @@ __device__ __forceinline__ float range_factor(float maxabs) {
   return ldexpf(1.0f, 8 - e);
 }
 
-// ------------------------------------------------------------------------------------------------
-// prologue
-// ------------------------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(D) void prologue_kernel(DecodeArgs a) {
-  const int bh = blockIdx.x;
-  const int i = threadIdx.x;
-  __shared__ float v[D];
-  __shared__ float red[D];
-  const tq_codebook_header *hk = (const tq_codebook_header *)a.kcb;
-  const uint32_t *sw = (const uint32_t *)(a.kcb + hk->signs_off);
-  float x = load_elem(a.q, (int64_t)bh * D + i, a.q_dtype);
-  if ((sw[i >> 5] >> (i & 31)) & 1u) x = -x;
-  v[i] = x;
-  __syncthreads();
-  for (int hs = 1; hs < D; hs <<= 1) {
-    float u = v[i], w = v[i ^ hs];
-    __syncthreads();
-    v[i] = (i & hs) ? (w - u) : (u + w);
-    __syncthreads();
-  }
-  const float qr = v[i] * (1.0f / D);  // (R q)_i / sqrt(d)
-  a.qrot[(int64_t)bh * D + i] = qr;
-  red[i] = fabsf(qr);
-  __syncthreads();
-  for (int s = D / 2; s > 0; s >>= 1) {
-    if (i < s) red[i] = fmaxf(red[i], red[i + s]);
-    __syncthreads();
-  }
-  if (i == 0) a.qscale[(int64_t)bh * 2] = range_factor(red[0]);
-  if (hk->mode == TQ_PROD) {
-    // q_s = S (R q) * sqrt(pi/2) / m, with (R q)_k = v_k / sqrt(d)
-    const float *S = (const float *)(a.kcb + hk->proj_off);
-    const float c = 1.2533141373155003f / (float)hk->qjl_rows * (D == 128 ? 0.088388347648318440f : 0.125f);
-    float acc = 0.f;
-    for (int k = 0; k < D; ++k) acc = fmaf(S[(int64_t)i * D + k], v[k], acc);
-    const float qs = acc * c;
-    a.qsk[(int64_t)bh * D + i] = qs;
-    __syncthreads();
-    red[i] = fabsf(qs);
-    __syncthreads();
-    for (int s = D / 2; s > 0; s >>= 1) {
-      if (i < s) red[i] = fmaxf(red[i], red[i + s]);
-      __syncthreads();
-    }
-    if (i == 0) a.qscale[(int64_t)bh * 2 + 1] = range_factor(red[0]);
-  }
-}
+// 2^x on the hardware exponential unit (results below 2^-126 flush to zero; 2^-inf = 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// ------------------------------------------------------------------------------------------------
-// split
-// ------------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
 
 // NBYTES bytes from p (aligned to ALIGN bytes) into dwords (little-endian).
 template <int NBYTES, int ALIGN>
@@ -147,15 +100,18 @@ __device__ __forceinline__ uint32_t bits_at(const uint32_t *w, int off) {
   return (uint32_t)(two >> sh) & ((1u << NB) - 1u);
 }
 
-__device__ __forceinline__ half8_t pack8(const uint16_t *hv) {
-  half8_t r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    _Float16 h;
-    __builtin_memcpy(&h, &hv[i], 2);
-    r[i] = h;
-  }
-  return r;
+__device__ __forceinline__ half8_t from_dwords(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3) {
+  union {
+    uint32_t u[4];
+    half8_t h;
+  } x;
+  x.u[0] = r0; x.u[1] = r1; x.u[2] = r2; x.u[3] = r3;
+  return x.h;
+}
+
+__device__ __forceinline__ half8_t from_halves(const uint16_t *hv) {
+  return from_dwords(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16),
+                     hv[4] | ((uint32_t)hv[5] << 16), hv[6] | ((uint32_t)hv[7] << 16));
 }
 
 __device__ __forceinline__ void split_hi_lo(float x, _Float16 &hi, _Float16 &lo) {
@@ -163,157 +119,396 @@ __device__ __forceinline__ void split_hi_lo(float x, _Float16 &hi, _Float16 &lo)
   lo = (_Float16)(x - (float)hi);
 }
 
-template <int D, int KB, bool KPROD, int VB>
-__global__ __launch_bounds__(64) void split_kernel(DecodeArgs a) {
-  constexpr int KBLK = D / 32;           // 32-coordinate blocks of the score contraction
-  constexpr int NB = D / 16;             // 16-coordinate blocks of the value contraction
-  constexpr int KCH = D / 4 * KB / 8;    // bytes of K codes per lane per token (D/4 coordinates)
-  constexpr int KREC = D * KB / 8;       // bytes of one K record
-  constexpr int VCH = 4 * VB;            // bytes of V codes per lane per page (4 tokens x one piece)
-  constexpr int KW = (KCH + 3) / 4 + 1;  // dwords (one spare for bit extraction across a boundary)
-  constexpr int VW = VCH / 4 + 1;
+// MFMA position p (0..7) of the K operand -> coordinate offset inside its 8-coordinate group.
+template <int KB>
+__device__ __forceinline__ constexpr int k_order(int p) {
+  return KB == 4 ? ((p < 4) ? 2 * p : 2 * (p - 4) + 1) : p;
+}
 
-  const int lane = threadIdx.x;
-  const int c = lane & 15;   // MFMA row/column index inside a 16-block
-  const int g4 = lane >> 4;  // which 8-deep slice of the contraction this lane holds
+// Byte tables of the fp16 levels for v_perm lookups.
+struct Tab {
+  uint32_t lo0, lo1, hi0, hi1;
+};
+
+// 4-bit codes: the 8 magnitudes (codes 8..15 of the code-indexed table); a clear top bit negates.
+__device__ __forceinline__ Tab make_tab_k4(const uint16_t *lut) {
+  Tab t{0, 0, 0, 0};
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const uint32_t h = lut[8 + m];
+    if (m < 4) {
+      t.lo0 |= (h & 0xFFu) << (8 * m);
+      t.hi0 |= (h >> 8) << (8 * m);
+    } else {
+      t.lo1 |= (h & 0xFFu) << (8 * (m - 4));
+      t.hi1 |= (h >> 8) << (8 * (m - 4));
+    }
+  }
+  return t;
+}
+
+// 2-bit codes: the four levels by code; low bytes in lo0, high bytes in hi0.
+__device__ __forceinline__ Tab make_tab_v2(const uint16_t *lut) {
+  Tab t{0, 0, 0, 0};
+#pragma unroll
+  for (int c2 = 0; c2 < 4; ++c2) {
+    t.lo0 |= ((uint32_t)lut[c2] & 0xFFu) << (8 * c2);
+    t.hi0 |= ((uint32_t)lut[c2] >> 8) << (8 * c2);
+  }
+  return t;
+}
+
+// Eight 4-bit sign-magnitude codes (coordinate e in nibble e) -> fp16 levels in MFMA order
+// e = 0,2,4,6,1,3,5,7: byte-table lookups of the magnitude, sign bit set when the code's top bit is clear.
+__device__ __forceinline__ half8_t lut_k4(uint32_t w, const Tab &T) {
+  const uint32_t me = w & 0x07070707u, mo = (w >> 4) & 0x07070707u;
+  const uint32_t le = perm(T.lo1, T.lo0, me);
+  const uint32_t he = perm(T.hi1, T.hi0, me) | (~(w << 4) & 0x80808080u);
+  const uint32_t lo = perm(T.lo1, T.lo0, mo);
+  const uint32_t ho = perm(T.hi1, T.hi0, mo) | (~w & 0x80808080u);
+  return from_dwords(perm(he, le, 0x05010400u), perm(he, le, 0x07030602u), perm(ho, lo, 0x05010400u),
+                     perm(ho, lo, 0x07030602u));
+}
+
+// Two 2-bit codes at bits 0-1 and 16-17 of x -> two fp16 levels.
+__device__ __forceinline__ uint32_t lut_v2_pair(uint32_t x, const Tab &T) {
+  return perm(T.hi0, T.lo0, (x & 0x00030003u) * 0x0101u + 0x04000400u);
+}
+
+// --------------------------------------------------------------------------------------------------
+// per page-pair register fragment
+// --------------------------------------------------------------------------------------------------
+template <int D, int KB, bool KPROD, int VB>
+struct Frag {
+  static constexpr int KCH = D / 4 * KB / 8;  // K code bytes per lane per token
+  static constexpr int VCH = 4 * VB;          // V code bytes per lane per page
+  static constexpr int KW = (KCH + 3) / 4 + 1;
+  static constexpr int VW = VCH / 4 + 1;
+  uint32_t kw[2][KW];
+  uint32_t vw[2][VW];
+  uint2 nk[2], nv[2];
+  uint32_t zb[2];
+  uint2 gm[2];
+  bool ok[2];
+};
+
+// Byte offsets, inside one page, of everything one lane reads (fixed for the whole launch).
+struct LaneOffsets {
+  uint32_t k, nk, nv, v, z, gm;
+};
+
+template <int D, int KB, int VB>
+__device__ __forceinline__ LaneOffsets lane_offsets(const DecodeArgs &a, int kvh, int c, int g4) {
+  constexpr int KREC = D * KB / 8;
+  constexpr int KCH = D / 4 * KB / 8;
+  LaneOffsets o;
+  o.k = (uint32_t)(a.k_codes + (int64_t)(kvh * TQ_PAGE_TOKENS + c) * KREC + g4 * KCH);
+  o.nk = (uint32_t)(a.k_norms + (int64_t)(kvh * TQ_PAGE_TOKENS + 4 * g4) * 2);
+  o.nv = (uint32_t)(a.v_norms + (int64_t)(kvh * TQ_PAGE_TOKENS + 4 * g4) * 2);
+  const int piece = (D / 16) * c / 8;
+  o.v = (uint32_t)(a.v_codes + ((int64_t)(kvh * (D / 8) + piece) * TQ_PAGE_TOKENS + 4 * g4) * VB);
+  o.z = (uint32_t)(a.k_qjl + (int64_t)(kvh * TQ_PAGE_TOKENS + c) * (D / 8) + g4 * (D / 32));
+  o.gm = (uint32_t)(a.k_gamma + (int64_t)(kvh * TQ_PAGE_TOKENS + 4 * g4) * 2);
+  return o;
+}
+
+template <int D, int KB, bool KPROD, int VB>
+__device__ __forceinline__ void load_pair(const DecodeArgs &a, const int *pid, const LaneOffsets &lo, int pp,
+                                          int p_begin, int p_end, Frag<D, KB, KPROD, VB> &f) {
+  using F = Frag<D, KB, KPROD, VB>;
+#pragma unroll
+  for (int q2 = 0; q2 < 2; ++q2) {
+    const int pi = pp + q2;
+    // the page id is the same for the whole wavefront: keep the page base in scalar registers
+    const int pg = __builtin_amdgcn_readfirstlane(pi < p_end ? pid[pi - p_begin] : -1);
+    const bool ok = pg >= 0 && pg < a.num_pages;
+    f.ok[q2] = ok;
+    const unsigned char *base = a.pages + (int64_t)(ok ? pg : 0) * a.page_bytes;
+    f.kw[q2][F::KW - 1] = 0;
+    load_bytes<F::KCH, (F::KCH % 16 == 0) ? 16 : ((F::KCH % 8 == 0) ? 8 : ((F::KCH % 4 == 0) ? 4 : 2))>(
+        base + lo.k, f.kw[q2]);
+    f.nk[q2] = *(const uint2 *)(base + lo.nk);
+    f.nv[q2] = *(const uint2 *)(base + lo.nv);
+    f.vw[q2][F::VW - 1] = 0;
+    load_bytes<F::VCH, 4>(base + lo.v, f.vw[q2]);
+    if constexpr (KPROD) {
+      if constexpr (D == 128) f.zb[q2] = *(const uint32_t *)(base + lo.z);
+      else f.zb[q2] = *(const uint16_t *)(base + lo.z);
+      f.gm[q2] = *(const uint2 *)(base + lo.gm);
+    }
+  }
+}
+
+__device__ __forceinline__ void unpack4(uint2 w, float *x) {
+  x[0] = half_bits_to_float(w.x & 0xFFFF);
+  x[1] = half_bits_to_float(w.x >> 16);
+  x[2] = half_bits_to_float(w.y & 0xFFFF);
+  x[3] = half_bits_to_float(w.y >> 16);
+}
+
+// In-place Walsh-Hadamard transform of `rows` rows of D floats in LDS (row stride D), all threads.
+template <int D, int NT>
+__device__ __forceinline__ void lds_wht(float (*buf)[D], int rows, int tid) {
+  for (int hs = 1; hs < D; hs <<= 1) {
+    for (int p = tid; p < rows * (D / 2); p += NT) {
+      const int r = p / (D / 2), j = p % (D / 2);
+      const int i1 = (j / hs) * 2 * hs + (j % hs), i2 = i1 + hs;
+      const float u = buf[r][i1], w = buf[r][i2];
+      buf[r][i1] = u + w;
+      buf[r][i2] = u - w;
+    }
+    __syncthreads();
+  }
+}
+
+template <int D, int KB, bool KPROD, int VB>
+__global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
+  constexpr int NT = 64 * kWaves;
+  constexpr int KBLK = D / 32;  // 32-coordinate blocks of the score contraction
+  constexpr int NB = D / 16;    // 16-coordinate blocks of the value contraction
+  constexpr int QF = 16 * D;    // floats in one [16][D] block
+  using F = Frag<D, KB, KPROD, VB>;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15;   // MFMA row/column inside a 16-block
+  const int g4 = lane >> 4;  // 8-deep slice of the contraction held by this lane
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = a.G;
   const int head0 = kvh * G;
 
-  __shared__ uint16_t lut_k[1 << KB];
-  __shared__ uint16_t lut_v[1 << VB];
-  {
-    const tq_codebook_header *hk = (const tq_codebook_header *)a.kcb;
-    const tq_codebook_header *hv = (const tq_codebook_header *)a.vcb;
-    for (int i = lane; i < (1 << KB); i += 64) lut_k[i] = ((const uint16_t *)(a.kcb + hk->levels_off))[i];
-    for (int i = lane; i < (1 << VB); i += 64) lut_v[i] = ((const uint16_t *)(a.vcb + hv->levels_off))[i];
+  // LDS arena reused by phase: queries (prologue), then the wave-merge tree
+  __shared__ __align__(16) float arena[4 * QF];
+  __shared__ int s_pid[kPidCap];
+  __shared__ float s_sig[16][2];
+  __shared__ uint16_t s_lutk[1 << KB];
+  __shared__ uint16_t s_lutv[1 << VB];
+  __shared__ float s_m[kWaves][16], s_l[kWaves][16];
+  __shared__ float s_rowm[16], s_rowl[16];
+  float(*s_q)[D] = (float(*)[D])arena;         // rotated queries / d
+  float(*s_qs)[D] = (float(*)[D])(arena + QF);  // sketch-domain queries
+
+  int seq_len = a.seq_lens[b];
+  seq_len = seq_len < 0 ? 0 : (seq_len > a.max_pages * TQ_PAGE_TOKENS ? a.max_pages * TQ_PAGE_TOKENS : seq_len);
+  const int npages = (seq_len + TQ_PAGE_TOKENS - 1) / TQ_PAGE_TOKENS;
+  const int p_begin = split * a.pps;
+  const int p_end = min(p_begin + a.pps, npages);
+  const int npairs = p_end > p_begin ? (p_end - p_begin + 1) / 2 : 0;
+
+  // ---- 0. every global read of the prologue issued together: page ids of this run, this wavefront's
+  //         query rows, the rotation signs of the query's coordinates, the level tables
+  for (int j = tid; j < p_end - p_begin; j += NT) s_pid[j] = a.page_table[(int64_t)b * a.max_pages + p_begin + j];
+  float qx[2][2];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int r = wave + rr * kWaves;
+    const int64_t base = ((int64_t)b * a.Hq + head0 + (r < G ? r : 0)) * D;
+    qx[rr][0] = r < G ? load_elem(a.q, base + lane, a.q_dtype) : 0.f;
+    qx[rr][1] = (D == 128 && r < G) ? load_elem(a.q, base + lane + 64, a.q_dtype) : 0.f;
+  }
+  const uint32_t *ksw = (const uint32_t *)(a.kcb + a.ko.signs);
+  const uint32_t sgn0 = ksw[lane >> 5];
+  const uint32_t sgn1 = D == 128 ? ksw[(lane + 64) >> 5] : 0u;
+  // code-indexed level tables: code c -> ascending level c (upper half) or half - 1 - c (lower half)
+  for (int j = tid; j < (1 << KB); j += NT) {
+    const int h2 = (1 << KB) >> 1;
+    s_lutk[j] = ((const uint16_t *)(a.kcb + a.ko.levels))[j >= h2 ? j : h2 - 1 - j];
+  }
+  for (int j = tid; j < (1 << VB); j += NT) {
+    const int h2 = (1 << VB) >> 1;
+    s_lutv[j] = ((const uint16_t *)(a.vcb + a.vo.levels))[j >= h2 ? j : h2 - 1 - j];
   }
   __syncthreads();
 
-  // Query operands: lane holds column c (query head head0 + c) for contraction rows
-  // 8*g4 .. 8*g4+7 of each 32-coordinate block, i.e. coordinates cbase + 8*kb + e.
+  // ---- 1. the first page pairs of this wavefront in flight before the query prologue
+  const LaneOffsets lo = lane_offsets<D, KB, VB>(a, kvh, c, g4);
+  // register budget: wide codes or the sketch leave room for fewer fragments in flight
+  constexpr int R = (KB >= 8 || VB >= 8) ? 2 : (KPROD ? 3 : 4);
+  F f[R];
+#pragma unroll
+  for (int r = 0; r + 1 < R; ++r)
+    if (wave + r * kWaves < npairs)
+      load_pair<D, KB, KPROD, VB>(a, s_pid, lo, p_begin + 2 * (wave + r * kWaves), p_begin, p_end, f[r]);
+
+  // ---- 2. query rotation, one row per wavefront: H (s * q) with cross-lane butterflies
+  {
+    const bool neg0 = (sgn0 >> (lane & 31)) & 1u;
+    const bool neg1 = (sgn1 >> (lane & 31)) & 1u;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int r = wave + rr * kWaves;
+      if (r >= G) continue;
+      float x0 = neg0 ? -qx[rr][0] : qx[rr][0];
+      float x1 = neg1 ? -qx[rr][1] : qx[rr][1];
+#pragma unroll
+      for (int h = 1; h < 64; h <<= 1) {
+        const float p0 = __shfl_xor(x0, h), p1 = __shfl_xor(x1, h);
+        x0 = (lane & h) ? (p0 - x0) : (x0 + p0);
+        x1 = (lane & h) ? (p1 - x1) : (x1 + p1);
+      }
+      if (D == 128) {
+        const float u = x0;
+        x0 = u + x1;
+        x1 = u - x1;
+      }
+      x0 *= (1.0f / D);
+      x1 *= (1.0f / D);
+      float mx = fmaxf(fabsf(x0), D == 128 ? fabsf(x1) : 0.f);
+#pragma unroll
+      for (int h = 1; h < 64; h <<= 1) mx = fmaxf(mx, __shfl_xor(mx, h));
+      s_q[r][lane] = x0;
+      if (D == 128) s_q[r][lane + 64] = x1;
+      if (lane == 0) s_sig[r][0] = range_factor(mx);
+    }
+  }
+  __syncthreads();
+  if constexpr (KPROD) {
+    // q_s = S (R q) sqrt(pi/2) / m with R q = (d * s_q) / sqrt(d)
+    const float *S = (const float *)(a.kcb + a.ko.proj);
+    const float cq = 1.2533141373155003f / (float)a.ko.qjl_rows * (float)D * (D == 128 ? 0.088388347648318440f : 0.125f);
+    for (int idx = tid; idx < G * D; idx += NT) {
+      const int r = idx / D, j = idx % D;
+      float acc = 0.f;
+      for (int k = 0; k < D; ++k) acc = fmaf(S[(int64_t)j * D + k], s_q[r][k], acc);
+      s_qs[r][j] = acc * cq;
+    }
+    __syncthreads();
+    for (int r = wave; r < G; r += kWaves) {
+      float mx = 0.f;
+      for (int k = lane; k < D; k += 64) mx = fmaxf(mx, fabsf(s_qs[r][k]));
+#pragma unroll
+      for (int h = 1; h < 64; h <<= 1) mx = fmaxf(mx, __shfl_xor(mx, h));
+      if (lane == 0) s_sig[r][1] = range_factor(mx);
+    }
+    __syncthreads();
+  }
+
+  // query operands: column c = query head head0 + c, contraction rows 8*g4.. of each 32-block,
+  // i.e. coordinates cbase + 8*kb + k_order(p)
   const int cbase = (D / 4) * g4;
   half8_t qhi[KBLK], qlo[KBLK];
   half8_t shi[KPROD ? KBLK : 1], slo[KPROD ? KBLK : 1];
-  float colscale = 0.f, skratio = 0.f;
+  float colscale, skratio;
   {
     const bool real = c < G;
-    const int64_t bh = (int64_t)b * a.Hq + head0 + (real ? c : 0);
-    const float sig = real ? a.qscale[bh * 2] : 1.f;
-    const float sig2 = (KPROD && real) ? a.qscale[bh * 2 + 1] : 1.f;
+    const int r = real ? c : 0;
+    const float sig = s_sig[r][0], sig2 = KPROD ? s_sig[r][1] : 1.f;
     colscale = real ? a.scale_log2 / sig : 0.f;
     skratio = sig / sig2;
 #pragma unroll
     for (int kb = 0; kb < KBLK; ++kb) {
+      // the lane's 8 consecutive coordinates as two 16-byte LDS reads
+      const float4 u0 = *(const float4 *)&s_q[r][cbase + 8 * kb];
+      const float4 u1 = *(const float4 *)&s_q[r][cbase + 8 * kb + 4];
+      const float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int coord = cbase + 8 * kb + e;
-        float x = real ? a.qrot[bh * D + coord] * sig : 0.f;
+      for (int p = 0; p < 8; ++p) {
+        const float x = real ? v[k_order<KB>(p)] * sig : 0.f;
         _Float16 h, l;
         split_hi_lo(x, h, l);
-        qhi[kb][e] = h;
-        qlo[kb][e] = l;
-        if constexpr (KPROD) {
-          float y = real ? a.qsk[bh * D + coord] * sig2 : 0.f;
+        qhi[kb][p] = h;
+        qlo[kb][p] = l;
+      }
+      if constexpr (KPROD) {
+        const float4 w0 = *(const float4 *)&s_qs[r][cbase + 8 * kb];
+        const float4 w1 = *(const float4 *)&s_qs[r][cbase + 8 * kb + 4];
+        const float z[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const float y = real ? z[p] * sig2 : 0.f;
+          _Float16 h, l;
           split_hi_lo(y, h, l);
-          shi[kb][e] = h;
-          slo[kb][e] = l;
+          shi[kb][p] = h;
+          slo[kb][p] = l;
         }
       }
     }
   }
+  Tab tk{0, 0, 0, 0}, tv{0, 0, 0, 0};
+  if constexpr (KB == 4) tk = make_tab_k4(s_lutk);
+  if constexpr (VB == 2) tv = make_tab_v2(s_lutv);
+  uint32_t negpair1 = 0;  // 1-bit levels: fp16 pattern of the negative level in both halves
+  if constexpr (KB == 1) negpair1 = (uint32_t)s_lutk[0] * 0x00010001u;
 
-  const int seq_len = clamp_len(a, b);
-  const int npages = (seq_len + TQ_PAGE_TOKENS - 1) / TQ_PAGE_TOKENS;
-  const int p_begin = split * a.pps;
-  const int p_end = min(p_begin + a.pps, npages);
-
+  // ---- 3. stream the page pairs
   float m_run = -INFINITY;
   float l_part = 0.f;
   floatx4_t O[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) O[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int pp = p_begin; pp < p_end; pp += 2) {
+  auto process = [&](const F &cur, int pi) {
+    const int pp = p_begin + 2 * pi;
     float s[2][4], nv[2][4];
-    uint32_t vw[2][VW];
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
-      const int pi = pp + q2;
-      int pg = pi < p_end ? a.page_table[(int64_t)b * a.max_pages + pi] : -1;
-      const bool pvalid = pg >= 0 && pg < a.num_pages;
-      const unsigned char *base = a.pages + (int64_t)(pvalid ? pg : 0) * a.page_bytes;
-
-      // ---- scores for the 16 tokens of this page
-      uint32_t kw[KW];
-      kw[KW - 1] = 0;
-      load_bytes<KCH, (KCH % 16 == 0) ? 16 : ((KCH % 8 == 0) ? 8 : ((KCH % 4 == 0) ? 4 : 2))>(
-          base + a.k_codes + (int64_t)(kvh * TQ_PAGE_TOKENS + c) * KREC + g4 * KCH, kw);
       floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KBLK; ++kb) {
-        uint16_t hv[8];
+        half8_t A;
+        if constexpr (KB == 4) {
+          A = lut_k4(cur.kw[q2][kb], tk);
+        } else if constexpr (KB == 1) {
+          const uint32_t z = cur.kw[q2][0] >> (8 * kb);
+          A = from_dwords(negpair1 ^ ((z & 1u) << 15) ^ ((z & 2u) << 30), negpair1 ^ ((z & 4u) << 13) ^ ((z & 8u) << 28),
+                          negpair1 ^ ((z & 16u) << 11) ^ ((z & 32u) << 26), negpair1 ^ ((z & 64u) << 9) ^ ((z & 128u) << 24));
+        } else {
+          uint16_t hv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) hv[e] = lut_k[bits_at<KB>(kw, KB * (8 * kb + e))];
-        const half8_t A = pack8(hv);
+          for (int p = 0; p < 8; ++p) hv[p] = s_lutk[bits_at<KB>(cur.kw[q2], KB * (8 * kb + p))];
+          A = from_halves(hv);
+        }
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qhi[kb], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qlo[kb], acc, 0, 0, 0);
       }
-      floatx4_t acc2 = {0.f, 0.f, 0.f, 0.f};
-      float gam[4] = {0.f, 0.f, 0.f, 0.f};
+      float raw[4] = {acc[0], acc[1], acc[2], acc[3]};
       if constexpr (KPROD) {
-        // sketch bits of token c for coordinates cbase .. cbase + D/4 - 1
-        uint32_t zb;
-        const unsigned char *zp = base + a.k_qjl + (int64_t)(kvh * TQ_PAGE_TOKENS + c) * (D / 8) + g4 * (D / 32);
-        if constexpr (D == 128) zb = *(const uint32_t *)zp;
-        else zb = *(const uint16_t *)zp;
+        floatx4_t acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KBLK; ++kb) {
-          uint16_t hv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) hv[e] = ((zb >> (8 * kb + e)) & 1u) ? 0x3C00 : 0xBC00;  // +1 / -1
-          const half8_t A = pack8(hv);
+          const uint32_t z = cur.zb[q2] >> (8 * kb);
+          const uint32_t NEG = 0xBC00BC00u;  // -1, -1; a set bit flips to +1
+          const half8_t A = from_dwords(NEG ^ ((z & 1u) << 15) ^ ((z & 2u) << 30), NEG ^ ((z & 4u) << 13) ^ ((z & 8u) << 28),
+                                        NEG ^ ((z & 16u) << 11) ^ ((z & 32u) << 26), NEG ^ ((z & 64u) << 9) ^ ((z & 128u) << 24));
           acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, shi[kb], acc2, 0, 0, 0);
           acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, slo[kb], acc2, 0, 0, 0);
         }
-        const uint2 gw = *(const uint2 *)(base + a.k_gamma + (int64_t)(kvh * TQ_PAGE_TOKENS + 4 * g4) * 2);
-        gam[0] = half_bits_to_float(gw.x & 0xFFFF);
-        gam[1] = half_bits_to_float(gw.x >> 16);
-        gam[2] = half_bits_to_float(gw.y & 0xFFFF);
-        gam[3] = half_bits_to_float(gw.y >> 16);
-      }
-      const uint2 nkw = *(const uint2 *)(base + a.k_norms + (int64_t)(kvh * TQ_PAGE_TOKENS + 4 * g4) * 2);
-      const uint2 nvw = *(const uint2 *)(base + a.v_norms + (int64_t)(kvh * TQ_PAGE_TOKENS + 4 * g4) * 2);
-      const float nk[4] = {half_bits_to_float(nkw.x & 0xFFFF), half_bits_to_float(nkw.x >> 16),
-                           half_bits_to_float(nkw.y & 0xFFFF), half_bits_to_float(nkw.y >> 16)};
-      nv[q2][0] = half_bits_to_float(nvw.x & 0xFFFF);
-      nv[q2][1] = half_bits_to_float(nvw.x >> 16);
-      nv[q2][2] = half_bits_to_float(nvw.y & 0xFFFF);
-      nv[q2][3] = half_bits_to_float(nvw.y >> 16);
+        float gam[4];
+        unpack4(cur.gm[q2], gam);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = pi * TQ_PAGE_TOKENS + 4 * g4 + j;
-        const bool ok = pvalid && t < seq_len && c < G;
-        float raw = acc[j];
-        if constexpr (KPROD) raw = fmaf(gam[j] * skratio, acc2[j], raw);
-        s[q2][j] = ok ? colscale * nk[j] * raw : -INFINITY;
+        for (int j = 0; j < 4; ++j) raw[j] = fmaf(gam[j] * skratio, acc2[j], raw[j]);
       }
-
-      // ---- V codes: piece holding coordinates (D/16)*c .. +NB-1, slots 4*g4 .. 4*g4+3
-      const int piece = (D / 16) * c / 8;
-      vw[q2][VW - 1] = 0;
-      load_bytes<VCH, 4>(base + a.v_codes + ((int64_t)(kvh * (D / 8) + piece) * TQ_PAGE_TOKENS + 4 * g4) * VB,
-                         vw[q2]);
+      float nk[4];
+      unpack4(cur.nk[q2], nk);
+      unpack4(cur.nv[q2], nv[q2]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[q2][j] = nk[j] * raw[j];  // score / (softmax scale * log2 e)
+    }
+    // tokens past the sequence end or in an invalid page: weight 0 (their bytes are not read as numbers)
+    const bool full = cur.ok[0] && cur.ok[1] && (pp + 2) * TQ_PAGE_TOKENS <= seq_len;
+    bool okm[2][4];
+    if (!full) {
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = (pp + q2) * TQ_PAGE_TOKENS + 4 * g4 + j;
+          okm[q2][j] = cur.ok[q2] && t < seq_len;
+          s[q2][j] = okm[q2][j] ? s[q2][j] : -INFINITY;
+          nv[q2][j] = okm[q2][j] ? nv[q2][j] : 0.f;
+        }
     }
 
-    // ---- online softmax over the 32 tokens (this lane: head column c, tokens 4*g4 .. +3 of each page)
+    // online softmax in base 2 (m_run is in units of scale * log2 e); this lane holds head column c,
+    // tokens 4*g4 .. 4*g4+3 of both pages
     float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = fmaxf(m_run, colscale * mx);
     if (__any(m_new > m_run)) {
-      const float alpha = (m_new > m_run) ? ((m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new)) : 1.f;
+      const float alpha = (m_new > m_run) ? ((m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new)) : 1.f;
       l_part *= alpha;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -327,101 +522,336 @@ __global__ __launch_bounds__(64) void split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p = (s[q2][j] == -INFINITY) ? 0.f : exp2f(s[q2][j] - m_run);
-        l_part += p;
-        const float pv = p > 0.f ? p * nv[q2][j] : 0.f;
-        _Float16 h, l;
-        split_hi_lo(pv, h, l);
-        phi[4 * q2 + j] = h;
-        plo[4 * q2 + j] = l;
+      for (int j = 0; j < 4; j += 2) {
+        float p0 = fast_exp2(fmaf(s[q2][j], colscale, -m_run));
+        float p1 = fast_exp2(fmaf(s[q2][j + 1], colscale, -m_run));
+        if (!full) {
+          p0 = okm[q2][j] ? p0 : 0.f;
+          p1 = okm[q2][j + 1] ? p1 : 0.f;
+        }
+        l_part += p0 + p1;
+        const float2_t pv = {p0 * nv[q2][j], p1 * nv[q2][j + 1]};
+        const half2_t h = __builtin_convertvector(pv, half2_t);
+        const half2_t l = __builtin_convertvector(pv - __builtin_convertvector(h, float2_t), half2_t);
+        phi[4 * q2 + j] = h[0];
+        phi[4 * q2 + j + 1] = h[1];
+        plo[4 * q2 + j] = l[0];
+        plo[4 * q2 + j + 1] = l[1];
       }
     }
 
-    // ---- values: O[rows][coords] += P'[rows][32 tokens] * Vhat[32 tokens][coords]
+    // values: O[rows][coords] += P'[rows][32 tokens] * Vhat[32 tokens][coords]
+    if constexpr (VB == 2 && D == 128) {
+      // code blocks nb and nb + 4 of a token sit one byte apart: one mask yields both selector sets
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int ci = (D == 128) ? nb : (4 * (c & 1) + nb);  // code index inside the 8-coordinate piece
-      uint16_t hv[8];
+      for (int k = 0; k < 4; ++k) {
+        uint32_t lo_[4], hi_[4];
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t y = (cur.vw[w >> 1][w & 1] >> (2 * k)) & 0x03030303u;
+          const uint32_t y4 = y | 0x04040404u;
+          lo_[w] = perm(tv.hi0, tv.lo0, perm(y4, y, 0x06020400u));  // code block k
+          hi_[w] = perm(tv.hi0, tv.lo0, perm(y4, y, 0x07030501u));  // code block k + 4
+        }
+        const half8_t B0 = from_dwords(lo_[0], lo_[1], lo_[2], lo_[3]);
+        const half8_t B1 = from_dwords(hi_[0], hi_[1], hi_[2], hi_[3]);
+        O[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, B0, O[k], 0, 0, 0);
+        O[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, B0, O[k], 0, 0, 0);
+        O[k + 4] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, B1, O[k + 4], 0, 0, 0);
+        O[k + 4] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, B1, O[k + 4], 0, 0, 0);
+      }
+    } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) hv[4 * q2 + j] = lut_v[bits_at<VB>(vw[q2], 8 * VB * j + VB * ci)];
-      const half8_t Bv = pack8(hv);
-      O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, Bv, O[nb], 0, 0, 0);
-      O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, Bv, O[nb], 0, 0, 0);
+      for (int nb = 0; nb < NB; ++nb) {
+        const int ci = (D == 128) ? nb : (4 * (c & 1) + nb);  // code index inside the token's 8-coordinate piece
+        half8_t Bv;
+        if constexpr (VB == 2) {
+          const int sh = 2 * ci;
+          Bv = from_dwords(lut_v2_pair(cur.vw[0][0] >> sh, tv), lut_v2_pair(cur.vw[0][1] >> sh, tv),
+                           lut_v2_pair(cur.vw[1][0] >> sh, tv), lut_v2_pair(cur.vw[1][1] >> sh, tv));
+        } else {
+          uint16_t hv[8];
+#pragma unroll
+          for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) hv[4 * q2 + j] = s_lutv[bits_at<VB>(cur.vw[q2], 8 * VB * j + VB * ci)];
+          Bv = from_halves(hv);
+        }
+        O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, Bv, O[nb], 0, 0, 0);
+        O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, Bv, O[nb], 0, 0, 0);
+      }
+    }
+  };
+
+  // ring of R fragments: R - 1 page pairs in flight while one is processed
+  for (int i = wave; i < npairs; i += R * kWaves) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int ii = i + r * kWaves;
+      if (ii >= npairs) break;
+      const int nx = ii + (R - 1) * kWaves;
+      if (nx < npairs) load_pair<D, KB, KPROD, VB>(a, s_pid, lo, p_begin + 2 * nx, p_begin, p_end, f[(r + R - 1) % R]);
+      process(f[r], ii);
     }
   }
 
-  float l_tot = l_part + __shfl_xor(l_part, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  const int64_t S = a.n_splits;
-  if (g4 == 0 && c < G) {
-    const int64_t bh = (int64_t)b * a.Hq + head0 + c;
-    a.part_ml[(bh * S + split) * 2] = m_run;
-    a.part_ml[(bh * S + split) * 2 + 1] = l_tot;
+  // ---- 4. merge the wavefronts of this work-group: rescale to the work-group max, then sum over the
+  //         waves in a fixed order (deterministic). Only rows < G are real query heads.
+  {
+    float l_tot = l_part + __shfl_xor(l_part, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (g4 == 0) {
+      s_m[wave][c] = m_run;
+      s_l[wave][c] = l_tot;
+    }
   }
+  __syncthreads();  // also: every wave is past its use of s_q / s_qs
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 4 * g4 + j;
     if (row < G) {
-      const int64_t bh = (int64_t)b * a.Hq + head0 + row;
+      float M = -INFINITY;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) a.part_o[(bh * S + split) * D + (D / 16) * c + nb] = O[nb][j];
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][row]);
+      const float e = (M == -INFINITY || s_m[wave][row] == -INFINITY) ? 0.f : fast_exp2(s_m[wave][row] - M);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) O[nb][j] *= e;
+    }
+  }
+  if (tid < G) {
+    const int row = tid;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][row]);
+    float L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+        if (s_m[w][row] != -INFINITY) L = fmaf(fast_exp2(s_m[w][row] - M), s_l[w][row], L);
+    }
+    s_rowm[row] = M;
+    s_rowl[row] = L;
+  }
+  // every wave deposits its real rows; one fixed-order pass sums them
+  constexpr int RMAX = (4 * QF) / (kWaves * D);  // rows that fit in the arena per wave (8)
+  float acc_out[(16 * D + NT - 1) / NT];         // this thread's merged elements (row-major over G x D)
+  if (G <= RMAX) {
+    float(*dep)[RMAX][D] = (float(*)[RMAX][D])arena;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 4 * g4 + j;
+      if (row < G) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) dep[wave][row][(D / 16) * c + nb] = O[nb][j];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < (16 * D + NT - 1) / NT; ++q) {
+      const int idx = tid + q * NT;
+      float t = 0.f;
+      if (idx < G * D) {
+        const int row = idx / D, k = idx % D;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) t += dep[w][row][k];
+      }
+      acc_out[q] = t;
+    }
+  } else {
+    float(*tree)[16][D] = (float(*)[16][D])arena;  // [kWaves / 2][16][D]
+#pragma unroll
+    for (int half = kWaves / 2; half >= 1; half >>= 1) {
+      if (wave >= half && wave < 2 * half) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) tree[wave - half][4 * g4 + j][(D / 16) * c + nb] = O[nb][j];
+      }
+      __syncthreads();
+      if (wave < half) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) O[nb][j] += tree[wave][4 * g4 + j][(D / 16) * c + nb];
+      }
+      __syncthreads();
+    }
+    if (wave == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) tree[0][4 * g4 + j][(D / 16) * c + nb] = O[nb][j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < (16 * D + NT - 1) / NT; ++q) {
+      const int idx = tid + q * NT;
+      acc_out[q] = idx < G * D ? tree[0][idx / D][idx % D] : 0.f;
+    }
+  }
+
+  // ---- 5. one run: finish here; several runs: write this run's partial for the combine kernel
+  const int64_t S = a.n_splits;
+  if (S > 1) {
+#pragma unroll
+    for (int q = 0; q < (16 * D + NT - 1) / NT; ++q) {
+      const int idx = tid + q * NT;
+      if (idx < G * D) {
+        const int row = idx / D, k = idx % D;
+        const int64_t bh = (int64_t)b * a.Hq + head0 + row;
+        a.part_o[(bh * S + split) * D + k] = acc_out[q];
+      }
+    }
+    if (tid < G) {
+      const int64_t bh = (int64_t)b * a.Hq + head0 + tid;
+      a.part_ml[(bh * S + split) * 2] = s_rowm[tid];
+      a.part_ml[(bh * S + split) * 2 + 1] = s_rowl[tid];
+    }
+    return;
+  }
+  __syncthreads();  // the deposit buffer is read before it becomes the output buffer
+  float(*fin)[D] = (float(*)[D])arena;
+#pragma unroll
+  for (int q = 0; q < (16 * D + NT - 1) / NT; ++q) {
+    const int idx = tid + q * NT;
+    if (idx < G * D) {
+      const int row = idx / D, k = idx % D;
+      const float L = s_rowl[row];
+      fin[row][k] = L > 0.f ? acc_out[q] / L : 0.f;
+    }
+  }
+  __syncthreads();
+  lds_wht<D, NT>(fin, G, tid);
+  {
+    const uint32_t *vsw = (const uint32_t *)(a.vcb + a.vo.signs);
+    for (int idx = tid; idx < G * D; idx += NT) {
+      const int row = idx / D, k = idx % D;
+      float o = fin[row][k] * (1.0f / D);
+      if ((vsw[k >> 5] >> (k & 31)) & 1u) o = -o;
+      a.out[((int64_t)b * a.Hq + head0 + row) * D + k] = o;
     }
   }
 }
 
-// ------------------------------------------------------------------------------------------------
-// combine
-// ------------------------------------------------------------------------------------------------
+// Merge of the runs of one (sequence, query head): log-sum-exp weights, weighted sum of the rotated value
+// sums, division by the total weight, then R_V^T (butterflies across one wavefront) and the fp32 row.
 template <int D>
-__global__ __launch_bounds__(D) void combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+  constexpr int NT = 256;
+  constexpr int ITEMS = D / 4;        // float4 columns of a row
+  constexpr int GROUPS = NT / ITEMS;  // runs are strided over this many thread groups
+  constexpr int PRE = 8;              // partial rows per thread loaded before the weights are known
   const int64_t bh = blockIdx.x;
-  const int i = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int S = a.n_splits;
-  __shared__ float v[D];
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_ml[(bh * S + s) * 2]);
-  float L = 0.f, acc = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float ms = a.part_ml[(bh * S + s) * 2];
-      if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - M);
-      L = fmaf(w, a.part_ml[(bh * S + s) * 2 + 1], L);
-      acc = fmaf(w, a.part_o[(bh * S + s) * D + i], acc);
+  __shared__ float s_w[kMlCap], s_lw[kMlCap];
+  __shared__ float4 red[NT];
+  __shared__ float row[D];
+  __shared__ float s_L;
+  const int k4 = tid % ITEMS, grp = tid / ITEMS;
+  const float4 *po = (const float4 *)(a.part_o + bh * S * D) + k4;
+  float4 pre[PRE];
+#pragma unroll
+  for (int q = 0; q < PRE; ++q) {
+    const int s2 = grp + q * GROUPS;
+    pre[q] = s2 < S ? po[(int64_t)s2 * ITEMS] : float4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int s2 = tid; s2 < S; s2 += NT) {
+    s_w[s2] = a.part_ml[(bh * S + s2) * 2];
+    s_lw[s2] = a.part_ml[(bh * S + s2) * 2 + 1];
+  }
+  __syncthreads();
+  if (tid < 64) {
+    float M = -INFINITY;
+    for (int s2 = lane; s2 < S; s2 += 64) M = fmaxf(M, s_w[s2]);
+#pragma unroll
+    for (int h = 1; h < 64; h <<= 1) M = fmaxf(M, __shfl_xor(M, h));
+    float L = 0.f;
+    for (int s2 = lane; s2 < S; s2 += 64) {
+      const float ms = s_w[s2];
+      const float e = (M == -INFINITY || ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
+      s_w[s2] = e;
+      L = fmaf(e, s_lw[s2], L);
+    }
+#pragma unroll
+    for (int h = 1; h < 64; h <<= 1) L += __shfl_xor(L, h);
+    if (lane == 0) s_L = L;
+  }
+  __syncthreads();
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < PRE; ++q) {
+    const int s2 = grp + q * GROUPS;
+    const float e = s2 < S ? s_w[s2] : 0.f;
+    acc.x = fmaf(e, pre[q].x, acc.x);
+    acc.y = fmaf(e, pre[q].y, acc.y);
+    acc.z = fmaf(e, pre[q].z, acc.z);
+    acc.w = fmaf(e, pre[q].w, acc.w);
+  }
+  for (int s2 = grp + PRE * GROUPS; s2 < S; s2 += GROUPS) {
+    const float e = s_w[s2];
+    const float4 v = po[(int64_t)s2 * ITEMS];
+    acc.x = fmaf(e, v.x, acc.x);
+    acc.y = fmaf(e, v.y, acc.y);
+    acc.z = fmaf(e, v.z, acc.z);
+    acc.w = fmaf(e, v.w, acc.w);
+  }
+  red[tid] = acc;
+  __syncthreads();
+  if (tid < ITEMS) {
+    float4 t = red[tid];
+    for (int gq = 1; gq < GROUPS; ++gq) {
+      const float4 u = red[gq * ITEMS + tid];
+      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+    }
+    const float inv = s_L > 0.f ? 1.0f / s_L : 0.f;
+    row[4 * tid] = t.x * inv;
+    row[4 * tid + 1] = t.y * inv;
+    row[4 * tid + 2] = t.z * inv;
+    row[4 * tid + 3] = t.w * inv;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // R_V^T = diag(s) H / sqrt(d), and the levels are in N(0,1) units (another 1 / sqrt(d))
+    float x0 = row[lane], x1 = D == 128 ? row[lane + 64] : 0.f;
+#pragma unroll
+    for (int h = 1; h < 64; h <<= 1) {
+      const float p0 = __shfl_xor(x0, h), p1 = __shfl_xor(x1, h);
+      x0 = (lane & h) ? (p0 - x0) : (x0 + p0);
+      x1 = (lane & h) ? (p1 - x1) : (x1 + p1);
+    }
+    if (D == 128) {
+      const float u = x0;
+      x0 = u + x1;
+      x1 = u - x1;
+    }
+    const uint32_t *sw = (const uint32_t *)(a.vcb + a.vo.signs);
+    x0 *= (1.0f / D);
+    if ((sw[lane >> 5] >> (lane & 31)) & 1u) x0 = -x0;
+    a.out[bh * D + lane] = x0;
+    if (D == 128) {
+      x1 *= (1.0f / D);
+      if ((sw[(lane + 64) >> 5] >> (lane & 31)) & 1u) x1 = -x1;
+      a.out[bh * D + lane + 64] = x1;
     }
   }
-  v[i] = L > 0.f ? acc / L : 0.f;
-  __syncthreads();
-  for (int hs = 1; hs < D; hs <<= 1) {
-    float u = v[i], w = v[i ^ hs];
-    __syncthreads();
-    v[i] = (i & hs) ? (w - u) : (u + w);
-    __syncthreads();
-  }
-  const tq_codebook_header *hv = (const tq_codebook_header *)a.vcb;
-  const uint32_t *sw = (const uint32_t *)(a.vcb + hv->signs_off);
-  float o = v[i] * (1.0f / D);
-  if ((sw[i >> 5] >> (i & 31)) & 1u) o = -o;
-  a.out[bh * D + i] = o;
 }
 
 template <int D, int KB, bool KPROD, int VB>
-void launch_split(const DecodeArgs &a, hipStream_t stream) {
+void launch(const DecodeArgs &a, hipStream_t stream) {
   dim3 grid(a.n_splits, a.Hkv, a.B);
-  hipLaunchKernelGGL((split_kernel<D, KB, KPROD, VB>), grid, dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<D, KB, KPROD, VB>), grid, dim3(64 * kWaves), 0, stream, a);
+  if (a.n_splits > 1) hipLaunchKernelGGL(combine_kernel<D>, dim3(a.B * a.Hq), dim3(256), 0, stream, a);
 }
 
 template <int D, int KB, bool KPROD>
 bool dispatch_v(int vb, const DecodeArgs &a, hipStream_t s) {
   switch (vb) {
-    case 1: launch_split<D, KB, KPROD, 1>(a, s); return true;
-    case 2: launch_split<D, KB, KPROD, 2>(a, s); return true;
-    case 3: launch_split<D, KB, KPROD, 3>(a, s); return true;
-    case 4: launch_split<D, KB, KPROD, 4>(a, s); return true;
-    case 8: launch_split<D, KB, KPROD, 8>(a, s); return true;
+    case 1: launch<D, KB, KPROD, 1>(a, s); return true;
+    case 2: launch<D, KB, KPROD, 2>(a, s); return true;
+    case 3: launch<D, KB, KPROD, 3>(a, s); return true;
+    case 4: launch<D, KB, KPROD, 4>(a, s); return true;
+    case 8: launch<D, KB, KPROD, 8>(a, s); return true;
   }
   return false;
 }
@@ -475,27 +905,17 @@ int launch_decode(const PageGeom &g, const DecodeWs &ws, const void *pages, int6
   a.scale_log2 = softmax_scale * kLog2e;
   a.kcb = (const unsigned char *)k_cb;
   a.vcb = (const unsigned char *)v_cb;
+  a.ko = g.kcb;
+  a.vo = g.vcb;
   unsigned char *w = (unsigned char *)workspace;
-  a.qrot = (float *)(w + ws.qrot_off);
-  a.qsk = (float *)(w + ws.qsk_off);
-  a.qscale = (float *)(w + ws.qscale_off);
   a.part_o = (float *)(w + ws.part_o_off);
   a.part_ml = (float *)(w + ws.part_ml_off);
   a.n_splits = ws.n_splits;
   a.pps = ws.pages_per_split;
   a.out = out;
-  const int bhq = batch * num_q_heads;
   const bool kprod = g.k_mode == TQ_PROD;
-  bool ok;
-  if (g.head_dim == 128) {
-    hipLaunchKernelGGL(prologue_kernel<128>, dim3(bhq), dim3(128), 0, stream, a);
-    ok = dispatch_k<128>(g.k_mse_bits, kprod, g.v_mse_bits, a, stream);
-    if (ok) hipLaunchKernelGGL(combine_kernel<128>, dim3(bhq), dim3(128), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(prologue_kernel<64>, dim3(bhq), dim3(64), 0, stream, a);
-    ok = dispatch_k<64>(g.k_mse_bits, kprod, g.v_mse_bits, a, stream);
-    if (ok) hipLaunchKernelGGL(combine_kernel<64>, dim3(bhq), dim3(64), 0, stream, a);
-  }
+  const bool ok = g.head_dim == 128 ? dispatch_k<128>(g.k_mse_bits, kprod, g.v_mse_bits, a, stream)
+                                    : dispatch_k<64>(g.k_mse_bits, kprod, g.v_mse_bits, a, stream);
   if (!ok) return TQ_ENOTSUP;
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
 }

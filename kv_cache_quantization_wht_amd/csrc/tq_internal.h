@@ -8,6 +8,14 @@
 
 namespace tq {
 
+// Byte offsets of the sections of a codebook blob; a pure function of (head_dim, bits, mode), so kernels
+// take them as arguments instead of reading the blob header first.
+struct BlobOffsets {
+  uint32_t levels, thresholds, signs, proj;
+  int qjl_rows;
+};
+BlobOffsets blob_offsets(int head_dim, int bits, int mode);
+
 // Everything a kernel needs to address one layer's page pool.
 struct PageGeom {
   int64_t page_bytes;
@@ -15,22 +23,25 @@ struct PageGeom {
   int64_t v_codes, v_norms, v_qjl, v_gamma;
   int head_dim, num_kv_heads;
   int k_mse_bits, k_mode, v_mse_bits, v_mode;
+  BlobOffsets kcb, vcb;
 };
+
 
 // Fills `g` from a validated layout; returns TQ_OK or TQ_EINVAL.
 int make_geom(const tq_layout *L, PageGeom *g);
 
-// Workspace carve-up of tq_decode_attention.
+// Workspace carve-up of tq_decode_attention (split partials, used when a sequence is cut into runs).
 struct DecodeWs {
   int n_splits;
   int pages_per_split;
-  size_t qrot_off;     // float [B][Hq][d]   rotated, 1/sqrt(d)-scaled query
-  size_t qsk_off;      // float [B][Hq][d]   sketch-domain query (prod K only)
-  size_t qscale_off;   // float [B][Hq][2]   power-of-two range factors for the fp16 split
-  size_t part_o_off;   // float [B][Hq][n_splits][d]
-  size_t part_ml_off;  // float [B][Hq][n_splits][2]
+  size_t part_o_off;    // float [B][Hq][n_splits][d]   un-normalised rotated value sums
+  size_t part_ml_off;   // float [B][Hq][n_splits][2]   (running max in log2 units, sum of weights)
   size_t total;
 };
+
+// Limits of one decode launch: page ids of one run held in LDS, runs merged by one combine work-group.
+constexpr int kDecodePidCap = 4096;
+constexpr int kDecodeMaxSplits = 2048;
 
 int plan_decode(const PageGeom &g, int batch, int num_q_heads, int max_pages_per_seq,
                 int pages_per_split, DecodeWs *ws);

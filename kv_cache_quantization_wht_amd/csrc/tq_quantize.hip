@@ -1,7 +1,7 @@
 // Quantize-on-write ("Closing - The Three-Step Summary", Steps 1-3): for every K and V vector,
 //   n = ||x||, y' = H (s * x) / n   (the rotated unit vector in N(0,1) units),
-//   code_i = #{j : y'_i >= t_j}     (Gaussian Lloyd-Max thresholds, midpoints of the fp16 levels),
-//   pack the b-bit codes, store n as fp16, and in prod mode also
+//   idx_i = #{j : y'_i >= t_j}      (Gaussian Lloyd-Max thresholds, midpoints of the fp16 levels),
+//   code_i = sign-magnitude form of idx_i, pack the b-bit codes, store n as fp16, and in prod mode also
 //   r = (y' - level[code]) / sqrt(d), gamma = ||r||, z_j = [(S r)_j >= 0].
 // One vector is handled by d/8 lanes that each own 8 consecutive coordinates: the three lowest
 // Walsh-Hadamard stages run in registers, the others exchange values between lanes. A lane's 8 codes
@@ -24,11 +24,35 @@ struct QuantArgs {
   const int64_t *slots;
   int64_t n_tok;
   const unsigned char *cb[2];
+  BlobOffsets cbo[2];  // section offsets inside the K and V codebook blobs
   int64_t codes_off[2], norms_off[2], qjl_off[2], gamma_off[2];
   int bits[2], mode[2];
   int H;
   int dtype;
 };
+
+// Eight consecutive elements of an input row (16-byte aligned) widened to fp32.
+__device__ __forceinline__ void load8(const void *p, int64_t i, int dtype, float *x) {
+  if (dtype == TQ_F32) {
+    const float4 u = *(const float4 *)((const float *)p + i);
+    const float4 w = *(const float4 *)((const float *)p + i + 4);
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+    x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
+  } else {
+    const uint4 u = *(const uint4 *)((const uint16_t *)p + i);
+    const uint32_t d[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (dtype == TQ_BF16) {
+        x[2 * k] = bf16_bits_to_float((uint16_t)(d[k] & 0xFFFF));
+        x[2 * k + 1] = bf16_bits_to_float((uint16_t)(d[k] >> 16));
+      } else {
+        x[2 * k] = half_bits_to_float((uint16_t)(d[k] & 0xFFFF));
+        x[2 * k + 1] = half_bits_to_float((uint16_t)(d[k] >> 16));
+      }
+    }
+  }
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
@@ -36,7 +60,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   constexpr int VPB = 256 / LANES;
   const int which = blockIdx.y;  // 0 = K, 1 = V
   const unsigned char *cb = a.cb[which];
-  const tq_codebook_header *hdr = (const tq_codebook_header *)cb;
+  const BlobOffsets bo = a.cbo[which];
   const int b = a.bits[which];
   const int mode = a.mode[which];
   const int nl = 1 << b;
@@ -44,10 +68,6 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   __shared__ float s_th[256];
   __shared__ float s_lv[256];
   __shared__ float s_r[VPB][D];
-  for (int i = threadIdx.x; i < nl - 1; i += 256) s_th[i] = ((const float *)(cb + hdr->thresholds_off))[i];
-  for (int i = threadIdx.x; i < nl; i += 256)
-    s_lv[i] = half_bits_to_float(((const uint16_t *)(cb + hdr->levels_off))[i]);
-  __syncthreads();
 
   const int lane = threadIdx.x % LANES;
   const int vl = threadIdx.x / LANES;
@@ -55,13 +75,19 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   const bool active = vid < a.n_tok * a.H;
   const int64_t tok = active ? vid / a.H : 0;
   const int h = active ? (int)(vid % a.H) : 0;
-  const int64_t slot = active ? a.slots[tok] : -1;
-  const bool valid = active && slot >= 0 && slot < a.num_slots;
 
+  // every global read issued before the first wait: slot, the lane's 8 inputs, its 8 sign bits, tables
+  const int64_t slot = active ? a.slots[tok] : -1;
   float x[8];
-  const int64_t base = tok * a.stride[which] + (int64_t)h * D + 8 * lane;
+  if (active) load8(a.in[which], tok * a.stride[which] + (int64_t)h * D + 8 * lane, a.dtype, x);
+  else
 #pragma unroll
-  for (int k = 0; k < 8; ++k) x[k] = active ? load_elem(a.in[which], base + k, a.dtype) : 0.f;
+    for (int k = 0; k < 8; ++k) x[k] = 0.f;
+  const uint32_t sword = ((const uint32_t *)(cb + bo.signs))[(8 * lane) >> 5];
+  for (int i = threadIdx.x; i < nl - 1; i += 256) s_th[i] = ((const float *)(cb + bo.thresholds))[i];
+  for (int i = threadIdx.x; i < nl; i += 256) s_lv[i] = half_bits_to_float(((const uint16_t *)(cb + bo.levels))[i]);
+  const bool valid = active && slot >= 0 && slot < a.num_slots;
+  __syncthreads();
 
   float ss = 0.f;
 #pragma unroll
@@ -71,8 +97,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   const float n = sqrtf(ss);
   const float inv = n > 0.f ? 1.0f / n : 0.f;
 
-  const uint32_t *sw = (const uint32_t *)(cb + hdr->signs_off);
-  const uint32_t sbits = (sw[(8 * lane) >> 5] >> ((8 * lane) & 31)) & 0xFFu;
+  const uint32_t sbits = (sword >> ((8 * lane) & 31)) & 0xFFu;
 #pragma unroll
   for (int k = 0; k < 8; ++k)
     if ((sbits >> k) & 1u) x[k] = -x[k];
@@ -97,15 +122,19 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     }
   }
 
-  int code[8];
+  // Lloyd-Max index (ties to the upper cell), then the stored sign-magnitude code: the top bit marks
+  // the non-negative half, the low bits count the rank away from zero.
+  int idx[8], code[8];
   float y[8];
+  const int half = nl >> 1;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     y[k] = x[k] * inv;
     int c = 0;
     for (int s = nl >> 1; s > 0; s >>= 1)
       if (y[k] >= s_th[c + s - 1]) c += s;
-    code[k] = c;
+    idx[k] = c;
+    code[k] = c >= half ? c : half - 1 - c;
   }
 
   const int64_t page = valid ? slot / TQ_PAGE_TOKENS : 0;
@@ -136,14 +165,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     float g2 = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      r[k] = (y[k] - s_lv[code[k]]) * inv_sqrt_d;
+      r[k] = (y[k] - s_lv[idx[k]]) * inv_sqrt_d;
       g2 = fmaf(r[k], r[k], g2);
       s_r[vl][8 * lane + k] = r[k];
     }
 #pragma unroll
     for (int o = 1; o < LANES; o <<= 1) g2 += __shfl_xor(g2, o, LANES);
     __syncthreads();
-    const float *S = (const float *)(cb + hdr->proj_off);
+    const float *S = (const float *)(cb + bo.proj);
     uint32_t zbits = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -178,6 +207,8 @@ int launch_quantize(const PageGeom &g, void *pages, int64_t num_pages, const voi
   a.n_tok = n_tok;
   a.cb[0] = (const unsigned char *)k_cb;
   a.cb[1] = (const unsigned char *)v_cb;
+  a.cbo[0] = g.kcb;
+  a.cbo[1] = g.vcb;
   a.codes_off[0] = g.k_codes;
   a.norms_off[0] = g.k_norms;
   a.qjl_off[0] = g.k_qjl;

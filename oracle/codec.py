@@ -21,9 +21,12 @@ Readings adopted where the pages are silent (each is listed in the design notes)
   * the stored codebook levels are the Lloyd-Max levels for N(0,1) rounded to fp16
     (the 1/sqrt(d) factor is applied in arithmetic), and the decision thresholds are
     the exact midpoints of those stored levels;
-  * the code of coordinate i is the number of thresholds t_j with y'_i >= t_j, where
-    y' = sqrt(d) * R u is the rotated unit vector in N(0,1) units rounded to fp32
+  * the Lloyd-Max index of coordinate i is the number of thresholds t_j with y'_i >= t_j,
+    where y' = sqrt(d) * R u is the rotated unit vector in N(0,1) units rounded to fp32
     (ties go to the upper cell);
+  * the stored b-bit code is the sign-magnitude form of that index (the codebook is symmetric):
+    the top bit is set for the non-negative half, the low b-1 bits count the level's rank away
+    from zero (index L/2 + r -> code L/2 + r; index L/2 - 1 - r -> code r, L = 2^b);
   * prod mode: r = y - yhat in the rotated unit-vector domain (y = R u,
     yhat_i = level[code_i] / sqrt(d)); gamma = ||r|| stored as fp16; the sketch bit
     z_j = [(S r)_j >= 0] for the m = d rows of a Gaussian matrix S;
@@ -48,6 +51,18 @@ SUPPORTED_BITS = (1, 2, 3, 4, 8)
 def mse_bits(bits: int, mode: int) -> int:
     """Bits of the Lloyd-Max index: b for MSE mode, b - 1 for prod mode."""
     return bits - 1 if mode == PROD else bits
+
+
+def stored_code(index, b: int) -> np.ndarray:
+    """Sign-magnitude code of Lloyd-Max indices (ascending levels 0 .. 2^b - 1)."""
+    idx = np.asarray(index, dtype=np.int64)
+    half = (1 << b) // 2
+    return np.where(idx >= half, idx, half - 1 - idx)
+
+
+def level_index(code, b: int) -> np.ndarray:
+    """Inverse of stored_code (the map is an involution on each half)."""
+    return stored_code(code, b)
 
 
 def fp16_round(x) -> np.ndarray:
@@ -103,7 +118,7 @@ def make_codebook(head_dim: int, bits: int, mode: int, sign_words, S=None) -> Co
 
 @dataclass
 class Encoded:
-    codes: np.ndarray  # (N, d) int64 Lloyd-Max indices
+    codes: np.ndarray  # (N, d) int64 stored (sign-magnitude) codes
     norm16: np.ndarray  # (N,) fp64 holding fp16 values
     norm: np.ndarray  # (N,) unrounded fp64 norms (for parity diagnostics)
     y: np.ndarray  # (N, d) rotated unit vectors R u (N(0,1/d) units)
@@ -122,10 +137,10 @@ def encode(x, cb: Codebook) -> Encoded:
     u = np.where(n[:, None] > 0, x / safe[:, None], 0.0)
     y = rotation.rotate(u, cb.sign_words)
     y32 = (y * math.sqrt(d)).astype(np.float32).astype(np.float64)
-    codes = np.searchsorted(cb.thresholds, y32, side="right").astype(np.int64)
-    enc = Encoded(codes=codes, norm16=fp16_round(n), norm=n, y=y)
+    index = np.searchsorted(cb.thresholds, y32, side="right").astype(np.int64)
+    enc = Encoded(codes=stored_code(index, cb.mse_bits), norm16=fp16_round(n), norm=n, y=y)
     if cb.mode == PROD:
-        yhat = cb.levels16[codes] / math.sqrt(d)
+        yhat = cb.levels16[index] / math.sqrt(d)
         r = y - yhat
         g = np.sqrt(np.sum(r * r, axis=1))
         Sr = r @ cb.S.T
@@ -142,7 +157,7 @@ def code_boundary_distance(enc: Encoded, cb: Codebook) -> np.ndarray:
 def dequantize_rotated(codes, norm16, cb: Codebook, gamma16=None, qjl=None) -> np.ndarray:
     """n * (yhat + [prod] gamma * sqrt(pi/2)/m * S^T (2z - 1)) in the rotated domain (N, d)."""
     d = cb.head_dim
-    yh = cb.levels16[np.asarray(codes)] / math.sqrt(d)
+    yh = cb.levels16[level_index(codes, cb.mse_bits)] / math.sqrt(d)
     if cb.mode == PROD:
         pm = 2.0 * np.asarray(qjl, dtype=np.float64) - 1.0
         yh = yh + (np.asarray(gamma16)[:, None] * math.sqrt(math.pi / 2.0) / cb.m) * (pm @ cb.S)

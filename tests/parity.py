@@ -53,7 +53,8 @@ def compare_records(got: dict, enc: codec.Encoded, cb: codec.Codebook, rep: Repo
     d = cb.head_dim
     mism = got["codes"] != enc.codes
     dist = codec.code_boundary_distance(enc, cb)
-    bad = mism & ~((dist <= CODE_BAND) & (np.abs(got["codes"] - enc.codes) == 1))
+    step = np.abs(codec.level_index(got["codes"], cb.mse_bits) - codec.level_index(enc.codes, cb.mse_bits))
+    bad = mism & ~((dist <= CODE_BAND) & (step == 1))
     assert not bad.any(), f"{tag}: {int(bad.sum())} code mismatches outside the 1e-6 band; first at {np.argwhere(bad)[:5]}"
     rep[tag + "_codes"] = int(enc.codes.size)
     rep[tag + "_code_flips"] = int(mism.sum())

@@ -276,6 +276,35 @@ def check_layout_positions():
     assert list(pool[koff:koff + 32]) == list(codec.pack_codes(enc.codes, 4)[0])
 
 
+def check_code_map_by_hand():
+    """Sign-magnitude codes: the top bit marks the non-negative half, the rest count the rank from zero."""
+    assert list(codec.stored_code(np.arange(4), 2)) == [1, 0, 2, 3]
+    assert list(codec.stored_code(np.arange(16), 4)) == [7, 6, 5, 4, 3, 2, 1, 0, 8, 9, 10, 11, 12, 13, 14, 15]
+    assert list(codec.stored_code([0, 1], 1)) == [0, 1]
+    for b in (1, 2, 3, 4, 8):
+        i = np.arange(1 << b)
+        assert np.array_equal(codec.level_index(codec.stored_code(i, b), b), i)
+
+
+def check_encode_known_cells(d=64, seed=6):
+    """A vector built so that its rotated coordinates sit exactly on chosen levels encodes to the codes
+    read off by hand: level k of the ascending table -> sign-magnitude code of k."""
+    sw = kvsynth.rotation_signs(seed, d)
+    for b in (2, 3, 4):
+        cb = codec.make_codebook(d, b, codec.MSE, sw)
+        L = 1 << b
+        yp = np.empty(d)
+        yp[:L] = cb.levels16  # coordinates 0..L-1 sit on the levels (cell centres)
+        rest = d - L
+        fill = math.sqrt((d - np.sum(yp[:L] ** 2)) / rest)  # so that ||y'|| = sqrt(d), i.e. y = y'/sqrt(d) is a unit vector
+        yp[L:] = fill * np.where(np.arange(rest) % 2 == 0, 1.0, -1.0)
+        x = 3.0 * rotation.unrotate((yp / math.sqrt(d))[None, :], sw)
+        e = codec.encode(x, cb)
+        half = L // 2
+        want = [half - 1 - k if k < half else k for k in range(L)]
+        assert list(e.codes[0, :L]) == want, (b, list(e.codes[0, :L]), want)
+
+
 def check_zero_vector():
     """A zero vector stores norm 0 and the first non-negative level (y = 0 lies on the middle threshold)."""
     for b in (1, 2, 3, 4, 8):

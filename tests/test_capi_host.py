@@ -136,6 +136,8 @@ def test_launch_argument_errors_need_no_gpu():
                                    8, 16, None) == -2  # workspace too small
     assert lib.tq_decode_attention(ctypes.byref(L), None, 4, 16, 1, 1, 32, 16, 10, 16, 0.1, 4, 16, 16, 16,
                                    1 << 30, 16, None) == -1
+    assert lib.tq_decode_attention(ctypes.byref(L), 16, 4, 16, 1, 1, 32, 16, 10, 16, -0.1, 4, 16, 16, 16,
+                                   1 << 30, 16, None) == -1  # negative softmax scale
     assert lib.tq_decode_attention(ctypes.byref(L), 16, 1, 16, 1, 0, 32, None, 10, None, 0.1, 4, None, None,
                                    None, 0, None, None) == 0  # empty batch
 

@@ -115,3 +115,10 @@ def test_large_key_norms():
     scale = 1 / math.sqrt(128)
     out = run_gpu(c, scale)
     assert parity.attention_error(out, run_ref(c, scale)) <= parity.ATTN_TOL
+
+
+def test_zero_softmax_scale_is_uniform_average():
+    """scale 0: every cached token gets the same weight (mean of the dequantized values)."""
+    c = build(2, 128, 8, 2, [130, 47], 4, 0, 2, 0, seed=31)
+    out = run_gpu(c, 0.0)
+    assert parity.attention_error(out, run_ref(c, 0.0)) <= parity.ATTN_TOL

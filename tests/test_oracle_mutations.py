@@ -149,3 +149,8 @@ def test_mutant_norm_scaled(monkeypatch, scale):
 
     monkeypatch.setattr(codec, "encode", scaled)
     assert _caught(pins.check_vector_mse)
+
+
+def test_mutant_codes_stored_as_plain_index(monkeypatch):
+    monkeypatch.setattr(codec, "stored_code", lambda index, b: np.asarray(index, dtype=np.int64))
+    assert _caught(pins.check_encode_known_cells, pins.check_code_map_by_hand)
