@@ -160,14 +160,20 @@ def main():
     out = torch.empty(1, Hq, d, dtype=torch.float32, device=dev)
     scale = wl.softmax_scale
 
-    def step(i, ev_pair=None):
+    def step(i, ev=None):
+        # one decode step: append the new token's K/V, then decode attention in its two passes
+        # (tq_decode_partial + tq_decode_combine is exactly tq_decode_attention)
         tq.quantize_kv(layout, pages, k_new[i:i + 1], v_new[i:i + 1], step_slots[i], kcb, vcb)
-        if ev_pair is not None:
-            ev_pair[0].record()
-        tq.decode_attention(layout, pages, qs[i], page_tables[step_copy[i]], step_lens[i], scale, kcb, vcb,
-                            workspace=ws, out=out)
-        if ev_pair is not None:
-            ev_pair[1].record()
+        if ev is not None:
+            ev[0].record()
+        tq.decode_partial(layout, pages, qs[i], page_tables[step_copy[i]], step_lens[i], scale, kcb, vcb, ws,
+                          out=out)
+        if ev is not None:
+            ev[1].record()
+        tq.decode_combine(layout, pages, qs[i], page_tables[step_copy[i]], step_lens[i], scale, kcb, vcb, ws,
+                          out=out)
+        if ev is not None:
+            ev[2].record()
 
     for i in range(W):
         step(i)
@@ -200,35 +206,51 @@ def main():
     bytes_timed = float(np.sum(step_bytes[W:]))
     value = bytes_timed / elapsed / 1e9
 
-    # ---- decode-kernel duration from HIP events around each decode launch (same steps, same stream)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    kmode = mode
-    try:
-        if graph is None:
-            raise RuntimeError("eager")
-        g2 = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g2):
-            for j, i in enumerate(range(W, total_steps)):
-                step(i, evs[j])
-        g2.replay()
+    # ---- split-K kernel duration from HIP events on the launch stream. Events recorded inside a captured
+    #      graph are not timed on this platform, so the K tq_decode_partial launches of the timed steps are
+    #      captured on their own (no other kernel between them) and one event pair brackets the replay:
+    #      average duration = elapsed / K. The same is done for the K tq_decode_combine launches.
+    def replay_avg(fn):
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gph):
+            for i in range(W, total_steps):
+                fn(i)
+        gph.replay()  # warm
         torch.cuda.synchronize()
-        durs = np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / K
+
+    def partial_only(i):
+        tq.decode_partial(layout, pages, qs[i], page_tables[step_copy[i]], step_lens[i], scale, kcb, vcb, ws, out=out)
+
+    def combine_only(i):
+        tq.decode_combine(layout, pages, qs[i], page_tables[step_copy[i]], step_lens[i], scale, kcb, vcb, ws, out=out)
+
+    kmode = "graph of the K launches, one event pair"
+    try:
+        durs = np.array([replay_avg(partial_only)])
+        comb = np.array([replay_avg(combine_only)])
     except Exception as e:  # noqa: BLE001
+        log(f"graph timing unavailable ({e!r}); events around eager launches")
         kmode = "eager+sleep"
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)]
         if hasattr(torch.cuda, "_sleep"):
             torch.cuda._sleep(50_000_000)  # keep the GPU busy while every launch is queued
         for j, i in enumerate(range(W, total_steps)):
             step(i, evs[j])
         torch.cuda.synchronize()
-        durs = np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3
-        if not isinstance(e, RuntimeError):
-            log(f"events in graph unavailable ({e!r})")
+        durs = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+        comb = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
     kern_s = float(np.mean(durs))
     alg_per_launch = float(np.mean(step_bytes[W:]))
     achieved = alg_per_launch / kern_s / 1e9
     traffic = load_traffic(alg_per_launch)
-    log(f"step {ms_per_step * 1e3:.2f} us ({mode}); decode kernel {kern_s * 1e6:.2f} us ({kmode}); "
-        f"{alg_per_launch / 1e6:.2f} MB/launch -> {achieved:.0f} GB/s")
+    log(f"step {ms_per_step * 1e3:.2f} us ({mode}); split-K decode kernel {kern_s * 1e6:.2f} us, combine "
+        f"{float(np.mean(comb)) * 1e6:.2f} us ({kmode}); {alg_per_launch / 1e6:.2f} MB/launch -> {achieved:.0f} GB/s")
 
     result = {
         "metric": "decode-attn compressed-KV GB/s (% of HBM peak); KV quantize vectors/s",
@@ -250,8 +272,9 @@ def main():
         "quantize_vectors_per_s": round(quant_vps, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "tq_decode_attention", "bytes_per_launch": round(alg_per_launch),
-                     "avg_launch_us": round(kern_s * 1e6, 3), "timing": kmode},
+                     "kernel": "decode_kernel<128,4,false,2> (tq_decode_partial)",
+                     "bytes_per_launch": round(alg_per_launch), "avg_launch_us": round(kern_s * 1e6, 3),
+                     "combine_avg_us": round(float(np.mean(comb)) * 1e6, 3), "timing": kmode},
         "cpu_baseline": None,
     }
 

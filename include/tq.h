@@ -18,6 +18,9 @@
  *                       Integration Is a Kernel Problem"), with scores and value sums formed in the
  *                       rotated domain and one inverse rotation per output ("Closing - The
  *                       Three-Step Summary", Step 1: the rotation keeps inner products).
+ *   tq_decode_partial, tq_decode_combine
+ *                       the two passes of tq_decode_attention, callable one by one: the split-K
+ *                       scan over the pages, then the merge of the runs and the inverse rotation.
  *
  * Conventions for every call:
  *   - Returns TQ_OK (0) or a negative TQ_E* status; never aborts, never allocates device memory.
@@ -185,6 +188,26 @@ int tq_decode_attention(const tq_layout *layout, const void *pages, int64_t num_
                         float softmax_scale, int pages_per_split, const void *k_cb,
                         const void *v_cb, void *workspace, size_t workspace_bytes, float *out,
                         void *stream);
+
+/* The two passes of tq_decode_attention. Called in this order on one stream with the same arguments,
+ * they produce exactly the bytes tq_decode_attention produces (which is this pair of calls).
+ *   tq_decode_partial  the split-K scan: every work-group reads one run of pages of one (sequence, KV
+ *                      head) and writes its (max, sum of weights, rotated value sums) to `workspace`;
+ *                      when the plan has a single run per sequence it finishes the rows into `out`.
+ *   tq_decode_combine  merges the runs of each (sequence, query head) with log-sum-exp weights and
+ *                      applies the inverse rotation into `out`; launches nothing when the plan has a
+ *                      single run per sequence.
+ * Argument rules and errors as for tq_decode_attention. */
+int tq_decode_partial(const tq_layout *layout, const void *pages, int64_t num_pages, const void *q,
+                      int q_dtype, int batch, int num_q_heads, const int32_t *page_table,
+                      int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
+                      int pages_per_split, const void *k_cb, const void *v_cb, void *workspace,
+                      size_t workspace_bytes, float *out, void *stream);
+int tq_decode_combine(const tq_layout *layout, const void *pages, int64_t num_pages, const void *q,
+                      int q_dtype, int batch, int num_q_heads, const int32_t *page_table,
+                      int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
+                      int pages_per_split, const void *k_cb, const void *v_cb, void *workspace,
+                      size_t workspace_bytes, float *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ _LIB = None
 
 C_SYMBOLS = (
     "tq_strerror", "tq_codebook_bytes", "tq_build_codebook", "tq_page_layout", "tq_quantize_kv",
-    "tq_decode_workspace_bytes", "tq_decode_attention",
+    "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_partial", "tq_decode_combine",
 )
 
 
@@ -60,6 +60,10 @@ def _lib():
         lib.tq_quantize_kv.argtypes = [ctypes.POINTER(_Layout), vp, i64, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp]
         lib.tq_decode_workspace_bytes.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32, i32, ctypes.POINTER(sz)]
         lib.tq_decode_attention.argtypes = [ctypes.POINTER(_Layout), vp, i64, vp, i32, i32, i32, vp, i32, vp,
+                                            ctypes.c_float, i32, vp, vp, vp, sz, vp, vp]
+        lib.tq_decode_partial.argtypes = [ctypes.POINTER(_Layout), vp, i64, vp, i32, i32, i32, vp, i32, vp,
+                                            ctypes.c_float, i32, vp, vp, vp, sz, vp, vp]
+        lib.tq_decode_combine.argtypes = [ctypes.POINTER(_Layout), vp, i64, vp, i32, i32, i32, vp, i32, vp,
                                             ctypes.c_float, i32, vp, vp, vp, sz, vp, vp]
         for name in C_SYMBOLS:
             getattr(lib, name).restype = ctypes.c_char_p if name == "tq_strerror" else ctypes.c_int
@@ -173,9 +177,8 @@ def decode_workspace_bytes(layout: Layout, batch: int, num_q_heads: int, max_pag
     return out.value
 
 
-def decode_attention(layout: Layout, pages, q, page_table, seq_lens, softmax_scale, k_cb, v_cb,
-                     workspace=None, out=None, pages_per_split: int = 0, stream=None):
-    """Decode attention for q [batch, num_q_heads, head_dim]; returns fp32 out of the same shape."""
+def _decode_call(entry: str, layout: Layout, pages, q, page_table, seq_lens, softmax_scale, k_cb, v_cb,
+                 workspace, out, pages_per_split, stream):
     import torch
 
     _need(pages, "pages", torch.uint8)
@@ -192,6 +195,8 @@ def decode_attention(layout: Layout, pages, q, page_table, seq_lens, softmax_sca
     maxp = page_table.shape[1]
     need = decode_workspace_bytes(layout, B, Hq, maxp, pages_per_split)
     if workspace is None:
+        if entry != "tq_decode_attention":
+            raise ValueError(f"{entry} needs the caller's workspace (shared by the two passes)")
         workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty(B, Hq, layout.head_dim, dtype=torch.float32, device=q.device)
@@ -200,9 +205,30 @@ def decode_attention(layout: Layout, pages, q, page_table, seq_lens, softmax_sca
         raise ValueError("out must be a contiguous fp32 tensor shaped like q")
     page_bytes = page_layout(layout)["page_bytes"]
     num_pages = pages.numel() // page_bytes
-    _check(_lib().tq_decode_attention(ctypes.byref(layout.c()), pages.data_ptr(), num_pages, q.data_ptr(),
-                                      _dtype_code(q), B, Hq, page_table.data_ptr(), maxp, seq_lens.data_ptr(),
-                                      float(softmax_scale), pages_per_split, k_cb.data_ptr(), v_cb.data_ptr(),
-                                      workspace.data_ptr(), workspace.numel(), out.data_ptr(), _stream(stream)),
-           "tq_decode_attention")
+    _check(getattr(_lib(), entry)(ctypes.byref(layout.c()), pages.data_ptr(), num_pages, q.data_ptr(),
+                                  _dtype_code(q), B, Hq, page_table.data_ptr(), maxp, seq_lens.data_ptr(),
+                                  float(softmax_scale), pages_per_split, k_cb.data_ptr(), v_cb.data_ptr(),
+                                  workspace.data_ptr(), workspace.numel(), out.data_ptr(), _stream(stream)),
+           entry)
     return out
+
+
+def decode_attention(layout: Layout, pages, q, page_table, seq_lens, softmax_scale, k_cb, v_cb,
+                     workspace=None, out=None, pages_per_split: int = 0, stream=None):
+    """Decode attention for q [batch, num_q_heads, head_dim]; returns fp32 out of the same shape."""
+    return _decode_call("tq_decode_attention", layout, pages, q, page_table, seq_lens, softmax_scale, k_cb, v_cb,
+                        workspace, out, pages_per_split, stream)
+
+
+def decode_partial(layout: Layout, pages, q, page_table, seq_lens, softmax_scale, k_cb, v_cb, workspace,
+                   out=None, pages_per_split: int = 0, stream=None):
+    """First pass of decode_attention (split-K scan into ``workspace``); same arguments."""
+    return _decode_call("tq_decode_partial", layout, pages, q, page_table, seq_lens, softmax_scale, k_cb, v_cb,
+                        workspace, out, pages_per_split, stream)
+
+
+def decode_combine(layout: Layout, pages, q, page_table, seq_lens, softmax_scale, k_cb, v_cb, workspace,
+                   out=None, pages_per_split: int = 0, stream=None):
+    """Second pass of decode_attention (merge of the runs, inverse rotation into ``out``); same arguments."""
+    return _decode_call("tq_decode_combine", layout, pages, q, page_table, seq_lens, softmax_scale, k_cb, v_cb,
+                        workspace, out, pages_per_split, stream)

@@ -27,11 +27,14 @@ COMMON = [
     "-Wno-unused-command-line-argument",
 ]
 SOURCES = ["tq_capi.cpp", "tq_quantize.hip", "tq_decode.hip"]
+# decode: no NaN reaches a max or compare on the product path (masked scores are finite), so the
+# NaN-quieting copies in front of every max are dropped
+EXTRA = {"tq_decode.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -367,12 +367,11 @@ int tq_decode_workspace_bytes(const tq_layout *layout, int batch, int num_q_head
   return TQ_OK;
 }
 
-int tq_decode_attention(const tq_layout *layout, const void *pages, int64_t num_pages,
-                        const void *q, int q_dtype, int batch, int num_q_heads,
-                        const int32_t *page_table, int max_pages_per_seq, const int32_t *seq_lens,
-                        float softmax_scale, int pages_per_split, const void *k_cb,
-                        const void *v_cb, void *workspace, size_t workspace_bytes, float *out,
-                        void *stream) {
+static int decode_passes(const tq_layout *layout, const void *pages, int64_t num_pages, const void *q,
+                         int q_dtype, int batch, int num_q_heads, const int32_t *page_table,
+                         int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
+                         int pages_per_split, const void *k_cb, const void *v_cb, void *workspace,
+                         size_t workspace_bytes, float *out, int passes, void *stream) {
   tq::PageGeom g;
   int st = tq::make_geom(layout, &g);
   if (st) return st;
@@ -389,8 +388,39 @@ int tq_decode_attention(const tq_layout *layout, const void *pages, int64_t num_
   if (st) return st;
   if (workspace_bytes < ws.total) return TQ_ENOSPC;
   return tq::launch_decode(g, ws, pages, num_pages, q, q_dtype, batch, num_q_heads, page_table,
-                           max_pages_per_seq, seq_lens, softmax_scale, k_cb, v_cb, workspace, out,
+                           max_pages_per_seq, seq_lens, softmax_scale, k_cb, v_cb, workspace, out, passes,
                            (hipStream_t)stream);
+}
+
+int tq_decode_attention(const tq_layout *layout, const void *pages, int64_t num_pages,
+                        const void *q, int q_dtype, int batch, int num_q_heads,
+                        const int32_t *page_table, int max_pages_per_seq, const int32_t *seq_lens,
+                        float softmax_scale, int pages_per_split, const void *k_cb,
+                        const void *v_cb, void *workspace, size_t workspace_bytes, float *out,
+                        void *stream) {
+  return decode_passes(layout, pages, num_pages, q, q_dtype, batch, num_q_heads, page_table, max_pages_per_seq,
+                       seq_lens, softmax_scale, pages_per_split, k_cb, v_cb, workspace, workspace_bytes, out,
+                       tq::kPassScan | tq::kPassCombine, stream);
+}
+
+int tq_decode_partial(const tq_layout *layout, const void *pages, int64_t num_pages, const void *q,
+                      int q_dtype, int batch, int num_q_heads, const int32_t *page_table,
+                      int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
+                      int pages_per_split, const void *k_cb, const void *v_cb, void *workspace,
+                      size_t workspace_bytes, float *out, void *stream) {
+  return decode_passes(layout, pages, num_pages, q, q_dtype, batch, num_q_heads, page_table, max_pages_per_seq,
+                       seq_lens, softmax_scale, pages_per_split, k_cb, v_cb, workspace, workspace_bytes, out,
+                       tq::kPassScan, stream);
+}
+
+int tq_decode_combine(const tq_layout *layout, const void *pages, int64_t num_pages, const void *q,
+                      int q_dtype, int batch, int num_q_heads, const int32_t *page_table,
+                      int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
+                      int pages_per_split, const void *k_cb, const void *v_cb, void *workspace,
+                      size_t workspace_bytes, float *out, void *stream) {
+  return decode_passes(layout, pages, num_pages, q, q_dtype, batch, num_q_heads, page_table, max_pages_per_seq,
+                       seq_lens, softmax_scale, pages_per_split, k_cb, v_cb, workspace, workspace_bytes, out,
+                       tq::kPassCombine, stream);
 }
 
 }  // extern "C"

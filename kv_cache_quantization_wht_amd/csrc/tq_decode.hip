@@ -20,6 +20,8 @@
 //      its (max, sum, O) partial and a second, small kernel merges the runs and finishes the rows.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "tq_common.h"
 #include "tq_internal.h"
 
@@ -48,6 +50,7 @@ struct DecodeArgs {
   float *part_o, *part_ml;
   int n_splits, pps;
   float *out;
+  int passes;  // kPassScan and/or kPassCombine
 };
 
 // Largest power of two sigma with max|x| * sigma < 256 (1 if x is all zero).
@@ -182,8 +185,8 @@ template <int D, int KB, bool KPROD, int VB>
 struct Frag {
   static constexpr int KCH = D / 4 * KB / 8;  // K code bytes per lane per token
   static constexpr int VCH = 4 * VB;          // V code bytes per lane per page
-  static constexpr int KW = (KCH + 3) / 4 + 1;
-  static constexpr int VW = VCH / 4 + 1;
+  static constexpr int KW = (KCH + 3) / 4;
+  static constexpr int VW = VCH / 4;
   uint32_t kw[2][KW];
   uint32_t vw[2][VW];
   uint2 nk[2], nv[2];
@@ -224,12 +227,10 @@ __device__ __forceinline__ void load_pair(const DecodeArgs &a, const int *pid, c
     const bool ok = pg >= 0 && pg < a.num_pages;
     f.ok[q2] = ok;
     const unsigned char *base = a.pages + (int64_t)(ok ? pg : 0) * a.page_bytes;
-    f.kw[q2][F::KW - 1] = 0;
     load_bytes<F::KCH, (F::KCH % 16 == 0) ? 16 : ((F::KCH % 8 == 0) ? 8 : ((F::KCH % 4 == 0) ? 4 : 2))>(
         base + lo.k, f.kw[q2]);
     f.nk[q2] = *(const uint2 *)(base + lo.nk);
     f.nv[q2] = *(const uint2 *)(base + lo.nv);
-    f.vw[q2][F::VW - 1] = 0;
     load_bytes<F::VCH, 4>(base + lo.v, f.vw[q2]);
     if constexpr (KPROD) {
       if constexpr (D == 128) f.zb[q2] = *(const uint32_t *)(base + lo.z);
@@ -298,7 +299,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 
   // ---- 0. every global read of the prologue issued together: page ids of this run, this wavefront's
   //         query rows, the rotation signs of the query's coordinates, the level tables
-  for (int j = tid; j < p_end - p_begin; j += NT) s_pid[j] = a.page_table[(int64_t)b * a.max_pages + p_begin + j];
+  int pids_ok = 1;
+  for (int j = tid; j < p_end - p_begin; j += NT) {
+    const int pg = a.page_table[(int64_t)b * a.max_pages + p_begin + j];
+    s_pid[j] = pg;
+    pids_ok &= (pg >= 0 && pg < a.num_pages) ? 1 : 0;
+  }
   float qx[2][2];
 #pragma unroll
   for (int rr = 0; rr < 2; ++rr) {
@@ -319,17 +325,20 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     const int h2 = (1 << VB) >> 1;
     s_lutv[j] = ((const uint16_t *)(a.vcb + a.vo.levels))[j >= h2 ? j : h2 - 1 - j];
   }
-  __syncthreads();
+  // a run of whole, valid page pairs needs no per-token masking
+  const bool run_full = __syncthreads_and(pids_ok) && ((p_end - p_begin) % 2 == 0) &&
+                        p_end * TQ_PAGE_TOKENS <= seq_len;
 
   // ---- 1. the first page pairs of this wavefront in flight before the query prologue
   const LaneOffsets lo = lane_offsets<D, KB, VB>(a, kvh, c, g4);
   // register budget: wide codes or the sketch leave room for fewer fragments in flight
-  constexpr int R = (KB >= 8 || VB >= 8) ? 2 : (KPROD ? 3 : 4);
+  constexpr int R = (KB >= 8 || VB >= 8) ? 2 : 3;
+  // Every fragment load is issued unconditionally (a pair past the run reads page 0 and is never used):
+  // with the same loads on every path the compiler's wait counts keep R - 1 pairs in flight.
   F f[R];
 #pragma unroll
   for (int r = 0; r + 1 < R; ++r)
-    if (wave + r * kWaves < npairs)
-      load_pair<D, KB, KPROD, VB>(a, s_pid, lo, p_begin + 2 * (wave + r * kWaves), p_begin, p_end, f[r]);
+    load_pair<D, KB, KPROD, VB>(a, s_pid, lo, p_begin + 2 * (wave + r * kWaves), p_begin, p_end, f[r]);
 
   // ---- 2. query rotation, one row per wavefront: H (s * q) with cross-lane butterflies
   {
@@ -438,7 +447,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) O[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto process = [&](const F &cur, int pi) {
+  // FULL: every token of the pair is a cached token of a valid page (no masking needed)
+  auto process = [&](const F &cur, int pi, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const int pp = p_begin + 2 * pi;
     float s[2][4], nv[2][4];
 #pragma unroll
@@ -485,17 +496,17 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) s[q2][j] = nk[j] * raw[j];  // score / (softmax scale * log2 e)
     }
-    // tokens past the sequence end or in an invalid page: weight 0 (their bytes are not read as numbers)
-    const bool full = cur.ok[0] && cur.ok[1] && (pp + 2) * TQ_PAGE_TOKENS <= seq_len;
+    // tokens past the sequence end or in an invalid page: weight 0 (their bytes are not read as numbers).
+    // A masked score is a finite, very negative value so that a zero softmax scale never meets an infinity.
     bool okm[2][4];
-    if (!full) {
+    if constexpr (!FULL) {
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t = (pp + q2) * TQ_PAGE_TOKENS + 4 * g4 + j;
           okm[q2][j] = cur.ok[q2] && t < seq_len;
-          s[q2][j] = okm[q2][j] ? s[q2][j] : -INFINITY;
+          s[q2][j] = okm[q2][j] ? s[q2][j] : -3.0e38f;
           nv[q2][j] = okm[q2][j] ? nv[q2][j] : 0.f;
         }
     }
@@ -525,7 +536,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       for (int j = 0; j < 4; j += 2) {
         float p0 = fast_exp2(fmaf(s[q2][j], colscale, -m_run));
         float p1 = fast_exp2(fmaf(s[q2][j + 1], colscale, -m_run));
-        if (!full) {
+        if constexpr (!FULL) {
           p0 = okm[q2][j] ? p0 : 0.f;
           p1 = okm[q2][j + 1] ? p1 : 0.f;
         }
@@ -584,16 +595,19 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   };
 
   // ring of R fragments: R - 1 page pairs in flight while one is processed
-  for (int i = wave; i < npairs; i += R * kWaves) {
+  auto stream_pairs = [&](auto full_tag) {
+    for (int i = wave; i < npairs; i += R * kWaves) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int ii = i + r * kWaves;
-      if (ii >= npairs) break;
-      const int nx = ii + (R - 1) * kWaves;
-      if (nx < npairs) load_pair<D, KB, KPROD, VB>(a, s_pid, lo, p_begin + 2 * nx, p_begin, p_end, f[(r + R - 1) % R]);
-      process(f[r], ii);
+      for (int r = 0; r < R; ++r) {
+        const int ii = i + r * kWaves;
+        const int nx = ii + (R - 1) * kWaves;
+        load_pair<D, KB, KPROD, VB>(a, s_pid, lo, p_begin + 2 * nx, p_begin, p_end, f[(r + R - 1) % R]);
+        if (ii < npairs) process(f[r], ii, full_tag);
+      }
     }
-  }
+  };
+  if (run_full) stream_pairs(std::true_type{});
+  else stream_pairs(std::false_type{});
 
   // ---- 4. merge the wavefronts of this work-group: rescale to the work-group max, then sum over the
   //         waves in a fixed order (deterministic). Only rows < G are real query heads.
@@ -839,9 +853,12 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 
 template <int D, int KB, bool KPROD, int VB>
 void launch(const DecodeArgs &a, hipStream_t stream) {
-  dim3 grid(a.n_splits, a.Hkv, a.B);
-  hipLaunchKernelGGL((decode_kernel<D, KB, KPROD, VB>), grid, dim3(64 * kWaves), 0, stream, a);
-  if (a.n_splits > 1) hipLaunchKernelGGL(combine_kernel<D>, dim3(a.B * a.Hq), dim3(256), 0, stream, a);
+  if (a.passes & kPassScan) {
+    dim3 grid(a.n_splits, a.Hkv, a.B);
+    hipLaunchKernelGGL((decode_kernel<D, KB, KPROD, VB>), grid, dim3(64 * kWaves), 0, stream, a);
+  }
+  if ((a.passes & kPassCombine) && a.n_splits > 1)
+    hipLaunchKernelGGL(combine_kernel<D>, dim3(a.B * a.Hq), dim3(256), 0, stream, a);
 }
 
 template <int D, int KB, bool KPROD>
@@ -882,7 +899,7 @@ int launch_decode(const PageGeom &g, const DecodeWs &ws, const void *pages, int6
                   const void *q, int q_dtype, int batch, int num_q_heads, const int32_t *page_table,
                   int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
                   const void *k_cb, const void *v_cb, void *workspace, float *out,
-                  hipStream_t stream) {
+                  int passes, hipStream_t stream) {
   DecodeArgs a;
   a.pages = (const unsigned char *)pages;
   a.num_pages = num_pages;
@@ -913,6 +930,7 @@ int launch_decode(const PageGeom &g, const DecodeWs &ws, const void *pages, int6
   a.n_splits = ws.n_splits;
   a.pps = ws.pages_per_split;
   a.out = out;
+  a.passes = passes;
   const bool kprod = g.k_mode == TQ_PROD;
   const bool ok = g.head_dim == 128 ? dispatch_k<128>(g.k_mse_bits, kprod, g.v_mse_bits, a, stream)
                                     : dispatch_k<64>(g.k_mse_bits, kprod, g.v_mse_bits, a, stream);

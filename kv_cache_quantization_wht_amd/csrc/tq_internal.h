@@ -50,10 +50,14 @@ int launch_quantize(const PageGeom &g, void *pages, int64_t num_pages, const voi
                     int dtype, int64_t n_tok, int64_t k_stride, int64_t v_stride,
                     const int64_t *slots, const void *k_cb, const void *v_cb, hipStream_t stream);
 
+// Passes of one decode launch: the split-K scan, the merge of the runs, or both in order.
+constexpr int kPassScan = 1;
+constexpr int kPassCombine = 2;
+
 int launch_decode(const PageGeom &g, const DecodeWs &ws, const void *pages, int64_t num_pages,
                   const void *q, int q_dtype, int batch, int num_q_heads, const int32_t *page_table,
                   int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
                   const void *k_cb, const void *v_cb, void *workspace, float *out,
-                  hipStream_t stream);
+                  int passes, hipStream_t stream);
 
 }  // namespace tq

@@ -126,20 +126,21 @@ def test_launch_argument_errors_need_no_gpu():
     assert lib.tq_decode_workspace_bytes(ctypes.byref(L), 1, 30, 10, 0, ctypes.byref(sz)) == -1  # 30 % 8
     assert lib.tq_decode_workspace_bytes(ctypes.byref(L), 1, 32, 10, 4, ctypes.byref(sz)) == 0
     assert sz.value > 0
-    big = tq.Layout(128, 1, 4, 0, 2, 0).c()
-    assert lib.tq_decode_attention(ctypes.byref(big), 16, 4, 16, 1, 1, 32, 16, 10, 16, 0.1, 4, 16, 16, 16,
-                                   1 << 30, 16, None) == -3  # 32 query heads per KV head
-    vprod = tq.Layout(128, 8, 4, 0, 2, 1).c()
-    assert lib.tq_decode_attention(ctypes.byref(vprod), 16, 4, 16, 1, 1, 32, 16, 10, 16, 0.1, 4, 16, 16, 16,
-                                   1 << 30, 16, None) == -3
-    assert lib.tq_decode_attention(ctypes.byref(L), 16, 4, 16, 1, 1, 32, 16, 10, 16, 0.1, 4, 16, 16, 16,
-                                   8, 16, None) == -2  # workspace too small
-    assert lib.tq_decode_attention(ctypes.byref(L), None, 4, 16, 1, 1, 32, 16, 10, 16, 0.1, 4, 16, 16, 16,
-                                   1 << 30, 16, None) == -1
-    assert lib.tq_decode_attention(ctypes.byref(L), 16, 4, 16, 1, 1, 32, 16, 10, 16, -0.1, 4, 16, 16, 16,
-                                   1 << 30, 16, None) == -1  # negative softmax scale
-    assert lib.tq_decode_attention(ctypes.byref(L), 16, 1, 16, 1, 0, 32, None, 10, None, 0.1, 4, None, None,
-                                   None, 0, None, None) == 0  # empty batch
+    for fn in (lib.tq_decode_attention, lib.tq_decode_partial, lib.tq_decode_combine):
+        big = tq.Layout(128, 1, 4, 0, 2, 0).c()
+        assert fn(ctypes.byref(big), 16, 4, 16, 1, 1, 32, 16, 10, 16, 0.1, 4, 16, 16, 16,
+                  1 << 30, 16, None) == -3  # 32 query heads per KV head
+        vprod = tq.Layout(128, 8, 4, 0, 2, 1).c()
+        assert fn(ctypes.byref(vprod), 16, 4, 16, 1, 1, 32, 16, 10, 16, 0.1, 4, 16, 16, 16,
+                  1 << 30, 16, None) == -3
+        assert fn(ctypes.byref(L), 16, 4, 16, 1, 1, 32, 16, 10, 16, 0.1, 4, 16, 16, 16,
+                  8, 16, None) == -2  # workspace too small
+        assert fn(ctypes.byref(L), None, 4, 16, 1, 1, 32, 16, 10, 16, 0.1, 4, 16, 16, 16,
+                  1 << 30, 16, None) == -1
+        assert fn(ctypes.byref(L), 16, 4, 16, 1, 1, 32, 16, 10, 16, -0.1, 4, 16, 16, 16,
+                  1 << 30, 16, None) == -1  # negative softmax scale
+        assert fn(ctypes.byref(L), 16, 1, 16, 1, 0, 32, None, 10, None, 0.1, 4, None, None,
+                  None, 0, None, None) == 0  # empty batch
 
 
 def test_workspace_grows_with_splits():

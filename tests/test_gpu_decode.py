@@ -122,3 +122,27 @@ def test_zero_softmax_scale_is_uniform_average():
     c = build(2, 128, 8, 2, [130, 47], 4, 0, 2, 0, seed=31)
     out = run_gpu(c, 0.0)
     assert parity.attention_error(out, run_ref(c, 0.0)) <= parity.ATTN_TOL
+
+
+def test_two_passes_equal_one_call():
+    """tq_decode_partial then tq_decode_combine (same arguments) give the bytes of tq_decode_attention,
+    with one run per sequence (combine launches nothing) and with several."""
+    import torch
+    import kv_cache_quantization_wht_amd as tq
+
+    c = build(2, 128, 8, 3, [700, 33, 290], 4, 0, 2, 0, seed=41)
+    scale = 1 / math.sqrt(128)
+    pt, sl = torch.from_numpy(c["pt"]).cuda(), torch.from_numpy(c["lens"]).cuda()
+    q = c["q"].cuda()
+    for pps in (0, 4, 64):
+        need = tq.decode_workspace_bytes(c["layout"], 3, 8, pt.shape[1], pps)
+        ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+        one = tq.decode_attention(c["layout"], c["pages"], q, pt, sl, scale, c["kcb"], c["vcb"], pages_per_split=pps)
+        two = torch.full_like(one, float("nan"))
+        tq.decode_partial(c["layout"], c["pages"], q, pt, sl, scale, c["kcb"], c["vcb"], ws, out=two,
+                          pages_per_split=pps)
+        tq.decode_combine(c["layout"], c["pages"], q, pt, sl, scale, c["kcb"], c["vcb"], ws, out=two,
+                          pages_per_split=pps)
+        torch.cuda.synchronize()
+        assert torch.equal(one, two), pps
+        assert parity.attention_error(two.cpu().numpy().astype(np.float64), run_ref(c, scale)) <= parity.ATTN_TOL
