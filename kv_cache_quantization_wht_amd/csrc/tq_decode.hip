@@ -64,6 +64,56 @@ __device__ __forceinline__ float range_factor(float maxabs) {
 // 2^x on the hardware exponential unit (results below 2^-126 flush to zero; 2^-inf = 0).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max over the lanes l, l ^ 16 (permlane16 swap: rows 0<->1 and 2<->3 of 16 lanes) and over l, l ^ 32.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16_32(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Value of lane (lane ^ H) within a wavefront, for H a power of two below 64: quad permutes for 1 and 2,
+// swizzles (32-lane groups) for 4, 8, the permlane swaps for 16 and 32. No LDS memory is touched.
+template <int H>
+__device__ __forceinline__ float xor_partner(float v, int lane) {
+  const int x = __float_as_int(v);
+  if constexpr (H == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
+  else if constexpr (H == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+  else if constexpr (H == 4 || H == 8) return __int_as_float(__builtin_amdgcn_ds_swizzle(x, (H << 10) | 0x1F));
+  else if constexpr (H == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  } else {
+    static_assert(H == 32, "xor distance");
+    const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+  }
+}
+
+// One Walsh-Hadamard butterfly stage across lanes at distance H: (a, b) -> (a + b, a - b).
+template <int H>
+__device__ __forceinline__ float wht_stage(float x, int lane) {
+  const float p = xor_partner<H>(x, lane);
+  return (lane & H) ? (p - x) : (x + p);
+}
+
+// Maximum over the 64 lanes of a wavefront.
+__device__ __forceinline__ float wave_max(float v, int lane) {
+  v = fmaxf(v, xor_partner<1>(v, lane));
+  v = fmaxf(v, xor_partner<2>(v, lane));
+  v = fmaxf(v, xor_partner<4>(v, lane));
+  v = fmaxf(v, xor_partner<8>(v, lane));
+  return max_xor32(max_xor16(v));
+}
+
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
@@ -215,15 +265,15 @@ __device__ __forceinline__ LaneOffsets lane_offsets(const DecodeArgs &a, int kvh
   return o;
 }
 
+// Both pages of one pair (page ids pg0, pg1; an id outside [0, num_pages) reads page 0 and is marked
+// invalid). The page id is the same for the whole wavefront: the page base stays in scalar registers.
 template <int D, int KB, bool KPROD, int VB>
-__device__ __forceinline__ void load_pair(const DecodeArgs &a, const int *pid, const LaneOffsets &lo, int pp,
-                                          int p_begin, int p_end, Frag<D, KB, KPROD, VB> &f) {
+__device__ __forceinline__ void load_pages(const DecodeArgs &a, const LaneOffsets &lo, int pg0, int pg1,
+                                           Frag<D, KB, KPROD, VB> &f) {
   using F = Frag<D, KB, KPROD, VB>;
 #pragma unroll
   for (int q2 = 0; q2 < 2; ++q2) {
-    const int pi = pp + q2;
-    // the page id is the same for the whole wavefront: keep the page base in scalar registers
-    const int pg = __builtin_amdgcn_readfirstlane(pi < p_end ? pid[pi - p_begin] : -1);
+    const int pg = __builtin_amdgcn_readfirstlane(q2 ? pg1 : pg0);
     const bool ok = pg >= 0 && pg < a.num_pages;
     f.ok[q2] = ok;
     const unsigned char *base = a.pages + (int64_t)(ok ? pg : 0) * a.page_bytes;
@@ -238,6 +288,14 @@ __device__ __forceinline__ void load_pair(const DecodeArgs &a, const int *pid, c
       f.gm[q2] = *(const uint2 *)(base + lo.gm);
     }
   }
+}
+
+// The pair starting at run page pp, page ids from the run's table in LDS (pid[0] = page p_begin).
+template <int D, int KB, bool KPROD, int VB>
+__device__ __forceinline__ void load_pair(const DecodeArgs &a, const int *pid, const LaneOffsets &lo, int pp,
+                                          int p_begin, int p_end, Frag<D, KB, KPROD, VB> &f) {
+  load_pages<D, KB, KPROD, VB>(a, lo, pp < p_end ? pid[pp - p_begin] : -1, pp + 1 < p_end ? pid[pp + 1 - p_begin] : -1,
+                               f);
 }
 
 __device__ __forceinline__ void unpack4(uint2 w, float *x) {
@@ -270,6 +328,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   constexpr int QF = 16 * D;    // floats in one [16][D] block
   using F = Frag<D, KB, KPROD, VB>;
 
+  // Every argument the prologue needs, fetched from the argument segment in one round trip (left to
+  // itself the compiler fetches them in several dependent rounds, each a full memory latency).
+  asm volatile("" ::"s"(a.pages), "s"(a.num_pages), "s"(a.page_bytes), "s"(a.k_codes), "s"(a.k_norms),
+               "s"(a.v_codes), "s"(a.v_norms), "s"(a.q), "s"(a.q_dtype), "s"(a.Hq), "s"(a.G), "s"(a.page_table),
+               "s"(a.max_pages), "s"(a.seq_lens), "s"(a.kcb), "s"(a.vcb), "s"(a.ko.signs), "s"(a.ko.levels),
+               "s"(a.vo.levels), "s"(a.pps), "s"(a.scale_log2), "s"(a.n_splits));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -279,7 +343,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   const int G = a.G;
   const int head0 = kvh * G;
 
-  // LDS arena reused by phase: queries (prologue), then the wave-merge tree
+  // LDS arena reused by phase: queries (prologue), then the wave-merge tree. Query rows are padded to
+  // QS floats so that the operand reads of different heads fall in different banks.
+  constexpr int QS = D + 4;
+  static_assert(2 * 16 * QS <= 4 * QF, "query rows fit in the arena");
   __shared__ __align__(16) float arena[4 * QF];
   __shared__ int s_pid[kPidCap];
   __shared__ float s_sig[16][2];
@@ -287,75 +354,123 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   __shared__ uint16_t s_lutv[1 << VB];
   __shared__ float s_m[kWaves][16], s_l[kWaves][16];
   __shared__ float s_rowm[16], s_rowl[16];
-  float(*s_q)[D] = (float(*)[D])arena;         // rotated queries / d
-  float(*s_qs)[D] = (float(*)[D])(arena + QF);  // sketch-domain queries
+  float(*s_q)[QS] = (float(*)[QS])arena;              // rotated queries / d
+  float(*s_qs)[QS] = (float(*)[QS])(arena + 16 * QS);  // sketch-domain queries
 
-  int seq_len = a.seq_lens[b];
+  // the run's pages in the table (p_begin .. p_cap) do not depend on the sequence length, so the page-id
+  // reads are issued alongside the length read instead of after it
+  const int p_begin = split * a.pps;
+  const int p_cap = min(p_begin + a.pps, a.max_pages);
+  typedef const __attribute__((address_space(4))) int32_t *const_i32;  // read through the scalar cache
+  int seq_len = ((const_i32)a.seq_lens)[b];
   seq_len = seq_len < 0 ? 0 : (seq_len > a.max_pages * TQ_PAGE_TOKENS ? a.max_pages * TQ_PAGE_TOKENS : seq_len);
   const int npages = (seq_len + TQ_PAGE_TOKENS - 1) / TQ_PAGE_TOKENS;
-  const int p_begin = split * a.pps;
   const int p_end = min(p_begin + a.pps, npages);
   const int npairs = p_end > p_begin ? (p_end - p_begin + 1) / 2 : 0;
 
-  // ---- 0. every global read of the prologue issued together: page ids of this run, this wavefront's
-  //         query rows, the rotation signs of the query's coordinates, the level tables
-  int pids_ok = 1;
-  for (int j = tid; j < p_end - p_begin; j += NT) {
-    const int pg = a.page_table[(int64_t)b * a.max_pages + p_begin + j];
-    s_pid[j] = pg;
-    pids_ok &= (pg >= 0 && pg < a.num_pages) ? 1 : 0;
+  // ---- 0. the small global reads of the prologue, into registers first (memory returns in issue order,
+  //         so these must not queue behind the page data): page ids of the run, this wavefront's query
+  //         rows, the rotation signs of the query's coordinates, the level tables
+  // page ids of this wavefront's first pairs through the scalar cache: the head of the longest chain
+  // (page id -> page data)
+  constexpr int R = (KB >= 8 || VB >= 8) ? 2 : 3;  // fragments in the ring (wide codes leave room for fewer)
+  int first_ids[R - 1][2];
+  {
+    const const_i32 ptab = (const_i32)(a.page_table) + (int64_t)b * a.max_pages;
+#pragma unroll
+    for (int r = 0; r + 1 < R; ++r) {
+      const int pp = p_begin + 2 * (wave + r * kWaves);
+      first_ids[r][0] = pp < p_cap ? ptab[pp] : -1;
+      first_ids[r][1] = pp + 1 < p_cap ? ptab[pp + 1] : -1;
+    }
   }
-  float qx[2][2];
+  // No loaded value is used (converted, compared, selected) before the page loads of step 1 are issued:
+  // addresses are clamped in bounds instead, so no wait lands here.
+  constexpr int PID_PER_THREAD = kPidCap / NT;
+  int pgv[PID_PER_THREAD];
+  {
+    const int32_t *row = a.page_table + (int64_t)b * a.max_pages;
+#pragma unroll
+    for (int u = 0; u < PID_PER_THREAD; ++u)
+      if (tid + u * NT < p_cap - p_begin) pgv[u] = row[p_begin + tid + u * NT];  // read below under the same bound
+  }
+  uint32_t qraw[2][2];
 #pragma unroll
   for (int rr = 0; rr < 2; ++rr) {
     const int r = wave + rr * kWaves;
-    const int64_t base = ((int64_t)b * a.Hq + head0 + (r < G ? r : 0)) * D;
-    qx[rr][0] = r < G ? load_elem(a.q, base + lane, a.q_dtype) : 0.f;
-    qx[rr][1] = (D == 128 && r < G) ? load_elem(a.q, base + lane + 64, a.q_dtype) : 0.f;
+    const int64_t base = ((int64_t)b * a.Hq + head0 + (r < G ? r : 0)) * D + lane;
+#pragma unroll
+    for (int h = 0; h < (D == 128 ? 2 : 1); ++h) {
+      if (a.q_dtype == TQ_F32) qraw[rr][h] = ((const uint32_t *)a.q)[base + 64 * h];
+      else qraw[rr][h] = ((const uint16_t *)a.q)[base + 64 * h];
+    }
+    if (D != 128) qraw[rr][1] = 0;
   }
   const uint32_t *ksw = (const uint32_t *)(a.kcb + a.ko.signs);
   const uint32_t sgn0 = ksw[lane >> 5];
   const uint32_t sgn1 = D == 128 ? ksw[(lane + 64) >> 5] : 0u;
   // code-indexed level tables: code c -> ascending level c (upper half) or half - 1 - c (lower half)
-  for (int j = tid; j < (1 << KB); j += NT) {
-    const int h2 = (1 << KB) >> 1;
-    s_lutk[j] = ((const uint16_t *)(a.kcb + a.ko.levels))[j >= h2 ? j : h2 - 1 - j];
+  uint16_t lk, lv;
+  {
+    const int nk = 1 << KB, nv = 1 << VB;
+    const int ck = tid < nk ? tid : 0, cv = tid < nv ? tid : 0;
+    lk = ((const uint16_t *)(a.kcb + a.ko.levels))[ck >= nk / 2 ? ck : nk / 2 - 1 - ck];
+    lv = ((const uint16_t *)(a.vcb + a.vo.levels))[cv >= nv / 2 ? cv : nv / 2 - 1 - cv];
   }
-  for (int j = tid; j < (1 << VB); j += NT) {
-    const int h2 = (1 << VB) >> 1;
-    s_lutv[j] = ((const uint16_t *)(a.vcb + a.vo.levels))[j >= h2 ? j : h2 - 1 - j];
-  }
-  // a run of whole, valid page pairs needs no per-token masking
-  const bool run_full = __syncthreads_and(pids_ok) && ((p_end - p_begin) % 2 == 0) &&
-                        p_end * TQ_PAGE_TOKENS <= seq_len;
 
-  // ---- 1. the first page pairs of this wavefront in flight before the query prologue
+  // ---- 1. this wavefront's first page pairs in flight: their page ids come through the scalar cache
+  //         (no LDS, no barrier). Every fragment load is issued unconditionally (a pair past the run
+  //         reads page 0 and is never used): with the same loads on every path the compiler's wait
+  //         counts keep R - 1 pairs in flight.
   const LaneOffsets lo = lane_offsets<D, KB, VB>(a, kvh, c, g4);
-  // register budget: wide codes or the sketch leave room for fewer fragments in flight
-  constexpr int R = (KB >= 8 || VB >= 8) ? 2 : 3;
-  // Every fragment load is issued unconditionally (a pair past the run reads page 0 and is never used):
-  // with the same loads on every path the compiler's wait counts keep R - 1 pairs in flight.
   F f[R];
 #pragma unroll
-  for (int r = 0; r + 1 < R; ++r)
-    load_pair<D, KB, KPROD, VB>(a, s_pid, lo, p_begin + 2 * (wave + r * kWaves), p_begin, p_end, f[r]);
+  for (int r = 0; r + 1 < R; ++r) {
+    const int pp = p_begin + 2 * (wave + r * kWaves);
+    load_pages<D, KB, KPROD, VB>(a, lo, pp < p_end ? first_ids[r][0] : -1, pp + 1 < p_end ? first_ids[r][1] : -1, f[r]);
+  }
 
-  // ---- 2. query rotation, one row per wavefront: H (s * q) with cross-lane butterflies
+  // the page ids and level tables into LDS (waits only for the small reads above)
+  int pids_ok = 1;
+#pragma unroll
+  for (int u = 0; u < PID_PER_THREAD; ++u) {
+    const int j = tid + u * NT;
+    if (j < p_end - p_begin) {
+      s_pid[j] = pgv[u];
+      pids_ok &= (pgv[u] >= 0 && pgv[u] < a.num_pages) ? 1 : 0;
+    }
+  }
+  if (tid < (1 << KB)) s_lutk[tid] = lk;
+  if (tid < (1 << VB)) s_lutv[tid] = lv;
+
+  // ---- 2. query rotation, one row per wavefront: H (s * q) with cross-lane butterflies (no barrier
+  //         needed before: the row and the signs are this wavefront's own loads)
   {
     const bool neg0 = (sgn0 >> (lane & 31)) & 1u;
     const bool neg1 = (sgn1 >> (lane & 31)) & 1u;
+    auto widen = [&](uint32_t u) {
+      return a.q_dtype == TQ_F32 ? __uint_as_float(u)
+                                 : (a.q_dtype == TQ_BF16 ? bf16_bits_to_float((uint16_t)u) : half_bits_to_float((uint16_t)u));
+    };
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const int r = wave + rr * kWaves;
       if (r >= G) continue;
-      float x0 = neg0 ? -qx[rr][0] : qx[rr][0];
-      float x1 = neg1 ? -qx[rr][1] : qx[rr][1];
-#pragma unroll
-      for (int h = 1; h < 64; h <<= 1) {
-        const float p0 = __shfl_xor(x0, h), p1 = __shfl_xor(x1, h);
-        x0 = (lane & h) ? (p0 - x0) : (x0 + p0);
-        x1 = (lane & h) ? (p1 - x1) : (x1 + p1);
-      }
+      const float q0 = widen(qraw[rr][0]), q1 = D == 128 ? widen(qraw[rr][1]) : 0.f;
+      float x0 = neg0 ? -q0 : q0;
+      float x1 = neg1 ? -q1 : q1;
+      x0 = wht_stage<1>(x0, lane);
+      x1 = wht_stage<1>(x1, lane);
+      x0 = wht_stage<2>(x0, lane);
+      x1 = wht_stage<2>(x1, lane);
+      x0 = wht_stage<4>(x0, lane);
+      x1 = wht_stage<4>(x1, lane);
+      x0 = wht_stage<8>(x0, lane);
+      x1 = wht_stage<8>(x1, lane);
+      x0 = wht_stage<16>(x0, lane);
+      x1 = wht_stage<16>(x1, lane);
+      x0 = wht_stage<32>(x0, lane);
+      x1 = wht_stage<32>(x1, lane);
       if (D == 128) {
         const float u = x0;
         x0 = u + x1;
@@ -363,15 +478,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       }
       x0 *= (1.0f / D);
       x1 *= (1.0f / D);
-      float mx = fmaxf(fabsf(x0), D == 128 ? fabsf(x1) : 0.f);
-#pragma unroll
-      for (int h = 1; h < 64; h <<= 1) mx = fmaxf(mx, __shfl_xor(mx, h));
+      const float mx = wave_max(fmaxf(fabsf(x0), D == 128 ? fabsf(x1) : 0.f), lane);
       s_q[r][lane] = x0;
       if (D == 128) s_q[r][lane + 64] = x1;
       if (lane == 0) s_sig[r][0] = range_factor(mx);
     }
   }
-  __syncthreads();
+  // a run of whole, valid page pairs needs no per-token masking; one barrier publishes the page ids,
+  // level tables and rotated queries
+  const bool run_full = __syncthreads_and(pids_ok) && ((p_end - p_begin) % 2 == 0) &&
+                        p_end * TQ_PAGE_TOKENS <= seq_len;
   if constexpr (KPROD) {
     // q_s = S (R q) sqrt(pi/2) / m with R q = (d * s_q) / sqrt(d)
     const float *S = (const float *)(a.kcb + a.ko.proj);
@@ -386,8 +502,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     for (int r = wave; r < G; r += kWaves) {
       float mx = 0.f;
       for (int k = lane; k < D; k += 64) mx = fmaxf(mx, fabsf(s_qs[r][k]));
-#pragma unroll
-      for (int h = 1; h < 64; h <<= 1) mx = fmaxf(mx, __shfl_xor(mx, h));
+      mx = wave_max(mx, lane);
       if (lane == 0) s_sig[r][1] = range_factor(mx);
     }
     __syncthreads();
@@ -447,6 +562,44 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) O[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
+  // fp16 V levels of one page pair as MFMA operands: Bop[nb] holds, for lane (c, g4), the level of
+  // coordinate (D / 16) * c + nb for the 8 tokens of contraction rows 8 * g4 .. 8 * g4 + 7.
+  auto v_operands = [&](const F &cur, half8_t *Bop) {
+    if constexpr (VB == 2 && D == 128) {
+      // code blocks nb and nb + 4 of a token sit one byte apart: one mask yields both selector sets
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t lo_[4], hi_[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t y = (cur.vw[w >> 1][w & 1] >> (2 * k)) & 0x03030303u;
+          const uint32_t y4 = y | 0x04040404u;
+          lo_[w] = perm(tv.hi0, tv.lo0, perm(y4, y, 0x06020400u));  // code block k
+          hi_[w] = perm(tv.hi0, tv.lo0, perm(y4, y, 0x07030501u));  // code block k + 4
+        }
+        Bop[k] = from_dwords(lo_[0], lo_[1], lo_[2], lo_[3]);
+        Bop[k + 4] = from_dwords(hi_[0], hi_[1], hi_[2], hi_[3]);
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int ci = (D == 128) ? nb : (4 * (c & 1) + nb);  // code index inside the token's 8-coordinate piece
+        if constexpr (VB == 2) {
+          const int sh = 2 * ci;
+          Bop[nb] = from_dwords(lut_v2_pair(cur.vw[0][0] >> sh, tv), lut_v2_pair(cur.vw[0][1] >> sh, tv),
+                                lut_v2_pair(cur.vw[1][0] >> sh, tv), lut_v2_pair(cur.vw[1][1] >> sh, tv));
+        } else {
+          uint16_t hv[8];
+#pragma unroll
+          for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) hv[4 * q2 + j] = s_lutv[bits_at<VB>(cur.vw[q2], 8 * VB * j + VB * ci)];
+          Bop[nb] = from_halves(hv);
+        }
+      }
+    }
+  };
+
   // FULL: every token of the pair is a cached token of a valid page (no masking needed)
   auto process = [&](const F &cur, int pi, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
@@ -496,6 +649,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) s[q2][j] = nk[j] * raw[j];  // score / (softmax scale * log2 e)
     }
+    // the V operands depend only on the codes: built here, their VALU work covers the latency of the
+    // score MFMAs and of the softmax reductions below
+    half8_t Bop[NB];
+    v_operands(cur, Bop);
+
     // tokens past the sequence end or in an invalid page: weight 0 (their bytes are not read as numbers).
     // A masked score is a finite, very negative value so that a zero softmax scale never meets an infinity.
     bool okm[2][4];
@@ -515,18 +673,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     // tokens 4*g4 .. 4*g4+3 of both pages
     float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     const float m_new = fmaxf(m_run, colscale * mx);
     if (__any(m_new > m_run)) {
+      // O holds head column c in this lane, as do m_run and l_part: the rescale stays in the lane
       const float alpha = (m_new > m_run) ? ((m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new)) : 1.f;
       l_part *= alpha;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float aj = __shfl(alpha, 4 * g4 + j);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) O[nb][j] *= aj;
-      }
+      for (int nb = 0; nb < NB; ++nb) O[nb] *= alpha;
       m_run = m_new;
     }
     half8_t phi, plo;
@@ -551,46 +705,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       }
     }
 
-    // values: O[rows][coords] += P'[rows][32 tokens] * Vhat[32 tokens][coords]
-    if constexpr (VB == 2 && D == 128) {
-      // code blocks nb and nb + 4 of a token sit one byte apart: one mask yields both selector sets
+    // values, transposed: O^T[coords][head columns] += Vhat^T[coords][32 tokens] * P'^T[32 tokens][heads].
+    // The V operand registers are the same as for Vhat as the right-hand operand; swapping the operands
+    // of the MFMA puts the query heads in the columns, next to their softmax state.
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint32_t lo_[4], hi_[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t y = (cur.vw[w >> 1][w & 1] >> (2 * k)) & 0x03030303u;
-          const uint32_t y4 = y | 0x04040404u;
-          lo_[w] = perm(tv.hi0, tv.lo0, perm(y4, y, 0x06020400u));  // code block k
-          hi_[w] = perm(tv.hi0, tv.lo0, perm(y4, y, 0x07030501u));  // code block k + 4
-        }
-        const half8_t B0 = from_dwords(lo_[0], lo_[1], lo_[2], lo_[3]);
-        const half8_t B1 = from_dwords(hi_[0], hi_[1], hi_[2], hi_[3]);
-        O[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, B0, O[k], 0, 0, 0);
-        O[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, B0, O[k], 0, 0, 0);
-        O[k + 4] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, B1, O[k + 4], 0, 0, 0);
-        O[k + 4] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, B1, O[k + 4], 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int ci = (D == 128) ? nb : (4 * (c & 1) + nb);  // code index inside the token's 8-coordinate piece
-        half8_t Bv;
-        if constexpr (VB == 2) {
-          const int sh = 2 * ci;
-          Bv = from_dwords(lut_v2_pair(cur.vw[0][0] >> sh, tv), lut_v2_pair(cur.vw[0][1] >> sh, tv),
-                           lut_v2_pair(cur.vw[1][0] >> sh, tv), lut_v2_pair(cur.vw[1][1] >> sh, tv));
-        } else {
-          uint16_t hv[8];
-#pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) hv[4 * q2 + j] = s_lutv[bits_at<VB>(cur.vw[q2], 8 * VB * j + VB * ci)];
-          Bv = from_halves(hv);
-        }
-        O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, Bv, O[nb], 0, 0, 0);
-        O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, Bv, O[nb], 0, 0, 0);
-      }
+    for (int nb = 0; nb < NB; ++nb) {
+      O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Bop[nb], phi, O[nb], 0, 0, 0);
+      O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Bop[nb], plo, O[nb], 0, 0, 0);
     }
   };
 
@@ -610,27 +731,23 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   else stream_pairs(std::false_type{});
 
   // ---- 4. merge the wavefronts of this work-group: rescale to the work-group max, then sum over the
-  //         waves in a fixed order (deterministic). Only rows < G are real query heads.
+  //         waves in a fixed order (deterministic). Lane (c, g4) holds head c (real when c < G) and,
+  //         in O[nb][j], coordinate (D / 16) * (4 * g4 + j) + nb of its rotated value sum.
   {
-    float l_tot = l_part + __shfl_xor(l_part, 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    const float l_tot = sum_xor16_32(l_part);
     if (g4 == 0) {
       s_m[wave][c] = m_run;
       s_l[wave][c] = l_tot;
     }
   }
   __syncthreads();  // also: every wave is past its use of s_q / s_qs
+  if (c < G) {
+    float M = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 4 * g4 + j;
-    if (row < G) {
-      float M = -INFINITY;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][c]);
+    const float e = (M == -INFINITY || m_run == -INFINITY) ? 0.f : fast_exp2(m_run - M);
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][row]);
-      const float e = (M == -INFINITY || s_m[wave][row] == -INFINITY) ? 0.f : fast_exp2(s_m[wave][row] - M);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) O[nb][j] *= e;
-    }
+    for (int nb = 0; nb < NB; ++nb) O[nb] *= e;
   }
   if (tid < G) {
     const int row = tid;
@@ -646,19 +763,32 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     s_rowm[row] = M;
     s_rowl[row] = L;
   }
+  // this lane's 4 x NB sums as float4 runs of consecutive coordinates of row (head) c
+  auto put_rows = [&](float *row_base) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int nb = 0; nb < NB; nb += 4)
+        *(float4 *)(row_base + (D / 16) * (4 * g4 + j) + nb) = float4{O[nb][j], O[nb + 1][j], O[nb + 2][j], O[nb + 3][j]};
+  };
+  auto add_rows = [&](const float *row_base) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int nb = 0; nb < NB; nb += 4) {
+        const float4 t = *(const float4 *)(row_base + (D / 16) * (4 * g4 + j) + nb);
+        O[nb][j] += t.x;
+        O[nb + 1][j] += t.y;
+        O[nb + 2][j] += t.z;
+        O[nb + 3][j] += t.w;
+      }
+  };
   // every wave deposits its real rows; one fixed-order pass sums them
   constexpr int RMAX = (4 * QF) / (kWaves * D);  // rows that fit in the arena per wave (8)
   float acc_out[(16 * D + NT - 1) / NT];         // this thread's merged elements (row-major over G x D)
   if (G <= RMAX) {
     float(*dep)[RMAX][D] = (float(*)[RMAX][D])arena;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 4 * g4 + j;
-      if (row < G) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) dep[wave][row][(D / 16) * c + nb] = O[nb][j];
-      }
-    }
+    if (c < G) put_rows(dep[wave][c]);
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < (16 * D + NT - 1) / NT; ++q) {
@@ -675,27 +805,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     float(*tree)[16][D] = (float(*)[16][D])arena;  // [kWaves / 2][16][D]
 #pragma unroll
     for (int half = kWaves / 2; half >= 1; half >>= 1) {
-      if (wave >= half && wave < 2 * half) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) tree[wave - half][4 * g4 + j][(D / 16) * c + nb] = O[nb][j];
-      }
+      if (wave >= half && wave < 2 * half) put_rows(tree[wave - half][c]);
       __syncthreads();
-      if (wave < half) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) O[nb][j] += tree[wave][4 * g4 + j][(D / 16) * c + nb];
-      }
+      if (wave < half) add_rows(tree[wave][c]);
       __syncthreads();
     }
-    if (wave == 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) tree[0][4 * g4 + j][(D / 16) * c + nb] = O[nb][j];
-    }
+    if (wave == 0) put_rows(tree[0][c]);
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < (16 * D + NT - 1) / NT; ++q) {
