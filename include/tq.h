@@ -173,8 +173,10 @@ int tq_decode_workspace_bytes(const tq_layout *layout, int batch, int num_q_head
  *               max_pages_per_seq*16); 0 gives a zero output row. Page-table entries < 0 or
  *               >= num_pages inside a sequence are treated as empty pages.
  *   softmax_scale    >= 0 (usually 1/sqrt(head_dim))
- *   pages_per_split  pages handled by one work-group before the split results are merged
- *               (0 = automatic). The result does not depend on it beyond fp32 rounding.
+ *   pages_per_split  pages of one run, handled by one work-group before the runs are merged
+ *               (rounded up to even, at most 2048; 0 = automatic). A sequence's runs start every
+ *               pages_per_split pages and its last run also takes the remainder (fewer than
+ *               pages_per_split more pages). The result does not depend on it beyond fp32 rounding.
  *   workspace   device scratch of at least tq_decode_workspace_bytes(...) bytes (no initial
  *               contents needed). Calls that share a workspace must not overlap in time.
  *   out         device fp32 [batch][num_q_heads][head_dim]

@@ -228,20 +228,22 @@ int plan_decode(const PageGeom &g, int batch, int num_q_heads, int max_pages_per
       int v = 0;
       if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     }
-    // about one 8-wave work-group per compute unit over all (sequence, KV head) pairs
+    // about one 8-wave work-group per compute unit over all (sequence, KV head) pairs, each run a whole
+    // number of 16-page rounds (one page pair per wavefront); the last run takes the remainder
     int64_t units = (int64_t)std::max(batch, 1) * g.num_kv_heads;
     int64_t want_splits = std::max<int64_t>(1, (cus + units - 1) / units);
-    pps = (int)std::max<int64_t>(2, (max_pages_per_seq + want_splits - 1) / want_splits);
+    pps = (int)std::max<int64_t>(16, (max_pages_per_seq / want_splits) / 16 * 16);
   }
   pps = (pps + 1) & ~1;  // whole page pairs
-  if (pps > kDecodePidCap) pps = kDecodePidCap;
-  if ((max_pages_per_seq + pps - 1) / pps > kDecodeMaxSplits) {
+  // the last run holds fewer than 2 * pps pages
+  if (pps > kDecodePidCap / 2) pps = kDecodePidCap / 2;
+  if (max_pages_per_seq / pps > kDecodeMaxSplits) {
     pps = (max_pages_per_seq + kDecodeMaxSplits - 1) / kDecodeMaxSplits;
     pps = (pps + 1) & ~1;
-    if (pps > kDecodePidCap) return TQ_EINVAL;
+    if (pps > kDecodePidCap / 2) return TQ_EINVAL;
   }
   ws->pages_per_split = pps;
-  ws->n_splits = (max_pages_per_seq + pps - 1) / pps;
+  ws->n_splits = std::max(1, max_pages_per_seq / pps);
   const size_t B = (size_t)std::max(batch, 0), Hq = (size_t)num_q_heads, d = (size_t)g.head_dim;
   const size_t S = (size_t)ws->n_splits;
   size_t off = 0;

@@ -20,6 +20,7 @@
 //      its (max, sum, O) partial and a second, small kernel merges the runs and finishes the rows.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "tq_common.h"
@@ -29,6 +30,7 @@ namespace tq {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kHeadroom = 4.0f;  // log2 units between the running maximum and the weight reference
 constexpr int kWaves = 8;
 constexpr int kMlCap = 2048;   // split partials merged by one combine work-group
 constexpr int kPidCap = 4096;  // page ids of one run held in LDS
@@ -36,6 +38,7 @@ constexpr int kPidCap = 4096;  // page ids of one run held in LDS
 struct DecodeArgs {
   const unsigned char *pages;
   int64_t num_pages;
+  int num_pages32;  // min(num_pages, INT32_MAX): page ids are int32, so the check stays in scalar registers
   int64_t page_bytes;
   int64_t k_codes, k_norms, k_qjl, k_gamma, v_codes, v_norms;
   const void *q;
@@ -265,8 +268,37 @@ __device__ __forceinline__ LaneOffsets lane_offsets(const DecodeArgs &a, int kvh
   return o;
 }
 
+// NBYTES bytes at byte offset off of a buffer resource, into dwords (little-endian).
+template <int NBYTES>
+__device__ __forceinline__ void buf_bytes(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t *w) {
+  if constexpr (NBYTES % 16 == 0) {
+#pragma unroll
+    for (int i = 0; i < NBYTES / 16; ++i) {
+      const uint4 t = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, 0));
+      w[4 * i] = t.x; w[4 * i + 1] = t.y; w[4 * i + 2] = t.z; w[4 * i + 3] = t.w;
+    }
+  } else if constexpr (NBYTES % 8 == 0) {
+#pragma unroll
+    for (int i = 0; i < NBYTES / 8; ++i) {
+      const uint2 t = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off + 8 * i, 0, 0));
+      w[2 * i] = t.x; w[2 * i + 1] = t.y;
+    }
+  } else if constexpr (NBYTES % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NBYTES / 4; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * i, 0, 0);
+  } else {
+    static_assert(NBYTES % 2 == 0, "even byte counts only");
+#pragma unroll
+    for (int i = 0; i < (NBYTES + 3) / 4; ++i) w[i] = 0;
+#pragma unroll
+    for (int i = 0; i < NBYTES / 2; ++i)
+      w[i >> 1] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off + 2 * i, 0, 0) << (16 * (i & 1));
+  }
+}
+
 // Both pages of one pair (page ids pg0, pg1; an id outside [0, num_pages) reads page 0 and is marked
-// invalid). The page id is the same for the whole wavefront: the page base stays in scalar registers.
+// invalid). The page id is the same for the whole wavefront: each page is a buffer resource in scalar
+// registers and every lane adds its fixed 32-bit offset.
 template <int D, int KB, bool KPROD, int VB>
 __device__ __forceinline__ void load_pages(const DecodeArgs &a, const LaneOffsets &lo, int pg0, int pg1,
                                            Frag<D, KB, KPROD, VB> &f) {
@@ -274,18 +306,23 @@ __device__ __forceinline__ void load_pages(const DecodeArgs &a, const LaneOffset
 #pragma unroll
   for (int q2 = 0; q2 < 2; ++q2) {
     const int pg = __builtin_amdgcn_readfirstlane(q2 ? pg1 : pg0);
-    const bool ok = pg >= 0 && pg < a.num_pages;
+    const bool ok = pg >= 0 && pg < a.num_pages32;
     f.ok[q2] = ok;
-    const unsigned char *base = a.pages + (int64_t)(ok ? pg : 0) * a.page_bytes;
-    load_bytes<F::KCH, (F::KCH % 16 == 0) ? 16 : ((F::KCH % 8 == 0) ? 8 : ((F::KCH % 4 == 0) ? 4 : 2))>(
-        base + lo.k, f.kw[q2]);
-    f.nk[q2] = *(const uint2 *)(base + lo.nk);
-    f.nv[q2] = *(const uint2 *)(base + lo.nv);
-    load_bytes<F::VCH, 4>(base + lo.v, f.vw[q2]);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.pages + (int64_t)(ok ? pg : 0) * a.page_bytes), (short)0, (int)a.page_bytes, 0x00020000);
+    buf_bytes<F::KCH>(r, lo.k, f.kw[q2]);
+    uint32_t t[2];
+    buf_bytes<8>(r, lo.nk, t);
+    f.nk[q2] = uint2{t[0], t[1]};
+    buf_bytes<8>(r, lo.nv, t);
+    f.nv[q2] = uint2{t[0], t[1]};
+    buf_bytes<F::VCH>(r, lo.v, f.vw[q2]);
     if constexpr (KPROD) {
-      if constexpr (D == 128) f.zb[q2] = *(const uint32_t *)(base + lo.z);
-      else f.zb[q2] = *(const uint16_t *)(base + lo.z);
-      f.gm[q2] = *(const uint2 *)(base + lo.gm);
+      uint32_t z[1];
+      buf_bytes<D / 32>(r, lo.z, z);
+      f.zb[q2] = z[0];
+      buf_bytes<8>(r, lo.gm, t);
+      f.gm[q2] = uint2{t[0], t[1]};
     }
   }
 }
@@ -297,6 +334,9 @@ __device__ __forceinline__ void load_pair(const DecodeArgs &a, const int *pid, c
   load_pages<D, KB, KPROD, VB>(a, lo, pp < p_end ? pid[pp - p_begin] : -1, pp + 1 < p_end ? pid[pp + 1 - p_begin] : -1,
                                f);
 }
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ half4_t as_half4(uint2 w) { return __builtin_bit_cast(half4_t, w); }
 
 __device__ __forceinline__ void unpack4(uint2 w, float *x) {
   x[0] = half_bits_to_float(w.x & 0xFFFF);
@@ -330,7 +370,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 
   // Every argument the prologue needs, fetched from the argument segment in one round trip (left to
   // itself the compiler fetches them in several dependent rounds, each a full memory latency).
-  asm volatile("" ::"s"(a.pages), "s"(a.num_pages), "s"(a.page_bytes), "s"(a.k_codes), "s"(a.k_norms),
+  asm volatile("" ::"s"(a.pages), "s"(a.num_pages32), "s"(a.page_bytes), "s"(a.k_codes), "s"(a.k_norms),
                "s"(a.v_codes), "s"(a.v_norms), "s"(a.q), "s"(a.q_dtype), "s"(a.Hq), "s"(a.G), "s"(a.page_table),
                "s"(a.max_pages), "s"(a.seq_lens), "s"(a.kcb), "s"(a.vcb), "s"(a.ko.signs), "s"(a.ko.levels),
                "s"(a.vo.levels), "s"(a.pps), "s"(a.scale_log2), "s"(a.n_splits));
@@ -359,13 +399,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 
   // the run's pages in the table (p_begin .. p_cap) do not depend on the sequence length, so the page-id
   // reads are issued alongside the length read instead of after it
+  // runs of pps pages; the last run of a sequence also takes the remainder (fewer than pps pages)
+  const bool last_run = split == a.n_splits - 1;
   const int p_begin = split * a.pps;
-  const int p_cap = min(p_begin + a.pps, a.max_pages);
+  const int p_cap = last_run ? a.max_pages : min(p_begin + a.pps, a.max_pages);
   typedef const __attribute__((address_space(4))) int32_t *const_i32;  // read through the scalar cache
   int seq_len = ((const_i32)a.seq_lens)[b];
   seq_len = seq_len < 0 ? 0 : (seq_len > a.max_pages * TQ_PAGE_TOKENS ? a.max_pages * TQ_PAGE_TOKENS : seq_len);
   const int npages = (seq_len + TQ_PAGE_TOKENS - 1) / TQ_PAGE_TOKENS;
-  const int p_end = min(p_begin + a.pps, npages);
+  const int p_end = last_run ? npages : min(p_begin + a.pps, npages);
   const int npairs = p_end > p_begin ? (p_end - p_begin + 1) / 2 : 0;
 
   // ---- 0. the small global reads of the prologue, into registers first (memory returns in issue order,
@@ -437,7 +479,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     const int j = tid + u * NT;
     if (j < p_end - p_begin) {
       s_pid[j] = pgv[u];
-      pids_ok &= (pgv[u] >= 0 && pgv[u] < a.num_pages) ? 1 : 0;
+      pids_ok &= (pgv[u] >= 0 && pgv[u] < a.num_pages32) ? 1 : 0;
     }
   }
   if (tid < (1 << KB)) s_lutk[tid] = lk;
@@ -486,8 +528,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   }
   // a run of whole, valid page pairs needs no per-token masking; one barrier publishes the page ids,
   // level tables and rotated queries
-  const bool run_full = __syncthreads_and(pids_ok) && ((p_end - p_begin) % 2 == 0) &&
-                        p_end * TQ_PAGE_TOKENS <= seq_len;
+  // pairs [0, n_full) of the run hold only cached tokens of valid pages: they need no masking
+  const bool all_ok = __syncthreads_and(pids_ok);
+  const int full_end = min(p_end, seq_len / TQ_PAGE_TOKENS);
+  const int n_full = (all_ok && full_end > p_begin) ? (full_end - p_begin) / 2 : 0;
   if constexpr (KPROD) {
     // q_s = S (R q) sqrt(pi/2) / m with R q = (d * s_q) / sqrt(d)
     const float *S = (const float *)(a.kcb + a.ko.proj);
@@ -604,9 +648,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   auto process = [&](const F &cur, int pi, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int pp = p_begin + 2 * pi;
-    float s[2][4], nv[2][4];
+    float s[2][4];
+    half4_t nv[2];
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
+      if constexpr (!FULL) {
+        if (q2 == 1 && !cur.ok[1]) {  // a run's odd last page: no second page to score
+#pragma unroll
+          for (int j = 0; j < 4; ++j) s[1][j] = -3.0e38f;
+          nv[1] = half4_t{0, 0, 0, 0};
+          continue;
+        }
+      }
       floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KBLK; ++kb) {
@@ -643,11 +696,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) raw[j] = fmaf(gam[j] * skratio, acc2[j], raw[j]);
       }
-      float nk[4];
-      unpack4(cur.nk[q2], nk);
-      unpack4(cur.nv[q2], nv[q2]);
+      // the fp16 norms enter mixed-precision FMAs directly (fma with a zero addend, not folded to a
+      // multiply since signed zeros are kept)
+      const half4_t nk = as_half4(cur.nk[q2]);
+      nv[q2] = as_half4(cur.nv[q2]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s[q2][j] = nk[j] * raw[j];  // score / (softmax scale * log2 e)
+      for (int j = 0; j < 4; ++j) s[q2][j] = fmaf((float)nk[j], raw[j], 0.f);  // score / (softmax scale * log2 e)
     }
     // the V operands depend only on the codes: built here, their VALU work covers the latency of the
     // score MFMAs and of the softmax reductions below
@@ -665,7 +719,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
           const int t = (pp + q2) * TQ_PAGE_TOKENS + 4 * g4 + j;
           okm[q2][j] = cur.ok[q2] && t < seq_len;
           s[q2][j] = okm[q2][j] ? s[q2][j] : -3.0e38f;
-          nv[q2][j] = okm[q2][j] ? nv[q2][j] : 0.f;
+          nv[q2][j] = okm[q2][j] ? nv[q2][j] : (_Float16)0.f;
         }
     }
 
@@ -673,15 +727,21 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     // tokens 4*g4 .. 4*g4+3 of both pages
     float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    // m_run is the reference the weights are taken against; it only has to bound the scores seen so
+    // far. When a score passes it, the new reference is set kHeadroom above the new maximum, so the
+    // rescale (which any reference allows: it cancels between the sums and the weights) runs only on
+    // real jumps of the maximum. Weights stay <= 1, the largest >= 2^-kHeadroom.
     mx = max_xor32(max_xor16(mx));
-    const float m_new = fmaxf(m_run, colscale * mx);
+    const float m_new = colscale * mx;
     if (__any(m_new > m_run)) {
       // O holds head column c in this lane, as do m_run and l_part: the rescale stays in the lane
-      const float alpha = (m_new > m_run) ? ((m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new)) : 1.f;
+      const bool up = m_new > m_run;
+      const float m_ref = up ? m_new + kHeadroom : m_run;
+      const float alpha = up ? ((m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_ref)) : 1.f;
       l_part *= alpha;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) O[nb] *= alpha;
-      m_run = m_new;
+      m_run = m_ref;
     }
     half8_t phi, plo;
 #pragma unroll
@@ -695,7 +755,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
           p1 = okm[q2][j + 1] ? p1 : 0.f;
         }
         l_part += p0 + p1;
-        const float2_t pv = {p0 * nv[q2][j], p1 * nv[q2][j + 1]};
+        const float2_t pv = {fmaf((float)nv[q2][j], p0, 0.f), fmaf((float)nv[q2][j + 1], p1, 0.f)};
         const half2_t h = __builtin_convertvector(pv, half2_t);
         const half2_t l = __builtin_convertvector(pv - __builtin_convertvector(h, float2_t), half2_t);
         phi[4 * q2 + j] = h[0];
@@ -716,19 +776,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   };
 
   // ring of R fragments: R - 1 page pairs in flight while one is processed
-  auto stream_pairs = [&](auto full_tag) {
-    for (int i = wave; i < npairs; i += R * kWaves) {
+  for (int i = wave; i < npairs; i += R * kWaves) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int ii = i + r * kWaves;
-        const int nx = ii + (R - 1) * kWaves;
-        load_pair<D, KB, KPROD, VB>(a, s_pid, lo, p_begin + 2 * nx, p_begin, p_end, f[(r + R - 1) % R]);
-        if (ii < npairs) process(f[r], ii, full_tag);
-      }
+    for (int r = 0; r < R; ++r) {
+      const int ii = i + r * kWaves;
+      const int nx = ii + (R - 1) * kWaves;
+      load_pair<D, KB, KPROD, VB>(a, s_pid, lo, p_begin + 2 * nx, p_begin, p_end, f[(r + R - 1) % R]);
+      if (ii < n_full) process(f[r], ii, std::true_type{});
+      else if (ii < npairs) process(f[r], ii, std::false_type{});
     }
-  };
-  if (run_full) stream_pairs(std::true_type{});
-  else stream_pairs(std::false_type{});
+  }
 
   // ---- 4. merge the wavefronts of this work-group: rescale to the work-group max, then sum over the
   //         waves in a fixed order (deterministic). Lane (c, g4) holds head c (real when c < G) and,
@@ -1018,6 +1075,7 @@ int launch_decode(const PageGeom &g, const DecodeWs &ws, const void *pages, int6
   DecodeArgs a;
   a.pages = (const unsigned char *)pages;
   a.num_pages = num_pages;
+  a.num_pages32 = (int)std::min<int64_t>(num_pages, 0x7FFFFFFF);
   a.page_bytes = g.page_bytes;
   a.k_codes = g.k_codes;
   a.k_norms = g.k_norms;
