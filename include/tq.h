@@ -48,7 +48,7 @@ extern "C" {
 #define TQ_OK 0
 #define TQ_EINVAL (-1)   /* null pointer, unsupported shape, bit width or mode, bad blob */
 #define TQ_ENOSPC (-2)   /* a caller buffer is smaller than required */
-#define TQ_ENOTSUP (-3)  /* a valid combination this build does not implement */
+#define TQ_ENOTSUP (-3)  /* a valid combination this library does not implement */
 #define TQ_EHIP (-4)     /* the HIP runtime reported an error */
 
 /* ---- modes and dtypes ------------------------------------------------------------------ */

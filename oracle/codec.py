@@ -14,7 +14,7 @@ Sources
   "Why the KV Cache Exists", section on PagedAttention: fixed-size pages allocated
     on demand.
 
-Readings adopted where the pages are silent (each is listed in the design notes):
+Readings adopted where the pages are silent:
   * the vector norm n = ||x||_2 is stored as fp16 (round to nearest even); the
     direction u = x / n is formed with the unrounded n; a zero vector has n = 0
     and u = 0;
