@@ -153,7 +153,8 @@ int tq_page_layout(const tq_layout *layout, tq_page_offsets *out);
  *   k_cb, v_cb  device copies of blobs built for (head_dim, k_bits, k_mode) and (head_dim, v_bits,
  *               v_mode)
  * Each vector's record (codes, norm, and in prod mode sketch and residual norm) is written in full;
- * no other byte of the pool is touched. n_tok = 0 launches nothing.
+ * no other byte of the pool is touched. n_tok = 0 launches nothing; n_tok * num_kv_heads must stay
+ * below 2^35 (one launch).
  * Errors: TQ_EINVAL (layout, dtype, strides, null pointers), TQ_ENOTSUP, TQ_EHIP. */
 int tq_quantize_kv(const tq_layout *layout, void *pages, int64_t num_pages, const void *k,
                    const void *v, int dtype, int64_t n_tok, int64_t k_stride_tok,

@@ -4,9 +4,10 @@
 //   code_i = sign-magnitude form of idx_i, pack the b-bit codes, store n as fp16, and in prod mode also
 //   r = (y' - level[code]) / sqrt(d), gamma = ||r||, z_j = [(S r)_j >= 0].
 // One vector is handled by d/8 lanes that each own 8 consecutive coordinates: the three lowest
-// Walsh-Hadamard stages run in registers, the others exchange values between lanes. A lane's 8 codes
-// are exactly b whole bytes of the vector's bit stream, so each lane writes its own bytes: that is a
-// contiguous run for K records and one V piece.
+// Walsh-Hadamard stages run in registers, the others exchange values between lanes with DPP moves inside
+// 16-lane rows. A lane's 8 codes are exactly b whole bytes of the vector's bit stream, so each lane writes
+// its own bytes: a contiguous run for K records and one V piece. The vectors of a work-group are
+// consecutive tokens of one head, so the records they write are neighbours in a page.
 #include <hip/hip_runtime.h>
 
 #include "tq_common.h"
@@ -31,6 +32,9 @@ struct QuantArgs {
   int dtype;
 };
 
+typedef const __attribute__((address_space(4))) int32_t *const_i32;  // read through the scalar cache
+constexpr int kQuantVectorsPerLane = 1;
+
 // Eight consecutive elements of an input row (16-byte aligned) widened to fp32.
 __device__ __forceinline__ void load8(const void *p, int64_t i, int dtype, float *x) {
   if (dtype == TQ_F32) {
@@ -44,8 +48,8 @@ __device__ __forceinline__ void load8(const void *p, int64_t i, int dtype, float
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       if (dtype == TQ_BF16) {
-        x[2 * k] = bf16_bits_to_float((uint16_t)(d[k] & 0xFFFF));
-        x[2 * k + 1] = bf16_bits_to_float((uint16_t)(d[k] >> 16));
+        x[2 * k] = __uint_as_float(d[k] << 16);
+        x[2 * k + 1] = __uint_as_float(d[k] & 0xFFFF0000u);
       } else {
         x[2 * k] = half_bits_to_float((uint16_t)(d[k] & 0xFFFF));
         x[2 * k + 1] = half_bits_to_float((uint16_t)(d[k] >> 16));
@@ -54,46 +58,81 @@ __device__ __forceinline__ void load8(const void *p, int64_t i, int dtype, float
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Value of lane (lane ^ M) inside the lane's 16-lane row, M in {1, 2, 4, 8}: quad permutes for 1 and 2,
+// a half-row mirror (lane ^ 7) then a quad permute (lane ^ 3) for 4, a row rotation by 8 for 8.
+template <int M>
+__device__ __forceinline__ float xor_lane(float v) {
+  if constexpr (M == 1) return dpp<0xB1>(v);
+  else if constexpr (M == 2) return dpp<0x4E>(v);
+  else if constexpr (M == 4) return dpp<0x1B>(dpp<0x141>(v));
+  else {
+    static_assert(M == 8, "xor distance inside a 16-lane row");
+    return dpp<0x128>(v);
+  }
+}
+
+// Sum over the LANES lanes of a vector's group.
+template <int LANES>
+__device__ __forceinline__ float group_sum(float v) {
+  v += xor_lane<1>(v);
+  v += xor_lane<2>(v);
+  v += xor_lane<4>(v);
+  if constexpr (LANES == 16) v += xor_lane<8>(v);
+  return v;
+}
+
+// Walsh-Hadamard butterfly across lanes at distance M: (a, b) -> (a + b, a - b).
+template <int M>
+__device__ __forceinline__ void wht_lanes(float *x, int lane) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float p = xor_lane<M>(x[k]);
+    x[k] = (lane & M) ? (p - x[k]) : (x[k] + p);
+  }
+}
+
+// Magnitude part of the sign-magnitude code for B <= 4 bits: the number of positive thresholds P[1..]
+// at or below z (z and P as the integer bit patterns of non-negative floats, which order like the floats).
+// A binary search over the 2^(B-1) - 1 ascending positive thresholds, all in registers.
+template <int B>
+__device__ __forceinline__ int magnitude(int z, const int *P) {
+  if constexpr (B == 1) {
+    return 0;
+  } else if constexpr (B == 2) {
+    return z >= P[1] ? 1 : 0;
+  } else if constexpr (B == 3) {
+    const int m = z >= P[2] ? 2 : 0;
+    return m + (z >= (m ? P[3] : P[1]) ? 1 : 0);
+  } else {
+    static_assert(B == 4, "register search covers up to 4 bits");
+    int m = z >= P[4] ? 4 : 0;
+    m += z >= (m ? P[6] : P[2]) ? 2 : 0;
+    const int t = (m & 4) ? ((m & 2) ? P[7] : P[5]) : ((m & 2) ? P[3] : P[1]);
+    return m + (z >= t ? 1 : 0);
+  }
+}
+
+// One vector: norm, signs, rotation, codes, record write (and the prod-mode residual sketch).
+template <int D, bool PROD>
+__device__ __forceinline__ void quantize_vector(const QuantArgs &a, int which, float *x, int64_t slot, bool active,
+                                                int h, int lane, int vl, uint32_t sword, const int *P,
+                                                const float *s_th, const float *s_lv, float (*s_r)[D]) {
   constexpr int LANES = D / 8;
-  constexpr int VPB = 256 / LANES;
-  const int which = blockIdx.y;  // 0 = K, 1 = V
   const unsigned char *cb = a.cb[which];
   const BlobOffsets bo = a.cbo[which];
   const int b = a.bits[which];
-  const int mode = a.mode[which];
-  const int nl = 1 << b;
-
-  __shared__ float s_th[256];
-  __shared__ float s_lv[256];
-  __shared__ float s_r[VPB][D];
-
-  const int lane = threadIdx.x % LANES;
-  const int vl = threadIdx.x / LANES;
-  const int64_t vid = (int64_t)blockIdx.x * VPB + vl;
-  const bool active = vid < a.n_tok * a.H;
-  const int64_t tok = active ? vid / a.H : 0;
-  const int h = active ? (int)(vid % a.H) : 0;
-
-  // every global read issued before the first wait: slot, the lane's 8 inputs, its 8 sign bits, tables
-  const int64_t slot = active ? a.slots[tok] : -1;
-  float x[8];
-  if (active) load8(a.in[which], tok * a.stride[which] + (int64_t)h * D + 8 * lane, a.dtype, x);
-  else
-#pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = 0.f;
-  const uint32_t sword = ((const uint32_t *)(cb + bo.signs))[(8 * lane) >> 5];
-  for (int i = threadIdx.x; i < nl - 1; i += 256) s_th[i] = ((const float *)(cb + bo.thresholds))[i];
-  for (int i = threadIdx.x; i < nl; i += 256) s_lv[i] = half_bits_to_float(((const uint16_t *)(cb + bo.levels))[i]);
+  const int half = (1 << b) >> 1;
   const bool valid = active && slot >= 0 && slot < a.num_slots;
-  __syncthreads();
 
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) ss = fmaf(x[k], x[k], ss);
-#pragma unroll
-  for (int o = 1; o < LANES; o <<= 1) ss += __shfl_xor(ss, o, LANES);
+  ss = group_sum<LANES>(ss);
   const float n = sqrtf(ss);
   const float inv = n > 0.f ? 1.0f / n : 0.f;
 
@@ -113,28 +152,37 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
       }
     }
   }
-#pragma unroll
-  for (int o = 1; o < LANES; o <<= 1) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      float p = __shfl_xor(x[k], o, LANES);
-      x[k] = (lane & o) ? (p - x[k]) : (x[k] + p);
-    }
-  }
+  wht_lanes<1>(x, lane);
+  wht_lanes<2>(x, lane);
+  wht_lanes<4>(x, lane);
+  if constexpr (LANES == 16) wht_lanes<8>(x, lane);
 
-  // Lloyd-Max index (ties to the upper cell), then the stored sign-magnitude code: the top bit marks
-  // the non-negative half, the low bits count the rank away from zero.
-  int idx[8], code[8];
+  // Lloyd-Max index (ties to the upper cell) in its stored sign-magnitude form: the top bit marks the
+  // non-negative half, the low bits count the rank away from zero. For y < 0 the rank counts thresholds
+  // strictly below |y|, i.e. thresholds at or below the next float under |y|.
+  int code[8];
   float y[8];
-  const int half = nl >> 1;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     y[k] = x[k] * inv;
-    int c = 0;
-    for (int s = nl >> 1; s > 0; s >>= 1)
-      if (y[k] >= s_th[c + s - 1]) c += s;
-    idx[k] = c;
-    code[k] = c >= half ? c : half - 1 - c;
+    const bool neg = y[k] < 0.f;
+    const int z = (int)(__float_as_uint(y[k]) & 0x7FFFFFFFu) - (neg ? 1 : 0);
+    int mag;
+    if (b <= 4) {
+      switch (b) {
+        case 1: mag = magnitude<1>(z, P); break;
+        case 2: mag = magnitude<2>(z, P); break;
+        case 3: mag = magnitude<3>(z, P); break;
+        default: mag = magnitude<4>(z, P); break;
+      }
+    } else {
+      // wide codes: binary search over all thresholds in LDS, then the sign-magnitude form
+      int c = 0;
+      for (int st = half; st > 0; st >>= 1)
+        if (y[k] >= s_th[c + st - 1]) c += st;
+      mag = c >= half ? c - half : half - 1 - c;
+    }
+    code[k] = neg ? mag : (half | mag);
   }
 
   const int64_t page = valid ? slot / TQ_PAGE_TOKENS : 0;
@@ -159,18 +207,20 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
       *(uint16_t *)(pg + a.norms_off[which] + (int64_t)(h * TQ_PAGE_TOKENS + off) * 2) = float_to_half_bits(n);
   }
 
-  if (mode == TQ_PROD) {
+  if constexpr (PROD) {
     const float inv_sqrt_d = D == 128 ? 0.088388347648318440f : 0.125f;
     float r[8];
     float g2 = 0.f;
+    __syncthreads();  // the previous vector's residuals have been read
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      r[k] = (y[k] - s_lv[idx[k]]) * inv_sqrt_d;
+      // ascending index of the stored code
+      const int idx = (code[k] & half) ? code[k] : half - 1 - code[k];
+      r[k] = (y[k] - s_lv[idx]) * inv_sqrt_d;
       g2 = fmaf(r[k], r[k], g2);
       s_r[vl][8 * lane + k] = r[k];
     }
-#pragma unroll
-    for (int o = 1; o < LANES; o <<= 1) g2 += __shfl_xor(g2, o, LANES);
+    g2 = group_sum<LANES>(g2);
     __syncthreads();
     const float *S = (const float *)(cb + bo.proj);
     uint32_t zbits = 0;
@@ -188,6 +238,72 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
             float_to_half_bits(sqrtf(g2));
     }
   }
+}
+
+// A work-group holds NV * VPB consecutive tokens of one head (K or V by blockIdx.y); each lane group
+// takes NV of them and issues all their loads before computing any, to keep bytes in flight.
+template <int D>
+__global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
+  constexpr int LANES = D / 8;
+  constexpr int VPB = 256 / LANES;
+  constexpr int NV = kQuantVectorsPerLane;
+  const int which = blockIdx.y;  // 0 = K, 1 = V
+  const unsigned char *cb = a.cb[which];
+  const BlobOffsets bo = a.cbo[which];
+  const int b = a.bits[which];
+  const int mode = a.mode[which];
+  const int nl = 1 << b;
+  const int half = nl >> 1;
+
+  __shared__ float s_th[256];
+  __shared__ float s_lv[256];
+  __shared__ float s_r[VPB][D];
+
+  const int lane = threadIdx.x % LANES;
+  const int vl = threadIdx.x / LANES;
+  const int h = blockIdx.x % a.H;
+  const int64_t tok0 = (int64_t)(blockIdx.x / a.H) * (VPB * NV) + vl;
+
+  const uint32_t sword = ((const uint32_t *)(cb + bo.signs))[(8 * lane) >> 5];
+  // positive thresholds P[1 .. half-1] (t[half-1] is 0 by symmetry), as integer bit patterns
+  int P[8];
+  if (b <= 4) {
+    const const_i32 th = (const_i32)(cb + bo.thresholds);
+#pragma unroll
+    for (int m = 1; m < 8; ++m) P[m] = m < half ? th[half - 1 + m] : 0x7F800000;
+  }
+  if (b > 4 || mode == TQ_PROD) {
+    for (int i = threadIdx.x; i < nl - 1; i += 256) s_th[i] = ((const float *)(cb + bo.thresholds))[i];
+    for (int i = threadIdx.x; i < nl; i += 256) s_lv[i] = half_bits_to_float(((const uint16_t *)(cb + bo.levels))[i]);
+    __syncthreads();
+  }
+  if (mode == TQ_PROD) {
+    // the residual sketch reads the same rows of S for every vector: one vector at a time, so that the
+    // compiler does not hold those rows across vectors
+#pragma unroll 1
+    for (int j = 0; j < NV; ++j) {
+      const int64_t t = tok0 + (int64_t)j * VPB;
+      const int64_t tc = t < a.n_tok ? t : 0;
+      float x[8];
+      load8(a.in[which], tc * a.stride[which] + (int64_t)h * D + 8 * lane, a.dtype, x);
+      quantize_vector<D, true>(a, which, x, a.slots[tc], t < a.n_tok, h, lane, vl, sword, P, s_th, s_lv, s_r);
+    }
+    return;
+  }
+  // every input read issued before the first use: slots and the lane's 8 inputs of each vector
+  int64_t slot[NV];
+  float x[NV][8];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int64_t t = tok0 + (int64_t)j * VPB;
+    const int64_t tc = t < a.n_tok ? t : 0;
+    slot[j] = a.slots[tc];
+    load8(a.in[which], tc * a.stride[which] + (int64_t)h * D + 8 * lane, a.dtype, x[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+    quantize_vector<D, false>(a, which, x[j], slot[j], tok0 + (int64_t)j * VPB < a.n_tok, h, lane, vl, sword, P,
+                              s_th, s_lv, s_r);
 }
 
 }  // namespace
@@ -223,14 +339,13 @@ int launch_quantize(const PageGeom &g, void *pages, int64_t num_pages, const voi
   a.mode[1] = g.v_mode;
   a.H = g.num_kv_heads;
   a.dtype = dtype;
-  const int64_t nvec = n_tok * g.num_kv_heads;
-  if (g.head_dim == 128) {
-    dim3 grid((unsigned)((nvec + 15) / 16), 2);
-    hipLaunchKernelGGL(quantize_kernel<128>, grid, dim3(256), 0, stream, a);
-  } else {
-    dim3 grid((unsigned)((nvec + 31) / 32), 2);
-    hipLaunchKernelGGL(quantize_kernel<64>, grid, dim3(256), 0, stream, a);
-  }
+  // work-groups: (token groups x heads, K/V)
+  const int vpb = (g.head_dim == 128 ? 16 : 32) * kQuantVectorsPerLane;
+  const int64_t blocks = (n_tok + vpb - 1) / vpb * g.num_kv_heads;
+  if (blocks > 0x7FFFFFFF) return TQ_EINVAL;
+  dim3 grid((unsigned)blocks, 2);
+  if (g.head_dim == 128) hipLaunchKernelGGL(quantize_kernel<128>, grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(quantize_kernel<64>, grid, dim3(256), 0, stream, a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
 }
 
