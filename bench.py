@@ -3,20 +3,21 @@
 
 Workload: the Llama-3.1-8B single-layer cache (8 KV heads, 32 query heads, head_dim 128, batch 1,
 32768 cached tokens, K 4-bit / V 2-bit MSE, bf16 inputs). One step is one decode step of that workload:
-quantize-on-write of the new token's K and V (8 heads each) into its page slot, then decode attention
-of the new query over all cached tokens (rotation of q, split-K scores/softmax/value sums on the packed
-pages, merge and inverse rotation).
+quantize-on-write of the new token's K and V (8 heads each) into its page slot and decode attention of the
+new query over all cached tokens (rotation of q, split-K scores/softmax/value sums on the packed pages,
+merge and inverse rotation), as tq_decode_step: the work-group owning the new token's page quantizes it,
+so the step is one split-K launch plus the merge launch.
 
 The cache of one layer is 26 MB, which would stay in the 256 MB Infinity Cache if the same layer were
 read step after step. A real model reads every other layer's cache before it comes back to this one, so
 the benchmark cycles through ``--copies`` independent copies of the layer cache (16 x 26 MB by default,
 more than the Infinity Cache) and each step works on the next copy: every step's bytes come from HBM.
 
-Prints one JSON line. ``value`` is compressed-KV bytes read by decode attention per step divided by the
-wall time of the whole step (both kernels), in GB/s; ``roofline`` reports the decode kernel alone
-(algorithmic bytes per launch / its average launch duration from HIP events); ``quantize_vectors_per_s``
-is the quantize kernel's rate on the 32768-token prefill of the layer (524288 vectors);
-``cpu_baseline`` times the CPU oracle on a bounded sample of the same cache.
+Prints one JSON line. ``value`` is the step's algorithmic bytes (compressed-KV records of every cached token,
+the new token's K/V input, page ids) divided by the wall time of the whole step (both launches), in GB/s;
+``roofline`` reports the split-K launch alone (algorithmic bytes per launch / its average launch duration
+from HIP events); ``quantize_vectors_per_s`` is the quantize kernel's rate on the 32768-token prefill of the
+layer (524288 vectors); ``cpu_baseline`` times the CPU oracle on a bounded sample of the same cache.
 """
 from __future__ import annotations
 
@@ -41,7 +42,7 @@ def log(msg):
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("tq_decode.hip", "tq_common.h"):
+    for f in ("tq_decode.hip", "tq_common.h", "tq_quant_common.h"):
         with open(os.path.join(ROOT, "kv_cache_quantization_wht_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -154,26 +155,19 @@ def main():
         lens[c] = t + 1
         step_lens.append(torch.tensor([t + 1], dtype=torch.int32, device=dev))
         step_copy.append(c)
-        step_bytes.append(H * (t + 1) * rec_bytes + 4 * ((t + 1 + 15) // 16))
+        # records of every cached token (t read, the new one written), the new token's K/V input, page ids
+        step_bytes.append(H * (t + 1) * rec_bytes + H * 2 * d * 2 + 4 * ((t + 1 + 15) // 16))
     ws_bytes = tq.decode_workspace_bytes(layout, 1, Hq, pages_per_copy)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty(1, Hq, d, dtype=torch.float32, device=dev)
     scale = wl.softmax_scale
 
-    def step(i, ev=None):
-        # one decode step: append the new token's K/V, then decode attention in its two passes
-        # (tq_decode_partial + tq_decode_combine is exactly tq_decode_attention)
-        tq.quantize_kv(layout, pages, k_new[i:i + 1], v_new[i:i + 1], step_slots[i], kcb, vcb)
-        if ev is not None:
-            ev[0].record()
-        tq.decode_partial(layout, pages, qs[i], page_tables[step_copy[i]], step_lens[i], scale, kcb, vcb, ws,
-                          out=out)
-        if ev is not None:
-            ev[1].record()
-        tq.decode_combine(layout, pages, qs[i], page_tables[step_copy[i]], step_lens[i], scale, kcb, vcb, ws,
-                          out=out)
-        if ev is not None:
-            ev[2].record()
+    def step(i):
+        # one decode step: the new token's K and V are quantized into their slot and the new query attends
+        # over every cached token, in one split-K launch (tq_decode_step_partial) plus the merge
+        # (tq_decode_combine); tq_decode_step is exactly that pair
+        tq.decode_step(layout, pages, k_new[i:i + 1], v_new[i:i + 1], qs[i], page_tables[step_copy[i]], step_lens[i],
+                       scale, kcb, vcb, workspace=ws, out=out)
 
     for i in range(W):
         step(i)
@@ -225,7 +219,8 @@ def main():
         return e0.elapsed_time(e1) * 1e-3 / K
 
     def partial_only(i):
-        tq.decode_partial(layout, pages, qs[i], page_tables[step_copy[i]], step_lens[i], scale, kcb, vcb, ws, out=out)
+        tq.decode_step(layout, pages, k_new[i:i + 1], v_new[i:i + 1], qs[i], page_tables[step_copy[i]], step_lens[i],
+                       scale, kcb, vcb, workspace=ws, out=out, first_pass_only=True)
 
     def combine_only(i):
         tq.decode_combine(layout, pages, qs[i], page_tables[step_copy[i]], step_lens[i], scale, kcb, vcb, ws, out=out)
@@ -241,7 +236,11 @@ def main():
         if hasattr(torch.cuda, "_sleep"):
             torch.cuda._sleep(50_000_000)  # keep the GPU busy while every launch is queued
         for j, i in enumerate(range(W, total_steps)):
-            step(i, evs[j])
+            evs[j][0].record()
+            partial_only(i)
+            evs[j][1].record()
+            combine_only(i)
+            evs[j][2].record()
         torch.cuda.synchronize()
         durs = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
         comb = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
@@ -272,7 +271,7 @@ def main():
         "quantize_vectors_per_s": round(quant_vps, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_kernel<128,4,false,2> (tq_decode_partial)",
+                     "kernel": "decode_kernel<128,4,false,2,true> (tq_decode_step_partial)",
                      "bytes_per_launch": round(alg_per_launch), "avg_launch_us": round(kern_s * 1e6, 3),
                      "combine_avg_us": round(float(np.mean(comb)) * 1e6, 3), "timing": kmode},
         "cpu_baseline": None,

@@ -18,6 +18,10 @@
  *                       Integration Is a Kernel Problem"), with scores and value sums formed in the
  *                       rotated domain and one inverse rotation per output ("Closing - The
  *                       Three-Step Summary", Step 1: the rotation keeps inner products).
+ *   tq_decode_step, tq_decode_step_partial
+ *                       one decode step: append the new token of each sequence (quantized by the
+ *                       work-group that owns its page) and decode attention over the cache; and its
+ *                       first pass alone.
  *   tq_decode_partial, tq_decode_combine
  *                       the two passes of tq_decode_attention, callable one by one: the split-K
  *                       scan over the pages, then the merge of the runs and the inverse rotation.
@@ -191,6 +195,36 @@ int tq_decode_attention(const tq_layout *layout, const void *pages, int64_t num_
                         float softmax_scale, int pages_per_split, const void *k_cb,
                         const void *v_cb, void *workspace, size_t workspace_bytes, float *out,
                         void *stream);
+
+/* One decode step ("Where This Fits in the Inference Stack", "Production Deployment: Tensor Parallelism":
+ * quantize the new K/V before it reaches HBM; "Why the KV Cache Exists", "The KV Cache Solution": the new
+ * query attends over every cached token including its own): appends the new token of each sequence and
+ * runs decode attention, with the same page bytes and output as tq_quantize_kv of the new tokens into
+ * their slots followed by tq_decode_attention.
+ *   pages       device page pool (written: the new token's records)
+ *   k_new, v_new device [batch][num_kv_heads][head_dim] of kv_dtype (TQ_F32, TQ_BF16 or TQ_F16), 16-byte
+ *               aligned: K and V of the new token of each sequence
+ *   seq_lens    device int32 [batch], counting the new token: sequence b's new token is position
+ *               seq_lens[b] - 1, written to slot page_table[b][(seq_lens[b]-1)/16]*16 + (seq_lens[b]-1)%16
+ *               (skipped, and not attended, if that page id is outside [0, num_pages)); 0 appends
+ *               nothing and gives a zero row
+ * All other arguments as for tq_decode_attention. The work-group that owns the new token's page
+ * quantizes it and scores it from its codes, so the step is one split-K launch plus the merge.
+ * Errors: as tq_decode_attention; TQ_ENOTSUP unless K and V use MSE codes of at most 4 bits. */
+int tq_decode_step(const tq_layout *layout, void *pages, int64_t num_pages, const void *k_new,
+                   const void *v_new, int kv_dtype, const void *q, int q_dtype, int batch, int num_q_heads,
+                   const int32_t *page_table, int max_pages_per_seq, const int32_t *seq_lens,
+                   float softmax_scale, int pages_per_split, const void *k_cb, const void *v_cb,
+                   void *workspace, size_t workspace_bytes, float *out, void *stream);
+
+/* The first pass of tq_decode_step (append + split-K scan); tq_decode_combine with the same arguments
+ * (its own argument list) completes it, exactly as tq_decode_partial / tq_decode_combine complete
+ * tq_decode_attention. Arguments and errors as tq_decode_step. */
+int tq_decode_step_partial(const tq_layout *layout, void *pages, int64_t num_pages, const void *k_new,
+                           const void *v_new, int kv_dtype, const void *q, int q_dtype, int batch,
+                           int num_q_heads, const int32_t *page_table, int max_pages_per_seq,
+                           const int32_t *seq_lens, float softmax_scale, int pages_per_split, const void *k_cb,
+                           const void *v_cb, void *workspace, size_t workspace_bytes, float *out, void *stream);
 
 /* The two passes of tq_decode_attention. Called in this order on one stream with the same arguments,
  * they produce exactly the bytes tq_decode_attention produces (which is this pair of calls).

@@ -26,6 +26,7 @@ _LIB = None
 C_SYMBOLS = (
     "tq_strerror", "tq_codebook_bytes", "tq_build_codebook", "tq_page_layout", "tq_quantize_kv",
     "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_partial", "tq_decode_combine",
+    "tq_decode_step", "tq_decode_step_partial",
 )
 
 
@@ -65,6 +66,9 @@ def _lib():
                                             ctypes.c_float, i32, vp, vp, vp, sz, vp, vp]
         lib.tq_decode_combine.argtypes = [ctypes.POINTER(_Layout), vp, i64, vp, i32, i32, i32, vp, i32, vp,
                                             ctypes.c_float, i32, vp, vp, vp, sz, vp, vp]
+        for nm in ("tq_decode_step", "tq_decode_step_partial"):
+            getattr(lib, nm).argtypes = [ctypes.POINTER(_Layout), vp, i64, vp, vp, i32, vp, i32, i32, i32, vp, i32,
+                                         vp, ctypes.c_float, i32, vp, vp, vp, sz, vp, vp]
         for name in C_SYMBOLS:
             getattr(lib, name).restype = ctypes.c_char_p if name == "tq_strerror" else ctypes.c_int
         _LIB = lib
@@ -232,3 +236,50 @@ def decode_combine(layout: Layout, pages, q, page_table, seq_lens, softmax_scale
     """Second pass of decode_attention (merge of the runs, inverse rotation into ``out``); same arguments."""
     return _decode_call("tq_decode_combine", layout, pages, q, page_table, seq_lens, softmax_scale, k_cb, v_cb,
                         workspace, out, pages_per_split, stream)
+
+
+def decode_step(layout: Layout, pages, k_new, v_new, q, page_table, seq_lens, softmax_scale, k_cb, v_cb,
+                workspace=None, out=None, pages_per_split: int = 0, stream=None, first_pass_only: bool = False):
+    """Append the new token of each sequence (k_new, v_new [batch, num_kv_heads, head_dim], position
+    seq_lens[b] - 1) and run decode attention for q [batch, num_q_heads, head_dim]; returns fp32 out.
+    ``first_pass_only`` calls tq_decode_step_partial (finish with decode_combine on the same workspace)."""
+    import torch
+
+    _need(pages, "pages", torch.uint8)
+    _need(q, "q")
+    _need(page_table, "page_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(t, name)
+        if t.dim() != 3 or t.shape[1] != layout.num_kv_heads or t.shape[2] != layout.head_dim or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [batch, num_kv_heads, head_dim] tensor")
+    if k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must share a dtype")
+    if q.dim() != 3 or q.shape[2] != layout.head_dim or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [batch, num_q_heads, head_dim] tensor")
+    B, Hq, _ = q.shape
+    if k_new.shape[0] != B or v_new.shape[0] != B:
+        raise ValueError("k_new / v_new need one row per sequence")
+    if page_table.dim() != 2 or page_table.shape[0] != B or not page_table.is_contiguous():
+        raise ValueError("page_table must be a contiguous [batch, max_pages_per_seq] int32 tensor")
+    if seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must hold one int32 per sequence")
+    maxp = page_table.shape[1]
+    need = decode_workspace_bytes(layout, B, Hq, maxp, pages_per_split)
+    if workspace is None:
+        if first_pass_only:
+            raise ValueError("the first pass alone needs the caller's workspace (shared with decode_combine)")
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(B, Hq, layout.head_dim, dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32)
+    if out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor shaped like q")
+    num_pages = pages.numel() // page_layout(layout)["page_bytes"]
+    entry = "tq_decode_step_partial" if first_pass_only else "tq_decode_step"
+    _check(getattr(_lib(), entry)(ctypes.byref(layout.c()), pages.data_ptr(), num_pages, k_new.data_ptr(),
+                                 v_new.data_ptr(), _dtype_code(k_new), q.data_ptr(), _dtype_code(q), B, Hq,
+                                 page_table.data_ptr(), maxp, seq_lens.data_ptr(), float(softmax_scale),
+                                 pages_per_split, k_cb.data_ptr(), v_cb.data_ptr(), workspace.data_ptr(),
+                                 workspace.numel(), out.data_ptr(), _stream(stream)), entry)
+    return out

@@ -26,15 +26,22 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
-SOURCES = ["tq_capi.cpp", "tq_quantize.hip", "tq_decode.hip"]
-# decode: no NaN reaches a max or compare on the product path (masked scores are finite), so the
-# NaN-quieting copies in front of every max are dropped
-EXTRA = {"tq_decode.hip": ["-fno-honor-nans"]}
+# (source, object, extra flags). The decode source is compiled in two parts (head_dim 128 with the
+# launcher, head_dim 64) so the two halves of its kernel instantiations build in parallel. No NaN reaches
+# a max or compare on the decode path (masked scores are finite), so the NaN-quieting copies in front of
+# every max are dropped there.
+SOURCES = [
+    ("tq_capi.cpp", "tq_capi.o", []),
+    ("tq_quantize.hip", "tq_quantize.o", []),
+    ("tq_decode.hip", "tq_decode_d128.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=1"]),
+    ("tq_decode.hip", "tq_decode_d64.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=2"]),
+]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(entry) -> str:
+    src, obj_name, extra = entry
+    obj = os.path.join(BUILD, obj_name)
+    cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

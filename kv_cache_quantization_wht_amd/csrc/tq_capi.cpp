@@ -373,7 +373,8 @@ static int decode_passes(const tq_layout *layout, const void *pages, int64_t num
                          int q_dtype, int batch, int num_q_heads, const int32_t *page_table,
                          int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
                          int pages_per_split, const void *k_cb, const void *v_cb, void *workspace,
-                         size_t workspace_bytes, float *out, int passes, void *stream) {
+                         size_t workspace_bytes, float *out, int passes, void *stream,
+                         const void *k_new = nullptr, const void *v_new = nullptr, int kv_dtype = TQ_BF16) {
   tq::PageGeom g;
   int st = tq::make_geom(layout, &g);
   if (st) return st;
@@ -391,7 +392,7 @@ static int decode_passes(const tq_layout *layout, const void *pages, int64_t num
   if (workspace_bytes < ws.total) return TQ_ENOSPC;
   return tq::launch_decode(g, ws, pages, num_pages, q, q_dtype, batch, num_q_heads, page_table,
                            max_pages_per_seq, seq_lens, softmax_scale, k_cb, v_cb, workspace, out, passes,
-                           (hipStream_t)stream);
+                           k_new, v_new, kv_dtype, (hipStream_t)stream);
 }
 
 int tq_decode_attention(const tq_layout *layout, const void *pages, int64_t num_pages,
@@ -403,6 +404,44 @@ int tq_decode_attention(const tq_layout *layout, const void *pages, int64_t num_
   return decode_passes(layout, pages, num_pages, q, q_dtype, batch, num_q_heads, page_table, max_pages_per_seq,
                        seq_lens, softmax_scale, pages_per_split, k_cb, v_cb, workspace, workspace_bytes, out,
                        tq::kPassScan | tq::kPassCombine, stream);
+}
+
+static int decode_step_passes(const tq_layout *layout, void *pages, int64_t num_pages, const void *k_new,
+                              const void *v_new, int kv_dtype, const void *q, int q_dtype, int batch,
+                              int num_q_heads, const int32_t *page_table, int max_pages_per_seq,
+                              const int32_t *seq_lens, float softmax_scale, int pages_per_split,
+                              const void *k_cb, const void *v_cb, void *workspace, size_t workspace_bytes,
+                              float *out, int passes, void *stream) {
+  tq::PageGeom g;
+  int st = tq::make_geom(layout, &g);
+  if (st) return st;
+  if (kv_dtype != TQ_F32 && kv_dtype != TQ_BF16 && kv_dtype != TQ_F16) return TQ_EINVAL;
+  if (batch > 0 && (!k_new || !v_new || (((uintptr_t)k_new | (uintptr_t)v_new) & 15))) return TQ_EINVAL;
+  // the appending work-group quantizes with register thresholds: MSE codes of up to 4 bits
+  if (g.k_mode != TQ_MSE || g.v_mode != TQ_MSE || g.k_mse_bits > 4 || g.v_mse_bits > 4) return TQ_ENOTSUP;
+  return decode_passes(layout, pages, num_pages, q, q_dtype, batch, num_q_heads, page_table, max_pages_per_seq,
+                       seq_lens, softmax_scale, pages_per_split, k_cb, v_cb, workspace, workspace_bytes, out,
+                       passes, stream, k_new, v_new, kv_dtype);
+}
+
+int tq_decode_step(const tq_layout *layout, void *pages, int64_t num_pages, const void *k_new,
+                   const void *v_new, int kv_dtype, const void *q, int q_dtype, int batch, int num_q_heads,
+                   const int32_t *page_table, int max_pages_per_seq, const int32_t *seq_lens,
+                   float softmax_scale, int pages_per_split, const void *k_cb, const void *v_cb,
+                   void *workspace, size_t workspace_bytes, float *out, void *stream) {
+  return decode_step_passes(layout, pages, num_pages, k_new, v_new, kv_dtype, q, q_dtype, batch, num_q_heads,
+                            page_table, max_pages_per_seq, seq_lens, softmax_scale, pages_per_split, k_cb, v_cb,
+                            workspace, workspace_bytes, out, tq::kPassScan | tq::kPassCombine, stream);
+}
+
+int tq_decode_step_partial(const tq_layout *layout, void *pages, int64_t num_pages, const void *k_new,
+                           const void *v_new, int kv_dtype, const void *q, int q_dtype, int batch,
+                           int num_q_heads, const int32_t *page_table, int max_pages_per_seq,
+                           const int32_t *seq_lens, float softmax_scale, int pages_per_split, const void *k_cb,
+                           const void *v_cb, void *workspace, size_t workspace_bytes, float *out, void *stream) {
+  return decode_step_passes(layout, pages, num_pages, k_new, v_new, kv_dtype, q, q_dtype, batch, num_q_heads,
+                            page_table, max_pages_per_seq, seq_lens, softmax_scale, pages_per_split, k_cb, v_cb,
+                            workspace, workspace_bytes, out, tq::kPassScan, stream);
 }
 
 int tq_decode_partial(const tq_layout *layout, const void *pages, int64_t num_pages, const void *q,

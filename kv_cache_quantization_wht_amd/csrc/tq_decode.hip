@@ -25,16 +25,11 @@
 
 #include "tq_common.h"
 #include "tq_internal.h"
+#include "tq_quant_common.h"
 
 namespace tq {
-namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kHeadroom = 4.0f;  // log2 units between the running maximum and the weight reference
-constexpr int kWaves = 8;
-constexpr int kMlCap = 2048;   // split partials merged by one combine work-group
-constexpr int kPidCap = 4096;  // page ids of one run held in LDS
-
+// Arguments of one decode launch (split-K kernel and merge kernel).
 struct DecodeArgs {
   const unsigned char *pages;
   int64_t num_pages;
@@ -54,7 +49,19 @@ struct DecodeArgs {
   int n_splits, pps;
   float *out;
   int passes;  // kPassScan and/or kPassCombine
+  // decode step (append): the new token of each sequence, quantized by the work-group that owns its page
+  const void *k_new, *v_new;
+  int kv_dtype;
 };
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kHeadroom = 4.0f;  // log2 units between the running maximum and the weight reference
+constexpr int kWaves = 8;
+constexpr int kMlCap = 2048;   // split partials merged by one combine work-group
+constexpr int kPidCap = 4096;  // page ids of one run held in LDS
+
 
 // Largest power of two sigma with max|x| * sigma < 256 (1 if x is all zero).
 __device__ __forceinline__ float range_factor(float maxabs) {
@@ -360,7 +367,89 @@ __device__ __forceinline__ void lds_wht(float (*buf)[D], int rows, int tid) {
   }
 }
 
-template <int D, int KB, bool KPROD, int VB>
+// One appended vector (K or V of the new token of one head), in two steps so that its reads join the
+// prologue's first round of reads: load (input row, sign word, positive thresholds), then quantize: the
+// d/8 lanes of its lane group quantize it exactly as the quantize kernel does, write its codes and fp16
+// norm into the page slot, and leave the fp16 levels of its codes (as fp32, one per coordinate) and the
+// rounded norm in LDS for the scoring of the new token.
+struct AppendIn {
+  float x[8];
+  uint32_t sword;
+  PosThresholds P;
+};
+
+// K lanes and V lanes run the same instruction stream: the code width is a per-lane value, the search
+// counts over thresholds padded with +inf, and only the final byte stores differ.
+template <int D>
+__device__ __forceinline__ void append_load(const DecodeArgs &a, bool is_v, int nbits, int kvh, int lq,
+                                            AppendIn &in) {
+  const void *src = is_v ? a.v_new : a.k_new;
+  const unsigned char *cb = is_v ? a.vcb : a.kcb;
+  const BlobOffsets bo = is_v ? a.vo : a.ko;
+  load8(src, ((int64_t)blockIdx.z * a.Hkv + kvh) * D + 8 * lq, a.kv_dtype, in.x);
+  in.sword = ((const uint32_t *)(cb + bo.signs))[(8 * lq) >> 5];
+  in.P = pos_thresholds((const int *)(cb + bo.thresholds), (1 << nbits) >> 1);
+}
+
+template <int D, int KB, int VB>
+__device__ __forceinline__ void append_quantize(const DecodeArgs &a, bool is_v, int kvh, int lq, AppendIn &in,
+                                                int64_t page_off, int slot, const uint16_t *lut, float *s_lev,
+                                                float *s_norm) {
+  const int nbits = is_v ? VB : KB;
+  const int half = (1 << nbits) >> 1;
+  float *x = in.x;
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) ss = fmaf(x[k], x[k], ss);
+  ss = group_sum<D / 8>(ss);
+  const float n = sqrtf(ss);
+  const float inv = n > 0.f ? 1.0f / n : 0.f;
+  const uint32_t sbits = (in.sword >> ((8 * lq) & 31)) & 0xFFu;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if ((sbits >> k) & 1u) x[k] = -x[k];
+#pragma unroll
+  for (int hs = 1; hs < 8; hs <<= 1) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (!(k & hs)) {
+        const float u = x[k], w = x[k + hs];
+        x[k] = u + w;
+        x[k + hs] = u - w;
+      }
+    }
+  }
+  wht_lanes<1>(x, lq);
+  wht_lanes<2>(x, lq);
+  wht_lanes<4>(x, lq);
+  if constexpr (D == 128) wht_lanes<8>(x, lq);
+  uint32_t packed = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float y = x[k] * inv;
+    const bool neg = y < 0.f;
+    const int z = (int)(__float_as_uint(y) & 0x7FFFFFFFu) - (neg ? 1 : 0);
+    const int mag = magnitude_count<4>(z, in.P);  // thresholds past the code's own are +inf
+    const int code = neg ? mag : (half | mag);
+    packed |= (uint32_t)code << (nbits * k);
+    s_lev[8 * lq + k] = half_bits_to_float(lut[code]);  // the stored fp16 level of the code
+  }
+  const uint16_t n16 = float_to_half_bits(n);
+  if (lq == 0) *s_norm = half_bits_to_float(n16);
+  unsigned char *pg = (unsigned char *)a.pages + page_off;
+  unsigned char *dst = is_v ? pg + a.v_codes + ((int64_t)(kvh * (D / 8) + lq) * TQ_PAGE_TOKENS + slot) * VB
+                            : pg + a.k_codes + (int64_t)(kvh * TQ_PAGE_TOKENS + slot) * (D * KB / 8) + lq * KB;
+  switch (nbits) {  // a lane's 8 codes are nbits whole bytes
+    case 1: *dst = (unsigned char)packed; break;
+    case 2: *(uint16_t *)dst = (uint16_t)packed; break;
+    case 4: *(uint32_t *)dst = packed; break;
+    default:
+      for (int i = 0; i < nbits; ++i) dst[i] = (unsigned char)(packed >> (8 * i));
+  }
+  if (lq == 0) *(uint16_t *)(pg + (is_v ? a.v_norms : a.k_norms) + (int64_t)(kvh * TQ_PAGE_TOKENS + slot) * 2) = n16;
+}
+
+template <int D, int KB, bool KPROD, int VB, bool APPEND>
 __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   constexpr int NT = 64 * kWaves;
   constexpr int KBLK = D / 32;  // 32-coordinate blocks of the score contraction
@@ -394,6 +483,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   __shared__ uint16_t s_lutv[1 << VB];
   __shared__ float s_m[kWaves][16], s_l[kWaves][16];
   __shared__ float s_rowm[16], s_rowl[16];
+  __shared__ __align__(16) float s_newlev[APPEND ? 2 : 1][APPEND ? D : 4];  // appended token: K and V levels
+  __shared__ float s_newnorm[2];
   float(*s_q)[QS] = (float(*)[QS])arena;              // rotated queries / d
   float(*s_qs)[QS] = (float(*)[QS])(arena + 16 * QS);  // sketch-domain queries
 
@@ -409,6 +500,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   const int npages = (seq_len + TQ_PAGE_TOKENS - 1) / TQ_PAGE_TOKENS;
   const int p_end = last_run ? npages : min(p_begin + a.pps, npages);
   const int npairs = p_end > p_begin ? (p_end - p_begin + 1) / 2 : 0;
+  // decode step: position seq_len - 1 is the appended token; the page loop reads positions before it
+  // and the work-group owning its page scores it from the codes it quantizes itself
+  const int seq_mem = APPEND ? max(seq_len - 1, 0) : seq_len;
+  const bool own_new = APPEND && seq_len >= 1 && (seq_len - 1) / TQ_PAGE_TOKENS >= p_begin &&
+                       (seq_len - 1) / TQ_PAGE_TOKENS < p_end;
 
   // ---- 0. the small global reads of the prologue, into registers first (memory returns in issue order,
   //         so these must not queue behind the page data): page ids of the run, this wavefront's query
@@ -425,6 +521,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       first_ids[r][0] = pp < p_cap ? ptab[pp] : -1;
       first_ids[r][1] = pp + 1 < p_cap ? ptab[pp + 1] : -1;
     }
+  }
+  // decode step: the appending wavefront's reads of the new K (lanes 0..) and V (lanes 32..)
+  AppendIn app;
+  const bool app_lane = APPEND && wave == kWaves - 1 && (lane & 31) < D / 8;
+  if constexpr (APPEND) {
+    if (app_lane) append_load<D>(a, lane >= 32, lane >= 32 ? VB : KB, kvh, lane & 31, app);
   }
   // No loaded value is used (converted, compared, selected) before the page loads of step 1 are issued:
   // addresses are clamped in bounds instead, so no wait lands here.
@@ -485,6 +587,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   if (tid < (1 << KB)) s_lutk[tid] = lk;
   if (tid < (1 << VB)) s_lutv[tid] = lv;
 
+  // ---- 1b. decode step: is the new token's page this run's, and a valid page?
+  bool new_ok = false;
+  int new_pg = 0;
+  if constexpr (APPEND) {
+    if (own_new) {
+      new_pg = ((const_i32)a.page_table)[(int64_t)b * a.max_pages + (seq_len - 1) / TQ_PAGE_TOKENS];
+      new_ok = new_pg >= 0 && new_pg < a.num_pages32;
+    }
+  }
+
   // ---- 2. query rotation, one row per wavefront: H (s * q) with cross-lane butterflies (no barrier
   //         needed before: the row and the signs are this wavefront's own loads)
   {
@@ -530,7 +642,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   // level tables and rotated queries
   // pairs [0, n_full) of the run hold only cached tokens of valid pages: they need no masking
   const bool all_ok = __syncthreads_and(pids_ok);
-  const int full_end = min(p_end, seq_len / TQ_PAGE_TOKENS);
+  const int full_end = min(p_end, seq_mem / TQ_PAGE_TOKENS);
   const int n_full = (all_ok && full_end > p_begin) ? (full_end - p_begin) / 2 : 0;
   if constexpr (KPROD) {
     // q_s = S (R q) sqrt(pi/2) / m with R q = (d * s_q) / sqrt(d)
@@ -605,6 +717,47 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   floatx4_t O[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) O[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  if constexpr (APPEND) {
+    // The last wavefront quantizes the appended K (lanes 0..) and V (lanes 32..) of this KV head into the
+    // new token's slot (after the barrier: no other wavefront waits for it), then starts its softmax state
+    // with the new token: score from the fp16 levels of its codes and its fp16 norm (as the page would give
+    // them), weight and value sum at the reference.
+    if (own_new && new_ok && wave == kWaves - 1) {
+      if (app_lane) {
+        const bool is_v = lane >= 32;
+        append_quantize<D, KB, VB>(a, is_v, kvh, lane & 31, app, (int64_t)new_pg * a.page_bytes,
+                                   (seq_len - 1) % TQ_PAGE_TOKENS, is_v ? s_lutv : s_lutk,
+                                   s_newlev[is_v ? (APPEND ? 1 : 0) : 0], &s_newnorm[is_v ? 1 : 0]);
+      }
+      const int r = c < G ? c : 0;
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < D / 4; i += 4) {
+        const int coord = (D / 4) * g4 + i;
+        const float4 qv = *(const float4 *)&s_q[r][coord];
+        const float4 kv = *(const float4 *)&s_newlev[0][coord];
+        part = fmaf(qv.x, kv.x, fmaf(qv.y, kv.y, fmaf(qv.z, kv.z, fmaf(qv.w, kv.w, part))));
+      }
+      const float raw = sum_xor16_32(part);
+      if (c < G) {
+        const float x = s_newnorm[0] * raw * a.scale_log2;
+        m_run = x + kHeadroom;
+        const float p = fast_exp2(-kHeadroom);
+        l_part = g4 == 0 ? p : 0.f;
+        const float pv = p * s_newnorm[1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int nb = 0; nb < NB; nb += 4) {
+            const float4 vv = *(const float4 *)&s_newlev[APPEND ? 1 : 0][(D / 16) * (4 * g4 + j) + nb];
+            O[nb][j] = pv * vv.x;
+            O[nb + 1][j] = pv * vv.y;
+            O[nb + 2][j] = pv * vv.z;
+            O[nb + 3][j] = pv * vv.w;
+          }
+      }
+    }
+  }
 
   // fp16 V levels of one page pair as MFMA operands: Bop[nb] holds, for lane (c, g4), the level of
   // coordinate (D / 16) * c + nb for the 8 tokens of contraction rows 8 * g4 .. 8 * g4 + 7.
@@ -703,10 +856,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) s[q2][j] = fmaf((float)nk[j], raw[j], 0.f);  // score / (softmax scale * log2 e)
     }
-    // the V operands depend only on the codes: built here, their VALU work covers the latency of the
-    // score MFMAs and of the softmax reductions below
-    half8_t Bop[NB];
-    v_operands(cur, Bop);
 
     // tokens past the sequence end or in an invalid page: weight 0 (their bytes are not read as numbers).
     // A masked score is a finite, very negative value so that a zero softmax scale never meets an infinity.
@@ -717,7 +866,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t = (pp + q2) * TQ_PAGE_TOKENS + 4 * g4 + j;
-          okm[q2][j] = cur.ok[q2] && t < seq_len;
+          okm[q2][j] = cur.ok[q2] && t < seq_mem;
           s[q2][j] = okm[q2][j] ? s[q2][j] : -3.0e38f;
           nv[q2][j] = okm[q2][j] ? nv[q2][j] : (_Float16)0.f;
         }
@@ -768,6 +917,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     // values, transposed: O^T[coords][head columns] += Vhat^T[coords][32 tokens] * P'^T[32 tokens][heads].
     // The V operand registers are the same as for Vhat as the right-hand operand; swapping the operands
     // of the MFMA puts the query heads in the columns, next to their softmax state.
+    half8_t Bop[NB];
+    v_operands(cur, Bop);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Bop[nb], phi, O[nb], 0, 0, 0);
@@ -1027,7 +1178,15 @@ template <int D, int KB, bool KPROD, int VB>
 void launch(const DecodeArgs &a, hipStream_t stream) {
   if (a.passes & kPassScan) {
     dim3 grid(a.n_splits, a.Hkv, a.B);
-    hipLaunchKernelGGL((decode_kernel<D, KB, KPROD, VB>), grid, dim3(64 * kWaves), 0, stream, a);
+    if constexpr (!KPROD && KB <= 4 && VB <= 4) {
+      if (a.k_new) {
+        hipLaunchKernelGGL((decode_kernel<D, KB, KPROD, VB, true>), grid, dim3(64 * kWaves), 0, stream, a);
+      } else {
+        hipLaunchKernelGGL((decode_kernel<D, KB, KPROD, VB, false>), grid, dim3(64 * kWaves), 0, stream, a);
+      }
+    } else {
+      hipLaunchKernelGGL((decode_kernel<D, KB, KPROD, VB, false>), grid, dim3(64 * kWaves), 0, stream, a);
+    }
   }
   if ((a.passes & kPassCombine) && a.n_splits > 1)
     hipLaunchKernelGGL(combine_kernel<D>, dim3(a.B * a.Hq), dim3(256), 0, stream, a);
@@ -1067,12 +1226,32 @@ bool dispatch_k(int kb, bool kprod, int vb, const DecodeArgs &a, hipStream_t s) 
 
 }  // namespace
 
+// The kernels are instantiated per head dimension in separate objects (this file is compiled once per
+// part, in parallel): part 1 holds head_dim 128 and the launcher, part 2 head_dim 64; no part = both.
+bool decode_dispatch_d128(int kb, bool kprod, int vb, const DecodeArgs &a, hipStream_t s);
+bool decode_dispatch_d64(int kb, bool kprod, int vb, const DecodeArgs &a, hipStream_t s);
+
+#if !defined(TQ_DECODE_PART) || TQ_DECODE_PART == 1
+bool decode_dispatch_d128(int kb, bool kprod, int vb, const DecodeArgs &a, hipStream_t s) {
+  return dispatch_k<128>(kb, kprod, vb, a, s);
+}
+#endif
+#if !defined(TQ_DECODE_PART) || TQ_DECODE_PART == 2
+bool decode_dispatch_d64(int kb, bool kprod, int vb, const DecodeArgs &a, hipStream_t s) {
+  return dispatch_k<64>(kb, kprod, vb, a, s);
+}
+#endif
+
+#if !defined(TQ_DECODE_PART) || TQ_DECODE_PART == 1
 int launch_decode(const PageGeom &g, const DecodeWs &ws, const void *pages, int64_t num_pages,
                   const void *q, int q_dtype, int batch, int num_q_heads, const int32_t *page_table,
                   int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
                   const void *k_cb, const void *v_cb, void *workspace, float *out,
-                  int passes, hipStream_t stream) {
+                  int passes, const void *k_new, const void *v_new, int kv_dtype, hipStream_t stream) {
   DecodeArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.kv_dtype = kv_dtype;
   a.pages = (const unsigned char *)pages;
   a.num_pages = num_pages;
   a.num_pages32 = (int)std::min<int64_t>(num_pages, 0x7FFFFFFF);
@@ -1105,10 +1284,11 @@ int launch_decode(const PageGeom &g, const DecodeWs &ws, const void *pages, int6
   a.out = out;
   a.passes = passes;
   const bool kprod = g.k_mode == TQ_PROD;
-  const bool ok = g.head_dim == 128 ? dispatch_k<128>(g.k_mse_bits, kprod, g.v_mse_bits, a, stream)
-                                    : dispatch_k<64>(g.k_mse_bits, kprod, g.v_mse_bits, a, stream);
+  const bool ok = g.head_dim == 128 ? decode_dispatch_d128(g.k_mse_bits, kprod, g.v_mse_bits, a, stream)
+                                    : decode_dispatch_d64(g.k_mse_bits, kprod, g.v_mse_bits, a, stream);
   if (!ok) return TQ_ENOTSUP;
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
 }
+#endif
 
 }  // namespace tq

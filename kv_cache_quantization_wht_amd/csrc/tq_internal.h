@@ -58,6 +58,6 @@ int launch_decode(const PageGeom &g, const DecodeWs &ws, const void *pages, int6
                   const void *q, int q_dtype, int batch, int num_q_heads, const int32_t *page_table,
                   int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
                   const void *k_cb, const void *v_cb, void *workspace, float *out,
-                  int passes, hipStream_t stream);
+                  int passes, const void *k_new, const void *v_new, int kv_dtype, hipStream_t stream);
 
 }  // namespace tq

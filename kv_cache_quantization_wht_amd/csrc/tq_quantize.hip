@@ -12,6 +12,7 @@
 
 #include "tq_common.h"
 #include "tq_internal.h"
+#include "tq_quant_common.h"
 
 namespace tq {
 namespace {
@@ -32,95 +33,12 @@ struct QuantArgs {
   int dtype;
 };
 
-typedef const __attribute__((address_space(4))) int32_t *const_i32;  // read through the scalar cache
 constexpr int kQuantVectorsPerLane = 1;
-
-// Eight consecutive elements of an input row (16-byte aligned) widened to fp32.
-__device__ __forceinline__ void load8(const void *p, int64_t i, int dtype, float *x) {
-  if (dtype == TQ_F32) {
-    const float4 u = *(const float4 *)((const float *)p + i);
-    const float4 w = *(const float4 *)((const float *)p + i + 4);
-    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
-    x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
-  } else {
-    const uint4 u = *(const uint4 *)((const uint16_t *)p + i);
-    const uint32_t d[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (dtype == TQ_BF16) {
-        x[2 * k] = __uint_as_float(d[k] << 16);
-        x[2 * k + 1] = __uint_as_float(d[k] & 0xFFFF0000u);
-      } else {
-        x[2 * k] = half_bits_to_float((uint16_t)(d[k] & 0xFFFF));
-        x[2 * k + 1] = half_bits_to_float((uint16_t)(d[k] >> 16));
-      }
-    }
-  }
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// Value of lane (lane ^ M) inside the lane's 16-lane row, M in {1, 2, 4, 8}: quad permutes for 1 and 2,
-// a half-row mirror (lane ^ 7) then a quad permute (lane ^ 3) for 4, a row rotation by 8 for 8.
-template <int M>
-__device__ __forceinline__ float xor_lane(float v) {
-  if constexpr (M == 1) return dpp<0xB1>(v);
-  else if constexpr (M == 2) return dpp<0x4E>(v);
-  else if constexpr (M == 4) return dpp<0x1B>(dpp<0x141>(v));
-  else {
-    static_assert(M == 8, "xor distance inside a 16-lane row");
-    return dpp<0x128>(v);
-  }
-}
-
-// Sum over the LANES lanes of a vector's group.
-template <int LANES>
-__device__ __forceinline__ float group_sum(float v) {
-  v += xor_lane<1>(v);
-  v += xor_lane<2>(v);
-  v += xor_lane<4>(v);
-  if constexpr (LANES == 16) v += xor_lane<8>(v);
-  return v;
-}
-
-// Walsh-Hadamard butterfly across lanes at distance M: (a, b) -> (a + b, a - b).
-template <int M>
-__device__ __forceinline__ void wht_lanes(float *x, int lane) {
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float p = xor_lane<M>(x[k]);
-    x[k] = (lane & M) ? (p - x[k]) : (x[k] + p);
-  }
-}
-
-// Magnitude part of the sign-magnitude code for B <= 4 bits: the number of positive thresholds P[1..]
-// at or below z (z and P as the integer bit patterns of non-negative floats, which order like the floats).
-// A binary search over the 2^(B-1) - 1 ascending positive thresholds, all in registers.
-template <int B>
-__device__ __forceinline__ int magnitude(int z, const int *P) {
-  if constexpr (B == 1) {
-    return 0;
-  } else if constexpr (B == 2) {
-    return z >= P[1] ? 1 : 0;
-  } else if constexpr (B == 3) {
-    const int m = z >= P[2] ? 2 : 0;
-    return m + (z >= (m ? P[3] : P[1]) ? 1 : 0);
-  } else {
-    static_assert(B == 4, "register search covers up to 4 bits");
-    int m = z >= P[4] ? 4 : 0;
-    m += z >= (m ? P[6] : P[2]) ? 2 : 0;
-    const int t = (m & 4) ? ((m & 2) ? P[7] : P[5]) : ((m & 2) ? P[3] : P[1]);
-    return m + (z >= t ? 1 : 0);
-  }
-}
 
 // One vector: norm, signs, rotation, codes, record write (and the prod-mode residual sketch).
 template <int D, bool PROD>
 __device__ __forceinline__ void quantize_vector(const QuantArgs &a, int which, float *x, int64_t slot, bool active,
-                                                int h, int lane, int vl, uint32_t sword, const int *P,
+                                                int h, int lane, int vl, uint32_t sword, const PosThresholds &P,
                                                 const float *s_th, const float *s_lv, float (*s_r)[D]) {
   constexpr int LANES = D / 8;
   const unsigned char *cb = a.cb[which];
@@ -265,13 +183,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   const int64_t tok0 = (int64_t)(blockIdx.x / a.H) * (VPB * NV) + vl;
 
   const uint32_t sword = ((const uint32_t *)(cb + bo.signs))[(8 * lane) >> 5];
-  // positive thresholds P[1 .. half-1] (t[half-1] is 0 by symmetry), as integer bit patterns
-  int P[8];
-  if (b <= 4) {
-    const const_i32 th = (const_i32)(cb + bo.thresholds);
-#pragma unroll
-    for (int m = 1; m < 8; ++m) P[m] = m < half ? th[half - 1 + m] : 0x7F800000;
-  }
+  // positive thresholds (t[half-1] is 0 by symmetry), as integer bit patterns
+  PosThresholds P{};
+  if (b <= 4) P = pos_thresholds((const_i32)(cb + bo.thresholds), half);
   if (b > 4 || mode == TQ_PROD) {
     for (int i = threadIdx.x; i < nl - 1; i += 256) s_th[i] = ((const float *)(cb + bo.thresholds))[i];
     for (int i = threadIdx.x; i < nl; i += 256) s_lv[i] = half_bits_to_float(((const uint16_t *)(cb + bo.levels))[i]);

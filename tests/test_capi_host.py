@@ -147,3 +147,23 @@ def test_workspace_grows_with_splits():
     a = tq.decode_workspace_bytes(tq.Layout(128, 8, 4, 0, 2, 0), 2, 32, 64, 2)
     b = tq.decode_workspace_bytes(tq.Layout(128, 8, 4, 0, 2, 0), 2, 32, 64, 32)
     assert a > b > 0
+
+
+def test_decode_step_argument_errors_need_no_gpu():
+    lib = tq._lib()
+    L = tq.Layout(128, 8, 4, 0, 2, 0).c()
+    kprod = tq.Layout(128, 8, 3, 1, 2, 0).c()
+    k8 = tq.Layout(128, 8, 8, 0, 2, 0).c()
+    args = (16, 4, 16, 16, 1, 16, 1, 1, 32, 16, 10, 16, 0.1, 4, 16, 16, 16, 1 << 30, 16, None)
+    assert lib.tq_decode_step(ctypes.byref(kprod), *args) == -3  # prod K is appended by tq_quantize_kv
+    assert lib.tq_decode_step(ctypes.byref(k8), *args) == -3  # 8-bit codes likewise
+    # (pages, num_pages, k_new, v_new, kv_dtype, q, ...): every case fails its checks before any launch
+    bad = list(args)
+    bad[4] = 9  # kv dtype
+    assert lib.tq_decode_step(ctypes.byref(L), *bad) == -1
+    bad = list(args)
+    bad[3] = 24  # misaligned v_new
+    assert lib.tq_decode_step(ctypes.byref(L), *bad) == -1
+    bad = list(args)
+    bad[2] = None  # null k_new
+    assert lib.tq_decode_step(ctypes.byref(L), *bad) == -1

@@ -13,12 +13,12 @@ pytestmark = pytest.mark.gpu
 
 
 def build(H, d, Hq, B, lens, kb, km, vb, vm, seed=0, shuffled=True, dtype="bf16", q_scale=1.0,
-          extra_pages=3, k_mult=1.0):
+          extra_pages=3, k_mult=1.0, min_pages=0):
     import torch
     import kv_cache_quantization_wht_amd as tq
 
     layout, Lo = parity.make_layout(H, d, kb, km, vb, vm)
-    pps = max(1, max((l + 15) // 16 for l in lens))
+    pps = max(1, min_pages, max((l + 15) // 16 for l in lens))
     pt, npages = kvsynth.page_table(B, pps, shuffled, seed=seed + 4, extra_pages=extra_pages)
     kcb, cbk = parity.device_codebook(d, kb, km, seed=seed + 1)
     vcb, cbv = parity.device_codebook(d, vb, vm, seed=seed + 2)
@@ -146,3 +146,60 @@ def test_two_passes_equal_one_call():
         torch.cuda.synchronize()
         assert torch.equal(one, two), pps
         assert parity.attention_error(two.cpu().numpy().astype(np.float64), run_ref(c, scale)) <= parity.ATTN_TOL
+
+
+STEP_CASES = [
+    # name, H, d, Hq, lens (counting the new token), kb, vb, kv dtype, pages_per_split
+    ("k4v2-ragged", 2, 128, 8, [700, 33, 1, 17], 4, 2, "bf16", 0),
+    ("k3v3-gqa4-splits", 2, 128, 8, [290, 257], 3, 3, "bf16", 2),
+    ("k2v2-gqa8", 2, 128, 16, [145, 64], 2, 2, "f16", 0),
+    ("k1v4-d64", 2, 64, 8, [99, 16, 32], 1, 4, "f32", 4),
+    ("k4v2-mha-d64", 4, 64, 4, [1, 200], 4, 2, "f32", 0),
+    ("k4v4-gqa16", 1, 128, 16, [513], 4, 4, "bf16", 0),
+]
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=[c[0] for c in STEP_CASES])
+def test_decode_step_equals_append_then_attention(case):
+    """tq_decode_step writes the same page bytes as tq_quantize_kv of the new tokens and gives the output of
+    tq_decode_attention over the result (and of the oracle on the written pool)."""
+    import torch
+    import kv_cache_quantization_wht_amd as tq
+
+    name, H, d, Hq, lens, kb, vb, dt, pps = case
+    print(f"decode step case {name}", flush=True)
+    prev = [max(L - 1, 0) for L in lens]
+    c = build(H, d, Hq, len(lens), prev, kb, 0, vb, 0, seed=7 + len(name), dtype=dt,
+              min_pages=max((L + 15) // 16 for L in lens))
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    g = torch.Generator().manual_seed(123 + len(name))
+    k_new = (torch.randn(len(lens), H, d, generator=g) * 3).to(tdt).cuda()
+    v_new = torch.randn(len(lens), H, d, generator=g).to(tdt).cuda()
+    pt = torch.from_numpy(c["pt"]).cuda()
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    q = c["q"].cuda()
+    scale = 1 / math.sqrt(d)
+    # path A: append through tq_quantize_kv into the new tokens' slots, then decode attention
+    pages_a = c["pages"].clone()
+    slots = [int(c["pt"][b, (L - 1) // 16]) * 16 + (L - 1) % 16 if L > 0 else -1 for b, L in enumerate(lens)]
+    for b, L in enumerate(lens):
+        if L > 0:
+            tq.quantize_kv(c["layout"], pages_a, k_new[b:b + 1].reshape(1, H, d), v_new[b:b + 1].reshape(1, H, d),
+                           torch.tensor([slots[b]], dtype=torch.int64, device="cuda"), c["kcb"], c["vcb"])
+    out_a = tq.decode_attention(c["layout"], pages_a, q, pt, sl, scale, c["kcb"], c["vcb"], pages_per_split=pps)
+    # path B: one decode step
+    pages_b = c["pages"].clone()
+    out_b = tq.decode_step(c["layout"], pages_b, k_new, v_new, q, pt, sl, scale, c["kcb"], c["vcb"],
+                           pages_per_split=pps)
+    torch.cuda.synchronize()
+    assert torch.equal(pages_a, pages_b)
+    oa, ob = out_a.cpu().numpy().astype(np.float64), out_b.cpu().numpy().astype(np.float64)
+    assert parity.attention_error(ob, oa) <= 1e-4
+    ref = attention.decode_attention(pages_b.cpu().numpy(), c["Lo"], c["cbk"], c["cbv"], q.cpu().double().numpy(),
+                                     c["pt"], np.array(lens, dtype=np.int32), scale)
+    err = parity.attention_error(ob, ref)
+    print(f"{name}: step vs oracle {err:.3e}")
+    assert err <= parity.ATTN_TOL
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(ob[b] == 0)
