@@ -26,15 +26,17 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
-# (source, object, extra flags). The decode source is compiled in two parts (head_dim 128 with the
-# launcher, head_dim 64) so the two halves of its kernel instantiations build in parallel. No NaN reaches
+# (source, object, extra flags). The decode source is compiled in four parts (head_dim 128 / 64, each
+# with packed or one-per-head query columns) so its kernel instantiations build in parallel. No NaN reaches
 # a max or compare on the decode path (masked scores are finite), so the NaN-quieting copies in front of
 # every max are dropped there.
 SOURCES = [
     ("tq_capi.cpp", "tq_capi.o", []),
     ("tq_quantize.hip", "tq_quantize.o", []),
-    ("tq_decode.hip", "tq_decode_d128.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=1"]),
-    ("tq_decode.hip", "tq_decode_d64.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=2"]),
+    ("tq_decode.hip", "tq_decode_d128_pk.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=1"]),
+    ("tq_decode.hip", "tq_decode_d128.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=2"]),
+    ("tq_decode.hip", "tq_decode_d64_pk.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=3"]),
+    ("tq_decode.hip", "tq_decode_d64.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=4"]),
 ]
 
 

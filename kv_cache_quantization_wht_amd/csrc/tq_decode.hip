@@ -449,7 +449,11 @@ __device__ __forceinline__ void append_quantize(const DecodeArgs &a, bool is_v, 
   if (lq == 0) *(uint16_t *)(pg + (is_v ? a.v_norms : a.k_norms) + (int64_t)(kvh * TQ_PAGE_TOKENS + slot) * 2) = n16;
 }
 
-template <int D, int KB, bool KPROD, int VB, bool APPEND>
+// PK (at most 8 query heads per KV head): MFMA column c carries query head c & 7, the high fp16 part of its
+// operand when c < 8 and the low part when c >= 8, so one MFMA does the work of the hi and lo pair. The
+// two partial scores meet by one row rotation; the two partial value sums are added once, before the merge.
+// Otherwise column c is query head c and every product is an hi + lo pair of MFMAs.
+template <int D, int KB, bool KPROD, int VB, bool APPEND, bool PK>
 __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   constexpr int NT = 64 * kWaves;
   constexpr int KBLK = D / 32;  // 32-coordinate blocks of the score contraction
@@ -468,6 +472,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15;   // MFMA row/column inside a 16-block
   const int g4 = lane >> 4;  // 8-deep slice of the contraction held by this lane
+  const int hc = PK ? (c & 7) : c;                // query head (inside the KV head's group) of column c
+  const bool lo_part = PK && c >= 8;              // PK: column c carries the low fp16 parts
+  const float lo_neg = lo_part ? -1.f : 0.f;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = a.G;
   const int head0 = kvh * G;
@@ -667,12 +674,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   // query operands: column c = query head head0 + c, contraction rows 8*g4.. of each 32-block,
   // i.e. coordinates cbase + 8*kb + k_order(p)
   const int cbase = (D / 4) * g4;
-  half8_t qhi[KBLK], qlo[KBLK];
-  half8_t shi[KPROD ? KBLK : 1], slo[KPROD ? KBLK : 1];
+  half8_t qhi[KBLK], qlo[PK ? 1 : KBLK];  // PK: qhi holds this column's part (high or low)
+  half8_t shi[KPROD ? KBLK : 1], slo[(KPROD && !PK) ? KBLK : 1];
   float colscale, skratio;
   {
-    const bool real = c < G;
-    const int r = real ? c : 0;
+    const bool real = hc < G;
+    const int r = real ? hc : 0;
     const float sig = s_sig[r][0], sig2 = KPROD ? s_sig[r][1] : 1.f;
     colscale = real ? a.scale_log2 / sig : 0.f;
     skratio = sig / sig2;
@@ -687,8 +694,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         const float x = real ? v[k_order<KB>(p)] * sig : 0.f;
         _Float16 h, l;
         split_hi_lo(x, h, l);
-        qhi[kb][p] = h;
-        qlo[kb][p] = l;
+        if constexpr (PK) {
+          qhi[kb][p] = lo_part ? l : h;
+        } else {
+          qhi[kb][p] = h;
+          qlo[kb][p] = l;
+        }
       }
       if constexpr (KPROD) {
         const float4 w0 = *(const float4 *)&s_qs[r][cbase + 8 * kb];
@@ -699,8 +710,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
           const float y = real ? z[p] * sig2 : 0.f;
           _Float16 h, l;
           split_hi_lo(y, h, l);
-          shi[kb][p] = h;
-          slo[kb][p] = l;
+          if constexpr (PK) {
+            shi[kb][p] = lo_part ? l : h;
+          } else {
+            shi[kb][p] = h;
+            slo[kb][p] = l;
+          }
         }
       }
     }
@@ -729,7 +744,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
                                    (seq_len - 1) % TQ_PAGE_TOKENS, is_v ? s_lutv : s_lutk,
                                    s_newlev[is_v ? (APPEND ? 1 : 0) : 0], &s_newnorm[is_v ? 1 : 0]);
       }
-      const int r = c < G ? c : 0;
+      const int r = hc < G ? hc : 0;
       float part = 0.f;
 #pragma unroll
       for (int i = 0; i < D / 4; i += 4) {
@@ -739,12 +754,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         part = fmaf(qv.x, kv.x, fmaf(qv.y, kv.y, fmaf(qv.z, kv.z, fmaf(qv.w, kv.w, part))));
       }
       const float raw = sum_xor16_32(part);
-      if (c < G) {
+      if (hc < G) {
         const float x = s_newnorm[0] * raw * a.scale_log2;
         m_run = x + kHeadroom;
         const float p = fast_exp2(-kHeadroom);
         l_part = g4 == 0 ? p : 0.f;
-        const float pv = p * s_newnorm[1];
+        const float pv = lo_part ? 0.f : p * s_newnorm[1];  // PK: the value enters once, in the high column
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -830,7 +845,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
           A = from_halves(hv);
         }
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qhi[kb], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qlo[kb], acc, 0, 0, 0);
+        if constexpr (!PK) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qlo[kb], acc, 0, 0, 0);
       }
       float raw[4] = {acc[0], acc[1], acc[2], acc[3]};
       if constexpr (KPROD) {
@@ -842,12 +857,17 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
           const half8_t A = from_dwords(NEG ^ ((z & 1u) << 15) ^ ((z & 2u) << 30), NEG ^ ((z & 4u) << 13) ^ ((z & 8u) << 28),
                                         NEG ^ ((z & 16u) << 11) ^ ((z & 32u) << 26), NEG ^ ((z & 64u) << 9) ^ ((z & 128u) << 24));
           acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, shi[kb], acc2, 0, 0, 0);
-          acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, slo[kb], acc2, 0, 0, 0);
+          if constexpr (!PK) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, slo[kb], acc2, 0, 0, 0);
         }
         float gam[4];
         unpack4(cur.gm[q2], gam);
 #pragma unroll
         for (int j = 0; j < 4; ++j) raw[j] = fmaf(gam[j] * skratio, acc2[j], raw[j]);
+      }
+      if constexpr (PK) {
+        // the partial scores of the high (column c) and low (column c ^ 8) query parts: both lanes get the sum
+#pragma unroll
+        for (int j = 0; j < 4; ++j) raw[j] += xor_lane<8>(raw[j]);
       }
       // the fp16 norms enter mixed-precision FMAs directly (fma with a zero addend, not folded to a
       // multiply since signed zeros are kept)
@@ -906,11 +926,20 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         l_part += p0 + p1;
         const float2_t pv = {fmaf((float)nv[q2][j], p0, 0.f), fmaf((float)nv[q2][j + 1], p1, 0.f)};
         const half2_t h = __builtin_convertvector(pv, half2_t);
-        const half2_t l = __builtin_convertvector(pv - __builtin_convertvector(h, float2_t), half2_t);
-        phi[4 * q2 + j] = h[0];
-        phi[4 * q2 + j + 1] = h[1];
-        plo[4 * q2 + j] = l[0];
-        plo[4 * q2 + j + 1] = l[1];
+        if constexpr (PK) {
+          // high column: P' rounded to fp16; low column: what that rounding left out
+          const float2_t hf = __builtin_convertvector(h, float2_t);
+          const float2_t t = {fmaf(lo_neg, hf[0], pv[0]), fmaf(lo_neg, hf[1], pv[1])};
+          const half2_t u = __builtin_convertvector(t, half2_t);
+          phi[4 * q2 + j] = u[0];
+          phi[4 * q2 + j + 1] = u[1];
+        } else {
+          const half2_t l = __builtin_convertvector(pv - __builtin_convertvector(h, float2_t), half2_t);
+          phi[4 * q2 + j] = h[0];
+          phi[4 * q2 + j + 1] = h[1];
+          plo[4 * q2 + j] = l[0];
+          plo[4 * q2 + j + 1] = l[1];
+        }
       }
     }
 
@@ -922,7 +951,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Bop[nb], phi, O[nb], 0, 0, 0);
-      O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Bop[nb], plo, O[nb], 0, 0, 0);
+      if constexpr (!PK) O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Bop[nb], plo, O[nb], 0, 0, 0);
     }
   };
 
@@ -941,6 +970,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   // ---- 4. merge the wavefronts of this work-group: rescale to the work-group max, then sum over the
   //         waves in a fixed order (deterministic). Lane (c, g4) holds head c (real when c < G) and,
   //         in O[nb][j], coordinate (D / 16) * (4 * g4 + j) + nb of its rotated value sum.
+  if constexpr (PK) {
+    // value sums of the high and low columns of each head: lanes c < 8 hold the total
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) O[nb][j] += xor_lane<8>(O[nb][j]);
+  }
   {
     const float l_tot = sum_xor16_32(l_part);
     if (g4 == 0) {
@@ -1174,71 +1210,84 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   }
 }
 
-template <int D, int KB, bool KPROD, int VB>
+template <int D, int KB, bool KPROD, int VB, bool PK>
 void launch(const DecodeArgs &a, hipStream_t stream) {
   if (a.passes & kPassScan) {
     dim3 grid(a.n_splits, a.Hkv, a.B);
     if constexpr (!KPROD && KB <= 4 && VB <= 4) {
       if (a.k_new) {
-        hipLaunchKernelGGL((decode_kernel<D, KB, KPROD, VB, true>), grid, dim3(64 * kWaves), 0, stream, a);
+        hipLaunchKernelGGL((decode_kernel<D, KB, KPROD, VB, true, PK>), grid, dim3(64 * kWaves), 0, stream, a);
       } else {
-        hipLaunchKernelGGL((decode_kernel<D, KB, KPROD, VB, false>), grid, dim3(64 * kWaves), 0, stream, a);
+        hipLaunchKernelGGL((decode_kernel<D, KB, KPROD, VB, false, PK>), grid, dim3(64 * kWaves), 0, stream, a);
       }
     } else {
-      hipLaunchKernelGGL((decode_kernel<D, KB, KPROD, VB, false>), grid, dim3(64 * kWaves), 0, stream, a);
+      hipLaunchKernelGGL((decode_kernel<D, KB, KPROD, VB, false, PK>), grid, dim3(64 * kWaves), 0, stream, a);
     }
   }
   if ((a.passes & kPassCombine) && a.n_splits > 1)
     hipLaunchKernelGGL(combine_kernel<D>, dim3(a.B * a.Hq), dim3(256), 0, stream, a);
 }
 
-template <int D, int KB, bool KPROD>
+template <int D, int KB, bool KPROD, bool PK>
 bool dispatch_v(int vb, const DecodeArgs &a, hipStream_t s) {
   switch (vb) {
-    case 1: launch<D, KB, KPROD, 1>(a, s); return true;
-    case 2: launch<D, KB, KPROD, 2>(a, s); return true;
-    case 3: launch<D, KB, KPROD, 3>(a, s); return true;
-    case 4: launch<D, KB, KPROD, 4>(a, s); return true;
-    case 8: launch<D, KB, KPROD, 8>(a, s); return true;
+    case 1: launch<D, KB, KPROD, 1, PK>(a, s); return true;
+    case 2: launch<D, KB, KPROD, 2, PK>(a, s); return true;
+    case 3: launch<D, KB, KPROD, 3, PK>(a, s); return true;
+    case 4: launch<D, KB, KPROD, 4, PK>(a, s); return true;
+    case 8: launch<D, KB, KPROD, 8, PK>(a, s); return true;
   }
   return false;
 }
 
-template <int D>
+template <int D, bool PK>
 bool dispatch_k(int kb, bool kprod, int vb, const DecodeArgs &a, hipStream_t s) {
   if (kprod) {
     switch (kb) {
-      case 1: return dispatch_v<D, 1, true>(vb, a, s);
-      case 2: return dispatch_v<D, 2, true>(vb, a, s);
-      case 3: return dispatch_v<D, 3, true>(vb, a, s);
+      case 1: return dispatch_v<D, 1, true, PK>(vb, a, s);
+      case 2: return dispatch_v<D, 2, true, PK>(vb, a, s);
+      case 3: return dispatch_v<D, 3, true, PK>(vb, a, s);
     }
     return false;
   }
   switch (kb) {
-    case 1: return dispatch_v<D, 1, false>(vb, a, s);
-    case 2: return dispatch_v<D, 2, false>(vb, a, s);
-    case 3: return dispatch_v<D, 3, false>(vb, a, s);
-    case 4: return dispatch_v<D, 4, false>(vb, a, s);
-    case 8: return dispatch_v<D, 8, false>(vb, a, s);
+    case 1: return dispatch_v<D, 1, false, PK>(vb, a, s);
+    case 2: return dispatch_v<D, 2, false, PK>(vb, a, s);
+    case 3: return dispatch_v<D, 3, false, PK>(vb, a, s);
+    case 4: return dispatch_v<D, 4, false, PK>(vb, a, s);
+    case 8: return dispatch_v<D, 8, false, PK>(vb, a, s);
   }
   return false;
 }
 
 }  // namespace
 
-// The kernels are instantiated per head dimension in separate objects (this file is compiled once per
-// part, in parallel): part 1 holds head_dim 128 and the launcher, part 2 head_dim 64; no part = both.
+// The kernels are instantiated in four objects (this file is compiled once per part, in parallel):
+// part 1 holds head_dim 128 with packed columns (at most 8 query heads per KV head) and the launcher,
+// part 2 head_dim 128 with one column per query head, parts 3 and 4 the same for head_dim 64; no part = all.
+bool decode_dispatch_d128_pk(int kb, bool kprod, int vb, const DecodeArgs &a, hipStream_t s);
 bool decode_dispatch_d128(int kb, bool kprod, int vb, const DecodeArgs &a, hipStream_t s);
+bool decode_dispatch_d64_pk(int kb, bool kprod, int vb, const DecodeArgs &a, hipStream_t s);
 bool decode_dispatch_d64(int kb, bool kprod, int vb, const DecodeArgs &a, hipStream_t s);
 
 #if !defined(TQ_DECODE_PART) || TQ_DECODE_PART == 1
-bool decode_dispatch_d128(int kb, bool kprod, int vb, const DecodeArgs &a, hipStream_t s) {
-  return dispatch_k<128>(kb, kprod, vb, a, s);
+bool decode_dispatch_d128_pk(int kb, bool kprod, int vb, const DecodeArgs &a, hipStream_t s) {
+  return dispatch_k<128, true>(kb, kprod, vb, a, s);
 }
 #endif
 #if !defined(TQ_DECODE_PART) || TQ_DECODE_PART == 2
+bool decode_dispatch_d128(int kb, bool kprod, int vb, const DecodeArgs &a, hipStream_t s) {
+  return dispatch_k<128, false>(kb, kprod, vb, a, s);
+}
+#endif
+#if !defined(TQ_DECODE_PART) || TQ_DECODE_PART == 3
+bool decode_dispatch_d64_pk(int kb, bool kprod, int vb, const DecodeArgs &a, hipStream_t s) {
+  return dispatch_k<64, true>(kb, kprod, vb, a, s);
+}
+#endif
+#if !defined(TQ_DECODE_PART) || TQ_DECODE_PART == 4
 bool decode_dispatch_d64(int kb, bool kprod, int vb, const DecodeArgs &a, hipStream_t s) {
-  return dispatch_k<64>(kb, kprod, vb, a, s);
+  return dispatch_k<64, false>(kb, kprod, vb, a, s);
 }
 #endif
 
@@ -1284,8 +1333,11 @@ int launch_decode(const PageGeom &g, const DecodeWs &ws, const void *pages, int6
   a.out = out;
   a.passes = passes;
   const bool kprod = g.k_mode == TQ_PROD;
-  const bool ok = g.head_dim == 128 ? decode_dispatch_d128(g.k_mse_bits, kprod, g.v_mse_bits, a, stream)
-                                    : decode_dispatch_d64(g.k_mse_bits, kprod, g.v_mse_bits, a, stream);
+  const int kb = g.k_mse_bits, vb = g.v_mse_bits;
+  const bool pk = a.G <= 8;
+  const bool ok = g.head_dim == 128
+                      ? (pk ? decode_dispatch_d128_pk(kb, kprod, vb, a, stream) : decode_dispatch_d128(kb, kprod, vb, a, stream))
+                      : (pk ? decode_dispatch_d64_pk(kb, kprod, vb, a, stream) : decode_dispatch_d64(kb, kprod, vb, a, stream));
   if (!ok) return TQ_ENOTSUP;
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
 }
