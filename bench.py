@@ -63,16 +63,24 @@ def load_traffic(bytes_per_launch_alg):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=128)
-    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 128; another workload: its own)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (default 16; another workload: 2)")
     ap.add_argument("--copies", type=int, default=16, help="independent layer caches cycled per step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch steps from Python instead of a captured graph")
+    ap.add_argument("--workload", default=None,
+                    help="another synthetic workload by name or index (default: the Llama-3.1-8B single layer); "
+                         "its steps run every layer of the workload, each layer its own cache")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="only run a plain device-to-device copy of MB megabytes (5 times), to scale the HBM "
                          "byte counters of rocprofv3")
     args = ap.parse_args()
+    args.steps_given, args.warmup_given = args.steps is not None, args.warmup is not None
+    if args.steps is None:
+        args.steps = 128
+    if args.warmup is None:
+        args.warmup = 16
     if args.calibrate_copy:
         import torch
 
@@ -99,6 +107,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.workload is not None:
+        names = [w.name for w in kvsynth.workloads()]
+        wi = int(args.workload) if args.workload.isdigit() else names.index(args.workload)
+        if wi != WORKLOAD_INDEX:
+            run_workload(args, wi)
+            return
     dev = "cuda"
     wl = kvsynth.workloads()[WORKLOAD_INDEX]
     H, Hq, d, T = wl.kv_heads, wl.q_heads, wl.head_dim, wl.seq_len
@@ -271,41 +285,39 @@ def main():
         "quantize_vectors_per_s": round(quant_vps, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_kernel<128,4,false,2,true> (tq_decode_step_partial)",
+                     "kernel": "decode_kernel<128,4,false,2,true,true> (tq_decode_step_partial)",
                      "bytes_per_launch": round(alg_per_launch), "avg_launch_us": round(kern_s * 1e6, 3),
                      "combine_avg_us": round(float(np.mean(comb)) * 1e6, 3), "timing": kmode},
         "cpu_baseline": None,
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(layout, offs, pages, page_tables[0], T, qs, scale, sw, args.cpu_seconds,
-                                              bits)
+        first = int(page_tables[0][0, 0].item())
+        npg = (T + 15) // 16
+        pool = pages[first * page_bytes:(first + npg) * page_bytes].cpu().numpy()
+        result["cpu_baseline"] = cpu_baseline(H, d, bits, pool, T, qs.double().cpu().numpy(), scale, sw, None,
+                                              args.cpu_seconds, rec_bytes, "copy 0")
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(layout, offs, pages, page_table, T, qs, scale, sw, budget_s, bits):
-    """Time the CPU oracle's decode attention on copy 0 of the cache: one KV head (its query heads) at a time,
-    over successive decode queries, until the time budget is spent."""
+def cpu_baseline(H, d, bits, pool, T, qall, scale, sw, S, budget_s, rec_bytes, what):
+    """Time the CPU oracle's decode attention over one sequence's T cached tokens (``pool`` holds its pages in
+    order): one KV head (its query heads) at a time, over successive decode queries, until the time budget is
+    spent. ``qall`` is [queries, batch, Hq, d]; batch row 0 is used."""
     from oracle import attention, codec
 
-    H, d = layout.num_kv_heads, layout.head_dim
-    pb = offs["page_bytes"]
-    npg = (T + 15) // 16
-    first = int(page_table[0, 0].item())
-    pool = pages[first * pb:(first + npg) * pb].cpu().numpy()
     Lo = codec.page_layout(H, d, bits.k_bits, bits.k_mode, bits.v_bits, bits.v_mode)
-    cbk = codec.make_codebook(d, bits.k_bits, bits.k_mode, sw)
-    cbv = codec.make_codebook(d, bits.v_bits, bits.v_mode, sw)
+    cbk = codec.make_codebook(d, bits.k_bits, bits.k_mode, sw, S)
+    cbv = codec.make_codebook(d, bits.v_bits, bits.v_mode, sw, S if bits.v_mode else None)
+    npg = (T + 15) // 16
     pt = np.arange(npg, dtype=np.int64)[None]
-    qall = qs.double().cpu().numpy()  # [steps, 1, Hq, d]
     G = qall.shape[2] // H
-    rec_bytes = offs["k_norms"] // (H * 16) + 2 + (offs["v_norms"] - offs["v_codes"]) // (H * 16) + 2
     done, t_used, step = 0, 0.0, 0
     t0 = time.perf_counter()
     while t_used < budget_s and step < qall.shape[0]:
         for g in range(H):
             heads = [(0, h) for h in range(g * G, (g + 1) * G)]
-            attention.decode_attention(pool, Lo, cbk, cbv, qall[step], pt, [T], scale, heads=heads)
+            attention.decode_attention(pool, Lo, cbk, cbv, qall[step][:1], pt, [T], scale, heads=heads)
             done += 1
             t_used = time.perf_counter() - t0
             if t_used > budget_s:
@@ -319,9 +331,187 @@ def cpu_baseline(layout, offs, pages, page_table, T, qs, scale, sw, budget_s, bi
     except Exception:  # noqa: BLE001
         cores = 1
     return {"value": round(bytes_done / t_used / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"fp64 oracle decode attention of copy 0 (T={T}, 8 KV heads x {G} query heads each): {done} "
+            "sample": f"fp64 oracle decode attention of {what} (T={T}, {H} KV heads x {G} query heads each): {done} "
                       f"(KV head, query) units over {step} decode queries in {t_used:.1f} s; same unit as value",
             "host_cpus": os.cpu_count()}
+
+
+def record_bytes(offs, H):
+    """Stored bytes of one token of one KV head (K and V records: codes, norms, sketch, gamma)."""
+    return offs["page_bytes"] // (H * 16)
+
+
+def run_workload(args, wi):
+    """A multi-layer or batched workload: every layer has its own cache (no copies needed: the layers
+    together exceed the Infinity Cache), prefilled through tq_quantize_kv; one step is one decode step of
+    the whole model: for every layer, the new token of every sequence is quantized into its slot and the
+    new queries attend (tq_decode_step where the format allows, tq_quantize_kv + tq_decode_attention for
+    prod K or 8-bit codes). The timed region replays the K steps as one HIP graph."""
+    import torch
+
+    import kvsynth
+    import kv_cache_quantization_wht_amd as tq
+
+    dev = "cuda"
+    wl = kvsynth.workloads()[wi]
+    L, H, Hq, d, B, T = wl.layers, wl.kv_heads, wl.q_heads, wl.head_dim, wl.batch, wl.seq_len
+    K = args.steps if args.steps_given else wl.decode_steps
+    W = args.warmup if args.warmup_given else 2
+    total = W + K
+    pps = (T + total + 15) // 16
+    layers = []
+    for l in range(L):
+        bits = wl.bits[l]
+        layout = tq.Layout(d, H, bits.k_bits, bits.k_mode, bits.v_bits, bits.v_mode)
+        offs = tq.page_layout(layout)
+        pt, npages = kvsynth.page_table(B, pps, wl.shuffled_pages, seed=4242 + l)
+        sw = kvsynth.rotation_signs(kvsynth.rotation_seed(l), d)
+        S = kvsynth.qjl_projection(kvsynth.rotation_seed(l), d) if bits.k_mode or bits.v_mode else None
+        layers.append(dict(bits=bits, layout=layout, offs=offs, pt=pt, ptd=torch.from_numpy(pt).to(dev), sw=sw, S=S,
+                           kcb=torch.from_numpy(tq.build_codebook(d, bits.k_bits, bits.k_mode, sw, S)).to(dev),
+                           vcb=torch.from_numpy(tq.build_codebook(d, bits.v_bits, bits.v_mode, sw, S)).to(dev),
+                           pages=torch.zeros(npages * offs["page_bytes"], dtype=torch.uint8, device=dev),
+                           fused=not bits.k_mode and not bits.v_mode and bits.k_bits <= 4 and bits.v_bits <= 4))
+    total_mb = sum(x["pages"].numel() for x in layers) / 1e6
+    log(f"workload {wl.name}: {L} layers, batch {B}, {T} cached tokens, {total_mb:.0f} MB of pages")
+
+    # ---- prefill every layer (all sequences of a layer in one launch); the largest launch is timed
+    slots_all = torch.from_numpy(np.concatenate([kvsynth.slots_for(layers[0]["pt"], b, 0, T) for b in range(B)])).to(dev)
+    quant_vps, qn = 0.0, 0
+    for l, x in enumerate(layers):
+        k, v = kvsynth.make_kv(wl, wi, l, B * T, device=dev)
+        sl_all = slots_all if l == 0 else torch.from_numpy(
+            np.concatenate([kvsynth.slots_for(x["pt"], b, 0, T) for b in range(B)])).to(dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        reps = 3 if l == 0 else 1
+        times = []
+        for _ in range(reps):
+            ev[0].record()
+            tq.quantize_kv(x["layout"], x["pages"], k, v, sl_all, x["kcb"], x["vcb"])
+            ev[1].record()
+            torch.cuda.synchronize()
+            times.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+        if l == 0:
+            qn = B * T * H * 2
+            quant_vps = qn / float(np.median(times))
+        del k, v
+        if l % 16 == 15:
+            log(f"  prefilled {l + 1} layers")
+    torch.cuda.synchronize()
+    log(f"prefill quantize (layer 0, {qn} vectors): {quant_vps / 1e9:.2f} G vectors/s")
+
+    # ---- per-step inputs, resident before timing
+    news = [kvsynth.make_kv(wl, wi, l, total * B, device=dev, token_offset_seed=1) for l in range(L)]
+    qs = [kvsynth.make_q(wl, wi, l, total * B, device=dev).view(total, B, Hq, d) for l in range(L)]
+    lens = [torch.full((B,), T + i + 1, dtype=torch.int32, device=dev) for i in range(total)]
+    step_slots = [[torch.from_numpy(x["pt"][:, (T + i) // 16].astype(np.int64) * 16 + (T + i) % 16).to(dev)
+                   for i in range(total)] for x in layers]
+    wss = {}
+    for x in layers:
+        key = (x["bits"].k_bits, x["bits"].k_mode, x["bits"].v_bits, x["bits"].v_mode)
+        if key not in wss:
+            wss[key] = torch.zeros(tq.decode_workspace_bytes(x["layout"], B, Hq, pps), dtype=torch.uint8, device=dev)
+        x["ws"] = wss[key]
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+    scale = wl.softmax_scale
+    step_bytes = []
+    for i in range(total):
+        tot = 0
+        for x in layers:
+            tot += B * H * (T + i + 1) * record_bytes(x["offs"], H) + B * H * 2 * d * 2 + 4 * B * ((T + i + 1 + 15) // 16)
+        step_bytes.append(tot)
+
+    def layer_step(l, i, first_pass_only=False):
+        x = layers[l]
+        kn, vn = news[l][0][i * B:(i + 1) * B], news[l][1][i * B:(i + 1) * B]
+        if x["fused"]:
+            tq.decode_step(x["layout"], x["pages"], kn, vn, qs[l][i], x["ptd"], lens[i], scale, x["kcb"], x["vcb"],
+                           workspace=x["ws"], out=out, first_pass_only=first_pass_only)
+        else:
+            if not first_pass_only:
+                tq.quantize_kv(x["layout"], x["pages"], kn, vn, step_slots[l][i], x["kcb"], x["vcb"])
+                tq.decode_attention(x["layout"], x["pages"], qs[l][i], x["ptd"], lens[i], scale, x["kcb"], x["vcb"],
+                                    workspace=x["ws"], out=out)
+            else:
+                tq.decode_partial(x["layout"], x["pages"], qs[l][i], x["ptd"], lens[i], scale, x["kcb"], x["vcb"],
+                                  x["ws"], out=out)
+
+    def step(i):
+        for l in range(L):
+            layer_step(l, i)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(W, total):
+            step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / K
+    value = float(np.sum(step_bytes[W:])) / elapsed / 1e9
+
+    # ---- the split-K launch of the most common layer format, alone: graph of its K launches, one event pair
+    fmt = max(set((x["bits"].k_bits, x["bits"].v_bits) for x in layers),
+              key=lambda f: sum(1 for x in layers if (x["bits"].k_bits, x["bits"].v_bits) == f))
+    lr = next(l for l, x in enumerate(layers) if (x["bits"].k_bits, x["bits"].v_bits) == fmt)
+    gph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gph):
+        for i in range(W, total):
+            layer_step(lr, i, first_pass_only=True)
+    gph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    gph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    kern_s = e0.elapsed_time(e1) * 1e-3 / K
+    xr = layers[lr]
+    alg = float(np.mean([B * H * (T + i + 1) * record_bytes(xr["offs"], H) + 4 * B * ((T + i + 1 + 15) // 16)
+                         + (B * H * 2 * d * 2 if xr["fused"] else 0) for i in range(W, total)]))
+    achieved = alg / kern_s / 1e9
+    b0 = xr["bits"]
+    kname = (f"decode_kernel<{d},{b0.k_bits - b0.k_mode},{'true' if b0.k_mode else 'false'},{b0.v_bits},"
+             f"{'true' if xr['fused'] else 'false'},{'true' if Hq // H <= 8 else 'false'}> "
+             f"({'tq_decode_step_partial' if xr['fused'] else 'tq_decode_partial'})")
+    log(f"step {ms_per_step * 1e3:.1f} us -> {value:.0f} GB/s; layer {lr} split-K kernel {kern_s * 1e6:.2f} us, "
+        f"{alg / 1e6:.1f} MB/launch -> {achieved:.0f} GB/s")
+    result = {
+        "metric": "decode-attn compressed-KV GB/s (% of HBM peak); KV quantize vectors/s",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16-mfma+fp32", "data": "synthetic",
+        "config": {"workload": wl.name, "layers": L, "kv_heads": H, "q_heads": Hq, "head_dim": d, "batch": B,
+                   "seq_len": T, "bits": sorted(set(f"K{x['bits'].k_bits}{'qjl' if x['bits'].k_mode else ''}"
+                                                    f"/V{x['bits'].v_bits}" for x in layers)),
+                   "page_tokens": 16, "shuffled_pages": wl.shuffled_pages, "launch": "graph"},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "quantize_vectors_per_s": round(quant_vps, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kname,
+                     "bytes_per_launch": round(alg), "avg_launch_us": round(kern_s * 1e6, 3),
+                     "timing": "graph of the K launches, one event pair"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        pool = _seq_pages(xr["pages"], xr["offs"]["page_bytes"], xr["pt"][0, :(T + 15) // 16])
+        result["cpu_baseline"] = cpu_baseline(H, d, b0, pool, T, qs[lr].double().cpu().numpy(), scale, xr["sw"],
+                                              xr["S"], args.cpu_seconds, record_bytes(xr["offs"], H),
+                                              f"layer {lr}, sequence 0")
+    print(json.dumps(result), flush=True)
+
+
+def _seq_pages(pages, page_bytes, ids):
+    """Host copy of the listed pages, in order."""
+    import torch
+
+    idx = torch.as_tensor(np.asarray(ids, dtype=np.int64), device=pages.device)
+    return pages.view(-1, page_bytes).index_select(0, idx).cpu().numpy().reshape(-1)
 
 
 if __name__ == "__main__":
