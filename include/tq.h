@@ -25,6 +25,8 @@
  *   tq_decode_partial, tq_decode_combine
  *                       the two passes of tq_decode_attention, callable one by one: the split-K
  *                       scan over the pages, then the merge of the runs and the inverse rotation.
+ *   tq_dense_*          the uncompressed comparator: the same paged decode attention over a bf16
+ *                       cache, to measure the compressed path against the bytes it saves.
  *
  * Conventions for every call:
  *   - Returns TQ_OK (0) or a negative TQ_E* status; never aborts, never allocates device memory.
@@ -245,6 +247,48 @@ int tq_decode_combine(const tq_layout *layout, const void *pages, int64_t num_pa
                       int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
                       int pages_per_split, const void *k_cb, const void *v_cb, void *workspace,
                       size_t workspace_bytes, float *out, void *stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * Uncompressed comparator ("Where This Fits in the Inference Stack", "What Changes When KV Cache Is
+ * 4x Smaller": decode reads the entire KV cache from HBM at every step, so a cache 4x smaller moves
+ * 4x fewer bytes). The same paged, split-K GQA decode attention over a bf16 cache, with no quantization
+ * and no rotation: the baseline the compressed path is measured against on the same GPU.
+ *
+ * Dense page layout (one pool per layer, 16 token slots per page, every KV head): K as
+ * [head][slot][head_dim] bf16, then V as [head][head_dim][slot] bf16 (each head's values of a page stored
+ * coordinate-major). Page bytes = 4 * num_kv_heads * 16 * head_dim. Token t of sequence b lives in page
+ * page_table[b][t / 16], slot t % 16.
+ *
+ * head_dim must be 64 or 128, num_kv_heads >= 1; errors as for the compressed calls.
+ * ------------------------------------------------------------------------------------------------ */
+
+/* Bytes of one dense page. */
+int tq_dense_page_bytes(int head_dim, int num_kv_heads, size_t *out);
+
+/* Write n_tok tokens' K and V into dense pages, rounded to bf16 (nearest even).
+ *   k, v   device [n_tok][num_kv_heads][head_dim] of `dtype` (TQ_F32, TQ_BF16 or TQ_F16), contiguous,
+ *          16-byte aligned
+ *   slots  device int64 [n_tok]: global slot (page * 16 + offset); a slot < 0 or >= num_pages * 16 is
+ *          skipped
+ * Errors: TQ_EINVAL for a bad head_dim / dtype, null or misaligned pointers, n_tok < 0. */
+int tq_dense_write_kv(int head_dim, int num_kv_heads, void *pages, int64_t num_pages, const void *k,
+                      const void *v, int dtype, int64_t n_tok, const int64_t *slots, void *stream);
+
+/* Workspace bytes of tq_dense_decode_attention for these sizes (the split plan is the compressed
+ * path's: same pages_per_split rule). */
+int tq_dense_decode_workspace_bytes(int head_dim, int num_kv_heads, int batch, int num_q_heads,
+                                    int max_pages_per_seq, int pages_per_split, size_t *out);
+
+/* out[b][h][:] = sum_t softmax_t(scale * <q[b][h], k_t>) v_t over the seq_lens[b] cached tokens of
+ * sequence b, query head h reading KV head h / (num_q_heads / num_kv_heads); fp32 out
+ * [batch][num_q_heads][head_dim]. Arguments as for tq_decode_attention (q of TQ_F32 / TQ_BF16 /
+ * TQ_F16, page_table, seq_lens, workspace), with the dense pool in place of the packed one.
+ * Errors as for tq_decode_attention; TQ_ENOTSUP for more than 16 query heads per KV head. */
+int tq_dense_decode_attention(int head_dim, int num_kv_heads, const void *pages, int64_t num_pages,
+                              const void *q, int q_dtype, int batch, int num_q_heads, const int32_t *page_table,
+                              int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
+                              int pages_per_split, void *workspace, size_t workspace_bytes, float *out,
+                              void *stream);
 
 #ifdef __cplusplus
 }

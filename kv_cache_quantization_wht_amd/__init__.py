@@ -27,6 +27,7 @@ C_SYMBOLS = (
     "tq_strerror", "tq_codebook_bytes", "tq_build_codebook", "tq_page_layout", "tq_quantize_kv",
     "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_partial", "tq_decode_combine",
     "tq_decode_step", "tq_decode_step_partial",
+    "tq_dense_page_bytes", "tq_dense_write_kv", "tq_dense_decode_workspace_bytes", "tq_dense_decode_attention",
 )
 
 
@@ -69,6 +70,11 @@ def _lib():
         for nm in ("tq_decode_step", "tq_decode_step_partial"):
             getattr(lib, nm).argtypes = [ctypes.POINTER(_Layout), vp, i64, vp, vp, i32, vp, i32, i32, i32, vp, i32,
                                          vp, ctypes.c_float, i32, vp, vp, vp, sz, vp, vp]
+        lib.tq_dense_page_bytes.argtypes = [i32, i32, ctypes.POINTER(sz)]
+        lib.tq_dense_write_kv.argtypes = [i32, i32, vp, i64, vp, vp, i32, i64, vp, vp]
+        lib.tq_dense_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+        lib.tq_dense_decode_attention.argtypes = [i32, i32, vp, i64, vp, i32, i32, i32, vp, i32, vp, ctypes.c_float,
+                                                  i32, vp, sz, vp, vp]
         for name in C_SYMBOLS:
             getattr(lib, name).restype = ctypes.c_char_p if name == "tq_strerror" else ctypes.c_int
         _LIB = lib
@@ -282,4 +288,74 @@ def decode_step(layout: Layout, pages, k_new, v_new, q, page_table, seq_lens, so
                                  page_table.data_ptr(), maxp, seq_lens.data_ptr(), float(softmax_scale),
                                  pages_per_split, k_cb.data_ptr(), v_cb.data_ptr(), workspace.data_ptr(),
                                  workspace.numel(), out.data_ptr(), _stream(stream)), entry)
+    return out
+
+
+# --------------------------------------------------------------------------------------------------
+# Uncompressed comparator: the same paged decode attention over a bf16 cache (K [head][slot][d], V
+# [head][d][slot] per page).
+# --------------------------------------------------------------------------------------------------
+
+def dense_page_bytes(head_dim: int, num_kv_heads: int) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib().tq_dense_page_bytes(head_dim, num_kv_heads, ctypes.byref(out)), "tq_dense_page_bytes")
+    return out.value
+
+
+def dense_write_kv(head_dim: int, num_kv_heads: int, pages, k, v, slots, stream=None) -> None:
+    """Write K, V [n_tok, num_kv_heads, head_dim] (contiguous) as bf16 into dense ``pages`` at ``slots``."""
+    import torch
+
+    _need(pages, "pages", torch.uint8)
+    _need(slots, "slots", torch.int64)
+    _need(k, "k")
+    _need(v, "v")
+    if k.dtype != v.dtype or k.shape != v.shape or k.dim() != 3 or k.shape[1:] != (num_kv_heads, head_dim):
+        raise ValueError("k, v must be [n_tok, num_kv_heads, head_dim] of one dtype")
+    if not (k.is_contiguous() and v.is_contiguous() and slots.is_contiguous()) or slots.numel() != k.shape[0]:
+        raise ValueError("k, v, slots must be contiguous, one slot per token")
+    num_pages = pages.numel() // dense_page_bytes(head_dim, num_kv_heads)
+    _check(_lib().tq_dense_write_kv(head_dim, num_kv_heads, pages.data_ptr(), num_pages, k.data_ptr(), v.data_ptr(),
+                                    _dtype_code(k), k.shape[0], slots.data_ptr(), _stream(stream)), "tq_dense_write_kv")
+
+
+def dense_decode_workspace_bytes(head_dim: int, num_kv_heads: int, batch: int, num_q_heads: int,
+                                 max_pages_per_seq: int, pages_per_split: int = 0) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib().tq_dense_decode_workspace_bytes(head_dim, num_kv_heads, batch, num_q_heads, max_pages_per_seq,
+                                                  pages_per_split, ctypes.byref(out)), "tq_dense_decode_workspace_bytes")
+    return out.value
+
+
+def dense_decode_attention(head_dim: int, num_kv_heads: int, pages, q, page_table, seq_lens, softmax_scale,
+                           workspace=None, out=None, pages_per_split: int = 0, stream=None):
+    """Decode attention over a dense bf16 pool for q [batch, num_q_heads, head_dim]; returns fp32 out."""
+    import torch
+
+    _need(pages, "pages", torch.uint8)
+    _need(q, "q")
+    _need(page_table, "page_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    if q.dim() != 3 or q.shape[2] != head_dim or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [batch, num_q_heads, head_dim] tensor")
+    B, Hq, _ = q.shape
+    if page_table.dim() != 2 or page_table.shape[0] != B or not page_table.is_contiguous():
+        raise ValueError("page_table must be a contiguous [batch, max_pages_per_seq] int32 tensor")
+    if seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must hold one int32 per sequence")
+    maxp = page_table.shape[1]
+    if workspace is None:
+        need = dense_decode_workspace_bytes(head_dim, num_kv_heads, B, Hq, maxp, pages_per_split)
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(B, Hq, head_dim, dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32)
+    if out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor shaped like q")
+    num_pages = pages.numel() // dense_page_bytes(head_dim, num_kv_heads)
+    _check(_lib().tq_dense_decode_attention(head_dim, num_kv_heads, pages.data_ptr(), num_pages, q.data_ptr(),
+                                            _dtype_code(q), B, Hq, page_table.data_ptr(), maxp, seq_lens.data_ptr(),
+                                            float(softmax_scale), pages_per_split, workspace.data_ptr(),
+                                            workspace.numel(), out.data_ptr(), _stream(stream)),
+           "tq_dense_decode_attention")
     return out

@@ -464,4 +464,73 @@ int tq_decode_combine(const tq_layout *layout, const void *pages, int64_t num_pa
                        tq::kPassCombine, stream);
 }
 
+static int dense_geom(int head_dim, int num_kv_heads, tq::PageGeom *g) {
+  if ((head_dim != 64 && head_dim != 128) || num_kv_heads < 1 || num_kv_heads > 4096) return TQ_EINVAL;
+  *g = tq::PageGeom{};
+  g->head_dim = head_dim;
+  g->num_kv_heads = num_kv_heads;
+  g->page_bytes = (int64_t)4 * num_kv_heads * TQ_PAGE_TOKENS * head_dim;
+  return TQ_OK;
+}
+
+int tq_dense_page_bytes(int head_dim, int num_kv_heads, size_t *out) {
+  tq::PageGeom g;
+  const int st = dense_geom(head_dim, num_kv_heads, &g);
+  if (st) return st;
+  if (!out) return TQ_EINVAL;
+  *out = (size_t)g.page_bytes;
+  return TQ_OK;
+}
+
+int tq_dense_write_kv(int head_dim, int num_kv_heads, void *pages, int64_t num_pages, const void *k,
+                      const void *v, int dtype, int64_t n_tok, const int64_t *slots, void *stream) {
+  tq::PageGeom g;
+  const int st = dense_geom(head_dim, num_kv_heads, &g);
+  if (st) return st;
+  if (dtype != TQ_F32 && dtype != TQ_BF16 && dtype != TQ_F16) return TQ_EINVAL;
+  if (n_tok < 0 || num_pages < 0) return TQ_EINVAL;
+  if (n_tok == 0) return TQ_OK;
+  if (!pages || !k || !v || !slots) return TQ_EINVAL;
+  if (((uintptr_t)pages | (uintptr_t)k | (uintptr_t)v) & 15) return TQ_EINVAL;
+  return tq::launch_dense_write(head_dim, num_kv_heads, pages, num_pages, k, v, dtype, n_tok, slots,
+                                (hipStream_t)stream);
+}
+
+int tq_dense_decode_workspace_bytes(int head_dim, int num_kv_heads, int batch, int num_q_heads,
+                                    int max_pages_per_seq, int pages_per_split, size_t *out) {
+  if (!out) return TQ_EINVAL;
+  tq::PageGeom g;
+  int st = dense_geom(head_dim, num_kv_heads, &g);
+  if (st) return st;
+  tq::DecodeWs ws;
+  st = tq::plan_decode(g, batch, num_q_heads, max_pages_per_seq, pages_per_split, &ws);
+  if (st) return st;
+  *out = ws.total;
+  return TQ_OK;
+}
+
+int tq_dense_decode_attention(int head_dim, int num_kv_heads, const void *pages, int64_t num_pages,
+                              const void *q, int q_dtype, int batch, int num_q_heads, const int32_t *page_table,
+                              int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
+                              int pages_per_split, void *workspace, size_t workspace_bytes, float *out,
+                              void *stream) {
+  tq::PageGeom g;
+  int st = dense_geom(head_dim, num_kv_heads, &g);
+  if (st) return st;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return TQ_EINVAL;
+  if (batch < 0 || num_q_heads < 1 || num_q_heads % num_kv_heads) return TQ_EINVAL;
+  if (num_q_heads / num_kv_heads > 16) return TQ_ENOTSUP;
+  if (max_pages_per_seq < 1 || num_pages < 1 || !std::isfinite(softmax_scale) || softmax_scale < 0.f) return TQ_EINVAL;
+  if (batch == 0) return TQ_OK;
+  if (!pages || !q || !page_table || !seq_lens || !workspace || !out) return TQ_EINVAL;
+  if (((uintptr_t)pages | (uintptr_t)workspace) & 15) return TQ_EINVAL;
+  tq::DecodeWs ws;
+  st = tq::plan_decode(g, batch, num_q_heads, max_pages_per_seq, pages_per_split, &ws);
+  if (st) return st;
+  if (workspace_bytes < ws.total) return TQ_ENOSPC;
+  return tq::launch_dense_decode(head_dim, num_kv_heads, ws, pages, num_pages, q, q_dtype, batch, num_q_heads,
+                                 page_table, max_pages_per_seq, seq_lens, softmax_scale, workspace, out,
+                                 tq::kPassScan | tq::kPassCombine, (hipStream_t)stream);
+}
+
 }  // extern "C"

@@ -25,6 +25,7 @@
 
 #include "tq_common.h"
 #include "tq_internal.h"
+#include "tq_lanes.h"
 #include "tq_quant_common.h"
 
 namespace tq {
@@ -69,59 +70,6 @@ __device__ __forceinline__ float range_factor(float maxabs) {
   int e;
   frexpf(maxabs, &e);  // maxabs in [2^(e-1), 2^e)
   return ldexpf(1.0f, 8 - e);
-}
-
-// 2^x on the hardware exponential unit (results below 2^-126 flush to zero; 2^-inf = 0).
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Max over the lanes l, l ^ 16 (permlane16 swap: rows 0<->1 and 2<->3 of 16 lanes) and over l, l ^ 32.
-__device__ __forceinline__ float max_xor16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_xor16_32(float v) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Value of lane (lane ^ H) within a wavefront, for H a power of two below 64: quad permutes for 1 and 2,
-// swizzles (32-lane groups) for 4, 8, the permlane swaps for 16 and 32. No LDS memory is touched.
-template <int H>
-__device__ __forceinline__ float xor_partner(float v, int lane) {
-  const int x = __float_as_int(v);
-  if constexpr (H == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
-  else if constexpr (H == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
-  else if constexpr (H == 4 || H == 8) return __int_as_float(__builtin_amdgcn_ds_swizzle(x, (H << 10) | 0x1F));
-  else if constexpr (H == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
-    return __uint_as_float((lane & 16) ? r[0] : r[1]);
-  } else {
-    static_assert(H == 32, "xor distance");
-    const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
-    return __uint_as_float((lane & 32) ? r[0] : r[1]);
-  }
-}
-
-// One Walsh-Hadamard butterfly stage across lanes at distance H: (a, b) -> (a + b, a - b).
-template <int H>
-__device__ __forceinline__ float wht_stage(float x, int lane) {
-  const float p = xor_partner<H>(x, lane);
-  return (lane & H) ? (p - x) : (x + p);
-}
-
-// Maximum over the 64 lanes of a wavefront.
-__device__ __forceinline__ float wave_max(float v, int lane) {
-  v = fmaxf(v, xor_partner<1>(v, lane));
-  v = fmaxf(v, xor_partner<2>(v, lane));
-  v = fmaxf(v, xor_partner<4>(v, lane));
-  v = fmaxf(v, xor_partner<8>(v, lane));
-  return max_xor32(max_xor16(v));
 }
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
@@ -1106,9 +1054,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   }
 }
 
-// Merge of the runs of one (sequence, query head): log-sum-exp weights, weighted sum of the rotated value
-// sums, division by the total weight, then R_V^T (butterflies across one wavefront) and the fp32 row.
-template <int D>
+// Merge of the runs of one (sequence, query head): log-sum-exp weights, weighted sum of the value sums,
+// division by the total weight, then (ROT: sums in the rotated domain) R_V^T by butterflies across one
+// wavefront, and the fp32 row.
+template <int D, bool ROT>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   constexpr int NT = 256;
   constexpr int ITEMS = D / 4;        // float4 columns of a row
@@ -1184,6 +1133,10 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     row[4 * tid + 3] = t.w * inv;
   }
   __syncthreads();
+  if constexpr (!ROT) {
+    for (int k = tid; k < D; k += NT) a.out[bh * D + k] = row[k];
+    return;
+  }
   if (tid < 64) {
     // R_V^T = diag(s) H / sqrt(d), and the levels are in N(0,1) units (another 1 / sqrt(d))
     float x0 = row[lane], x1 = D == 128 ? row[lane + 64] : 0.f;
@@ -1225,7 +1178,7 @@ void launch(const DecodeArgs &a, hipStream_t stream) {
     }
   }
   if ((a.passes & kPassCombine) && a.n_splits > 1)
-    hipLaunchKernelGGL(combine_kernel<D>, dim3(a.B * a.Hq), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((combine_kernel<D, true>), dim3(a.B * a.Hq), dim3(256), 0, stream, a);
 }
 
 template <int D, int KB, bool KPROD, bool PK>
@@ -1292,6 +1245,21 @@ bool decode_dispatch_d64(int kb, bool kprod, int vb, const DecodeArgs &a, hipStr
 #endif
 
 #if !defined(TQ_DECODE_PART) || TQ_DECODE_PART == 1
+int launch_combine_plain(const float *part_o, const float *part_ml, int n_splits, int64_t rows, int head_dim,
+                         float *out, hipStream_t stream) {
+  DecodeArgs a{};
+  a.part_o = const_cast<float *>(part_o);
+  a.part_ml = const_cast<float *>(part_ml);
+  a.n_splits = n_splits;
+  a.out = out;
+  if (head_dim == 128) {
+    hipLaunchKernelGGL((combine_kernel<128, false>), dim3(rows), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((combine_kernel<64, false>), dim3(rows), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
 int launch_decode(const PageGeom &g, const DecodeWs &ws, const void *pages, int64_t num_pages,
                   const void *q, int q_dtype, int batch, int num_q_heads, const int32_t *page_table,
                   int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,

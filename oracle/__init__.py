@@ -18,6 +18,9 @@ Modules
   attention  brute-force GQA decode attention over the dequantized cache, and
              the same result computed in the rotated domain ("Why the KV Cache
              Exists", sections "The KV Cache Solution" and "What's in the KV Cache").
+  dense      the uncompressed (bf16) paged cache and decode attention over it:
+             the comparator's oracle ("Where This Fits in the Inference Stack",
+             "What Changes When KV Cache Is 4x Smaller").
 
 Every function is pinned by tests under ``tests/`` that check it against closed
 forms, textbook tables, library routines and brute force rather than against

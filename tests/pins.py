@@ -16,7 +16,7 @@ import numpy as np
 from scipy.integrate import quad
 
 import kvsynth
-from oracle import attention, codec, lloyd_max, rotation
+from oracle import attention, codec, dense, lloyd_max, rotation
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 PANTER_DITE = math.sqrt(3.0) * math.pi / 2.0  # high-resolution Gaussian constant, ~2.7207
@@ -507,3 +507,81 @@ def check_attention_error_shrinks_with_bits():
         D = {b: lloyd_max.distortion(lloyd_max.levels(b), lloyd_max.thresholds_of(lloyd_max.levels(b))) for b in (2, bits)}
         ratio = (e / errs[0]) / math.sqrt(D[bits] / D[2])
         assert 0.5 < ratio < 2.0, (bits, ratio)
+
+
+# --------------------------------------------------------------------------------------------
+# Uncompressed comparator (bf16 pages)
+# --------------------------------------------------------------------------------------------
+
+
+def check_dense_bf16_rounding(seed=51):
+    """Round-to-nearest-even to bf16 against torch's conversion, ties and carries included."""
+    import torch
+
+    rng = np.random.Generator(np.random.Philox(seed))
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    u = x.view(np.uint32)
+    ties = np.concatenate([(u[:500] & 0xFFFF0000) | 0x8000, (u[500:1000] | 0x10000) & 0xFFFF0000 | 0x8000,
+                           np.array([0x3F7FFFFF, 0x3F7F8000, 0x3F808000, 0x00000000, 0x80000000], np.uint32)])
+    x = np.concatenate([x, ties.view(np.float32)])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(dense.bf16_bits(x), want)
+    assert np.array_equal(dense.bf16_value(want), torch.from_numpy(want.view(np.int16)).view(torch.bfloat16).double().numpy())
+
+
+def check_dense_layout_by_hand():
+    """Byte positions of one token written by hand: K row contiguous, V column strided by 16 slots."""
+    H, d = 2, 8
+    L = dense.page_layout(H, d)
+    assert L["page_bytes"] == 2 * (H * 16 * d * 2) and L["v"] == H * 16 * d * 2
+    pool = np.zeros(3 * L["page_bytes"], np.uint8)
+    k = np.arange(1, 9, dtype=np.float64)[None]  # exactly representable in bf16
+    v = -np.arange(1, 9, dtype=np.float64)[None]
+    dense.write(pool, L, [19], 1, k, v)  # page 1, slot 3, head 1
+    w = pool.view(np.uint16)
+    for i in range(d):
+        kb = L["page_bytes"] + ((1 * 16 + 3) * d + i) * 2
+        vb = L["page_bytes"] + L["v"] + ((1 * d + i) * 16 + 3) * 2
+        assert w[kb // 2] == np.float32(i + 1).view(np.uint32) >> 16
+        assert w[vb // 2] == np.float32(-(i + 1)).view(np.uint32) >> 16
+    assert np.count_nonzero(w) == 2 * d
+
+
+def check_dense_attention_vs_torch_sdpa():
+    """Against torch's scaled_dot_product_attention (fp64, CPU) on the stored bf16 values, GQA expanded."""
+    import torch
+
+    H, d, Hq, B, lens = 2, 64, 8, 2, [45, 70]
+    rng = np.random.Generator(np.random.Philox(52))
+    L = dense.page_layout(H, d)
+    pt, npages = kvsynth.page_table(B, 5, True, seed=53)
+    pool = np.zeros(npages * L["page_bytes"], np.uint8)
+    K = rng.standard_normal((B, 80, H, d))
+    V = rng.standard_normal((B, 80, H, d))
+    for b in range(B):
+        for h in range(H):
+            dense.write(pool, L, kvsynth.slots_for(pt, b, 0, lens[b]), h, K[b, :lens[b], h], V[b, :lens[b], h])
+    q = rng.standard_normal((B, Hq, d))
+    out = dense.decode_attention(pool, L, q, pt, lens, 0.2)
+    for b in range(B):
+        Kt = torch.tensor(K[b, :lens[b]].transpose(1, 0, 2)).to(torch.bfloat16).double().repeat_interleave(Hq // H, 0)
+        Vt = torch.tensor(V[b, :lens[b]].transpose(1, 0, 2)).to(torch.bfloat16).double().repeat_interleave(Hq // H, 0)
+        ref = torch.nn.functional.scaled_dot_product_attention(torch.tensor(q[b])[:, None, :], Kt, Vt, scale=0.2)
+        assert np.allclose(out[b], ref[:, 0, :].numpy(), rtol=1e-10, atol=1e-12), b
+
+
+def check_dense_special_cases():
+    """One cached token gives its (bf16) value; equal keys give the mean value; length 0 gives zeros."""
+    H, d = 1, 64
+    L = dense.page_layout(H, d)
+    rng = np.random.Generator(np.random.Philox(54))
+    pool = np.zeros(4 * L["page_bytes"], np.uint8)
+    pt = np.array([[2, 0, 3, 1]], np.int32)
+    k = np.repeat(rng.standard_normal((1, d)), 40, axis=0)
+    v = rng.standard_normal((40, d))
+    dense.write(pool, L, kvsynth.slots_for(pt, 0, 0, 40), 0, k, v)
+    q = rng.standard_normal((1, 4, d))
+    vb = dense.bf16_value(dense.bf16_bits(v))
+    assert np.allclose(dense.decode_attention(pool, L, q, pt, [1], 0.3)[0], vb[0][None, :], atol=1e-13)
+    assert np.allclose(dense.decode_attention(pool, L, q, pt, [40], 0.3)[0], vb.mean(axis=0)[None, :], atol=1e-13)
+    assert np.all(dense.decode_attention(pool, L, q, pt, [0], 0.3) == 0)

@@ -167,3 +167,31 @@ def test_decode_step_argument_errors_need_no_gpu():
     bad = list(args)
     bad[2] = None  # null k_new
     assert lib.tq_decode_step(ctypes.byref(L), *bad) == -1
+
+
+def test_dense_argument_errors_need_no_gpu():
+    lib = tq._lib()
+    sz = ctypes.c_size_t()
+    assert lib.tq_dense_page_bytes(128, 8, ctypes.byref(sz)) == 0 and sz.value == 4 * 8 * 16 * 128
+    assert lib.tq_dense_page_bytes(96, 8, ctypes.byref(sz)) == -1
+    assert lib.tq_dense_page_bytes(128, 0, ctypes.byref(sz)) == -1
+    assert lib.tq_dense_decode_workspace_bytes(128, 8, 1, 32, 2049, 0, ctypes.byref(sz)) == 0
+    assert sz.value >= 4 * 32 * 130  # at least one run's partials
+    assert lib.tq_dense_decode_workspace_bytes(128, 8, 1, 30, 2049, 0, ctypes.byref(sz)) == -1  # Hq % Hkv
+    # (head_dim, H, pages, num_pages, k, v, dtype, n_tok, slots, stream): checks fail before any launch
+    w = (128, 8, 16, 4, 16, 16, 1, 10, 16, None)
+    for i, val, want in ((0, 96, -1), (6, 7, -1), (7, -1, -1), (2, None, -1), (4, 24, -1)):
+        bad = list(w)
+        bad[i] = val
+        assert lib.tq_dense_write_kv(*bad) == want, (i, val)
+    assert lib.tq_dense_write_kv(128, 8, 16, 4, 16, 16, 1, 0, 16, None) == 0  # nothing to write
+    # (head_dim, H, pages, num_pages, q, q_dtype, B, Hq, page_table, maxp, seq_lens, scale, pps, ws, ws_bytes, out, s)
+    a = (128, 8, 16, 4, 16, 1, 1, 32, 16, 10, 16, 0.1, 0, 16, 1 << 30, 16, None)
+    for i, val, want in ((7, 30, -1), (7, 8 * 17, -3), (11, -1.0, -1), (11, float("inf"), -1), (9, 0, -1),
+                         (2, None, -1), (13, 24, -1), (14, 4, -2), (5, 9, -1)):
+        bad = list(a)
+        bad[i] = val
+        assert lib.tq_dense_decode_attention(*bad) == want, (i, val)
+    bad = list(a)
+    bad[6] = 0  # empty batch: nothing to do
+    assert lib.tq_dense_decode_attention(*bad) == 0

@@ -9,7 +9,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle import attention, codec, lloyd_max, rotation
+from oracle import attention, codec, dense, lloyd_max, rotation
 from tests import pins
 
 
@@ -154,3 +154,38 @@ def test_mutant_norm_scaled(monkeypatch, scale):
 def test_mutant_codes_stored_as_plain_index(monkeypatch):
     monkeypatch.setattr(codec, "stored_code", lambda index, b: np.asarray(index, dtype=np.int64))
     assert _caught(pins.check_encode_known_cells, pins.check_code_map_by_hand)
+
+
+def test_mutant_dense_bf16_truncates(monkeypatch):
+    monkeypatch.setattr(dense, "bf16_bits",
+                        lambda x: (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16))
+    assert _caught(pins.check_dense_bf16_rounding)
+
+
+def test_mutant_dense_v_token_major(monkeypatch):
+    # V stored like K ([head][slot][d]) instead of coordinate-major within the page
+    monkeypatch.setattr(dense, "_v_index",
+                        lambda L, page, slot, head: (np.asarray(page, np.int64) * L["page_bytes"] + L["v"]) // 2
+                        + (head * dense.PAGE_TOKENS + np.asarray(slot)) * L["d"])
+
+    def write(pool, L, slots, head, k, v):
+        slots = np.asarray(slots, dtype=np.int64)
+        words = pool.view(np.uint16)
+        page, slot = slots // dense.PAGE_TOKENS, slots % dense.PAGE_TOKENS
+        d = L["d"]
+        words[dense._k_index(L, page, slot, head)[:, None] + np.arange(d)[None, :]] = dense.bf16_bits(k)
+        words[dense._v_index(L, page, slot, head)[:, None] + np.arange(d)[None, :]] = dense.bf16_bits(v)
+
+    monkeypatch.setattr(dense, "write", write)
+    assert _caught(pins.check_dense_layout_by_hand)
+
+
+def test_mutant_dense_wrong_kv_head(monkeypatch):
+    # query head h reading KV head h % H instead of h // G
+    orig = dense.gather
+
+    def gather(pool, L, page_row, seq_len, head):
+        return orig(pool, L, page_row, seq_len, (head + 1) % L["H"])
+
+    monkeypatch.setattr(dense, "gather", gather)
+    assert _caught(pins.check_dense_attention_vs_torch_sdpa)
