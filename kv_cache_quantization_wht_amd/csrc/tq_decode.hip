@@ -1067,8 +1067,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int S = a.n_splits;
   __shared__ float s_w[kMlCap], s_lw[kMlCap];
-  __shared__ float4 red[NT];
-  __shared__ float row[D];
+  __shared__ __align__(16) float red[GROUPS][D];
   __shared__ float s_L;
   const int k4 = tid % ITEMS, grp = tid / ITEMS;
   const float4 *po = (const float4 *)(a.part_o + bh * S * D) + k4;
@@ -1078,16 +1077,17 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     const int s2 = grp + q * GROUPS;
     pre[q] = s2 < S ? po[(int64_t)s2 * ITEMS] : float4{0.f, 0.f, 0.f, 0.f};
   }
-  for (int s2 = tid; s2 < S; s2 += NT) {
-    s_w[s2] = a.part_ml[(bh * S + s2) * 2];
-    s_lw[s2] = a.part_ml[(bh * S + s2) * 2 + 1];
-  }
-  __syncthreads();
+  // wavefront 0: the runs' maxima and sums, the log-sum-exp weights of the runs and the total weight
+  // (cross-lane reductions in registers, no LDS round trips)
   if (tid < 64) {
     float M = -INFINITY;
-    for (int s2 = lane; s2 < S; s2 += 64) M = fmaxf(M, s_w[s2]);
-#pragma unroll
-    for (int h = 1; h < 64; h <<= 1) M = fmaxf(M, __shfl_xor(M, h));
+    for (int s2 = lane; s2 < S; s2 += 64) {
+      const float m = a.part_ml[(bh * S + s2) * 2];
+      s_w[s2] = m;
+      s_lw[s2] = a.part_ml[(bh * S + s2) * 2 + 1];
+      M = fmaxf(M, m);
+    }
+    M = wave_max(M, lane);
     float L = 0.f;
     for (int s2 = lane; s2 < S; s2 += 64) {
       const float ms = s_w[s2];
@@ -1095,8 +1095,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
       s_w[s2] = e;
       L = fmaf(e, s_lw[s2], L);
     }
-#pragma unroll
-    for (int h = 1; h < 64; h <<= 1) L += __shfl_xor(L, h);
+    L = wave_sum(L, lane);
     if (lane == 0) s_L = L;
   }
   __syncthreads();
@@ -1118,34 +1117,33 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     acc.z = fmaf(e, v.z, acc.z);
     acc.w = fmaf(e, v.w, acc.w);
   }
-  red[tid] = acc;
+  *(float4 *)&red[grp][4 * k4] = acc;
   __syncthreads();
-  if (tid < ITEMS) {
-    float4 t = red[tid];
-    for (int gq = 1; gq < GROUPS; ++gq) {
-      const float4 u = red[gq * ITEMS + tid];
-      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
-    }
-    const float inv = s_L > 0.f ? 1.0f / s_L : 0.f;
-    row[4 * tid] = t.x * inv;
-    row[4 * tid + 1] = t.y * inv;
-    row[4 * tid + 2] = t.z * inv;
-    row[4 * tid + 3] = t.w * inv;
-  }
-  __syncthreads();
-  if constexpr (!ROT) {
-    for (int k = tid; k < D; k += NT) a.out[bh * D + k] = row[k];
-    return;
-  }
-  if (tid < 64) {
-    // R_V^T = diag(s) H / sqrt(d), and the levels are in N(0,1) units (another 1 / sqrt(d))
-    float x0 = row[lane], x1 = D == 128 ? row[lane + 64] : 0.f;
+  if (tid >= 64) return;
+  // wavefront 0: the group sums of coordinates lane (and lane + 64), divided by the total weight, then
+  // (ROT) R_V^T = diag(s) H / sqrt(d) on the levels' N(0,1) units (another 1 / sqrt(d)) by butterflies
+  const float inv = s_L > 0.f ? 1.0f / s_L : 0.f;
+  float x0 = 0.f, x1 = 0.f;
 #pragma unroll
-    for (int h = 1; h < 64; h <<= 1) {
-      const float p0 = __shfl_xor(x0, h), p1 = __shfl_xor(x1, h);
-      x0 = (lane & h) ? (p0 - x0) : (x0 + p0);
-      x1 = (lane & h) ? (p1 - x1) : (x1 + p1);
-    }
+  for (int g = 0; g < GROUPS; ++g) {
+    x0 += red[g][lane];
+    if constexpr (D == 128) x1 += red[g][lane + 64];
+  }
+  x0 *= inv;
+  x1 *= inv;
+  if constexpr (ROT) {
+    x0 = wht_stage<1>(x0, lane);
+    x1 = wht_stage<1>(x1, lane);
+    x0 = wht_stage<2>(x0, lane);
+    x1 = wht_stage<2>(x1, lane);
+    x0 = wht_stage<4>(x0, lane);
+    x1 = wht_stage<4>(x1, lane);
+    x0 = wht_stage<8>(x0, lane);
+    x1 = wht_stage<8>(x1, lane);
+    x0 = wht_stage<16>(x0, lane);
+    x1 = wht_stage<16>(x1, lane);
+    x0 = wht_stage<32>(x0, lane);
+    x1 = wht_stage<32>(x1, lane);
     if (D == 128) {
       const float u = x0;
       x0 = u + x1;
@@ -1154,13 +1152,13 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     const uint32_t *sw = (const uint32_t *)(a.vcb + a.vo.signs);
     x0 *= (1.0f / D);
     if ((sw[lane >> 5] >> (lane & 31)) & 1u) x0 = -x0;
-    a.out[bh * D + lane] = x0;
     if (D == 128) {
       x1 *= (1.0f / D);
       if ((sw[(lane + 64) >> 5] >> (lane & 31)) & 1u) x1 = -x1;
-      a.out[bh * D + lane + 64] = x1;
     }
   }
+  a.out[bh * D + lane] = x0;
+  if (D == 128) a.out[bh * D + lane + 64] = x1;
 }
 
 template <int D, int KB, bool KPROD, int VB, bool PK>

@@ -60,4 +60,14 @@ __device__ __forceinline__ float wave_max(float v, int lane) {
   return max_xor32(max_xor16(v));
 }
 
+// Sum over the 64 lanes of a wavefront (the xor-butterfly tree: every lane ends with the same total).
+__device__ __forceinline__ float wave_sum(float v, int lane) {
+  v += xor_partner<1>(v, lane);
+  v += xor_partner<2>(v, lane);
+  v += xor_partner<4>(v, lane);
+  v += xor_partner<8>(v, lane);
+  v += xor_partner<16>(v, lane);
+  return v + xor_partner<32>(v, lane);
+}
+
 }  // namespace tq
