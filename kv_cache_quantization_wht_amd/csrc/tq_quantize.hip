@@ -8,6 +8,8 @@
 // 16-lane rows. A lane's 8 codes are exactly b whole bytes of the vector's bit stream, so each lane writes
 // its own bytes: a contiguous run for K records and one V piece. The vectors of a work-group are
 // consecutive tokens of one head, so the records they write are neighbours in a page.
+// Prod mode runs in its own kernel: the residual sketch S r is a dense d x d product per vector, done on
+// MFMA for 16 vectors at a time (Z^T = R S^T) with S held in registers for a long run of tokens.
 #include <hip/hip_runtime.h>
 
 #include "tq_common.h"
@@ -31,15 +33,20 @@ struct QuantArgs {
   int bits[2], mode[2];
   int H;
   int dtype;
+  int which_of_y[2];  // tensor (0 = K, 1 = V) of each grid row
 };
 
 constexpr int kQuantVectorsPerLane = 1;
+constexpr int kProdChunk = 1024;  // tokens per work-group of the prod kernel (S is loaded once per work-group)
 
-// One vector: norm, signs, rotation, codes, record write (and the prod-mode residual sketch).
-template <int D, bool PROD>
+// One vector: norm, signs, rotation, codes, record write. Leaves the rotated unit vector y (N(0,1)/sqrt(d)
+// units), the stored codes, whether the slot is valid and the byte offset of the record's page for the
+// prod kernel's residual.
+template <int D>
 __device__ __forceinline__ void quantize_vector(const QuantArgs &a, int which, float *x, int64_t slot, bool active,
-                                                int h, int lane, int vl, uint32_t sword, const PosThresholds &P,
-                                                const float *s_th, const float *s_lv, float (*s_r)[D]) {
+                                                int h, int lane, uint32_t sword, const PosThresholds &P,
+                                                const float *s_th, float *y, int *code, bool &valid_out,
+                                                int64_t &page_base, int &slot_off, float &norm) {
   constexpr int LANES = D / 8;
   const unsigned char *cb = a.cb[which];
   const BlobOffsets bo = a.cbo[which];
@@ -78,8 +85,6 @@ __device__ __forceinline__ void quantize_vector(const QuantArgs &a, int which, f
   // Lloyd-Max index (ties to the upper cell) in its stored sign-magnitude form: the top bit marks the
   // non-negative half, the low bits count the rank away from zero. For y < 0 the rank counts thresholds
   // strictly below |y|, i.e. thresholds at or below the next float under |y|.
-  int code[8];
-  float y[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     y[k] = x[k] * inv;
@@ -125,57 +130,27 @@ __device__ __forceinline__ void quantize_vector(const QuantArgs &a, int which, f
       *(uint16_t *)(pg + a.norms_off[which] + (int64_t)(h * TQ_PAGE_TOKENS + off) * 2) = float_to_half_bits(n);
   }
 
-  if constexpr (PROD) {
-    const float inv_sqrt_d = D == 128 ? 0.088388347648318440f : 0.125f;
-    float r[8];
-    float g2 = 0.f;
-    __syncthreads();  // the previous vector's residuals have been read
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      // ascending index of the stored code
-      const int idx = (code[k] & half) ? code[k] : half - 1 - code[k];
-      r[k] = (y[k] - s_lv[idx]) * inv_sqrt_d;
-      g2 = fmaf(r[k], r[k], g2);
-      s_r[vl][8 * lane + k] = r[k];
-    }
-    g2 = group_sum<LANES>(g2);
-    __syncthreads();
-    const float *S = (const float *)(cb + bo.proj);
-    uint32_t zbits = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float *row = S + (int64_t)(8 * lane + k) * D;
-      float acc = 0.f;
-      for (int i = 0; i < D; ++i) acc = fmaf(row[i], s_r[vl][i], acc);
-      zbits |= (acc >= 0.f ? 1u : 0u) << k;
-    }
-    if (valid) {
-      pg[a.qjl_off[which] + (int64_t)(h * TQ_PAGE_TOKENS + off) * (D / 8) + lane] = (unsigned char)zbits;
-      if (lane == 0)
-        *(uint16_t *)(pg + a.gamma_off[which] + (int64_t)(h * TQ_PAGE_TOKENS + off) * 2) =
-            float_to_half_bits(sqrtf(g2));
-    }
-  }
+  valid_out = valid;
+  page_base = page * a.page_bytes;
+  slot_off = off;
+  norm = n;
 }
 
-// A work-group holds NV * VPB consecutive tokens of one head (K or V by blockIdx.y); each lane group
-// takes NV of them and issues all their loads before computing any, to keep bytes in flight.
+// A work-group holds NV * VPB consecutive tokens of one head (K or V, MSE mode); each lane group takes NV
+// of them and issues all their loads before computing any, to keep bytes in flight.
 template <int D>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   constexpr int LANES = D / 8;
   constexpr int VPB = 256 / LANES;
   constexpr int NV = kQuantVectorsPerLane;
-  const int which = blockIdx.y;  // 0 = K, 1 = V
+  const int which = a.which_of_y[blockIdx.y];  // 0 = K, 1 = V
   const unsigned char *cb = a.cb[which];
   const BlobOffsets bo = a.cbo[which];
   const int b = a.bits[which];
-  const int mode = a.mode[which];
   const int nl = 1 << b;
   const int half = nl >> 1;
 
   __shared__ float s_th[256];
-  __shared__ float s_lv[256];
-  __shared__ float s_r[VPB][D];
 
   const int lane = threadIdx.x % LANES;
   const int vl = threadIdx.x / LANES;
@@ -186,23 +161,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   // positive thresholds (t[half-1] is 0 by symmetry), as integer bit patterns
   PosThresholds P{};
   if (b <= 4) P = pos_thresholds((const_i32)(cb + bo.thresholds), half);
-  if (b > 4 || mode == TQ_PROD) {
+  if (b > 4) {
     for (int i = threadIdx.x; i < nl - 1; i += 256) s_th[i] = ((const float *)(cb + bo.thresholds))[i];
-    for (int i = threadIdx.x; i < nl; i += 256) s_lv[i] = half_bits_to_float(((const uint16_t *)(cb + bo.levels))[i]);
     __syncthreads();
-  }
-  if (mode == TQ_PROD) {
-    // the residual sketch reads the same rows of S for every vector: one vector at a time, so that the
-    // compiler does not hold those rows across vectors
-#pragma unroll 1
-    for (int j = 0; j < NV; ++j) {
-      const int64_t t = tok0 + (int64_t)j * VPB;
-      const int64_t tc = t < a.n_tok ? t : 0;
-      float x[8];
-      load8(a.in[which], tc * a.stride[which] + (int64_t)h * D + 8 * lane, a.dtype, x);
-      quantize_vector<D, true>(a, which, x, a.slots[tc], t < a.n_tok, h, lane, vl, sword, P, s_th, s_lv, s_r);
-    }
-    return;
   }
   // every input read issued before the first use: slots and the lane's 8 inputs of each vector
   int64_t slot[NV];
@@ -215,9 +176,168 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     load8(a.in[which], tc * a.stride[which] + (int64_t)h * D + 8 * lane, a.dtype, x[j]);
   }
 #pragma unroll
-  for (int j = 0; j < NV; ++j)
-    quantize_vector<D, false>(a, which, x[j], slot[j], tok0 + (int64_t)j * VPB < a.n_tok, h, lane, vl, sword, P,
-                              s_th, s_lv, s_r);
+  for (int j = 0; j < NV; ++j) {
+    float y[8], n;
+    int code[8], off;
+    bool valid;
+    int64_t base;
+    quantize_vector<D>(a, which, x[j], slot[j], tok0 + (int64_t)j * VPB < a.n_tok, h, lane, sword, P, s_th, y, code,
+                       valid, base, off, n);
+  }
+}
+
+// Largest power of two sigma with max|x| * sigma < 256 (1 if x is all zero).
+__device__ __forceinline__ float pow2_range(float maxabs) {
+  if (!(maxabs > 0.f)) return 1.0f;
+  int e;
+  frexpf(maxabs, &e);
+  return ldexpf(1.0f, 8 - e);
+}
+
+__device__ __forceinline__ void split16(float x, _Float16 &hi, _Float16 &lo) {
+  hi = (_Float16)x;
+  lo = (_Float16)(x - (float)hi);
+}
+
+// Prod mode ("Closing - The Three-Step Summary", Step 3): the MSE steps at bits - 1, then the residual
+// r = y - level[code] (the rotated unit-vector domain), gamma = ||r|| and the 1-bit sketch z_j = [(S r)_j >= 0].
+// A work-group takes kProdChunk consecutive tokens of one head, VPB at a time: the lane groups run the MSE
+// steps and leave r (scaled per vector by a power of two, which keeps every sign of S r) in LDS; then the
+// four wavefronts compute Z^T[vectors][rows] = R[vectors][d] S^T[d][rows] on MFMA, each for its d / 4 rows of
+// S, which it holds in registers as fp16 high + low parts for the whole run (16 S, exact); r enters as high
+// + low parts too, and the three products hi*hi, hi*lo, lo*hi carry ~22 bits. The signs of the 16 x 16
+// output blocks come out of wave ballots as 16-bit runs of the sketch bytes.
+template <int D>
+__global__ __launch_bounds__(256) void quantize_prod_kernel(QuantArgs a) {
+  constexpr int LANES = D / 8;
+  constexpr int VPB = 256 / LANES;  // vectors per round: 16 (d = 128) or 32 (d = 64)
+  constexpr int MB = VPB / 16;      // 16-vector MFMA row blocks per round
+  constexpr int NBW = D / 64;       // 16-row blocks of S per wavefront: 2 (d = 128) or 1 (d = 64)
+  constexpr int KBLK = D / 32;
+  constexpr int RS = D + 4;         // padded LDS row of residuals
+  const int which = a.which_of_y[blockIdx.y];
+  const unsigned char *cb = a.cb[which];
+  const BlobOffsets bo = a.cbo[which];
+  const int b = a.bits[which];
+  const int nl = 1 << b;
+  const int half = nl >> 1;
+
+  __shared__ float s_th[256];
+  __shared__ float s_lv[256];
+  __shared__ __align__(16) float s_r[VPB][RS];
+  __shared__ long long s_zoff[VPB];  // byte offset of each vector's sketch in the pool, or -1
+
+  const int tid = threadIdx.x;
+  const int lane = tid % LANES, vl = tid / LANES;
+  const int l64 = tid & 63, wave = tid >> 6, c = l64 & 15, g4 = l64 >> 4;
+  const int h = blockIdx.x % a.H;
+  const int64_t t0 = (int64_t)(blockIdx.x / a.H) * kProdChunk;
+  const int64_t t_end = t0 + kProdChunk < a.n_tok ? t0 + kProdChunk : a.n_tok;
+
+  const uint32_t sword = ((const uint32_t *)(cb + bo.signs))[(8 * lane) >> 5];
+  PosThresholds P{};
+  if (b <= 4) P = pos_thresholds((const_i32)(cb + bo.thresholds), half);
+  for (int i = tid; i < nl - 1; i += 256) s_th[i] = ((const float *)(cb + bo.thresholds))[i];
+  for (int i = tid; i < nl; i += 256) s_lv[i] = half_bits_to_float(((const uint16_t *)(cb + bo.levels))[i]);
+
+  // this wavefront's rows of 16 S: row 16 * (NBW * wave + nb) + c, contraction rows 8 * g4 .. of block kb =
+  // coordinates 32 * kb + 8 * g4 + p
+  half8_t shi[NBW][KBLK], slo[NBW][KBLK];
+  {
+    const float *S = (const float *)(cb + bo.proj);
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      const int row = 16 * (NBW * wave + nb) + c;
+#pragma unroll
+      for (int kb = 0; kb < KBLK; ++kb) {
+        const float4 u0 = *(const float4 *)(S + (int64_t)row * D + 32 * kb + 8 * g4);
+        const float4 u1 = *(const float4 *)(S + (int64_t)row * D + 32 * kb + 8 * g4 + 4);
+        const float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          _Float16 hi, lo;
+          split16(16.0f * v[p], hi, lo);
+          shi[nb][kb][p] = hi;
+          slo[nb][kb][p] = lo;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  const float inv_sqrt_d = D == 128 ? 0.088388347648318440f : 0.125f;
+  for (int64_t tb = t0; tb < t_end; tb += VPB) {
+    // ---- the MSE steps, the residual, gamma
+    const int64_t t = tb + vl;
+    const bool act = t < t_end;
+    const int64_t tc = act ? t : 0;
+    float x[8], y[8], n;
+    int code[8], off;
+    bool valid;
+    int64_t base;
+    load8(a.in[which], tc * a.stride[which] + (int64_t)h * D + 8 * lane, a.dtype, x);
+    quantize_vector<D>(a, which, x, a.slots[tc], act, h, lane, sword, P, s_th, y, code, valid, base, off, n);
+    float r[8], g2 = 0.f, mx = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int idx = (code[k] & half) ? code[k] : half - 1 - code[k];  // ascending index of the stored code
+      r[k] = (y[k] - s_lv[idx]) * inv_sqrt_d;
+      g2 = fmaf(r[k], r[k], g2);
+      mx = fmaxf(mx, fabsf(r[k]));
+    }
+    g2 = group_sum<LANES>(g2);
+#pragma unroll
+    for (int m = 1; m < LANES; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m, LANES));
+    const float sc = pow2_range(mx);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s_r[vl][8 * lane + k] = r[k] * sc;
+    unsigned char *pg = a.pages + base;
+    if (valid && lane == 0)
+      *(uint16_t *)(pg + a.gamma_off[which] + (int64_t)(h * TQ_PAGE_TOKENS + off) * 2) = float_to_half_bits(sqrtf(g2));
+    if (lane == 0) s_zoff[vl] = valid ? base + a.qjl_off[which] + (int64_t)(h * TQ_PAGE_TOKENS + off) * (D / 8) : -1;
+    __syncthreads();
+
+    // ---- sketch signs: Z^T = R S^T on MFMA, 16 vectors x 16 rows per block
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      half8_t ahi[KBLK], alo[KBLK];
+#pragma unroll
+      for (int kb = 0; kb < KBLK; ++kb) {
+        const float4 w0 = *(const float4 *)&s_r[16 * mb + c][32 * kb + 8 * g4];
+        const float4 w1 = *(const float4 *)&s_r[16 * mb + c][32 * kb + 8 * g4 + 4];
+        const float v[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          _Float16 hi, lo;
+          split16(v[p], hi, lo);
+          ahi[kb][p] = hi;
+          alo[kb][p] = lo;
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KBLK; ++kb) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kb], shi[nb][kb], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kb], slo[nb][kb], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[kb], shi[nb][kb], acc, 0, 0, 0);
+        }
+        // lane (c, g4) holds rows 4 * g4 + j (vectors) of column c (row of S): one ballot per j gives, for
+        // vector 4 * g4 + j, its 16 sign bits of this block in bits 16 * g4 ..
+        const unsigned long long m0 = __ballot(acc[0] >= 0.f), m1 = __ballot(acc[1] >= 0.f);
+        const unsigned long long m2 = __ballot(acc[2] >= 0.f), m3 = __ballot(acc[3] >= 0.f);
+        if (l64 < 16) {
+          const int vv = l64;  // vector of the block this lane writes
+          const unsigned long long m = (vv & 3) == 0 ? m0 : (vv & 3) == 1 ? m1 : (vv & 3) == 2 ? m2 : m3;
+          const long long zo = s_zoff[16 * mb + vv];
+          if (zo >= 0)
+            *(uint16_t *)(a.pages + zo + 2 * (NBW * wave + nb)) = (uint16_t)(m >> (16 * (vv >> 2)));
+        }
+      }
+    }
+    __syncthreads();  // the residuals of this round are read before the next round writes them
+  }
 }
 
 }  // namespace
@@ -253,14 +373,36 @@ int launch_quantize(const PageGeom &g, void *pages, int64_t num_pages, const voi
   a.mode[1] = g.v_mode;
   a.H = g.num_kv_heads;
   a.dtype = dtype;
-  // work-groups: (token groups x heads, K/V)
-  const int vpb = (g.head_dim == 128 ? 16 : 32) * kQuantVectorsPerLane;
-  const int64_t blocks = (n_tok + vpb - 1) / vpb * g.num_kv_heads;
-  if (blocks > 0x7FFFFFFF) return TQ_EINVAL;
-  dim3 grid((unsigned)blocks, 2);
-  if (g.head_dim == 128) hipLaunchKernelGGL(quantize_kernel<128>, grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(quantize_kernel<64>, grid, dim3(256), 0, stream, a);
-  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+  // MSE tensors: work-groups of consecutive tokens of one head; prod tensors: long runs of one head
+  int n_mse = 0, n_prod = 0, mse_of[2] = {0, 0}, prod_of[2] = {0, 0};
+  for (int w = 0; w < 2; ++w) {
+    if (a.mode[w] == TQ_PROD) prod_of[n_prod++] = w;
+    else mse_of[n_mse++] = w;
+  }
+  if (n_mse) {
+    QuantArgs m = a;
+    m.which_of_y[0] = mse_of[0];
+    m.which_of_y[1] = mse_of[1];
+    const int vpb = (g.head_dim == 128 ? 16 : 32) * kQuantVectorsPerLane;
+    const int64_t blocks = (n_tok + vpb - 1) / vpb * g.num_kv_heads;
+    if (blocks > 0x7FFFFFFF) return TQ_EINVAL;
+    const dim3 grid((unsigned)blocks, n_mse);
+    if (g.head_dim == 128) hipLaunchKernelGGL(quantize_kernel<128>, grid, dim3(256), 0, stream, m);
+    else hipLaunchKernelGGL(quantize_kernel<64>, grid, dim3(256), 0, stream, m);
+    if (hipGetLastError() != hipSuccess) return TQ_EHIP;
+  }
+  if (n_prod) {
+    QuantArgs p = a;
+    p.which_of_y[0] = prod_of[0];
+    p.which_of_y[1] = prod_of[1];
+    const int64_t blocks = (n_tok + kProdChunk - 1) / kProdChunk * g.num_kv_heads;
+    if (blocks > 0x7FFFFFFF) return TQ_EINVAL;
+    const dim3 grid((unsigned)blocks, n_prod);
+    if (g.head_dim == 128) hipLaunchKernelGGL(quantize_prod_kernel<128>, grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL(quantize_prod_kernel<64>, grid, dim3(256), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return TQ_EHIP;
+  }
+  return TQ_OK;
 }
 
 }  // namespace tq
