@@ -36,13 +36,14 @@ struct QuantArgs {
   int which_of_y[2];  // tensor (0 = K, 1 = V) of each grid row
 };
 
-constexpr int kQuantVectorsPerLane = 1;
+constexpr int kQuantVectorsPerLane = 4;
 constexpr int kProdChunk = 1024;  // tokens per work-group of the prod kernel (S is loaded once per work-group)
 
 // One vector: norm, signs, rotation, codes, record write. Leaves the rotated unit vector y (N(0,1)/sqrt(d)
 // units), the stored codes, whether the slot is valid and the byte offset of the record's page for the
-// prod kernel's residual.
-template <int D>
+// prod kernel's residual. BT: the code width when it is 1..4 (then every shift, search and store is fixed
+// at compile time), 0 for wide codes (the width read from the arguments).
+template <int D, int BT>
 __device__ __forceinline__ void quantize_vector(const QuantArgs &a, int which, float *x, int64_t slot, bool active,
                                                 int h, int lane, uint32_t sword, const PosThresholds &P,
                                                 const float *s_th, float *y, int *code, bool &valid_out,
@@ -50,7 +51,7 @@ __device__ __forceinline__ void quantize_vector(const QuantArgs &a, int which, f
   constexpr int LANES = D / 8;
   const unsigned char *cb = a.cb[which];
   const BlobOffsets bo = a.cbo[which];
-  const int b = a.bits[which];
+  const int b = BT ? BT : a.bits[which];
   const int half = (1 << b) >> 1;
   const bool valid = active && slot >= 0 && slot < a.num_slots;
 
@@ -91,13 +92,8 @@ __device__ __forceinline__ void quantize_vector(const QuantArgs &a, int which, f
     const bool neg = y[k] < 0.f;
     const int z = (int)(__float_as_uint(y[k]) & 0x7FFFFFFFu) - (neg ? 1 : 0);
     int mag;
-    if (b <= 4) {
-      switch (b) {
-        case 1: mag = magnitude<1>(z, P); break;
-        case 2: mag = magnitude<2>(z, P); break;
-        case 3: mag = magnitude<3>(z, P); break;
-        default: mag = magnitude<4>(z, P); break;
-      }
+    if constexpr (BT >= 1) {
+      mag = magnitude<BT>(z, P);
     } else {
       // wide codes: binary search over all thresholds in LDS, then the sign-magnitude form
       int c = 0;
@@ -138,19 +134,16 @@ __device__ __forceinline__ void quantize_vector(const QuantArgs &a, int which, f
 
 // A work-group holds NV * VPB consecutive tokens of one head (K or V, MSE mode); each lane group takes NV
 // of them and issues all their loads before computing any, to keep bytes in flight.
-template <int D>
-__global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
+template <int D, int BT>
+__device__ __forceinline__ void quantize_tokens(const QuantArgs &a, int which, float *s_th) {
   constexpr int LANES = D / 8;
   constexpr int VPB = 256 / LANES;
   constexpr int NV = kQuantVectorsPerLane;
-  const int which = a.which_of_y[blockIdx.y];  // 0 = K, 1 = V
   const unsigned char *cb = a.cb[which];
   const BlobOffsets bo = a.cbo[which];
-  const int b = a.bits[which];
+  const int b = BT ? BT : a.bits[which];
   const int nl = 1 << b;
   const int half = nl >> 1;
-
-  __shared__ float s_th[256];
 
   const int lane = threadIdx.x % LANES;
   const int vl = threadIdx.x / LANES;
@@ -160,8 +153,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   const uint32_t sword = ((const uint32_t *)(cb + bo.signs))[(8 * lane) >> 5];
   // positive thresholds (t[half-1] is 0 by symmetry), as integer bit patterns
   PosThresholds P{};
-  if (b <= 4) P = pos_thresholds((const_i32)(cb + bo.thresholds), half);
-  if (b > 4) {
+  if constexpr (BT >= 1) {
+    P = pos_thresholds((const_i32)(cb + bo.thresholds), half);
+  } else {
     for (int i = threadIdx.x; i < nl - 1; i += 256) s_th[i] = ((const float *)(cb + bo.thresholds))[i];
     __syncthreads();
   }
@@ -181,8 +175,21 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     int code[8], off;
     bool valid;
     int64_t base;
-    quantize_vector<D>(a, which, x[j], slot[j], tok0 + (int64_t)j * VPB < a.n_tok, h, lane, sword, P, s_th, y, code,
-                       valid, base, off, n);
+    quantize_vector<D, BT>(a, which, x[j], slot[j], tok0 + (int64_t)j * VPB < a.n_tok, h, lane, sword, P, s_th, y,
+                           code, valid, base, off, n);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
+  __shared__ float s_th[256];
+  const int which = a.which_of_y[blockIdx.y];  // 0 = K, 1 = V
+  switch (a.bits[which]) {  // uniform over the work-group
+    case 1: quantize_tokens<D, 1>(a, which, s_th); break;
+    case 2: quantize_tokens<D, 2>(a, which, s_th); break;
+    case 3: quantize_tokens<D, 3>(a, which, s_th); break;
+    case 4: quantize_tokens<D, 4>(a, which, s_th); break;
+    default: quantize_tokens<D, 0>(a, which, s_th); break;
   }
 }
 
@@ -207,7 +214,7 @@ __device__ __forceinline__ void split16(float x, _Float16 &hi, _Float16 &lo) {
 // S, which it holds in registers as fp16 high + low parts for the whole run (16 S, exact); r enters as high
 // + low parts too, and the three products hi*hi, hi*lo, lo*hi carry ~22 bits. The signs of the 16 x 16
 // output blocks come out of wave ballots as 16-bit runs of the sketch bytes.
-template <int D>
+template <int D, int BT>
 __global__ __launch_bounds__(256) void quantize_prod_kernel(QuantArgs a) {
   constexpr int LANES = D / 8;
   constexpr int VPB = 256 / LANES;  // vectors per round: 16 (d = 128) or 32 (d = 64)
@@ -218,7 +225,7 @@ __global__ __launch_bounds__(256) void quantize_prod_kernel(QuantArgs a) {
   const int which = a.which_of_y[blockIdx.y];
   const unsigned char *cb = a.cb[which];
   const BlobOffsets bo = a.cbo[which];
-  const int b = a.bits[which];
+  const int b = BT ? BT : a.bits[which];
   const int nl = 1 << b;
   const int half = nl >> 1;
 
@@ -236,7 +243,7 @@ __global__ __launch_bounds__(256) void quantize_prod_kernel(QuantArgs a) {
 
   const uint32_t sword = ((const uint32_t *)(cb + bo.signs))[(8 * lane) >> 5];
   PosThresholds P{};
-  if (b <= 4) P = pos_thresholds((const_i32)(cb + bo.thresholds), half);
+  if constexpr (BT >= 1) P = pos_thresholds((const_i32)(cb + bo.thresholds), half);
   for (int i = tid; i < nl - 1; i += 256) s_th[i] = ((const float *)(cb + bo.thresholds))[i];
   for (int i = tid; i < nl; i += 256) s_lv[i] = half_bits_to_float(((const uint16_t *)(cb + bo.levels))[i]);
 
@@ -276,7 +283,7 @@ __global__ __launch_bounds__(256) void quantize_prod_kernel(QuantArgs a) {
     bool valid;
     int64_t base;
     load8(a.in[which], tc * a.stride[which] + (int64_t)h * D + 8 * lane, a.dtype, x);
-    quantize_vector<D>(a, which, x, a.slots[tc], act, h, lane, sword, P, s_th, y, code, valid, base, off, n);
+    quantize_vector<D, BT>(a, which, x, a.slots[tc], act, h, lane, sword, P, s_th, y, code, valid, base, off, n);
     float r[8], g2 = 0.f, mx = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -340,6 +347,11 @@ __global__ __launch_bounds__(256) void quantize_prod_kernel(QuantArgs a) {
   }
 }
 
+template <int D, int BT>
+void launch_prod(dim3 grid, const QuantArgs &p, hipStream_t stream) {
+  hipLaunchKernelGGL((quantize_prod_kernel<D, BT>), grid, dim3(256), 0, stream, p);
+}
+
 }  // namespace
 
 int launch_quantize(const PageGeom &g, void *pages, int64_t num_pages, const void *k, const void *v,
@@ -391,15 +403,19 @@ int launch_quantize(const PageGeom &g, void *pages, int64_t num_pages, const voi
     else hipLaunchKernelGGL(quantize_kernel<64>, grid, dim3(256), 0, stream, m);
     if (hipGetLastError() != hipSuccess) return TQ_EHIP;
   }
-  if (n_prod) {
+  for (int i = 0; i < n_prod; ++i) {  // one launch per prod tensor, its code width fixed at compile time
     QuantArgs p = a;
-    p.which_of_y[0] = prod_of[0];
-    p.which_of_y[1] = prod_of[1];
+    p.which_of_y[0] = prod_of[i];
     const int64_t blocks = (n_tok + kProdChunk - 1) / kProdChunk * g.num_kv_heads;
     if (blocks > 0x7FFFFFFF) return TQ_EINVAL;
-    const dim3 grid((unsigned)blocks, n_prod);
-    if (g.head_dim == 128) hipLaunchKernelGGL(quantize_prod_kernel<128>, grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL(quantize_prod_kernel<64>, grid, dim3(256), 0, stream, p);
+    const dim3 grid((unsigned)blocks, 1);
+    const bool d128 = g.head_dim == 128;
+    switch (a.bits[prod_of[i]]) {
+      case 1: d128 ? launch_prod<128, 1>(grid, p, stream) : launch_prod<64, 1>(grid, p, stream); break;
+      case 2: d128 ? launch_prod<128, 2>(grid, p, stream) : launch_prod<64, 2>(grid, p, stream); break;
+      case 3: d128 ? launch_prod<128, 3>(grid, p, stream) : launch_prod<64, 3>(grid, p, stream); break;
+      default: d128 ? launch_prod<128, 0>(grid, p, stream) : launch_prod<64, 0>(grid, p, stream); break;
+    }
     if (hipGetLastError() != hipSuccess) return TQ_EHIP;
   }
   return TQ_OK;
