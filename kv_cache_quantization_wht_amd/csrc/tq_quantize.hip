@@ -36,7 +36,6 @@ struct QuantArgs {
   int which_of_y[2];  // tensor (0 = K, 1 = V) of each grid row
 };
 
-constexpr int kQuantVectorsPerLane = 4;
 constexpr int kProdChunk = 1024;  // tokens per work-group of the prod kernel (S is loaded once per work-group)
 
 // One vector: norm, signs, rotation, codes, record write. Leaves the rotated unit vector y (N(0,1)/sqrt(d)
@@ -132,52 +131,155 @@ __device__ __forceinline__ void quantize_vector(const QuantArgs &a, int which, f
   norm = n;
 }
 
-// A work-group holds NV * VPB consecutive tokens of one head (K or V, MSE mode); each lane group takes NV
-// of them and issues all their loads before computing any, to keep bytes in flight.
+// The MSE kernel's layout: a vector is handled by D / 32 lanes that each own 32 consecutive coordinates (the
+// Walsh-Hadamard stages of stride 1 .. 16 in registers, 32 and 64 across lanes), so the per-vector work
+// (norm, reciprocal, record addresses) is shared by fewer lanes and a lane writes 4b bytes of a K record or
+// four b-byte V pieces. The norm's partial sums (8 coordinates, then pairs, then lanes) and the butterflies
+// (ascending strides) are taken in the same order as the 8-coordinate layout of the prod kernel and of the
+// decode step's append, so every layout writes the same bytes.
+template <int D, int BT>
+__device__ __forceinline__ void quantize_vector32(const QuantArgs &a, int which, float *x, int64_t slot, bool active,
+                                                  int h, int lane, uint32_t sword, const PosThresholds &P,
+                                                  const float *s_th) {
+  constexpr int LANES = D / 32;
+  static_assert(BT >= 1 && BT <= 8 && BT != 5 && BT != 6 && BT != 7, "MSE code widths 1, 2, 3, 4, 8");
+  constexpr int half = (1 << BT) >> 1;
+  const bool valid = active && slot >= 0 && slot < a.num_slots;
+
+  float s8[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t = fmaf(x[8 * g + k], x[8 * g + k], t);
+    s8[g] = t;
+  }
+  float ss = (s8[0] + s8[1]) + (s8[2] + s8[3]);
+  ss += xor_lane<1>(ss);
+  if constexpr (LANES == 4) ss += xor_lane<2>(ss);
+  const float n = sqrtf(ss);
+  const float inv = n > 0.f ? 1.0f / n : 0.f;
+
+#pragma unroll
+  for (int k = 0; k < 32; ++k)
+    if ((sword >> k) & 1u) x[k] = -x[k];
+#pragma unroll
+  for (int hs = 1; hs < 32; hs <<= 1) {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      if (!(k & hs)) {
+        const float u = x[k], w = x[k + hs];
+        x[k] = u + w;
+        x[k + hs] = u - w;
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const float p = xor_lane<1>(x[k]);
+    x[k] = (lane & 1) ? (p - x[k]) : (x[k] + p);
+  }
+  if constexpr (LANES == 4) {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const float p = xor_lane<2>(x[k]);
+      x[k] = (lane & 2) ? (p - x[k]) : (x[k] + p);
+    }
+  }
+
+  // codes (sign-magnitude, ties to the upper cell), packed into the lane's 32 * b bits as they come
+  constexpr int BW = BT;  // dwords of the lane's 32 * BT bit stream
+  uint32_t w[BW];
+#pragma unroll
+  for (int i = 0; i < BW; ++i) w[i] = 0u;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const float y = x[k] * inv;
+    const bool neg = y < 0.f;
+    const int z = (int)(__float_as_uint(y) & 0x7FFFFFFFu) - (neg ? 1 : 0);
+    int mag;
+    if constexpr (BT <= 4) {
+      mag = magnitude<BT>(z, P);
+    } else {  // 8-bit codes: binary search over all thresholds in LDS
+      int c = 0;
+      for (int st = half; st > 0; st >>= 1)
+        if (y >= s_th[c + st - 1]) c += st;
+      mag = c >= half ? c - half : half - 1 - c;
+    }
+    const uint32_t code = (uint32_t)(neg ? mag : (half | mag));
+    const int bit = BT * k;
+    w[bit >> 5] |= code << (bit & 31);
+    if ((bit & 31) + BT > 32) w[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
+  }
+  if (!valid) return;
+  const int64_t page = slot / TQ_PAGE_TOKENS;
+  const int off = (int)(slot % TQ_PAGE_TOKENS);
+  unsigned char *pg = a.pages + page * a.page_bytes;
+  if (which == 0) {
+    uint32_t *dst = (uint32_t *)(pg + a.codes_off[0] + (int64_t)(h * TQ_PAGE_TOKENS + off) * (D * BT / 8) + lane * 4 * BT);
+    if constexpr (BT == 8) {
+      ((uint4 *)dst)[0] = uint4{w[0], w[1], w[2], w[3]};
+      ((uint4 *)dst)[1] = uint4{w[4], w[5], w[6], w[7]};
+    } else if constexpr (BT == 4) {
+      *(uint4 *)dst = uint4{w[0], w[1], w[2], w[3]};
+    } else if constexpr (BT == 2) {
+      *(uint2 *)dst = uint2{w[0], w[1]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < BT; ++i) dst[i] = w[i];
+    }
+  } else {
+    // piece i (codes 8i .. 8i + 7 of the lane) = bits 8 * BT * i .. of the lane's stream
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      unsigned char *dst = pg + a.codes_off[1] + ((int64_t)(h * (D / 8) + 4 * lane + i) * TQ_PAGE_TOKENS + off) * BT;
+      const int bit = 8 * BT * i;
+      const uint64_t two = (uint64_t)w[bit >> 5] | ((bit >> 5) + 1 < BW ? (uint64_t)w[(bit >> 5) + 1] << 32 : 0ull);
+      const uint64_t piece = two >> (bit & 31);
+      if constexpr (BT == 1) *dst = (unsigned char)piece;
+      else if constexpr (BT == 2) *(uint16_t *)dst = (uint16_t)piece;
+      else if constexpr (BT == 4) *(uint32_t *)dst = (uint32_t)piece;
+      else if constexpr (BT == 8) *(uint64_t *)dst = piece;
+      else {
+#pragma unroll
+        for (int q = 0; q < BT; ++q) dst[q] = (unsigned char)(piece >> (8 * q));
+      }
+    }
+  }
+  if (lane == 0)
+    *(uint16_t *)(pg + a.norms_off[which] + (int64_t)(h * TQ_PAGE_TOKENS + off) * 2) = float_to_half_bits(n);
+}
+
+// A work-group holds VPB consecutive tokens of one head (K or V, MSE mode), one vector per D / 32 lanes.
 template <int D, int BT>
 __device__ __forceinline__ void quantize_tokens(const QuantArgs &a, int which, float *s_th) {
-  constexpr int LANES = D / 8;
+  constexpr int LANES = D / 32;
   constexpr int VPB = 256 / LANES;
-  constexpr int NV = kQuantVectorsPerLane;
   const unsigned char *cb = a.cb[which];
   const BlobOffsets bo = a.cbo[which];
-  const int b = BT ? BT : a.bits[which];
-  const int nl = 1 << b;
-  const int half = nl >> 1;
+  constexpr int nl = 1 << BT;
+  constexpr int half = nl >> 1;
 
   const int lane = threadIdx.x % LANES;
   const int vl = threadIdx.x / LANES;
   const int h = blockIdx.x % a.H;
-  const int64_t tok0 = (int64_t)(blockIdx.x / a.H) * (VPB * NV) + vl;
+  const int64_t t = (int64_t)(blockIdx.x / a.H) * VPB + vl;
+  const int64_t tc = t < a.n_tok ? t : 0;
 
-  const uint32_t sword = ((const uint32_t *)(cb + bo.signs))[(8 * lane) >> 5];
+  const uint32_t sword = ((const uint32_t *)(cb + bo.signs))[lane];
   // positive thresholds (t[half-1] is 0 by symmetry), as integer bit patterns
   PosThresholds P{};
-  if constexpr (BT >= 1) {
+  if constexpr (BT <= 4) {
     P = pos_thresholds((const_i32)(cb + bo.thresholds), half);
   } else {
     for (int i = threadIdx.x; i < nl - 1; i += 256) s_th[i] = ((const float *)(cb + bo.thresholds))[i];
     __syncthreads();
   }
-  // every input read issued before the first use: slots and the lane's 8 inputs of each vector
-  int64_t slot[NV];
-  float x[NV][8];
+  const int64_t slot = a.slots[tc];
+  float x[32];
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int64_t t = tok0 + (int64_t)j * VPB;
-    const int64_t tc = t < a.n_tok ? t : 0;
-    slot[j] = a.slots[tc];
-    load8(a.in[which], tc * a.stride[which] + (int64_t)h * D + 8 * lane, a.dtype, x[j]);
-  }
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    float y[8], n;
-    int code[8], off;
-    bool valid;
-    int64_t base;
-    quantize_vector<D, BT>(a, which, x[j], slot[j], tok0 + (int64_t)j * VPB < a.n_tok, h, lane, sword, P, s_th, y,
-                           code, valid, base, off, n);
-  }
+  for (int g = 0; g < 4; ++g) load8(a.in[which], tc * a.stride[which] + (int64_t)h * D + 32 * lane + 8 * g, a.dtype, x + 8 * g);
+  quantize_vector32<D, BT>(a, which, x, slot, t < a.n_tok, h, lane, sword, P, s_th);
 }
 
 template <int D>
@@ -189,7 +291,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     case 2: quantize_tokens<D, 2>(a, which, s_th); break;
     case 3: quantize_tokens<D, 3>(a, which, s_th); break;
     case 4: quantize_tokens<D, 4>(a, which, s_th); break;
-    default: quantize_tokens<D, 0>(a, which, s_th); break;
+    default: quantize_tokens<D, 8>(a, which, s_th); break;  // MSE widths are 1, 2, 3, 4 or 8
   }
 }
 
@@ -395,7 +497,7 @@ int launch_quantize(const PageGeom &g, void *pages, int64_t num_pages, const voi
     QuantArgs m = a;
     m.which_of_y[0] = mse_of[0];
     m.which_of_y[1] = mse_of[1];
-    const int vpb = (g.head_dim == 128 ? 16 : 32) * kQuantVectorsPerLane;
+    const int vpb = 256 / (g.head_dim / 32);  // vectors per work-group: one per D / 32 lanes
     const int64_t blocks = (n_tok + vpb - 1) / vpb * g.num_kv_heads;
     if (blocks > 0x7FFFFFFF) return TQ_EINVAL;
     const dim3 grid((unsigned)blocks, n_mse);
