@@ -87,23 +87,41 @@ __device__ __forceinline__ PosThresholds pos_thresholds(Ptr t, int half) {
   return PosThresholds{at(1), at(2), at(3), at(4), at(5), at(6), at(7)};
 }
 
-// Magnitude part of the sign-magnitude code for B <= 4 bits: the number of positive thresholds at or
-// below z, by a binary search over the 2^(B-1) - 1 ascending positive thresholds, all in registers.
+// Magnitude part of the sign-magnitude code for B <= 4 bits: the number of positive thresholds at or below z,
+// by a binary search over the 2^(B-1) - 1 ascending positive thresholds, held as per-lane (vector register)
+// copies: every selection is one v_cndmask between two registers, and the thresholds are plain values, never
+// a table (a selection between the fields of a scalar struct can be turned into an indexed memory copy).
+struct PosThresholdsV {
+  int p1, p2, p3, p4, p5, p6, p7;
+};
+__device__ __forceinline__ int to_vgpr(int s) {
+  int v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "s"(s));
+  return v;
+}
+__device__ __forceinline__ PosThresholdsV thresholds_in_vgprs(const PosThresholds &P) {
+  return PosThresholdsV{to_vgpr(P.p1), to_vgpr(P.p2), to_vgpr(P.p3), to_vgpr(P.p4),
+                        to_vgpr(P.p5), to_vgpr(P.p6), to_vgpr(P.p7)};
+}
 template <int B>
-__device__ __forceinline__ int magnitude(int z, const PosThresholds &P) {
+__device__ __forceinline__ int magnitude_v(int z, const PosThresholdsV &P) {
   if constexpr (B == 1) {
     return 0;
   } else if constexpr (B == 2) {
     return z >= P.p1 ? 1 : 0;
   } else if constexpr (B == 3) {
-    const int m = z >= P.p2 ? 2 : 0;
-    return m + (z >= (m ? P.p3 : P.p1) ? 1 : 0);
+    const bool h2 = z >= P.p2;
+    const int t = h2 ? P.p3 : P.p1;
+    return (h2 ? 2 : 0) + (z >= t ? 1 : 0);
   } else {
     static_assert(B == 4, "register search covers up to 4 bits");
     const bool h4 = z >= P.p4;
-    const bool h2 = z >= (h4 ? P.p6 : P.p2);
-    const int t = h4 ? (h2 ? P.p7 : P.p5) : (h2 ? P.p3 : P.p1);
-    return (h4 ? 4 : 0) + (h2 ? 2 : 0) + (z >= t ? 1 : 0);
+    const int t2 = h4 ? P.p6 : P.p2;
+    const bool h2 = z >= t2;
+    const int ta = h2 ? P.p3 : P.p1;
+    const int tb = h2 ? P.p7 : P.p5;
+    const int t1 = h4 ? tb : ta;
+    return (h4 ? 4 : 0) + (h2 ? 2 : 0) + (z >= t1 ? 1 : 0);
   }
 }
 

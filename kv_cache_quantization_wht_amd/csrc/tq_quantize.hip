@@ -85,6 +85,7 @@ __device__ __forceinline__ void quantize_vector(const QuantArgs &a, int which, f
   // Lloyd-Max index (ties to the upper cell) in its stored sign-magnitude form: the top bit marks the
   // non-negative half, the low bits count the rank away from zero. For y < 0 the rank counts thresholds
   // strictly below |y|, i.e. thresholds at or below the next float under |y|.
+  const PosThresholdsV PV = thresholds_in_vgprs(P);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     y[k] = x[k] * inv;
@@ -92,7 +93,7 @@ __device__ __forceinline__ void quantize_vector(const QuantArgs &a, int which, f
     const int z = (int)(__float_as_uint(y[k]) & 0x7FFFFFFFu) - (neg ? 1 : 0);
     int mag;
     if constexpr (BT >= 1) {
-      mag = magnitude<BT>(z, P);
+      mag = magnitude_v<BT>(z, PV);
     } else {
       // wide codes: binary search over all thresholds in LDS, then the sign-magnitude form
       int c = 0;
@@ -189,6 +190,7 @@ __device__ __forceinline__ void quantize_vector32(const QuantArgs &a, int which,
 
   // codes (sign-magnitude, ties to the upper cell), packed into the lane's 32 * b bits as they come
   constexpr int BW = BT;  // dwords of the lane's 32 * BT bit stream
+  const PosThresholdsV PV = thresholds_in_vgprs(P);
   uint32_t w[BW];
 #pragma unroll
   for (int i = 0; i < BW; ++i) w[i] = 0u;
@@ -199,7 +201,7 @@ __device__ __forceinline__ void quantize_vector32(const QuantArgs &a, int which,
     const int z = (int)(__float_as_uint(y) & 0x7FFFFFFFu) - (neg ? 1 : 0);
     int mag;
     if constexpr (BT <= 4) {
-      mag = magnitude<BT>(z, P);
+      mag = magnitude_v<BT>(z, PV);
     } else {  // 8-bit codes: binary search over all thresholds in LDS
       int c = 0;
       for (int st = half; st > 0; st >>= 1)
