@@ -3,13 +3,15 @@
 //   idx_i = #{j : y'_i >= t_j}      (Gaussian Lloyd-Max thresholds, midpoints of the fp16 levels),
 //   code_i = sign-magnitude form of idx_i, pack the b-bit codes, store n as fp16, and in prod mode also
 //   r = (y' - level[code]) / sqrt(d), gamma = ||r||, z_j = [(S r)_j >= 0].
-// One vector is handled by d/8 lanes that each own 8 consecutive coordinates: the three lowest
-// Walsh-Hadamard stages run in registers, the others exchange values between lanes with DPP moves inside
-// 16-lane rows. A lane's 8 codes are exactly b whole bytes of the vector's bit stream, so each lane writes
-// its own bytes: a contiguous run for K records and one V piece. The vectors of a work-group are
-// consecutive tokens of one head, so the records they write are neighbours in a page.
-// Prod mode runs in its own kernel: the residual sketch S r is a dense d x d product per vector, done on
-// MFMA for 16 vectors at a time (Z^T = R S^T) with S held in registers for a long run of tokens.
+// MSE mode: one vector is handled by d/32 lanes that each own 32 consecutive coordinates: the five lowest
+// Walsh-Hadamard stages run in registers, the others exchange values between lanes with DPP moves. A lane's
+// 32 codes are 4b whole bytes of the vector's bit stream (four whole V pieces), so each lane writes its own
+// bytes. The vectors of a work-group are consecutive tokens of one head, so the records they write are
+// neighbours in a page. The code width is a compile-time parameter (one uniform switch per work-group).
+// Prod mode runs in its own kernel: the MSE steps with d/8 lanes of 8 coordinates per vector, then the
+// residual sketch S r, a dense d x d product per vector, on MFMA for 16 vectors at a time (Z^T = R S^T) with
+// S held in registers for a long run of tokens. Both layouts (and the decode step's append) take the norm's
+// partial sums and the butterflies in the same order, so they write the same bytes.
 #include <hip/hip_runtime.h>
 
 #include "tq_common.h"
