@@ -585,3 +585,101 @@ def check_dense_special_cases():
     assert np.allclose(dense.decode_attention(pool, L, q, pt, [1], 0.3)[0], vb[0][None, :], atol=1e-13)
     assert np.allclose(dense.decode_attention(pool, L, q, pt, [40], 0.3)[0], vb.mean(axis=0)[None, :], atol=1e-13)
     assert np.all(dense.decode_attention(pool, L, q, pt, [0], 0.3) == 0)
+
+
+# --------------------------------------------------------------------------------------------
+# Uncompressed comparator (FP8 E4M3 pages, one scale per tensor)
+# --------------------------------------------------------------------------------------------
+
+
+def check_fp8_value_table():
+    """Every byte's value against torch's float8_e4m3fn, NaN patterns included."""
+    import torch
+
+    b = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(b).view(torch.float8_e4m3fn).double().numpy()
+    got = dense.fp8_value(b)
+    assert np.array_equal(np.isnan(want), np.isnan(got)) and np.isnan(got).sum() == 2
+    assert np.array_equal(got[~np.isnan(got)], want[~np.isnan(want)])
+    assert dense.fp8_value(0x7E) == 448.0 and dense.fp8_value(0x01) == 2.0 ** -9 and dense.fp8_value(0x08) == 2.0 ** -6
+
+
+def check_fp8_rounding_vs_torch(seed=55):
+    """Round-to-nearest-even to E4M3 against torch's conversion: random values over the whole range, every
+    representable value and every midpoint between neighbours (the ties), both signs."""
+    import torch
+
+    rng = np.random.Generator(np.random.Philox(seed))
+    x = (rng.standard_normal(40000) * np.exp(rng.uniform(-14, 7, 40000))).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    b = np.arange(0x7F, dtype=np.uint8)
+    vals = dense.fp8_value(b)
+    mids = (vals[1:] + vals[:-1]) / 2  # exact in fp32
+    x = np.concatenate([x, vals, mids, -vals, -mids]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(dense.fp8_bits(x), want)
+
+
+def check_fp8_rounding_brute_force(seed=56):
+    """Nearest finite E4M3 value by exhaustive search, ties to the even code; saturation above 448."""
+    rng = np.random.Generator(np.random.Philox(seed))
+    y = np.concatenate([rng.uniform(-460, 460, 3000), rng.standard_normal(3000) * 0.02,
+                        np.float64([464.0, 1e6, -1e30, 449.0, 2 ** -10, -(2 ** -10), 3 * 2 ** -11])]).astype(np.float32)
+    codes = np.arange(256)
+    vals = dense.fp8_value(codes)
+    fin = ~np.isnan(vals)
+    got = dense.fp8_bits(y)
+    for yi, gi in zip(y.astype(np.float64), got):
+        sign = 0x80 if np.signbit(yi) else 0
+        cand = codes[fin & ((codes & 0x80) == sign)]
+        dist = np.abs(np.abs(dense.fp8_value(cand)) - min(abs(yi), 448.0))
+        best = cand[dist == dist.min()]
+        best = best[(best & 1) == 0] if len(best) > 1 else best
+        assert len(best) == 1 and best[0] == gi, (yi, gi, best)
+
+
+def check_fp8_scale_and_layout_by_hand():
+    """The scale divides before rounding and multiplies on read; byte positions of one token written by hand
+    (K row contiguous, V column strided by 16 slots, 1 byte per element)."""
+    H, d = 2, 8
+    L = dense.page_layout(H, d, "fp8", k_scale=0.5, v_scale=4.0)
+    assert L["page_bytes"] == 2 * H * 16 * d and L["v"] == H * 16 * d
+    pool = np.zeros(3 * L["page_bytes"], np.uint8)
+    k = np.arange(1, 9, dtype=np.float64)[None] * 0.5  # k / 0.5 = 1..8, exact in E4M3
+    v = -np.arange(1, 9, dtype=np.float64)[None] * 4.0  # v / 4 = -1..-8
+    dense.write(pool, L, [19], 1, k, v)  # page 1, slot 3, head 1
+    for i in range(d):
+        kb = L["page_bytes"] + (1 * 16 + 3) * d + i
+        vb = L["page_bytes"] + L["v"] + (1 * d + i) * 16 + 3
+        assert dense.fp8_value(pool[kb]) == i + 1 and dense.fp8_value(pool[vb]) == -(i + 1)
+    assert np.count_nonzero(pool) == 2 * d
+    K, V = dense.gather(pool, L, [0, 1], 20, 1)
+    assert np.array_equal(K[19], k[0]) and np.array_equal(V[19], v[0]) and not K[:19].any()
+
+
+def check_dense_fp8_attention_vs_torch_sdpa():
+    """Against torch's scaled_dot_product_attention (fp64, CPU) on scale * E4M3(x / scale) made by torch's
+    own conversion, GQA expanded."""
+    import torch
+
+    H, d, Hq, B, lens, ks, vs = 2, 64, 8, 2, [45, 70], 0.25, 3.0
+    rng = np.random.Generator(np.random.Philox(57))
+    L = dense.page_layout(H, d, "fp8", k_scale=ks, v_scale=vs)
+    pt, npages = kvsynth.page_table(B, 5, True, seed=58)
+    pool = np.zeros(npages * L["page_bytes"], np.uint8)
+    K = rng.standard_normal((B, 80, H, d))
+    V = rng.standard_normal((B, 80, H, d)) * 20
+    for b in range(B):
+        for h in range(H):
+            dense.write(pool, L, kvsynth.slots_for(pt, b, 0, lens[b]), h, K[b, :lens[b], h], V[b, :lens[b], h])
+    q = rng.standard_normal((B, Hq, d))
+    out = dense.decode_attention(pool, L, q, pt, lens, 0.2)
+
+    def f8(x, s):
+        return (torch.tensor(x).float() / s).to(torch.float8_e4m3fn).double() * s
+
+    for b in range(B):
+        Kt = f8(K[b, :lens[b]].transpose(1, 0, 2), ks).repeat_interleave(Hq // H, 0)
+        Vt = f8(V[b, :lens[b]].transpose(1, 0, 2), vs).repeat_interleave(Hq // H, 0)
+        ref = torch.nn.functional.scaled_dot_product_attention(torch.tensor(q[b])[:, None, :], Kt, Vt, scale=0.2)
+        assert np.allclose(out[b], ref[:, 0, :].numpy(), rtol=1e-10, atol=1e-12), b

@@ -189,3 +189,53 @@ def test_mutant_dense_wrong_kv_head(monkeypatch):
 
     monkeypatch.setattr(dense, "gather", gather)
     assert _caught(pins.check_dense_attention_vs_torch_sdpa)
+
+
+def test_mutant_fp8_truncates(monkeypatch):
+    # round toward zero instead of to nearest: step down one code wherever the nearest value overshoots
+    orig = dense.fp8_bits
+
+    def trunc(x, scale=1.0):
+        b = orig(x, scale).astype(np.int64)
+        y = np.abs(np.asarray(x, dtype=np.float32) / np.float32(scale)).astype(np.float64)
+        over = (np.abs(dense.fp8_value(b)) > y) & ((b & 0x7F) > 0)
+        return (b - over).astype(np.uint8)
+
+    monkeypatch.setattr(dense, "fp8_bits", trunc)
+    assert _caught(pins.check_fp8_rounding_vs_torch) and _caught(pins.check_fp8_rounding_brute_force)
+
+
+def test_mutant_fp8_overflow_to_nan(monkeypatch):
+    orig = dense.fp8_bits
+
+    def nosat(x, scale=1.0):
+        b = orig(x, scale)
+        big = np.abs(np.asarray(x, dtype=np.float32) / np.float32(scale)) > 464
+        return np.where(big, b | 0x7F, b).astype(np.uint8)
+
+    monkeypatch.setattr(dense, "fp8_bits", nosat)
+    assert _caught(pins.check_fp8_rounding_brute_force)
+
+
+def test_mutant_fp8_scale_multiplies_on_write(monkeypatch):
+    orig = dense.fp8_bits
+    monkeypatch.setattr(dense, "fp8_bits", lambda x, scale=1.0: orig(np.asarray(x, np.float32) * np.float32(scale)))
+    assert _caught(pins.check_fp8_scale_and_layout_by_hand) and _caught(pins.check_dense_fp8_attention_vs_torch_sdpa)
+
+
+def test_mutant_fp8_read_ignores_scale(monkeypatch):
+    orig = dense._decode
+    monkeypatch.setattr(dense, "_decode", lambda L, bits, scale: orig(L, bits, 1.0))
+    assert _caught(pins.check_fp8_scale_and_layout_by_hand, pins.check_dense_fp8_attention_vs_torch_sdpa) == 2
+
+
+def test_mutant_fp8_subnormal_step(monkeypatch):
+    orig = dense.fp8_value
+
+    def value(bits):
+        v = orig(bits)
+        b = np.asarray(bits, dtype=np.int64)
+        return np.where(((b >> 3) & 15) == 0, v / 2, v)
+
+    monkeypatch.setattr(dense, "fp8_value", value)
+    assert _caught(pins.check_fp8_value_table)
