@@ -68,7 +68,7 @@ def main():
     ap.add_argument("--copies", type=int, default=16, help="independent layer caches cycled per step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-dense", action="store_true", help="skip the uncompressed bf16 comparator")
+    ap.add_argument("--no-dense", action="store_true", help="skip the uncompressed bf16 and FP8 comparators")
     ap.add_argument("--eager", action="store_true", help="launch steps from Python instead of a captured graph")
     ap.add_argument("--workload", default=None,
                     help="another synthetic workload by name or index (default: the Llama-3.1-8B single layer); "
@@ -300,6 +300,8 @@ def main():
 
     if not args.no_dense:
         result["dense_bf16"] = dense_comparator(wl, k_pre, v_pre, k_new, v_new, qs, W, K, ms_per_step, step_bytes)
+        result["dense_fp8"] = dense_comparator(wl, k_pre, v_pre, k_new, v_new, qs, W, K, ms_per_step, step_bytes,
+                                               fmt="fp8")
     if not args.no_cpu_baseline:
         first = int(page_tables[0][0, 0].item())
         npg = (T + 15) // 16
@@ -398,11 +400,13 @@ def study_prod_vs_mse(B=4, T=4096):
                       "kv_heads": H, "q_heads": Hq, "head_dim": d, "rows": rows}), flush=True)
 
 
-def dense_comparator(wl, k_pre, v_pre, k_new, v_new, qs, W, K, ms_compressed, step_bytes):
-    """The same decode steps over an uncompressed bf16 cache of the layer: per step, the new token's K/V is
-    written into its slot (tq_dense_write_kv) and the new query attends over every cached token
-    (tq_dense_decode_attention: split-K launch + merge). 4 copies of the layer cache (4 x 134 MB, more than
-    the Infinity Cache) are cycled as for the compressed cache; the K steps replay as one HIP graph."""
+def dense_comparator(wl, k_pre, v_pre, k_new, v_new, qs, W, K, ms_compressed, step_bytes, fmt="bf16"):
+    """The same decode steps over an uncompressed cache of the layer, bf16 or FP8 E4M3 (one scale per tensor,
+    amax / 448 of the prefilled K and V): per step, the new token's K/V is written into its slot
+    (tq_dense_write_kv / tq_dense_fp8_write_kv) and the new query attends over every cached token
+    (tq_dense_decode_attention / tq_dense_fp8_decode_attention: split-K launch + merge). 4 copies of the
+    layer cache (4 x 134 MB in bf16, more than the Infinity Cache) are cycled as for the compressed cache;
+    the K steps replay as one HIP graph."""
     import torch
 
     import kv_cache_quantization_wht_amd as tq
@@ -412,11 +416,21 @@ def dense_comparator(wl, k_pre, v_pre, k_new, v_new, qs, W, K, ms_compressed, st
     C = 4
     total = W + K
     ppc = (T + (total + C - 1) // C + 1 + 15) // 16
-    pb = tq.dense_page_bytes(d, H)
+    fp8 = fmt == "fp8"
+    elem = 1 if fp8 else 2
+    ks, vs = (k_pre.abs().max().item() / 448.0, v_pre.abs().max().item() / 448.0) if fp8 else (1.0, 1.0)
+    pb = tq.dense_fp8_page_bytes(d, H) if fp8 else tq.dense_page_bytes(d, H)
     pages = torch.zeros(C * ppc * pb, dtype=torch.uint8, device=dev)
     slots0 = torch.arange(T, dtype=torch.int64, device=dev)
+
+    def write(k, v, slots):
+        if fp8:
+            tq.dense_fp8_write_kv(d, H, pages, k, v, slots, ks, vs)
+        else:
+            tq.dense_write_kv(d, H, pages, k, v, slots)
+
     for c in range(C):
-        tq.dense_write_kv(d, H, pages, k_pre, v_pre, slots0 + c * ppc * 16)
+        write(k_pre, v_pre, slots0 + c * ppc * 16)
     pts = [torch.arange(c * ppc, (c + 1) * ppc, dtype=torch.int32, device=dev)[None] for c in range(C)]
     lens = [T] * C
     st_slots, st_lens, st_copy, st_bytes = [], [], [], []
@@ -427,14 +441,18 @@ def dense_comparator(wl, k_pre, v_pre, k_new, v_new, qs, W, K, ms_compressed, st
         lens[c] = t + 1
         st_lens.append(torch.tensor([t + 1], dtype=torch.int32, device=dev))
         st_copy.append(c)
-        st_bytes.append(H * (t + 1) * d * 2 * 2 + H * 2 * d * 2 + 4 * ((t + 1 + 15) // 16))
+        st_bytes.append(H * (t + 1) * d * elem * 2 + H * 2 * d * elem + 4 * ((t + 1 + 15) // 16))
     ws = torch.zeros(tq.dense_decode_workspace_bytes(d, H, 1, Hq, ppc), dtype=torch.uint8, device=dev)
     out = torch.empty(1, Hq, d, dtype=torch.float32, device=dev)
 
     def step(i):
-        tq.dense_write_kv(d, H, pages, k_new[i:i + 1], v_new[i:i + 1], st_slots[i])
-        tq.dense_decode_attention(d, H, pages, qs[i], pts[st_copy[i]], st_lens[i], wl.softmax_scale, workspace=ws,
-                                  out=out)
+        write(k_new[i:i + 1], v_new[i:i + 1], st_slots[i])
+        if fp8:
+            tq.dense_fp8_decode_attention(d, H, pages, qs[i], pts[st_copy[i]], st_lens[i], wl.softmax_scale, ks, vs,
+                                          workspace=ws, out=out)
+        else:
+            tq.dense_decode_attention(d, H, pages, qs[i], pts[st_copy[i]], st_lens[i], wl.softmax_scale,
+                                      workspace=ws, out=out)
 
     for i in range(W):
         step(i)
@@ -451,14 +469,15 @@ def dense_comparator(wl, k_pre, v_pre, k_new, v_new, qs, W, K, ms_compressed, st
     ms = elapsed * 1e3 / K
     dense_bytes = float(np.mean(st_bytes[W:]))
     comp_bytes = float(np.mean(step_bytes[W:]))
-    log(f"dense bf16 comparator: step {ms * 1e3:.2f} us, {dense_bytes / 1e6:.1f} MB/step -> "
+    log(f"dense {fmt} comparator: step {ms * 1e3:.2f} us, {dense_bytes / 1e6:.1f} MB/step -> "
         f"{dense_bytes / (ms * 1e-3) / 1e9:.0f} GB/s; compressed step is {ms / ms_compressed:.2f}x faster "
         f"on {dense_bytes / comp_bytes:.2f}x fewer bytes")
     return {"ms_per_step": round(ms, 6), "bytes_per_step": round(dense_bytes),
             "gbs": round(dense_bytes / (ms * 1e-3) / 1e9, 1), "compressed_speedup": round(ms / ms_compressed, 3),
             "bytes_ratio": round(dense_bytes / comp_bytes, 3),
-            "what": "tq_dense_write_kv + tq_dense_decode_attention per step over a bf16 cache of the same layer "
-                    "(4 cycled copies), one HIP graph of the K steps"}
+            "what": (f"tq_dense{'_fp8' if fp8 else ''}_write_kv + tq_dense{'_fp8' if fp8 else ''}_decode_attention "
+                     f"per step over a{'n FP8 E4M3 (per-tensor scales)' if fp8 else ' bf16'} cache of the same layer "
+                     "(4 cycled copies), one HIP graph of the K steps")}
 
 
 def cpu_baseline(H, d, bits, pool, T, qall, scale, sw, S, budget_s, rec_bytes, what):

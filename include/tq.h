@@ -25,8 +25,9 @@
  *   tq_decode_partial, tq_decode_combine
  *                       the two passes of tq_decode_attention, callable one by one: the split-K
  *                       scan over the pages, then the merge of the runs and the inverse rotation.
- *   tq_dense_*          the uncompressed comparator: the same paged decode attention over a bf16
- *                       cache, to measure the compressed path against the bytes it saves.
+ *   tq_dense_*          the uncompressed comparators: the same paged decode attention over a bf16
+ *                       cache and (tq_dense_fp8_*) over an FP8 E4M3 cache with per-tensor scales, to
+ *                       measure the compressed path against the bytes it saves.
  *
  * Conventions for every call:
  *   - Returns TQ_OK (0) or a negative TQ_E* status; never aborts, never allocates device memory.
@@ -289,6 +290,35 @@ int tq_dense_decode_attention(int head_dim, int num_kv_heads, const void *pages,
                               int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
                               int pages_per_split, void *workspace, size_t workspace_bytes, float *out,
                               void *stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * FP8 comparator ("Who Should Care", its KV8 line; "The Three Layers of Compression", the KV cache layer;
+ * "Quality vs. Compression: The Full Comparison": an 8-bit floating-point KV cache is the
+ * hardware-native 2x baseline that serving stacks ship). The pages fix no format: the cache holds OCP
+ * E4M3 bytes (bias 7, no infinities, 0x7F / 0xFF are NaN, largest finite 448) with one scale per tensor,
+ * a byte standing for scale * its value. Same page layout and calls as the bf16 comparator with 1-byte
+ * elements: page bytes = 2 * num_kv_heads * 16 * head_dim; workspace from
+ * tq_dense_decode_workspace_bytes (the split plan does not depend on the element size).
+ * k_scale, v_scale must be finite and > 0 (else TQ_EINVAL).
+ * ------------------------------------------------------------------------------------------------ */
+
+/* Bytes of one FP8 dense page. */
+int tq_dense_fp8_page_bytes(int head_dim, int num_kv_heads, size_t *out);
+
+/* Write n_tok tokens' K and V into FP8 pages: each element is the fp32 quotient x / scale (correctly
+ * rounded), rounded to the nearest E4M3 value, ties to even, saturated to +-448. Arguments and errors as
+ * for tq_dense_write_kv; inputs must be finite (a NaN input stores an unspecified byte). */
+int tq_dense_fp8_write_kv(int head_dim, int num_kv_heads, void *pages, int64_t num_pages, const void *k,
+                          const void *v, int dtype, int64_t n_tok, const int64_t *slots, float k_scale,
+                          float v_scale, void *stream);
+
+/* tq_dense_decode_attention over FP8 pages: keys and values are k_scale * byte value and v_scale * byte
+ * value. Arguments and errors as for tq_dense_decode_attention. */
+int tq_dense_fp8_decode_attention(int head_dim, int num_kv_heads, const void *pages, int64_t num_pages,
+                                  const void *q, int q_dtype, int batch, int num_q_heads,
+                                  const int32_t *page_table, int max_pages_per_seq, const int32_t *seq_lens,
+                                  float softmax_scale, float k_scale, float v_scale, int pages_per_split,
+                                  void *workspace, size_t workspace_bytes, float *out, void *stream);
 
 #ifdef __cplusplus
 }

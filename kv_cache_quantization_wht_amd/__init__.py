@@ -28,6 +28,7 @@ C_SYMBOLS = (
     "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_partial", "tq_decode_combine",
     "tq_decode_step", "tq_decode_step_partial",
     "tq_dense_page_bytes", "tq_dense_write_kv", "tq_dense_decode_workspace_bytes", "tq_dense_decode_attention",
+    "tq_dense_fp8_page_bytes", "tq_dense_fp8_write_kv", "tq_dense_fp8_decode_attention",
 )
 
 
@@ -75,6 +76,11 @@ def _lib():
         lib.tq_dense_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         lib.tq_dense_decode_attention.argtypes = [i32, i32, vp, i64, vp, i32, i32, i32, vp, i32, vp, ctypes.c_float,
                                                   i32, vp, sz, vp, vp]
+        f32 = ctypes.c_float
+        lib.tq_dense_fp8_page_bytes.argtypes = [i32, i32, ctypes.POINTER(sz)]
+        lib.tq_dense_fp8_write_kv.argtypes = [i32, i32, vp, i64, vp, vp, i32, i64, vp, f32, f32, vp]
+        lib.tq_dense_fp8_decode_attention.argtypes = [i32, i32, vp, i64, vp, i32, i32, i32, vp, i32, vp, f32, f32, f32,
+                                                      i32, vp, sz, vp, vp]
         for name in C_SYMBOLS:
             getattr(lib, name).restype = ctypes.c_char_p if name == "tq_strerror" else ctypes.c_int
         _LIB = lib
@@ -292,8 +298,8 @@ def decode_step(layout: Layout, pages, k_new, v_new, q, page_table, seq_lens, so
 
 
 # --------------------------------------------------------------------------------------------------
-# Uncompressed comparator: the same paged decode attention over a bf16 cache (K [head][slot][d], V
-# [head][d][slot] per page).
+# Uncompressed comparators: the same paged decode attention over a bf16 cache and over an FP8 (E4M3,
+# one scale per tensor) cache (K [head][slot][d], V [head][d][slot] per page).
 # --------------------------------------------------------------------------------------------------
 
 def dense_page_bytes(head_dim: int, num_kv_heads: int) -> int:
@@ -302,8 +308,13 @@ def dense_page_bytes(head_dim: int, num_kv_heads: int) -> int:
     return out.value
 
 
-def dense_write_kv(head_dim: int, num_kv_heads: int, pages, k, v, slots, stream=None) -> None:
-    """Write K, V [n_tok, num_kv_heads, head_dim] (contiguous) as bf16 into dense ``pages`` at ``slots``."""
+def dense_fp8_page_bytes(head_dim: int, num_kv_heads: int) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib().tq_dense_fp8_page_bytes(head_dim, num_kv_heads, ctypes.byref(out)), "tq_dense_fp8_page_bytes")
+    return out.value
+
+
+def _dense_write_args(head_dim, num_kv_heads, pages, k, v, slots):
     import torch
 
     _need(pages, "pages", torch.uint8)
@@ -314,9 +325,25 @@ def dense_write_kv(head_dim: int, num_kv_heads: int, pages, k, v, slots, stream=
         raise ValueError("k, v must be [n_tok, num_kv_heads, head_dim] of one dtype")
     if not (k.is_contiguous() and v.is_contiguous() and slots.is_contiguous()) or slots.numel() != k.shape[0]:
         raise ValueError("k, v, slots must be contiguous, one slot per token")
+
+
+def dense_write_kv(head_dim: int, num_kv_heads: int, pages, k, v, slots, stream=None) -> None:
+    """Write K, V [n_tok, num_kv_heads, head_dim] (contiguous) as bf16 into dense ``pages`` at ``slots``."""
+    _dense_write_args(head_dim, num_kv_heads, pages, k, v, slots)
     num_pages = pages.numel() // dense_page_bytes(head_dim, num_kv_heads)
     _check(_lib().tq_dense_write_kv(head_dim, num_kv_heads, pages.data_ptr(), num_pages, k.data_ptr(), v.data_ptr(),
                                     _dtype_code(k), k.shape[0], slots.data_ptr(), _stream(stream)), "tq_dense_write_kv")
+
+
+def dense_fp8_write_kv(head_dim: int, num_kv_heads: int, pages, k, v, slots, k_scale: float, v_scale: float,
+                       stream=None) -> None:
+    """Write K, V [n_tok, num_kv_heads, head_dim] (contiguous) as E4M3 bytes of x / scale into FP8 dense
+    ``pages`` at ``slots``."""
+    _dense_write_args(head_dim, num_kv_heads, pages, k, v, slots)
+    num_pages = pages.numel() // dense_fp8_page_bytes(head_dim, num_kv_heads)
+    _check(_lib().tq_dense_fp8_write_kv(head_dim, num_kv_heads, pages.data_ptr(), num_pages, k.data_ptr(),
+                                        v.data_ptr(), _dtype_code(k), k.shape[0], slots.data_ptr(), float(k_scale),
+                                        float(v_scale), _stream(stream)), "tq_dense_fp8_write_kv")
 
 
 def dense_decode_workspace_bytes(head_dim: int, num_kv_heads: int, batch: int, num_q_heads: int,
@@ -327,9 +354,7 @@ def dense_decode_workspace_bytes(head_dim: int, num_kv_heads: int, batch: int, n
     return out.value
 
 
-def dense_decode_attention(head_dim: int, num_kv_heads: int, pages, q, page_table, seq_lens, softmax_scale,
-                           workspace=None, out=None, pages_per_split: int = 0, stream=None):
-    """Decode attention over a dense bf16 pool for q [batch, num_q_heads, head_dim]; returns fp32 out."""
+def _dense_decode_args(head_dim, num_kv_heads, pages, q, page_table, seq_lens, workspace, out, pages_per_split):
     import torch
 
     _need(pages, "pages", torch.uint8)
@@ -352,10 +377,34 @@ def dense_decode_attention(head_dim: int, num_kv_heads: int, pages, q, page_tabl
     _need(out, "out", torch.float32)
     if out.shape != q.shape or not out.is_contiguous():
         raise ValueError("out must be a contiguous fp32 tensor shaped like q")
+    return B, Hq, maxp, workspace, out
+
+
+def dense_decode_attention(head_dim: int, num_kv_heads: int, pages, q, page_table, seq_lens, softmax_scale,
+                           workspace=None, out=None, pages_per_split: int = 0, stream=None):
+    """Decode attention over a dense bf16 pool for q [batch, num_q_heads, head_dim]; returns fp32 out."""
+    B, Hq, maxp, workspace, out = _dense_decode_args(head_dim, num_kv_heads, pages, q, page_table, seq_lens,
+                                                     workspace, out, pages_per_split)
     num_pages = pages.numel() // dense_page_bytes(head_dim, num_kv_heads)
     _check(_lib().tq_dense_decode_attention(head_dim, num_kv_heads, pages.data_ptr(), num_pages, q.data_ptr(),
                                             _dtype_code(q), B, Hq, page_table.data_ptr(), maxp, seq_lens.data_ptr(),
                                             float(softmax_scale), pages_per_split, workspace.data_ptr(),
                                             workspace.numel(), out.data_ptr(), _stream(stream)),
            "tq_dense_decode_attention")
+    return out
+
+
+def dense_fp8_decode_attention(head_dim: int, num_kv_heads: int, pages, q, page_table, seq_lens, softmax_scale,
+                               k_scale: float, v_scale: float, workspace=None, out=None, pages_per_split: int = 0,
+                               stream=None):
+    """Decode attention over an FP8 (E4M3, per-tensor scales) dense pool; returns fp32 out."""
+    B, Hq, maxp, workspace, out = _dense_decode_args(head_dim, num_kv_heads, pages, q, page_table, seq_lens,
+                                                     workspace, out, pages_per_split)
+    num_pages = pages.numel() // dense_fp8_page_bytes(head_dim, num_kv_heads)
+    _check(_lib().tq_dense_fp8_decode_attention(head_dim, num_kv_heads, pages.data_ptr(), num_pages, q.data_ptr(),
+                                                _dtype_code(q), B, Hq, page_table.data_ptr(), maxp,
+                                                seq_lens.data_ptr(), float(softmax_scale), float(k_scale),
+                                                float(v_scale), pages_per_split, workspace.data_ptr(),
+                                                workspace.numel(), out.data_ptr(), _stream(stream)),
+           "tq_dense_fp8_decode_attention")
     return out

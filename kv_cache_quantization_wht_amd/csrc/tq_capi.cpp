@@ -464,43 +464,82 @@ int tq_decode_combine(const tq_layout *layout, const void *pages, int64_t num_pa
                        tq::kPassCombine, stream);
 }
 
-static int dense_geom(int head_dim, int num_kv_heads, tq::PageGeom *g) {
+static int dense_geom(int head_dim, int num_kv_heads, bool fp8, tq::PageGeom *g) {
   if ((head_dim != 64 && head_dim != 128) || num_kv_heads < 1 || num_kv_heads > 4096) return TQ_EINVAL;
   *g = tq::PageGeom{};
   g->head_dim = head_dim;
   g->num_kv_heads = num_kv_heads;
-  g->page_bytes = (int64_t)4 * num_kv_heads * TQ_PAGE_TOKENS * head_dim;
+  g->page_bytes = (int64_t)(fp8 ? 2 : 4) * num_kv_heads * TQ_PAGE_TOKENS * head_dim;
   return TQ_OK;
 }
 
-int tq_dense_page_bytes(int head_dim, int num_kv_heads, size_t *out) {
+static bool valid_scale(float s) { return std::isfinite(s) && s > 0.f; }
+
+static int dense_page_bytes(int head_dim, int num_kv_heads, bool fp8, size_t *out) {
   tq::PageGeom g;
-  const int st = dense_geom(head_dim, num_kv_heads, &g);
+  const int st = dense_geom(head_dim, num_kv_heads, fp8, &g);
   if (st) return st;
   if (!out) return TQ_EINVAL;
   *out = (size_t)g.page_bytes;
   return TQ_OK;
 }
 
-int tq_dense_write_kv(int head_dim, int num_kv_heads, void *pages, int64_t num_pages, const void *k,
-                      const void *v, int dtype, int64_t n_tok, const int64_t *slots, void *stream) {
+static int dense_write(int head_dim, int num_kv_heads, const tq::DenseFormat &fmt, void *pages, int64_t num_pages,
+                       const void *k, const void *v, int dtype, int64_t n_tok, const int64_t *slots, void *stream) {
   tq::PageGeom g;
-  const int st = dense_geom(head_dim, num_kv_heads, &g);
+  const int st = dense_geom(head_dim, num_kv_heads, fmt.fp8, &g);
   if (st) return st;
   if (dtype != TQ_F32 && dtype != TQ_BF16 && dtype != TQ_F16) return TQ_EINVAL;
   if (n_tok < 0 || num_pages < 0) return TQ_EINVAL;
+  if (!valid_scale(fmt.k_scale) || !valid_scale(fmt.v_scale)) return TQ_EINVAL;
   if (n_tok == 0) return TQ_OK;
   if (!pages || !k || !v || !slots) return TQ_EINVAL;
   if (((uintptr_t)pages | (uintptr_t)k | (uintptr_t)v) & 15) return TQ_EINVAL;
-  return tq::launch_dense_write(head_dim, num_kv_heads, pages, num_pages, k, v, dtype, n_tok, slots,
+  return tq::launch_dense_write(head_dim, num_kv_heads, fmt, pages, num_pages, k, v, dtype, n_tok, slots,
                                 (hipStream_t)stream);
+}
+
+static int dense_decode(int head_dim, int num_kv_heads, const tq::DenseFormat &fmt, const void *pages,
+                        int64_t num_pages, const void *q, int q_dtype, int batch, int num_q_heads,
+                        const int32_t *page_table, int max_pages_per_seq, const int32_t *seq_lens,
+                        float softmax_scale, int pages_per_split, void *workspace, size_t workspace_bytes,
+                        float *out, void *stream) {
+  tq::PageGeom g;
+  int st = dense_geom(head_dim, num_kv_heads, fmt.fp8, &g);
+  if (st) return st;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return TQ_EINVAL;
+  if (batch < 0 || num_q_heads < 1 || num_q_heads % num_kv_heads) return TQ_EINVAL;
+  if (num_q_heads / num_kv_heads > 16) return TQ_ENOTSUP;
+  if (max_pages_per_seq < 1 || num_pages < 1 || !std::isfinite(softmax_scale) || softmax_scale < 0.f) return TQ_EINVAL;
+  if (!valid_scale(fmt.k_scale) || !valid_scale(fmt.v_scale)) return TQ_EINVAL;
+  if (batch == 0) return TQ_OK;
+  if (!pages || !q || !page_table || !seq_lens || !workspace || !out) return TQ_EINVAL;
+  if (((uintptr_t)pages | (uintptr_t)workspace) & 15) return TQ_EINVAL;
+  tq::DecodeWs ws;
+  st = tq::plan_decode(g, batch, num_q_heads, max_pages_per_seq, pages_per_split, &ws);
+  if (st) return st;
+  if (workspace_bytes < ws.total) return TQ_ENOSPC;
+  return tq::launch_dense_decode(head_dim, num_kv_heads, fmt, ws, pages, num_pages, q, q_dtype, batch, num_q_heads,
+                                 page_table, max_pages_per_seq, seq_lens, softmax_scale, workspace, out,
+                                 tq::kPassScan | tq::kPassCombine, (hipStream_t)stream);
+}
+
+static const tq::DenseFormat kBf16Format{false, 1.f, 1.f};
+
+int tq_dense_page_bytes(int head_dim, int num_kv_heads, size_t *out) {
+  return dense_page_bytes(head_dim, num_kv_heads, false, out);
+}
+
+int tq_dense_write_kv(int head_dim, int num_kv_heads, void *pages, int64_t num_pages, const void *k,
+                      const void *v, int dtype, int64_t n_tok, const int64_t *slots, void *stream) {
+  return dense_write(head_dim, num_kv_heads, kBf16Format, pages, num_pages, k, v, dtype, n_tok, slots, stream);
 }
 
 int tq_dense_decode_workspace_bytes(int head_dim, int num_kv_heads, int batch, int num_q_heads,
                                     int max_pages_per_seq, int pages_per_split, size_t *out) {
   if (!out) return TQ_EINVAL;
   tq::PageGeom g;
-  int st = dense_geom(head_dim, num_kv_heads, &g);
+  int st = dense_geom(head_dim, num_kv_heads, false, &g);
   if (st) return st;
   tq::DecodeWs ws;
   st = tq::plan_decode(g, batch, num_q_heads, max_pages_per_seq, pages_per_split, &ws);
@@ -514,23 +553,30 @@ int tq_dense_decode_attention(int head_dim, int num_kv_heads, const void *pages,
                               int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
                               int pages_per_split, void *workspace, size_t workspace_bytes, float *out,
                               void *stream) {
-  tq::PageGeom g;
-  int st = dense_geom(head_dim, num_kv_heads, &g);
-  if (st) return st;
-  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return TQ_EINVAL;
-  if (batch < 0 || num_q_heads < 1 || num_q_heads % num_kv_heads) return TQ_EINVAL;
-  if (num_q_heads / num_kv_heads > 16) return TQ_ENOTSUP;
-  if (max_pages_per_seq < 1 || num_pages < 1 || !std::isfinite(softmax_scale) || softmax_scale < 0.f) return TQ_EINVAL;
-  if (batch == 0) return TQ_OK;
-  if (!pages || !q || !page_table || !seq_lens || !workspace || !out) return TQ_EINVAL;
-  if (((uintptr_t)pages | (uintptr_t)workspace) & 15) return TQ_EINVAL;
-  tq::DecodeWs ws;
-  st = tq::plan_decode(g, batch, num_q_heads, max_pages_per_seq, pages_per_split, &ws);
-  if (st) return st;
-  if (workspace_bytes < ws.total) return TQ_ENOSPC;
-  return tq::launch_dense_decode(head_dim, num_kv_heads, ws, pages, num_pages, q, q_dtype, batch, num_q_heads,
-                                 page_table, max_pages_per_seq, seq_lens, softmax_scale, workspace, out,
-                                 tq::kPassScan | tq::kPassCombine, (hipStream_t)stream);
+  return dense_decode(head_dim, num_kv_heads, kBf16Format, pages, num_pages, q, q_dtype, batch, num_q_heads,
+                      page_table, max_pages_per_seq, seq_lens, softmax_scale, pages_per_split, workspace,
+                      workspace_bytes, out, stream);
+}
+
+int tq_dense_fp8_page_bytes(int head_dim, int num_kv_heads, size_t *out) {
+  return dense_page_bytes(head_dim, num_kv_heads, true, out);
+}
+
+int tq_dense_fp8_write_kv(int head_dim, int num_kv_heads, void *pages, int64_t num_pages, const void *k,
+                          const void *v, int dtype, int64_t n_tok, const int64_t *slots, float k_scale,
+                          float v_scale, void *stream) {
+  return dense_write(head_dim, num_kv_heads, tq::DenseFormat{true, k_scale, v_scale}, pages, num_pages, k, v, dtype,
+                     n_tok, slots, stream);
+}
+
+int tq_dense_fp8_decode_attention(int head_dim, int num_kv_heads, const void *pages, int64_t num_pages,
+                                  const void *q, int q_dtype, int batch, int num_q_heads,
+                                  const int32_t *page_table, int max_pages_per_seq, const int32_t *seq_lens,
+                                  float softmax_scale, float k_scale, float v_scale, int pages_per_split,
+                                  void *workspace, size_t workspace_bytes, float *out, void *stream) {
+  return dense_decode(head_dim, num_kv_heads, tq::DenseFormat{true, k_scale, v_scale}, pages, num_pages, q, q_dtype,
+                      batch, num_q_heads, page_table, max_pages_per_seq, seq_lens, softmax_scale, pages_per_split,
+                      workspace, workspace_bytes, out, stream);
 }
 
 }  // extern "C"

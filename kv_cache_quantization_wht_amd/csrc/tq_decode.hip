@@ -251,8 +251,9 @@ __device__ __forceinline__ void buf_bytes(__amdgpu_buffer_rsrc_t r, uint32_t off
   }
 }
 
-// Both pages of one pair (page ids pg0, pg1; an id outside [0, num_pages) reads page 0 and is marked
-// invalid). The page id is the same for the whole wavefront: each page is a buffer resource in scalar
+// Both pages of one pair (page ids pg0, pg1; an id outside [0, num_pages) - a pair past the end of the run
+// included - is marked invalid and gets a zero-size buffer, so its loads return zeros without a memory
+// request). The page id is the same for the whole wavefront: each page is a buffer resource in scalar
 // registers and every lane adds its fixed 32-bit offset.
 template <int D, int KB, bool KPROD, int VB>
 __device__ __forceinline__ void load_pages(const DecodeArgs &a, const LaneOffsets &lo, int pg0, int pg1,
@@ -264,7 +265,7 @@ __device__ __forceinline__ void load_pages(const DecodeArgs &a, const LaneOffset
     const bool ok = pg >= 0 && pg < a.num_pages32;
     f.ok[q2] = ok;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.pages + (int64_t)(ok ? pg : 0) * a.page_bytes), (short)0, (int)a.page_bytes, 0x00020000);
+        (void *)(a.pages + (int64_t)(ok ? pg : 0) * a.page_bytes), (short)0, ok ? (int)a.page_bytes : 0, 0x00020000);
     buf_bytes<F::KCH>(r, lo.k, f.kw[q2]);
     uint32_t t[2];
     buf_bytes<8>(r, lo.nk, t);

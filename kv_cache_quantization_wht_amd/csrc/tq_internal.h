@@ -65,13 +65,19 @@ int launch_decode(const PageGeom &g, const DecodeWs &ws, const void *pages, int6
 int launch_combine_plain(const float *part_o, const float *part_ml, int n_splits, int64_t rows, int head_dim,
                          float *out, hipStream_t stream);
 
-// Uncompressed comparator: bf16 pages, K [head][16][d] then V [head][d][16] (each head's V block of a page
-// transposed), page bytes = 4 * num_kv_heads * 16 * head_dim.
-int launch_dense_write(int head_dim, int num_kv_heads, void *pages, int64_t num_pages, const void *k,
-                       const void *v, int dtype, int64_t n_tok, const int64_t *slots, hipStream_t stream);
-int launch_dense_decode(int head_dim, int num_kv_heads, const DecodeWs &ws, const void *pages, int64_t num_pages,
-                        const void *q, int q_dtype, int batch, int num_q_heads, const int32_t *page_table,
-                        int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale, void *workspace,
-                        float *out, int passes, hipStream_t stream);
+// Uncompressed comparators: pages of K [head][16][d] then V [head][d][16] (each head's V block of a page
+// transposed), one element = bf16 (page bytes = 4 * num_kv_heads * 16 * head_dim) or, with `fp8`, one
+// E4M3 byte standing for scale * its value (page bytes = 2 * num_kv_heads * 16 * head_dim).
+struct DenseFormat {
+  bool fp8;
+  float k_scale, v_scale;  // 1 for bf16
+};
+int launch_dense_write(int head_dim, int num_kv_heads, const DenseFormat &fmt, void *pages, int64_t num_pages,
+                       const void *k, const void *v, int dtype, int64_t n_tok, const int64_t *slots,
+                       hipStream_t stream);
+int launch_dense_decode(int head_dim, int num_kv_heads, const DenseFormat &fmt, const DecodeWs &ws,
+                        const void *pages, int64_t num_pages, const void *q, int q_dtype, int batch,
+                        int num_q_heads, const int32_t *page_table, int max_pages_per_seq, const int32_t *seq_lens,
+                        float softmax_scale, void *workspace, float *out, int passes, hipStream_t stream);
 
 }  // namespace tq

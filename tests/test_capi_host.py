@@ -195,3 +195,30 @@ def test_dense_argument_errors_need_no_gpu():
     bad = list(a)
     bad[6] = 0  # empty batch: nothing to do
     assert lib.tq_dense_decode_attention(*bad) == 0
+
+
+def test_dense_fp8_argument_errors_need_no_gpu():
+    lib = tq._lib()
+    sz = ctypes.c_size_t()
+    assert lib.tq_dense_fp8_page_bytes(128, 8, ctypes.byref(sz)) == 0 and sz.value == 2 * 8 * 16 * 128
+    assert lib.tq_dense_fp8_page_bytes(64, 3, ctypes.byref(sz)) == 0 and sz.value == 2 * 3 * 16 * 64
+    assert lib.tq_dense_fp8_page_bytes(96, 8, ctypes.byref(sz)) == -1
+    # (head_dim, H, pages, num_pages, k, v, dtype, n_tok, slots, k_scale, v_scale, stream)
+    w = (128, 8, 16, 4, 16, 16, 1, 10, 16, 0.5, 0.5, None)
+    for i, val in ((0, 96), (6, 7), (7, -1), (2, None), (4, 24), (9, 0.0), (10, -1.0), (9, float("nan")),
+                   (10, float("inf"))):
+        bad = list(w)
+        bad[i] = val
+        assert lib.tq_dense_fp8_write_kv(*bad) == -1, (i, val)
+    assert lib.tq_dense_fp8_write_kv(128, 8, 16, 4, 16, 16, 1, 0, 16, 0.5, 0.5, None) == 0  # nothing to write
+    # (head_dim, H, pages, num_pages, q, q_dtype, B, Hq, page_table, maxp, seq_lens, scale, k_scale, v_scale,
+    #  pps, ws, ws_bytes, out, s)
+    a = (128, 8, 16, 4, 16, 1, 1, 32, 16, 10, 16, 0.1, 0.5, 0.5, 0, 16, 1 << 30, 16, None)
+    for i, val, want in ((7, 30, -1), (7, 8 * 17, -3), (11, -1.0, -1), (12, 0.0, -1), (13, float("nan"), -1),
+                         (9, 0, -1), (2, None, -1), (15, 24, -1), (16, 4, -2), (5, 9, -1)):
+        bad = list(a)
+        bad[i] = val
+        assert lib.tq_dense_fp8_decode_attention(*bad) == want, (i, val)
+    bad = list(a)
+    bad[6] = 0  # empty batch: nothing to do
+    assert lib.tq_dense_fp8_decode_attention(*bad) == 0

@@ -1,5 +1,6 @@
-"""The uncompressed comparator through the C ABI: tq_dense_write_kv bytes against the oracle's dense
-layout (bit-exact), and tq_dense_decode_attention against the oracle run on the GPU's own pool."""
+"""The uncompressed comparators through the C ABI: tq_dense_write_kv / tq_dense_fp8_write_kv bytes against
+the oracle's dense layouts (bit-exact), and tq_dense_decode_attention / tq_dense_fp8_decode_attention
+against the oracle run on the GPU's own pool (max relative error <= 2e-3)."""
 import math
 
 import numpy as np
@@ -12,12 +13,40 @@ from tests import parity
 pytestmark = pytest.mark.gpu
 
 
-def build(H, d, Hq, B, lens, seed=0, dtype="bf16", shuffled=True, min_pages=0, q_scale=1.0):
+# per-tensor scales of the FP8 cases: K and V of the "plain" recipe are about unit normal
+FP8_SCALES = (0.0625, 0.03)
+
+
+def write_kv(tq, L, pages, k, v, slots):
+    if L["fmt"] == "fp8":
+        tq.dense_fp8_write_kv(L["d"], L["H"], pages, k, v, slots, L["k_scale"], L["v_scale"])
+    else:
+        tq.dense_write_kv(L["d"], L["H"], pages, k, v, slots)
+
+
+def attend(tq, c, q, pt, lens, scale, pps=0):
+    L = c["L"]
+    if L["fmt"] == "fp8":
+        return tq.dense_fp8_decode_attention(L["d"], L["H"], c["pages"], q, pt, lens, scale, L["k_scale"], L["v_scale"],
+                                             pages_per_split=pps)
+    return tq.dense_decode_attention(L["d"], L["H"], c["pages"], q, pt, lens, scale, pages_per_split=pps)
+
+
+def layout(tq, H, d, fmt, scales=FP8_SCALES):
+    if fmt == "fp8":
+        L = dense.page_layout(H, d, "fp8", *scales)
+        assert tq.dense_fp8_page_bytes(d, H) == L["page_bytes"]
+    else:
+        L = dense.page_layout(H, d)
+        assert tq.dense_page_bytes(d, H) == L["page_bytes"]
+    return L
+
+
+def build(H, d, Hq, B, lens, seed=0, dtype="bf16", shuffled=True, min_pages=0, q_scale=1.0, fmt="bf16"):
     import torch
     import kv_cache_quantization_wht_amd as tq
 
-    L = dense.page_layout(H, d)
-    assert tq.dense_page_bytes(d, H) == L["page_bytes"]
+    L = layout(tq, H, d, fmt)
     pps = max(1, min_pages, max((l + 15) // 16 for l in lens))
     pt, npages = kvsynth.page_table(B, pps, shuffled, seed=seed + 4, extra_pages=2)
     pages = torch.full((npages * L["page_bytes"],), 0x5A, dtype=torch.uint8, device="cuda")
@@ -28,7 +57,7 @@ def build(H, d, Hq, B, lens, seed=0, dtype="bf16", shuffled=True, min_pages=0, q
             continue
         k, v = parity.seeded_kv(lens[b], H, d, seed=seed * 100 + b, recipe="plain", dtype=dtype)
         slots = kvsynth.slots_for(pt, b, 0, lens[b])
-        tq.dense_write_kv(d, H, pages, k.cuda(), v.cuda(), torch.from_numpy(slots).cuda())
+        write_kv(tq, L, pages, k.cuda(), v.cuda(), torch.from_numpy(slots).cuda())
         for h in range(H):
             dense.write(pool, L, slots, h, k[:, h].double().numpy(), v[:, h].double().numpy())
     g = torch.Generator().manual_seed(seed + 77)
@@ -49,18 +78,18 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_dense_matches_oracle(case):
+def test_dense_matches_oracle(case, fmt):
     import torch
     import kv_cache_quantization_wht_amd as tq
 
     name, H, d, Hq, B, lens, dt, pps = case
-    print(f"dense case {name}", flush=True)
-    c = build(H, d, Hq, B, lens, seed=len(name), dtype=dt)
+    print(f"dense case {name} {fmt}", flush=True)
+    c = build(H, d, Hq, B, lens, seed=len(name), dtype=dt, fmt=fmt)
     assert np.array_equal(c["pages"].cpu().numpy(), c["pool"]), "dense pages differ from the oracle's layout"
     scale = 1.0 / math.sqrt(d)
-    out = tq.dense_decode_attention(d, H, c["pages"], c["q"].cuda(), torch.from_numpy(c["pt"]).cuda(),
-                                    torch.from_numpy(c["lens"]).cuda(), scale, pages_per_split=pps)
+    out = attend(tq, c, c["q"].cuda(), torch.from_numpy(c["pt"]).cuda(), torch.from_numpy(c["lens"]).cuda(), scale, pps)
     torch.cuda.synchronize()
     ref = dense.decode_attention(c["pool"], c["L"], c["q"].double().numpy(), c["pt"], c["lens"], scale)
     err = parity.attention_error(out.cpu().numpy().astype(np.float64), ref)
@@ -68,17 +97,18 @@ def test_dense_matches_oracle(case):
     assert err <= parity.ATTN_TOL
 
 
-def test_dense_skips_out_of_range_slots():
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_dense_skips_out_of_range_slots(fmt):
     import torch
     import kv_cache_quantization_wht_amd as tq
 
     H, d = 2, 64
-    L = dense.page_layout(H, d)
+    L = layout(tq, H, d, fmt)
     pages = torch.zeros(3 * L["page_bytes"], dtype=torch.uint8, device="cuda")
     k = torch.randn(4, H, d, device="cuda")
     v = torch.randn(4, H, d, device="cuda")
     slots = torch.tensor([-1, 5, 48, 47], dtype=torch.int64, device="cuda")  # 48 is past 3 pages
-    tq.dense_write_kv(d, H, pages, k, v, slots)
+    write_kv(tq, L, pages, k, v, slots)
     pool = np.zeros(3 * L["page_bytes"], np.uint8)
     for h in range(H):
         dense.write(pool, L, [5, 47], h, k[[1, 3], h].double().cpu().numpy(), v[[1, 3], h].double().cpu().numpy())
@@ -86,7 +116,36 @@ def test_dense_skips_out_of_range_slots():
     assert np.array_equal(pages.cpu().numpy(), pool)
 
 
-def test_dense_full_size_8b_layer():
+def test_fp8_write_range_bit_exact():
+    """Every part of the E4M3 range through the write kernel, scale 1: subnormals, all binades, values past
+    448 (saturated), both signs; f32 inputs; bytes against the oracle, bit-exact."""
+    import torch
+    import kv_cache_quantization_wht_amd as tq
+
+    H, d, n = 2, 128, 40
+    L = dense.page_layout(H, d, "fp8", 1.0, 1.0)
+    g = torch.Generator().manual_seed(99)
+    mag = torch.exp(torch.empty(n, H, d).uniform_(-14.0, 8.0, generator=g))
+    sgn = torch.where(torch.rand(n, H, d, generator=g) < 0.5, -1.0, 1.0)
+    k = (mag * sgn).float()
+    b = torch.arange(0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).float()
+    mids = (b[1:] + b[:-1]) / 2  # ties between neighbours
+    v = torch.cat([b, mids, -b, -mids, torch.tensor([448.0, 464.0, 1e6, -1e6, 0.0, -0.0])])
+    v = v.repeat(n * H * d // v.numel() + 1)[: n * H * d].reshape(n, H, d).contiguous()
+    pt = np.arange(3, dtype=np.int32)[None]
+    slots = kvsynth.slots_for(pt, 0, 0, n)
+    pages = torch.zeros(3 * L["page_bytes"], dtype=torch.uint8, device="cuda")
+    tq.dense_fp8_write_kv(d, H, pages, k.cuda(), v.cuda(), torch.from_numpy(slots).cuda(), 1.0, 1.0)
+    pool = np.zeros(3 * L["page_bytes"], np.uint8)
+    for h in range(H):
+        dense.write(pool, L, slots, h, k[:, h].double().numpy(), v[:, h].double().numpy())
+    torch.cuda.synchronize()
+    got = pages.cpu().numpy()
+    assert np.array_equal(got, pool), int((got != pool).sum())
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_dense_full_size_8b_layer(fmt):
     """The 8B single-layer shape at full length (32768 tokens, 8 KV heads, 32 query heads) in the automatic
     split plan; sampled (KV head) outputs against the oracle."""
     import torch
@@ -94,15 +153,16 @@ def test_dense_full_size_8b_layer():
 
     wl = kvsynth.workloads()[1]
     H, Hq, d, T = wl.kv_heads, wl.q_heads, wl.head_dim, wl.seq_len
-    L = dense.page_layout(H, d)
+    k, v = kvsynth.make_kv(wl, 1, 0, T, device="cuda")
+    # FP8: one scale per tensor from its largest magnitude (amax / 448)
+    L = layout(tq, H, d, fmt, (k.abs().max().item() / 448.0, v.abs().max().item() / 448.0))
     pps = (T + 15) // 16
     pt, npages = kvsynth.page_table(1, pps, False)
     pages = torch.zeros(npages * L["page_bytes"], dtype=torch.uint8, device="cuda")
-    k, v = kvsynth.make_kv(wl, 1, 0, T, device="cuda")
-    tq.dense_write_kv(d, H, pages, k, v, torch.from_numpy(kvsynth.slots_for(pt, 0, 0, T)).cuda())
+    write_kv(tq, L, pages, k, v, torch.from_numpy(kvsynth.slots_for(pt, 0, 0, T)).cuda())
     q = kvsynth.make_q(wl, 1, 0, 1, device="cuda")
-    out = tq.dense_decode_attention(d, H, pages, q, torch.from_numpy(pt).cuda(),
-                                    torch.tensor([T], dtype=torch.int32, device="cuda"), wl.softmax_scale)
+    out = attend(tq, dict(L=L, pages=pages), q, torch.from_numpy(pt).cuda(),
+                 torch.tensor([T], dtype=torch.int32, device="cuda"), wl.softmax_scale)
     torch.cuda.synchronize()
     pool = pages.cpu().numpy()
     G = Hq // H
