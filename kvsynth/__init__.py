@@ -29,6 +29,7 @@ MASK64 = (1 << 64) - 1
 GOLDEN_GAMMA = 0x9E3779B97F4A7C15
 SIGN_STREAM = 0x5349474E  # "SIGN"
 QJL_STREAM = 0x514A4C53  # "QJLS"
+QR_STREAM = 0x51524753  # "QRGS"
 PAGE_TOKENS = 16
 
 
@@ -71,6 +72,15 @@ def qjl_projection(seed: int, head_dim: int, rows: int | None = None) -> np.ndar
     rows = head_dim if rows is None else rows
     g = torch.Generator(device="cpu").manual_seed((seed ^ QJL_STREAM) & 0x7FFFFFFFFFFFFFFF)
     return torch.randn(rows, head_dim, generator=g, dtype=torch.float64).to(torch.float32).numpy()
+
+
+def qr_gaussian(seed: int, head_dim: int) -> np.ndarray:
+    """The random draw of the dense (QR) rotation: a ``head_dim x head_dim`` fp64 matrix of iid N(0,1) entries,
+    row-major (the orthogonal factor of its QR decomposition is the rotation)."""
+    import torch
+
+    g = torch.Generator(device="cpu").manual_seed((seed ^ QR_STREAM) & 0x7FFFFFFFFFFFFFFF)
+    return torch.randn(head_dim, head_dim, generator=g, dtype=torch.float64).numpy()
 
 
 # --------------------------------------------------------------------------------------------

@@ -25,7 +25,7 @@ import math
 
 import numpy as np
 
-from . import codec, rotation
+from . import codec
 
 PAGE_TOKENS = codec.PAGE_TOKENS
 
@@ -80,7 +80,7 @@ def decode_attention_rotated(pool, L, cb_k, cb_v, q, page_table, seq_lens, scale
     Hkv = L["H"]
     G = Hq // Hkv
     out = np.zeros((B, Hq, d))
-    q_rot = rotation.rotate(q.reshape(-1, d), cb_k.sign_words).reshape(B, Hq, d)
+    q_rot = cb_k.rotate(q.reshape(-1, d)).reshape(B, Hq, d)
     for b in range(B):
         T = int(seq_lens[b])
         if T == 0:
@@ -92,7 +92,7 @@ def decode_attention_rotated(pool, L, cb_k, cb_v, q, page_table, seq_lens, scale
             Kr = codec.dequantize_rotated(rk["codes"], rk["norm16"], cb_k, rk.get("gamma16"), rk.get("qjl"))
             Vr = codec.dequantize_rotated(rv["codes"], rv["norm16"], cb_v, rv.get("gamma16"), rv.get("qjl"))
             w = _softmax_weights(scale * (q_rot[b, hs] @ Kr.T))
-            out[b, hs] = rotation.unrotate(w @ Vr, cb_v.sign_words)
+            out[b, hs] = cb_v.unrotate(w @ Vr)
     return out
 
 

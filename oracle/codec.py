@@ -85,6 +85,7 @@ class Codebook:
     thresholds: np.ndarray  # 2**mse_bits - 1 midpoints (N(0,1) units), exact in fp32
     sign_words: np.ndarray  # head_dim/32 uint32
     S: np.ndarray | None  # (m, head_dim) projection, fp32 values held in fp64
+    dense: np.ndarray | None = None  # (head_dim, head_dim) dense orthogonal rotation in place of the WHT
 
     @property
     def signs(self) -> np.ndarray:
@@ -92,14 +93,30 @@ class Codebook:
 
     @property
     def R(self) -> np.ndarray:
+        if self.dense is not None:
+            return self.dense
         return rotation.rotation_matrix(self.sign_words, self.head_dim)
+
+    def rotate(self, u) -> np.ndarray:
+        """Rows of u mapped to R u (the WHT rotation, or the dense one when the codebook carries it)."""
+        if self.dense is not None:
+            return np.asarray(u, dtype=np.float64) @ self.dense.T
+        return rotation.rotate(u, self.sign_words)
+
+    def unrotate(self, y) -> np.ndarray:
+        """Rows of y mapped to R^T y."""
+        if self.dense is not None:
+            return np.asarray(y, dtype=np.float64) @ self.dense
+        return rotation.unrotate(y, self.sign_words)
 
     @property
     def m(self) -> int:
         return 0 if self.S is None else self.S.shape[0]
 
 
-def make_codebook(head_dim: int, bits: int, mode: int, sign_words, S=None) -> Codebook:
+def make_codebook(head_dim: int, bits: int, mode: int, sign_words, S=None, dense=None) -> Codebook:
+    """Levels and thresholds of the b-bit (MSE) or (b-1)-bit (prod) Lloyd-Max quantizer, the rotation (signs of
+    the WHT, or ``dense``: a d x d orthogonal matrix from ``rotation.qr_rotation``) and, for prod mode, S."""
     if bits not in SUPPORTED_BITS:
         raise ValueError("bits must be one of 1, 2, 3, 4, 8")
     if mode == PROD and bits < 2:
@@ -113,7 +130,8 @@ def make_codebook(head_dim: int, bits: int, mode: int, sign_words, S=None) -> Co
         if S is None:
             raise ValueError("prod mode needs the projection matrix S")
         proj = np.asarray(S, dtype=np.float32).astype(np.float64)
-    return Codebook(head_dim, bits, mode, b, lv, th, np.asarray(sign_words, dtype=np.uint32), proj)
+    R = None if dense is None else np.asarray(dense, dtype=np.float64)
+    return Codebook(head_dim, bits, mode, b, lv, th, np.asarray(sign_words, dtype=np.uint32), proj, R)
 
 
 @dataclass
@@ -135,7 +153,7 @@ def encode(x, cb: Codebook) -> Encoded:
     n = np.sqrt(np.sum(x * x, axis=1))
     safe = np.where(n > 0, n, 1.0)
     u = np.where(n[:, None] > 0, x / safe[:, None], 0.0)
-    y = rotation.rotate(u, cb.sign_words)
+    y = cb.rotate(u)
     y32 = (y * math.sqrt(d)).astype(np.float32).astype(np.float64)
     index = np.searchsorted(cb.thresholds, y32, side="right").astype(np.int64)
     enc = Encoded(codes=stored_code(index, cb.mse_bits), norm16=fp16_round(n), norm=n, y=y)
@@ -166,7 +184,7 @@ def dequantize_rotated(codes, norm16, cb: Codebook, gamma16=None, qjl=None) -> n
 
 def dequantize(codes, norm16, cb: Codebook, gamma16=None, qjl=None) -> np.ndarray:
     """Reconstructed vectors in the original domain: R^T applied to the rotated reconstruction."""
-    return rotation.unrotate(dequantize_rotated(codes, norm16, cb, gamma16, qjl), cb.sign_words)
+    return cb.unrotate(dequantize_rotated(codes, norm16, cb, gamma16, qjl))
 
 
 # ---------------------------------------------------------------------------------------------

@@ -5,7 +5,9 @@ multiplied by a random rotation, in practice a Walsh-Hadamard transform combined
 with random signs; the rotation is a change of coordinates that keeps inner
 products unchanged. "What the Paper Doesn't Tell You", Finding 4: the WHT needs
 only one random sign vector (16 bytes at d=128) and O(d log d) work instead of a
-dense d x d matrix.
+dense d x d matrix. The same finding names the paper's own rotation: a dense random
+orthogonal matrix from a QR decomposition (a d x d matrix, O(d^2) work per vector),
+kept here as ``qr_rotation`` for the comparison.
 
 Reading adopted (the pages give no formula): R = H_d diag(s) / sqrt(d), with H_d
 the Sylvester Hadamard matrix in natural order (H_1 = [1], H_2n = [[H_n, H_n],
@@ -55,3 +57,14 @@ def unrotate(y: np.ndarray, sign_words) -> np.ndarray:
     y = np.asarray(y, dtype=np.float64)
     R = rotation_matrix(sign_words, y.shape[-1])
     return y @ R
+
+
+def qr_rotation(gauss) -> np.ndarray:
+    """The dense random rotation: the orthogonal factor Q of the QR decomposition G = Q T of a square iid
+    Gaussian matrix G, made unique by the convention diag(T) > 0 (T upper triangular), which makes Q
+    Haar-distributed. The pages name the decomposition, not the convention; the rotation is y = Q u. Pins:
+    orthogonality, the triangular factor, and classical Gram-Schmidt on a small matrix (tests/pins.py)."""
+    G = np.asarray(gauss, dtype=np.float64)
+    Q, T = np.linalg.qr(G)
+    s = np.where(np.diag(T) < 0, -1.0, 1.0)
+    return Q * s[None, :]

@@ -401,14 +401,17 @@ def check_determinism(d=128):
 # --------------------------------------------------------------------------------------------
 
 
-def build_cache(H, d, Hq, B, lens, kb, km, vb, vm, seed=0, shuffled=True, q_scale=1.0):
-    """Encode random K/V for B sequences into a page pool; returns everything the checks need."""
+def build_cache(H, d, Hq, B, lens, kb, km, vb, vm, seed=0, shuffled=True, q_scale=1.0, dense=False):
+    """Encode random K/V for B sequences into a page pool; returns everything the checks need. ``dense``:
+    QR rotations (their own draws for K and V) in place of the WHT."""
     rng = np.random.Generator(np.random.Philox(seed))
     sw_k = kvsynth.rotation_signs(seed + 1, d)
     sw_v = kvsynth.rotation_signs(seed + 2, d)
     S = kvsynth.qjl_projection(seed + 3, d)
-    cbk = codec.make_codebook(d, kb, km, sw_k, S if km == codec.PROD else None)
-    cbv = codec.make_codebook(d, vb, vm, sw_v, S if vm == codec.PROD else None)
+    dk = rotation.qr_rotation(kvsynth.qr_gaussian(seed + 5, d)) if dense else None
+    dv = rotation.qr_rotation(kvsynth.qr_gaussian(seed + 6, d)) if dense else None
+    cbk = codec.make_codebook(d, kb, km, sw_k, S if km == codec.PROD else None, dense=dk)
+    cbv = codec.make_codebook(d, vb, vm, sw_v, S if vm == codec.PROD else None, dense=dv)
     L = codec.page_layout(H, d, kb, km, vb, vm)
     pps = max(1, max((l + 15) // 16 for l in lens))
     pt, npages = kvsynth.page_table(B, pps, shuffled, seed=seed + 4)
@@ -683,3 +686,86 @@ def check_dense_fp8_attention_vs_torch_sdpa():
         Vt = f8(V[b, :lens[b]].transpose(1, 0, 2), vs).repeat_interleave(Hq // H, 0)
         ref = torch.nn.functional.scaled_dot_product_attention(torch.tensor(q[b])[:, None, :], Kt, Vt, scale=0.2)
         assert np.allclose(out[b], ref[:, 0, :].numpy(), rtol=1e-10, atol=1e-12), b
+
+
+
+# --------------------------------------------------------------------------------------------
+# Dense random (QR) rotation
+# --------------------------------------------------------------------------------------------
+
+
+def check_qr_rotation_factorization(d=64, seed=61):
+    """Q is orthogonal, Q^T G is upper triangular with a positive diagonal and Q (Q^T G) = G."""
+    G = kvsynth.qr_gaussian(seed, d)
+    Q = rotation.qr_rotation(G)
+    assert np.abs(Q.T @ Q - np.eye(d)).max() < 1e-13 and np.abs(Q @ Q.T - np.eye(d)).max() < 1e-13
+    T = Q.T @ G
+    assert np.abs(np.tril(T, -1)).max() < 1e-12 and np.all(np.diag(T) > 0)
+    assert np.abs(Q @ np.triu(T) - G).max() < 1e-12
+
+
+def check_qr_rotation_gram_schmidt(d=8, seed=62):
+    """Against classical Gram-Schmidt on the columns of G written out by hand (the QR with a positive
+    triangular diagonal is unique)."""
+    G = kvsynth.qr_gaussian(seed, d)
+    cols = []
+    for j in range(d):
+        v = [G[i][j] for i in range(d)]
+        for q in cols:
+            dot = sum(q[i] * G[i][j] for i in range(d))
+            v = [v[i] - dot * q[i] for i in range(d)]
+        nrm = math.sqrt(sum(t * t for t in v))
+        cols.append([t / nrm for t in v])
+    Q = np.array(cols).T
+    assert np.abs(rotation.qr_rotation(G) - Q).max() < 1e-12
+    # a triangular G with a positive diagonal is its own T: Q = I
+    U = np.triu(G) + np.diag(np.abs(np.diag(G)) + 1.0 - np.diag(G))
+    assert np.abs(rotation.qr_rotation(U) - np.eye(d)).max() < 1e-14
+
+
+def check_dense_rotation_reduces_to_known_paths(d=64, n=400, seed=63):
+    """The codec's dense branch against the two rotations it can reproduce: the WHT matrix given as a dense
+    matrix encodes and decodes exactly as the sign-vector codebook does, and the identity quantizes the
+    coordinates of u themselves."""
+    rng = np.random.Generator(np.random.Philox(seed))
+    x = rng.standard_normal((n, d)) * np.exp(rng.standard_normal(d))
+    sw = kvsynth.rotation_signs(seed, d)
+    for b in (2, 4):
+        cw = codec.make_codebook(d, b, codec.MSE, sw)
+        cd = codec.make_codebook(d, b, codec.MSE, np.zeros(d // 32, np.uint32), dense=rotation.rotation_matrix(sw, d))
+        ew, ed = codec.encode(x, cw), codec.encode(x, cd)
+        assert np.array_equal(ew.codes, ed.codes) and np.array_equal(ew.norm16, ed.norm16)
+        assert np.abs(codec.dequantize(ed.codes, ed.norm16, cd) - codec.dequantize(ew.codes, ew.norm16, cw)).max() < 1e-12
+        ci = codec.make_codebook(d, b, codec.MSE, sw, dense=np.eye(d))
+        ei = codec.encode(x, ci)
+        u = x / np.linalg.norm(x, axis=1, keepdims=True)
+        want = np.searchsorted(ci.thresholds, (u * math.sqrt(d)).astype(np.float32).astype(np.float64), side="right")
+        assert np.array_equal(codec.level_index(ei.codes, b), want)
+        # no rotation: the reconstruction is the per-coordinate quantization of u itself
+        assert np.abs(codec.dequantize(ei.codes, np.ones(n), ci) - ci.levels16[want] / math.sqrt(d)).max() < 1e-15
+
+
+def check_dense_rotation_mse(d=128, n=3000, seed=64):
+    """Gaussian vectors through a QR rotation: E||u - uhat||^2 matches the Lloyd-Max distortion D_b, as for the
+    WHT; outlier channels (x 10 on four coordinates) are spread by the rotation just as well."""
+    rng = np.random.Generator(np.random.Philox(seed))
+    x = rng.standard_normal((n, d))
+    x[:, :4] *= 10.0
+    u = x / np.linalg.norm(x, axis=1, keepdims=True)
+    Q = rotation.qr_rotation(kvsynth.qr_gaussian(seed, d))
+    for b in (2, 3, 4):
+        cb = codec.make_codebook(d, b, codec.MSE, np.zeros(d // 32, np.uint32), dense=Q)
+        e = codec.encode(x, cb)
+        mse = np.mean(np.sum((u - codec.dequantize(e.codes, np.ones(n), cb)) ** 2, axis=1))
+        c = lloyd_max.levels(b)
+        D = lloyd_max.distortion(c, lloyd_max.thresholds_of(c))
+        assert abs(mse / D - 1) < 0.05, (b, mse, D)
+
+
+def check_dense_attention_two_routes():
+    """Decode attention with QR-rotated K and V: dequantize-then-attend equals attend-in-the-rotated-domain."""
+    for (kb, km, vb, vm) in ((4, 0, 2, 0), (3, 0, 3, 0)):
+        c = build_cache(2, 64, 8, 2, [37, 70], kb, km, vb, vm, seed=70 + kb, dense=True)
+        o1 = attention.decode_attention(c["pool"], c["L"], c["cbk"], c["cbv"], c["q"], c["pt"], c["lens"], 0.125)
+        o2 = attention.decode_attention_rotated(c["pool"], c["L"], c["cbk"], c["cbv"], c["q"], c["pt"], c["lens"], 0.125)
+        assert attention.relative_error(o1, o2) < 1e-10

@@ -239,3 +239,20 @@ def test_mutant_fp8_subnormal_step(monkeypatch):
 
     monkeypatch.setattr(dense, "fp8_value", value)
     assert _caught(pins.check_fp8_value_table)
+
+
+def test_mutant_qr_no_sign_convention(monkeypatch):
+    monkeypatch.setattr(rotation, "qr_rotation", lambda g: np.linalg.qr(np.asarray(g, dtype=np.float64))[0])
+    assert _caught(pins.check_qr_rotation_factorization) and _caught(pins.check_qr_rotation_gram_schmidt)
+
+
+def test_mutant_dense_rotation_transposed(monkeypatch):
+    monkeypatch.setattr(codec.Codebook, "rotate", lambda self, u: np.asarray(u, dtype=np.float64) @ self.R
+                        if self.dense is not None else rotation.rotate(u, self.sign_words))
+    assert _caught(pins.check_dense_rotation_reduces_to_known_paths)
+
+
+def test_mutant_dense_unrotate_transposed(monkeypatch):
+    monkeypatch.setattr(codec.Codebook, "unrotate", lambda self, y: np.asarray(y, dtype=np.float64) @ self.R.T
+                        if self.dense is not None else rotation.unrotate(y, self.sign_words))
+    assert _caught(pins.check_dense_rotation_reduces_to_known_paths) and _caught(pins.check_dense_rotation_mse)
