@@ -25,6 +25,9 @@
  *   tq_decode_partial, tq_decode_combine
  *                       the two passes of tq_decode_attention, callable one by one: the split-K
  *                       scan over the pages, then the merge of the runs and the inverse rotation.
+ *   tq_qr_rotation, tq_rotate_rows, tq_quantize_kv_qr, tq_decode_attention_qr
+ *                       the dense random (QR) rotation in place of the WHT: the same codes and
+ *                       attention with a d x d orthogonal matrix, for the comparison of the two.
  *   tq_dense_*          the uncompressed comparators: the same paged decode attention over a bf16
  *                       cache and (tq_dense_fp8_*) over an FP8 E4M3 cache with per-tensor scales, to
  *                       measure the compressed path against the bytes it saves.
@@ -319,6 +322,59 @@ int tq_dense_fp8_decode_attention(int head_dim, int num_kv_heads, const void *pa
                                   const int32_t *page_table, int max_pages_per_seq, const int32_t *seq_lens,
                                   float softmax_scale, float k_scale, float v_scale, int pages_per_split,
                                   void *workspace, size_t workspace_bytes, float *out, void *stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * Dense random (QR) rotation ("What the Paper Doesn't Tell You", Finding 4: the paper's rotation is a
+ * dense random orthogonal matrix from a QR decomposition, d x d storage and O(d^2) work per vector; the
+ * WHT with random signs replaces it). The rotation is Q, the orthogonal factor of G = Q T for a caller-drawn
+ * iid N(0,1) matrix G, unique under diag(T) > 0. Codes, norms, page layout and attention are those of the
+ * compressed path with R = Q in place of H diag(s) / sqrt(d).
+ *
+ * Realisation: the kernels of the WHT path apply W = H diag(s) / sqrt(d) with the codebook's signs s. The
+ * rows are first rotated on the matrix cores by M = W^T Q (tq_rotate_rows), so that W M = Q: keys and
+ * values before tq_quantize_kv, queries (by the keys' M) before tq_decode_attention, and its output by the
+ * transpose of the values' M. The extra pass costs one read of the rows and one fp32 write and read.
+ * ------------------------------------------------------------------------------------------------ */
+
+/* Host only. Q from the Householder QR of `gauss` (host fp64, row-major head_dim x head_dim, iid N(0,1)) in
+ * fp64 with the sign convention diag(T) > 0, then fwd = M = diag(s) H Q / sqrt(head_dim) as fp32 row-major
+ * (host, head_dim^2 floats) and, if `inv` is not null, its transpose. `sign_words`: host, the head_dim/32
+ * sign words of the codebook that M will be used with (null: no signs). head_dim 64 or 128.
+ * Errors: TQ_EINVAL (head_dim, null gauss / fwd, a singular or non-finite matrix). */
+int tq_qr_rotation(int head_dim, const double *gauss, const uint32_t *sign_words, float *fwd, float *inv);
+
+/* y[r] = mat x[r] for rows r < rows: x device [rows][head_dim] of x_dtype (TQ_F32, TQ_BF16, TQ_F16),
+ * contiguous; mat device fp32 row-major head_dim x head_dim; y device fp32 [rows][head_dim] (not
+ * overlapping x). All 16-byte aligned. Matrix cores with fp16 high/low splits of both operands (three
+ * products): about 2^-22 relative error per product. rows = 0 launches nothing.
+ * Errors: TQ_EINVAL (head_dim, dtype, null or misaligned pointers, rows < 0), TQ_EHIP. */
+int tq_rotate_rows(int head_dim, const float *mat, const void *x, int x_dtype, int64_t rows, float *y, void *stream);
+
+/* Workspace bytes of tq_quantize_kv_qr for n_tok tokens (two fp32 copies of the rotated rows). Host only. */
+int tq_quantize_kv_qr_workspace_bytes(const tq_layout *layout, int64_t n_tok, size_t *out);
+
+/* tq_quantize_kv with the dense rotation: k, v device [n_tok][num_kv_heads][head_dim] of `dtype`, contiguous,
+ * 16-byte aligned; k_rot, v_rot device fp32 `fwd` matrices of tq_qr_rotation built with the sign words of
+ * k_cb and v_cb respectively; workspace device, at least tq_quantize_kv_qr_workspace_bytes bytes. Other
+ * arguments, the bytes written and the errors as for tq_quantize_kv (TQ_ENOSPC for a small workspace). */
+int tq_quantize_kv_qr(const tq_layout *layout, void *pages, int64_t num_pages, const void *k, const void *v,
+                      int dtype, int64_t n_tok, const int64_t *slots, const void *k_cb, const void *v_cb,
+                      const float *k_rot, const float *v_rot, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* Workspace bytes of tq_decode_attention_qr (tq_decode_workspace_bytes plus two fp32 rows per query head).
+ * Host only. */
+int tq_decode_qr_workspace_bytes(const tq_layout *layout, int batch, int num_q_heads, int max_pages_per_seq,
+                                 int pages_per_split, size_t *out);
+
+/* tq_decode_attention over a cache written by tq_quantize_kv_qr: k_rot the keys' `fwd` matrix, v_inv the
+ * values' `inv` matrix (device fp32, 16-byte aligned); q and out 16-byte aligned; workspace at least
+ * tq_decode_qr_workspace_bytes bytes. Other arguments and errors as for tq_decode_attention. */
+int tq_decode_attention_qr(const tq_layout *layout, const void *pages, int64_t num_pages, const void *q, int q_dtype,
+                           int batch, int num_q_heads, const int32_t *page_table, int max_pages_per_seq,
+                           const int32_t *seq_lens, float softmax_scale, int pages_per_split, const void *k_cb,
+                           const void *v_cb, const float *k_rot, const float *v_inv, void *workspace,
+                           size_t workspace_bytes, float *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -29,6 +29,8 @@ C_SYMBOLS = (
     "tq_decode_step", "tq_decode_step_partial",
     "tq_dense_page_bytes", "tq_dense_write_kv", "tq_dense_decode_workspace_bytes", "tq_dense_decode_attention",
     "tq_dense_fp8_page_bytes", "tq_dense_fp8_write_kv", "tq_dense_fp8_decode_attention",
+    "tq_qr_rotation", "tq_rotate_rows", "tq_quantize_kv_qr_workspace_bytes", "tq_quantize_kv_qr",
+    "tq_decode_qr_workspace_bytes", "tq_decode_attention_qr",
 )
 
 
@@ -81,6 +83,14 @@ def _lib():
         lib.tq_dense_fp8_write_kv.argtypes = [i32, i32, vp, i64, vp, vp, i32, i64, vp, f32, f32, vp]
         lib.tq_dense_fp8_decode_attention.argtypes = [i32, i32, vp, i64, vp, i32, i32, i32, vp, i32, vp, f32, f32, f32,
                                                       i32, vp, sz, vp, vp]
+        lay = ctypes.POINTER(_Layout)
+        lib.tq_qr_rotation.argtypes = [i32, vp, vp, vp, vp]
+        lib.tq_rotate_rows.argtypes = [i32, vp, vp, i32, i64, vp, vp]
+        lib.tq_quantize_kv_qr_workspace_bytes.argtypes = [lay, i64, ctypes.POINTER(sz)]
+        lib.tq_quantize_kv_qr.argtypes = [lay, vp, i64, vp, vp, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.tq_decode_qr_workspace_bytes.argtypes = [lay, i32, i32, i32, i32, ctypes.POINTER(sz)]
+        lib.tq_decode_attention_qr.argtypes = [lay, vp, i64, vp, i32, i32, i32, vp, i32, vp, f32, i32, vp, vp, vp,
+                                               vp, vp, sz, vp, vp]
         for name in C_SYMBOLS:
             getattr(lib, name).restype = ctypes.c_char_p if name == "tq_strerror" else ctypes.c_int
         _LIB = lib
@@ -407,4 +417,113 @@ def dense_fp8_decode_attention(head_dim: int, num_kv_heads: int, pages, q, page_
                                                 float(v_scale), pages_per_split, workspace.data_ptr(),
                                                 workspace.numel(), out.data_ptr(), _stream(stream)),
            "tq_dense_fp8_decode_attention")
+    return out
+
+
+# --------------------------------------------------------------------------------------------------
+# Dense random (QR) rotation in place of the WHT: the rotation matrices (host), the row rotation on the
+# matrix cores, and quantize / decode attention with it.
+# --------------------------------------------------------------------------------------------------
+
+def qr_rotation(head_dim: int, gauss, sign_words=None):
+    """(fwd, inv) fp32 [head_dim, head_dim] numpy arrays: fwd = diag(s) H Q / sqrt(d) for Q the orthogonal QR
+    factor of ``gauss`` (fp64 [head_dim, head_dim]) and s the codebook's ``sign_words``; inv = fwd^T."""
+    g = np.ascontiguousarray(gauss, dtype=np.float64)
+    if g.shape != (head_dim, head_dim):
+        raise ValueError("gauss must be [head_dim, head_dim]")
+    sw = None if sign_words is None else np.ascontiguousarray(sign_words, dtype=np.uint32)
+    fwd = np.empty((head_dim, head_dim), np.float32)
+    inv = np.empty((head_dim, head_dim), np.float32)
+    _check(_lib().tq_qr_rotation(head_dim, g.ctypes.data, None if sw is None else sw.ctypes.data, fwd.ctypes.data,
+                                 inv.ctypes.data), "tq_qr_rotation")
+    return fwd, inv
+
+
+def rotate_rows(head_dim: int, mat, x, y=None, stream=None):
+    """y[r] = mat x[r] for x [..., head_dim] (contiguous, fp32 / bf16 / f16); returns fp32 y shaped like x."""
+    import torch
+
+    _need(mat, "mat", torch.float32)
+    _need(x, "x")
+    if x.shape[-1] != head_dim or not x.is_contiguous() or not mat.is_contiguous() or mat.shape != (head_dim, head_dim):
+        raise ValueError("x must be contiguous [..., head_dim] and mat [head_dim, head_dim]")
+    if y is None:
+        y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    _need(y, "y", torch.float32)
+    if y.shape != x.shape or not y.is_contiguous():
+        raise ValueError("y must be a contiguous fp32 tensor shaped like x")
+    _check(_lib().tq_rotate_rows(head_dim, mat.data_ptr(), x.data_ptr(), _dtype_code(x), x.numel() // head_dim,
+                                 y.data_ptr(), _stream(stream)), "tq_rotate_rows")
+    return y
+
+
+def quantize_kv_qr(layout: Layout, pages, k, v, slots, k_cb, v_cb, k_rot, v_rot, workspace=None, stream=None):
+    """quantize_kv with the dense rotation: k, v contiguous [n_tok, num_kv_heads, head_dim]; k_rot, v_rot the
+    device fp32 ``fwd`` matrices of qr_rotation built with the codebooks' sign words."""
+    import torch
+
+    _need(pages, "pages", torch.uint8)
+    _need(slots, "slots", torch.int64)
+    _need(k, "k")
+    _need(v, "v")
+    _need(k_rot, "k_rot", torch.float32)
+    _need(v_rot, "v_rot", torch.float32)
+    if k.dtype != v.dtype or k.shape != v.shape or k.dim() != 3 or k.shape[1:] != (layout.num_kv_heads, layout.head_dim):
+        raise ValueError("k, v must be [n_tok, num_kv_heads, head_dim] of one dtype")
+    if not (k.is_contiguous() and v.is_contiguous() and slots.is_contiguous()) or slots.numel() != k.shape[0]:
+        raise ValueError("k, v, slots must be contiguous, one slot per token")
+    out = ctypes.c_size_t()
+    _check(_lib().tq_quantize_kv_qr_workspace_bytes(ctypes.byref(layout.c()), k.shape[0], ctypes.byref(out)),
+           "tq_quantize_kv_qr_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(max(out.value, 16), dtype=torch.uint8, device=k.device)
+    num_pages = pages.numel() // page_layout(layout)["page_bytes"]
+    _check(_lib().tq_quantize_kv_qr(ctypes.byref(layout.c()), pages.data_ptr(), num_pages, k.data_ptr(), v.data_ptr(),
+                                    _dtype_code(k), k.shape[0], slots.data_ptr(), k_cb.data_ptr(), v_cb.data_ptr(),
+                                    k_rot.data_ptr(), v_rot.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                    _stream(stream)), "tq_quantize_kv_qr")
+
+
+def decode_qr_workspace_bytes(layout: Layout, batch: int, num_q_heads: int, max_pages_per_seq: int,
+                              pages_per_split: int = 0) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib().tq_decode_qr_workspace_bytes(ctypes.byref(layout.c()), batch, num_q_heads, max_pages_per_seq,
+                                               pages_per_split, ctypes.byref(out)), "tq_decode_qr_workspace_bytes")
+    return out.value
+
+
+def decode_attention_qr(layout: Layout, pages, q, page_table, seq_lens, softmax_scale, k_cb, v_cb, k_rot, v_inv,
+                        workspace=None, out=None, pages_per_split: int = 0, stream=None):
+    """decode_attention over a cache written by quantize_kv_qr: k_rot the keys' ``fwd`` matrix, v_inv the
+    values' ``inv`` matrix (device fp32)."""
+    import torch
+
+    _need(pages, "pages", torch.uint8)
+    _need(q, "q")
+    _need(page_table, "page_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(k_rot, "k_rot", torch.float32)
+    _need(v_inv, "v_inv", torch.float32)
+    if q.dim() != 3 or q.shape[2] != layout.head_dim or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [batch, num_q_heads, head_dim] tensor")
+    B, Hq, _ = q.shape
+    if page_table.dim() != 2 or page_table.shape[0] != B or not page_table.is_contiguous():
+        raise ValueError("page_table must be a contiguous [batch, max_pages_per_seq] int32 tensor")
+    if seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must hold one int32 per sequence")
+    maxp = page_table.shape[1]
+    if workspace is None:
+        need = decode_qr_workspace_bytes(layout, B, Hq, maxp, pages_per_split)
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(B, Hq, layout.head_dim, dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32)
+    if out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor shaped like q")
+    num_pages = pages.numel() // page_layout(layout)["page_bytes"]
+    _check(_lib().tq_decode_attention_qr(ctypes.byref(layout.c()), pages.data_ptr(), num_pages, q.data_ptr(),
+                                         _dtype_code(q), B, Hq, page_table.data_ptr(), maxp, seq_lens.data_ptr(),
+                                         float(softmax_scale), pages_per_split, k_cb.data_ptr(), v_cb.data_ptr(),
+                                         k_rot.data_ptr(), v_inv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                         out.data_ptr(), _stream(stream)), "tq_decode_attention_qr")
     return out

@@ -34,6 +34,8 @@ SOURCES = [
     ("tq_capi.cpp", "tq_capi.o", []),
     ("tq_quantize.hip", "tq_quantize.o", []),
     ("tq_dense.hip", "tq_dense.o", ["-fno-honor-nans"]),
+    ("tq_rotate.hip", "tq_rotate.o", []),
+    ("tq_qr.cpp", "tq_qr.o", []),
     ("tq_decode.hip", "tq_decode_d128_pk.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=1"]),
     ("tq_decode.hip", "tq_decode_d128.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=2"]),
     ("tq_decode.hip", "tq_decode_d64_pk.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=3"]),

@@ -80,4 +80,9 @@ int launch_dense_decode(int head_dim, int num_kv_heads, const DenseFormat &fmt, 
                         int num_q_heads, const int32_t *page_table, int max_pages_per_seq, const int32_t *seq_lens,
                         float softmax_scale, void *workspace, float *out, int passes, hipStream_t stream);
 
+// Rows of x (rows x head_dim, dtype TQ_F32 / TQ_BF16 / TQ_F16, contiguous) times a dense row-major
+// head_dim x head_dim fp32 matrix: y[r] = mat x[r], fp32 (matrix cores, three fp16 hi/lo products).
+int launch_rotate_rows(int head_dim, const float *mat, const void *x, int x_dtype, int64_t rows, float *y,
+                       hipStream_t stream);
+
 }  // namespace tq

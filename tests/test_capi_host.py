@@ -222,3 +222,60 @@ def test_dense_fp8_argument_errors_need_no_gpu():
     bad = list(a)
     bad[6] = 0  # empty batch: nothing to do
     assert lib.tq_dense_fp8_decode_attention(*bad) == 0
+
+
+def test_qr_rotation_host_matches_oracle():
+    """tq_qr_rotation (host Householder QR, fp64) against the oracle's QR: the WHT path's W times the returned
+    M is Q within fp32 rounding, with and without sign words; inv is M^T; M is orthogonal."""
+    from oracle import rotation
+
+    for d, seed in ((64, 1), (128, 2)):
+        G = kvsynth.qr_gaussian(seed, d)
+        Q = rotation.qr_rotation(G)
+        for sw in (None, kvsynth.rotation_signs(seed, d)):
+            fwd, inv = tq.qr_rotation(d, G, sw)
+            W = rotation.rotation_matrix(np.zeros(d // 32, np.uint32) if sw is None else sw, d)
+            assert np.abs(W @ fwd.astype(np.float64) - Q).max() < 5e-8
+            assert np.array_equal(inv, fwd.T)
+            assert np.abs(fwd.astype(np.float64) @ fwd.T.astype(np.float64) - np.eye(d)).max() < 5e-7
+
+
+def test_qr_argument_errors_need_no_gpu():
+    lib = tq._lib()
+    d = 64
+    g = np.ascontiguousarray(kvsynth.qr_gaussian(3, d))
+    fwd = np.zeros((d, d), np.float32)
+    assert lib.tq_qr_rotation(96, g.ctypes.data, None, fwd.ctypes.data, None) == -1
+    assert lib.tq_qr_rotation(d, None, None, fwd.ctypes.data, None) == -1
+    assert lib.tq_qr_rotation(d, g.ctypes.data, None, None, None) == -1
+    z = np.zeros((d, d))
+    assert lib.tq_qr_rotation(d, z.ctypes.data, None, fwd.ctypes.data, None) == -1  # singular
+    assert lib.tq_qr_rotation(d, g.ctypes.data, None, fwd.ctypes.data, None) == 0  # inv may be null
+    # (head_dim, mat, x, x_dtype, rows, y, stream)
+    for args in ((96, 16, 16, 0, 4, 16, None), (64, 16, 16, 7, 4, 16, None), (64, 16, 16, 0, -1, 16, None),
+                 (64, None, 16, 0, 4, 16, None), (64, 16, 24, 0, 4, 16, None)):
+        assert lib.tq_rotate_rows(*args) == -1, args
+    assert lib.tq_rotate_rows(64, 16, 16, 0, 0, 16, None) == 0  # nothing to do
+    L = tq.Layout(128, 8, 4, 0, 2, 0).c()
+    sz = ctypes.c_size_t()
+    assert lib.tq_quantize_kv_qr_workspace_bytes(ctypes.byref(L), 10, ctypes.byref(sz)) == 0
+    assert sz.value == 2 * 10 * 8 * 128 * 4
+    need = sz.value
+    # (layout, pages, num_pages, k, v, dtype, n_tok, slots, k_cb, v_cb, k_rot, v_rot, ws, ws_bytes, stream)
+    a = [ctypes.byref(L), 16, 4, 16, 16, 1, 10, 16, 16, 16, 16, 16, 16, need, None]
+    for i, val, want in ((5, 9, -1), (10, None, -1), (13, need - 1, -2), (3, 24, -1)):
+        bad = list(a)
+        bad[i] = val
+        assert lib.tq_quantize_kv_qr(*bad) == want, (i, val)
+    assert lib.tq_decode_qr_workspace_bytes(ctypes.byref(L), 2, 32, 100, 0, ctypes.byref(sz)) == 0
+    dec = ctypes.c_size_t()
+    assert lib.tq_decode_workspace_bytes(ctypes.byref(L), 2, 32, 100, 0, ctypes.byref(dec)) == 0
+    assert sz.value >= dec.value + 2 * 2 * 32 * 128 * 4
+    need = sz.value
+    # (layout, pages, num_pages, q, q_dtype, B, Hq, pt, maxp, lens, scale, pps, k_cb, v_cb, k_rot, v_inv, ws,
+    #  ws_bytes, out, stream)
+    a = [ctypes.byref(L), 16, 4, 16, 1, 2, 32, 16, 100, 16, 0.1, 0, 16, 16, 16, 16, 16, need, 16, None]
+    for i, val, want in ((4, 9, -1), (15, None, -1), (17, need - 1, -2), (6, 30, -1), (18, 24, -1)):
+        bad = list(a)
+        bad[i] = val
+        assert lib.tq_decode_attention_qr(*bad) == want, (i, val)
