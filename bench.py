@@ -73,9 +73,6 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="another synthetic workload by name or index (default: the Llama-3.1-8B single layer); "
                          "its steps run every layer of the workload, each layer its own cache")
-    ap.add_argument("--study", default=None, choices=["prod-vs-mse"],
-                    help="prod-vs-mse: attention error of MSE and prod (MSE + QJL) keys at 3 and 4 bits against "
-                         "exact attention, on the 8B single-layer recipe (prints one JSON line)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="only run a plain device-to-device copy of MB megabytes (5 times), to scale the HBM "
                          "byte counters of rocprofv3")
@@ -111,9 +108,6 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    if args.study == "prod-vs-mse":
-        study_prod_vs_mse()
-        return
     if args.workload is not None:
         names = [w.name for w in kvsynth.workloads()]
         wi = int(args.workload) if args.workload.isdigit() else names.index(args.workload)
@@ -309,95 +303,6 @@ def main():
         result["cpu_baseline"] = cpu_baseline(H, d, bits, pool, T, qs.double().cpu().numpy(), scale, sw, None,
                                               args.cpu_seconds, rec_bytes, "copy 0")
     print(json.dumps(result), flush=True)
-
-
-def study_prod_vs_mse(B=4, T=4096):
-    """Keys quantized in MSE mode or prod mode (MSE at bits-1 plus the 1-bit QJL sketch of the residual) at
-    3 and 4 bits, values at 2 bits MSE, on the 8B single-layer recipe (K norms ~50x V norms): the GPU path
-    quantizes and attends; exact attention over the unquantized bf16 inputs is the reference (fp64). Two
-    query regimes: the recipe's queries (logits with a standard deviation near 50, an almost one-hot softmax)
-    and the same queries scaled so that the exact logits have a standard deviation of 2. Per configuration:
-    output error ||o - o_exact|| / ||o_exact|| over (sequence, query head), the score slope
-    sum(s_hat s) / sum(s^2) (1 = unbiased) and relative RMS score error (from the GPU's own codes, dequantized
-    by the oracle), and the KL divergence of the softmax weights from the exact ones."""
-    import torch
-
-    import kvsynth
-    import kv_cache_quantization_wht_amd as tq
-    from oracle import attention, codec
-
-    dev = "cuda"
-    wl = kvsynth.workloads()[WORKLOAD_INDEX]
-    H, Hq, d = wl.kv_heads, wl.q_heads, wl.head_dim
-    G, scale = Hq // H, wl.softmax_scale
-    k, v = kvsynth.make_kv(wl, WORKLOAD_INDEX, 0, B * T, device=dev, token_offset_seed=5)
-    q1 = kvsynth.make_q(wl, WORKLOAD_INDEX, 0, B, device=dev, step=5)
-    kh = k.double().cpu().numpy().reshape(B, T, H, d)
-    vh = v.double().cpu().numpy().reshape(B, T, H, d)
-    pps = T // 16
-    pt = np.arange(B * pps, dtype=np.int32).reshape(B, pps)
-    ptd = torch.from_numpy(pt).to(dev)
-    lens = torch.full((B,), T, dtype=torch.int32, device=dev)
-    slots = torch.arange(B * T, dtype=torch.int64, device=dev)
-    s1 = np.stack([np.stack([q1[b, h].double().cpu().numpy() @ kh[b, :, h // G].T for h in range(Hq)]) for b in range(B)])
-    qsc = 2.0 / float(np.std(scale * s1))
-    sw = kvsynth.rotation_signs(kvsynth.rotation_seed(0), d)
-    S = kvsynth.qjl_projection(kvsynth.rotation_seed(0), d)
-    cfgs = []
-    for kbits, kmode in ((3, 0), (3, 1), (4, 0), (4, 1)):
-        layout = tq.Layout(d, H, kbits, kmode, 2, 0)
-        Lo = codec.page_layout(H, d, kbits, kmode, 2, 0)
-        kcb = torch.from_numpy(tq.build_codebook(d, kbits, kmode, sw, S if kmode else None)).to(dev)
-        vcb = torch.from_numpy(tq.build_codebook(d, 2, 0, sw)).to(dev)
-        cbk = codec.make_codebook(d, kbits, kmode, sw, S if kmode else None)
-        pages = torch.zeros(B * pps * Lo["page_bytes"], dtype=torch.uint8, device=dev)
-        tq.quantize_kv(layout, pages, k, v, slots, kcb, vcb)
-        torch.cuda.synchronize()
-        pool = pages.cpu().numpy()
-        khat = {}
-        for b in range(B):
-            for g in range(H):
-                rk = attention.gather(pool, Lo, "k", pt[b], T, g)
-                khat[b, g] = codec.dequantize(rk["codes"], rk["norm16"], cbk, rk.get("gamma16"), rk.get("qjl"))
-        cfgs.append((kbits, kmode, layout, kcb, vcb, pages, khat))
-    rows = []
-    for regime, qs in (("recipe queries (exact logit std %.0f)" % float(np.std(scale * s1)), 1.0),
-                       ("queries scaled to exact logit std 2", qsc)):
-        q = (q1.float() * qs).to(q1.dtype)
-        qh = q.double().cpu().numpy()
-        s_exact = np.stack([np.stack([qh[b, h] @ kh[b, :, h // G].T for h in range(Hq)]) for b in range(B)])
-        exact = np.zeros((B, Hq, d))
-        for b in range(B):
-            for h in range(Hq):
-                w = np.exp(scale * (s_exact[b, h] - s_exact[b, h].max()))
-                exact[b, h] = (w / w.sum()) @ vh[b, :, h // G]
-        for kbits, kmode, layout, kcb, vcb, pages, khat in cfgs:
-            out = tq.decode_attention(layout, pages, q, ptd, lens, scale, kcb, vcb)
-            torch.cuda.synchronize()
-            out = out.double().cpu().numpy()
-            errs, kls, num, den, sq = [], [], 0.0, 0.0, 0.0
-            for b in range(B):
-                for h in range(Hq):
-                    s_hat = qh[b, h] @ khat[b, h // G].T
-                    se = s_exact[b, h]
-                    num += float(s_hat @ se)
-                    den += float(se @ se)
-                    sq += float(((s_hat - se) ** 2).sum())
-                    pe = np.exp(scale * (se - se.max()))
-                    pe /= pe.sum()
-                    ph = np.exp(scale * (s_hat - s_hat.max()))
-                    ph /= ph.sum()
-                    kls.append(float(np.sum(pe * (np.log(pe + 1e-300) - np.log(ph + 1e-300)))))
-                    errs.append(float(np.linalg.norm(out[b, h] - exact[b, h]) / np.linalg.norm(exact[b, h])))
-            row = {"queries": regime, "k": f"K{kbits}-{'prod' if kmode else 'mse'}", "v": "V2-mse",
-                   "output_rel_err_mean": round(float(np.mean(errs)), 5),
-                   "output_rel_err_p95": round(float(np.percentile(errs, 95)), 5),
-                   "score_slope": round(num / den, 5), "score_rel_rms_err": round(math.sqrt(sq / den), 5),
-                   "softmax_kl_mean": round(float(np.mean(kls)), 6)}
-            log(json.dumps(row))
-            rows.append(row)
-    print(json.dumps({"study": "prod-vs-mse", "workload": wl.name + " recipe", "batch": B, "seq_len": T,
-                      "kv_heads": H, "q_heads": Hq, "head_dim": d, "rows": rows}), flush=True)
 
 
 def dense_comparator(wl, k_pre, v_pre, k_new, v_new, qs, W, K, ms_compressed, step_bytes, fmt="bf16"):
