@@ -331,9 +331,10 @@ int tq_dense_fp8_decode_attention(int head_dim, int num_kv_heads, const void *pa
  * compressed path with R = Q in place of H diag(s) / sqrt(d).
  *
  * Realisation: the kernels of the WHT path apply W = H diag(s) / sqrt(d) with the codebook's signs s. The
- * rows are first rotated on the matrix cores by M = W^T Q (tq_rotate_rows), so that W M = Q: keys and
- * values before tq_quantize_kv, queries (by the keys' M) before tq_decode_attention, and its output by the
- * transpose of the values' M. The extra pass costs one read of the rows and one fp32 write and read.
+ * rows are first rotated on the matrix cores by M = W^T Q, so that W M = Q: keys and values inside the
+ * quantize kernel when both are in MSE mode (otherwise by tq_rotate_rows ahead of tq_quantize_kv), queries
+ * (by the keys' M) before tq_decode_attention and its output by the transpose of the values' M
+ * (tq_rotate_rows).
  * ------------------------------------------------------------------------------------------------ */
 
 /* Host only. Q from the Householder QR of `gauss` (host fp64, row-major head_dim x head_dim, iid N(0,1)) in
@@ -350,7 +351,8 @@ int tq_qr_rotation(int head_dim, const double *gauss, const uint32_t *sign_words
  * Errors: TQ_EINVAL (head_dim, dtype, null or misaligned pointers, rows < 0), TQ_EHIP. */
 int tq_rotate_rows(int head_dim, const float *mat, const void *x, int x_dtype, int64_t rows, float *y, void *stream);
 
-/* Workspace bytes of tq_quantize_kv_qr for n_tok tokens (two fp32 copies of the rotated rows). Host only. */
+/* Workspace bytes of tq_quantize_kv_qr for n_tok tokens (two fp32 copies of the rotated rows, used when a
+ * tensor is in prod mode; MSE keys and values need none but the size is the same). Host only. */
 int tq_quantize_kv_qr_workspace_bytes(const tq_layout *layout, int64_t n_tok, size_t *out);
 
 /* tq_quantize_kv with the dense rotation: k, v device [n_tok][num_kv_heads][head_dim] of `dtype`, contiguous,

@@ -80,6 +80,12 @@ int launch_dense_decode(int head_dim, int num_kv_heads, const DenseFormat &fmt, 
                         int num_q_heads, const int32_t *page_table, int max_pages_per_seq, const int32_t *seq_lens,
                         float softmax_scale, void *workspace, float *out, int passes, hipStream_t stream);
 
+// Quantize with the dense rotation fused ahead of the MSE steps (K and V in MSE mode; TQ_ENOTSUP otherwise):
+// k, v contiguous [n_tok][num_kv_heads][head_dim]; k_rot, v_rot the fp32 matrices M (row-major).
+int launch_quantize_qr(const PageGeom &g, void *pages, int64_t num_pages, const void *k, const void *v, int dtype,
+                       int64_t n_tok, const int64_t *slots, const void *k_cb, const void *v_cb, const float *k_rot,
+                       const float *v_rot, hipStream_t stream);
+
 // Rows of x (rows x head_dim, dtype TQ_F32 / TQ_BF16 / TQ_F16, contiguous) times a dense row-major
 // head_dim x head_dim fp32 matrix: y[r] = mat x[r], fp32 (matrix cores, three fp16 hi/lo products).
 int launch_rotate_rows(int head_dim, const float *mat, const void *x, int x_dtype, int64_t rows, float *y,

@@ -5,9 +5,11 @@
 //
 // The quantize and decode kernels apply W = H diag(s) / sqrt(d) (H Sylvester's Hadamard matrix, s the
 // codebook's signs). For the dense rotation Q the rows are first rotated by M = W^T Q on the matrix cores;
-// the unchanged kernels then apply W, and W M = Q, so the codes are those of Q u. The queries go through the
-// same M of the keys (scores <W M q, yhat> = <Q q, yhat>), and the decode output - returned by the unchanged
-// kernels in the coordinates of M x - is brought back by the transpose of the values' M.
+// the kernels then apply W, and W M = Q, so the codes are those of Q u. For MSE keys and values the rotation
+// runs inside the quantize kernel (rows through LDS); a sketched tensor takes a separate rotation pass. The
+// queries go through the same M of the keys (scores <W M q, yhat> = <Q q, yhat>), and the decode output -
+// returned by the unchanged kernels in the coordinates of M x - is brought back by the transpose of the
+// values' M.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -71,7 +73,10 @@ int tq_qr_rotation(int head_dim, const double *gauss, const uint32_t *sign_words
     const bool neg = sign_words && ((sign_words[i >> 5] >> (i & 31)) & 1u);
     for (int j = 0; j < d; ++j) {
       double t = 0.0;
-      for (int l = 0; l < d; ++l) t += (__builtin_popcount((unsigned)(i & l)) & 1) ? -Q[(size_t)l * d + j] : Q[(size_t)l * d + j];
+      for (int l = 0; l < d; ++l) {
+        const double q = Q[(size_t)l * d + j];
+        t += (__builtin_popcount((unsigned)(i & l)) & 1) ? -q : q;
+      }
       const float m = (float)((neg ? -t : t) * rs);
       fwd[(size_t)i * d + j] = m;
       if (inv) inv[(size_t)j * d + i] = m;
@@ -110,6 +115,15 @@ int tq_quantize_kv_qr(const tq_layout *layout, void *pages, int64_t num_pages, c
   if (((uintptr_t)k | (uintptr_t)v | (uintptr_t)k_rot | (uintptr_t)v_rot | (uintptr_t)workspace) & 15) return TQ_EINVAL;
   if (workspace_bytes < need) return TQ_ENOSPC;
   const int d = layout->head_dim;
+  if (layout->k_mode != TQ_PROD && layout->v_mode != TQ_PROD) {
+    // MSE keys and values: the rotation fused into the quantize kernel (same bytes as the two passes below)
+    tq::PageGeom g;
+    if ((st = tq::make_geom(layout, &g))) return st;
+    if (n_tok * layout->num_kv_heads >= ((int64_t)1 << 35)) return TQ_EINVAL;
+    return tq::launch_quantize_qr(g, pages, num_pages, k, v, dtype, n_tok, slots, k_cb, v_cb, k_rot, v_rot,
+                                  (hipStream_t)stream);
+  }
+  // a sketched tensor: the rows rotated in their own pass, then tq_quantize_kv over the fp32 rows
   const int64_t rows = n_tok * layout->num_kv_heads;
   float *wk = (float *)workspace;
   float *wv = (float *)((unsigned char *)workspace + need / 2);

@@ -14,8 +14,11 @@
 // partial sums and the butterflies in the same order, so they write the same bytes.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "tq_common.h"
 #include "tq_internal.h"
+#include "tq_lanes.h"
 #include "tq_quant_common.h"
 
 namespace tq {
@@ -36,6 +39,7 @@ struct QuantArgs {
   int H;
   int dtype;
   int which_of_y[2];  // tensor (0 = K, 1 = V) of each grid row
+  const float *rot[2];  // dense-rotation launches: the K and V matrices M applied ahead of the WHT
 };
 
 constexpr int kProdChunk = 1024;  // tokens per work-group of the prod kernel (S is loaded once per work-group)
@@ -299,6 +303,176 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   }
 }
 
+// Dense random (QR) rotation ahead of the MSE steps ("What the Paper Doesn't Tell You", Finding 4), fused:
+// a work-group takes VPB consecutive tokens of one head at a time (a persistent loop over the tiles of its
+// tensor). The tile's rows go to LDS as fp32; the four wavefronts rotate them by the tensor's matrix M on
+// MFMA - M held in registers as fp16 high + low parts (16 M, exact to ~2^-22) for the whole launch, wavefront w
+// computing the 16-coordinate output blocks w, w + 4; each row scaled by the power of two that puts its
+// largest magnitude in [2^13, 2^14), split into high + low parts, three products hi.hi + hi.lo + lo.hi - into a
+// second LDS tile; then the MSE steps above run on the rotated rows (the WHT with the codebook's signs follows,
+// and W M is the dense rotation). The arithmetic is that of tq_rotate_rows followed by quantize_kernel on its
+// fp32 output, so both routes write the same bytes; the fused one saves the fp32 round trip through HBM.
+__device__ __forceinline__ void qr_split(float x, _Float16 &hi, _Float16 &lo) {
+  hi = (_Float16)x;
+  lo = (_Float16)(x - (float)hi);
+}
+
+template <int D, int BT>
+__device__ __forceinline__ void quantize_qr_tiles(const QuantArgs &a, int which, float *s_x, float *s_y,
+                                                  float *s_th) {
+  constexpr int LANES = D / 32;           // lanes per vector in the MSE steps
+  constexpr int VPB = 256 / LANES;        // vectors of a tile
+  constexpr int XS = D + 4;               // LDS row stride (floats)
+  constexpr int JB = D / 32;              // 32-wide blocks of the rotation's contraction
+  constexpr int IB = D / 16 / 4;          // 16-coordinate output blocks of one wavefront
+  constexpr float kMat = 16.f;
+  const unsigned char *cb = a.cb[which];
+  const BlobOffsets bo = a.cbo[which];
+  constexpr int half = (1 << BT) >> 1;
+  const int tid = threadIdx.x;
+  const int l64 = tid & 63, wave = tid >> 6;
+  const int c = l64 & 15, g4 = l64 >> 4;
+  const int ln = tid % LANES, vl = tid / LANES;
+
+  half8_t ahi[IB][JB], alo[IB][JB];
+  {
+    const float *mat = a.rot[which];
+#pragma unroll
+    for (int ib = 0; ib < IB; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) {
+        const float *src = mat + (16 * (wave + 4 * ib) + c) * D + 32 * jb + 8 * g4;
+        const float4 u0 = *(const float4 *)src;
+        const float4 u1 = *(const float4 *)(src + 4);
+        const float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          _Float16 hh, ll;
+          qr_split(v[p] * kMat, hh, ll);
+          ahi[ib][jb][p] = hh;
+          alo[ib][jb][p] = ll;
+        }
+      }
+  }
+  const uint32_t sword = ((const uint32_t *)(cb + bo.signs))[ln];
+  PosThresholds P{};
+  if constexpr (BT <= 4) {
+    P = pos_thresholds((const_i32)(cb + bo.thresholds), half);
+  } else {
+    for (int i = tid; i < (1 << BT) - 1; i += 256) s_th[i] = ((const float *)(cb + bo.thresholds))[i];
+    __syncthreads();
+  }
+
+  const int64_t tiles = (a.n_tok + VPB - 1) / VPB * a.H;
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const int h = (int)(tile % a.H);
+    const int64_t t0 = tile / a.H * VPB;
+    // the tile's rows into LDS (rows past the last token are zero): every load in flight before the stores
+    {
+      constexpr int PER = VPB * (D / 8) / 256;
+      float xv[PER][8];
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int idx = tid + 256 * u;
+        const int64_t t = t0 + idx / (D / 8);
+        if (t < a.n_tok) {
+          load8(a.in[which], t * a.stride[which] + (int64_t)h * D + 8 * (idx % (D / 8)), a.dtype, xv[u]);
+        } else {
+#pragma unroll
+          for (int p = 0; p < 8; ++p) xv[u][p] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int idx = tid + 256 * u;
+        float *dst = &s_x[(idx / (D / 8)) * XS + 8 * (idx % (D / 8))];
+        *(float4 *)dst = float4{xv[u][0], xv[u][1], xv[u][2], xv[u][3]};
+        *(float4 *)(dst + 4) = float4{xv[u][4], xv[u][5], xv[u][6], xv[u][7]};
+      }
+    }
+    __syncthreads();
+    // rotation, 16 rows at a time
+#pragma unroll 1
+    for (int rt = 0; rt < VPB / 16; ++rt) {
+      const int v = 16 * rt + c;
+      float xv[JB][8];
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) {
+        const float4 u0 = *(const float4 *)&s_x[v * XS + 32 * jb + 8 * g4];
+        const float4 u1 = *(const float4 *)&s_x[v * XS + 32 * jb + 8 * g4 + 4];
+        xv[jb][0] = u0.x; xv[jb][1] = u0.y; xv[jb][2] = u0.z; xv[jb][3] = u0.w;
+        xv[jb][4] = u1.x; xv[jb][5] = u1.y; xv[jb][6] = u1.z; xv[jb][7] = u1.w;
+      }
+      float mx = 0.f;
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+        for (int p = 0; p < 8; ++p) mx = fmaxf(mx, fabsf(xv[jb][p]));
+      mx = max_xor32(max_xor16(mx));
+      int e = 0;
+      (void)frexpf(mx, &e);
+      const float sc = mx > 0.f ? ldexpf(1.f, 14 - e) : 1.f;
+      const float back = 1.f / (kMat * sc);
+      half8_t xhi[JB], xlo[JB];
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          _Float16 hh, ll;
+          qr_split(xv[jb][p] * sc, hh, ll);
+          xhi[jb][p] = hh;
+          xlo[jb][p] = ll;
+        }
+#pragma unroll
+      for (int ib = 0; ib < IB; ++ib) {
+        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[ib][jb], xhi[jb], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[ib][jb], xlo[jb], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[ib][jb], xhi[jb], acc, 0, 0, 0);
+        }
+        *(float4 *)&s_y[v * XS + 16 * (wave + 4 * ib) + 4 * g4] =
+            float4{acc[0] * back, acc[1] * back, acc[2] * back, acc[3] * back};
+      }
+    }
+    __syncthreads();
+    // the MSE steps on the rotated rows
+    {
+      const int64_t t = t0 + vl;
+      const int64_t tc = t < a.n_tok ? t : 0;
+      const int64_t slot = a.slots[tc];
+      float x[32];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float4 u = *(const float4 *)&s_y[vl * XS + 32 * ln + 4 * k];
+        x[4 * k] = u.x;
+        x[4 * k + 1] = u.y;
+        x[4 * k + 2] = u.z;
+        x[4 * k + 3] = u.w;
+      }
+      quantize_vector32<D, BT>(a, which, x, slot, t < a.n_tok, h, ln, sword, P, s_th);
+    }
+    __syncthreads();
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void quantize_qr_kernel(QuantArgs a) {
+  constexpr int VPB = 256 / (D / 32);
+  __shared__ __align__(16) float s_x[VPB * (D + 4)];
+  __shared__ __align__(16) float s_y[VPB * (D + 4)];
+  __shared__ float s_th[256];
+  const int which = blockIdx.y;  // 0 = K, 1 = V
+  switch (a.bits[which]) {       // uniform over the work-group
+    case 1: quantize_qr_tiles<D, 1>(a, which, s_x, s_y, s_th); break;
+    case 2: quantize_qr_tiles<D, 2>(a, which, s_x, s_y, s_th); break;
+    case 3: quantize_qr_tiles<D, 3>(a, which, s_x, s_y, s_th); break;
+    case 4: quantize_qr_tiles<D, 4>(a, which, s_x, s_y, s_th); break;
+    default: quantize_qr_tiles<D, 8>(a, which, s_x, s_y, s_th); break;
+  }
+}
+
 // Largest power of two sigma with max|x| * sigma < 256 (1 if x is all zero).
 __device__ __forceinline__ float pow2_range(float maxabs) {
   if (!(maxabs > 0.f)) return 1.0f;
@@ -460,9 +634,11 @@ void launch_prod(dim3 grid, const QuantArgs &p, hipStream_t stream) {
 
 }  // namespace
 
-int launch_quantize(const PageGeom &g, void *pages, int64_t num_pages, const void *k, const void *v,
-                    int dtype, int64_t n_tok, int64_t k_stride, int64_t v_stride,
-                    const int64_t *slots, const void *k_cb, const void *v_cb, hipStream_t stream) {
+namespace {
+
+QuantArgs quant_args(const PageGeom &g, void *pages, int64_t num_pages, const void *k, const void *v, int dtype,
+                     int64_t n_tok, int64_t k_stride, int64_t v_stride, const int64_t *slots, const void *k_cb,
+                     const void *v_cb) {
   QuantArgs a;
   a.pages = (unsigned char *)pages;
   a.num_slots = num_pages * TQ_PAGE_TOKENS;
@@ -491,6 +667,36 @@ int launch_quantize(const PageGeom &g, void *pages, int64_t num_pages, const voi
   a.mode[1] = g.v_mode;
   a.H = g.num_kv_heads;
   a.dtype = dtype;
+  a.rot[0] = a.rot[1] = nullptr;
+  a.which_of_y[0] = 0;
+  a.which_of_y[1] = 1;
+  return a;
+}
+
+}  // namespace
+
+int launch_quantize_qr(const PageGeom &g, void *pages, int64_t num_pages, const void *k, const void *v, int dtype,
+                       int64_t n_tok, const int64_t *slots, const void *k_cb, const void *v_cb, const float *k_rot,
+                       const float *v_rot, hipStream_t stream) {
+  if (g.k_mode == TQ_PROD || g.v_mode == TQ_PROD) return TQ_ENOTSUP;
+  const int64_t stride = (int64_t)g.num_kv_heads * g.head_dim;
+  QuantArgs a = quant_args(g, pages, num_pages, k, v, dtype, n_tok, stride, stride, slots, k_cb, v_cb);
+  a.rot[0] = k_rot;
+  a.rot[1] = v_rot;
+  const int vpb = 256 / (g.head_dim / 32);
+  const int64_t tiles = (n_tok + vpb - 1) / vpb * g.num_kv_heads;
+  if (tiles == 0) return TQ_OK;
+  // a persistent loop over the tiles: the matrix is loaded once per work-group
+  const dim3 grid((unsigned)std::min<int64_t>(tiles, 512), 2);
+  if (g.head_dim == 128) hipLaunchKernelGGL(quantize_qr_kernel<128>, grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(quantize_qr_kernel<64>, grid, dim3(256), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+int launch_quantize(const PageGeom &g, void *pages, int64_t num_pages, const void *k, const void *v,
+                    int dtype, int64_t n_tok, int64_t k_stride, int64_t v_stride,
+                    const int64_t *slots, const void *k_cb, const void *v_cb, hipStream_t stream) {
+  QuantArgs a = quant_args(g, pages, num_pages, k, v, dtype, n_tok, k_stride, v_stride, slots, k_cb, v_cb);
   // MSE tensors: work-groups of consecutive tokens of one head; prod tensors: long runs of one head
   int n_mse = 0, n_prod = 0, mse_of[2] = {0, 0}, prod_of[2] = {0, 0};
   for (int w = 0; w < 2; ++w) {

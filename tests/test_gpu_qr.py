@@ -181,3 +181,30 @@ def test_qr_full_size_8b_layer():
                                      ref[:, g * G:(g + 1) * G])
         print(f"  KV head {g}: max relative error {err:.2e}", flush=True)
         assert err <= parity.ATTN_TOL, (g, err)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("bits", [(4, 2), (3, 3), (1, 8)])
+def test_qr_fused_quantize_matches_two_passes(d, bits):
+    """MSE keys and values: tq_quantize_kv_qr rotates inside the quantize kernel; its pages are byte-identical to
+    tq_rotate_rows followed by tq_quantize_kv over the fp32 rows (the same arithmetic), ragged token count."""
+    import torch
+    import kv_cache_quantization_wht_amd as tq
+
+    kb, vb = bits
+    H, n = 3, 333
+    print(f"qr fused d={d} bits={bits}", flush=True)
+    layout, Lo = parity.make_layout(H, d, kb, 0, vb, 0)
+    c = qr_codebooks(d, kb, 0, vb, 0, seed=21)
+    npages = (n + 15) // 16 + 1
+    k, v = parity.seeded_kv(n, H, d, seed=22, dtype="bf16")
+    k, v = k.cuda(), v.cuda()
+    slots = torch.arange(n, dtype=torch.int64, device="cuda") + 16  # from page 1
+    fused = torch.full((npages * Lo["page_bytes"],), 0x33, dtype=torch.uint8, device="cuda")
+    tq.quantize_kv_qr(layout, fused, k, v, slots, c["k"]["blob"], c["v"]["blob"], c["k"]["fwd"], c["v"]["fwd"])
+    two = torch.full_like(fused, 0x33)
+    kr = tq.rotate_rows(d, c["k"]["fwd"], k)
+    vr = tq.rotate_rows(d, c["v"]["fwd"], v)
+    tq.quantize_kv(layout, two, kr, vr, slots, c["k"]["blob"], c["v"]["blob"])
+    torch.cuda.synchronize()
+    assert torch.equal(fused, two)
