@@ -133,7 +133,7 @@ __device__ __forceinline__ void split_hi_lo(float x, _Float16 &hi, _Float16 &lo)
 // MFMA position p (0..7) of the K operand -> coordinate offset inside its 8-coordinate group.
 template <int KB>
 __device__ __forceinline__ constexpr int k_order(int p) {
-  return KB == 4 ? ((p < 4) ? 2 * p : 2 * (p - 4) + 1) : p;
+  return (KB == 4 || KB == 3) ? ((p < 4) ? 2 * p : 2 * (p - 4) + 1) : p;
 }
 
 // Byte tables of the fp16 levels for v_perm lookups.
@@ -158,6 +158,17 @@ __device__ __forceinline__ Tab make_tab_k4(const uint16_t *lut) {
   return t;
 }
 
+// 3-bit sign-magnitude codes: the four magnitudes (levels of codes 4..7), low bytes in lo0, high bytes in hi0.
+__device__ __forceinline__ Tab make_tab_k3(const uint16_t *lut) {
+  Tab t{0, 0, 0, 0};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    t.lo0 |= ((uint32_t)lut[4 + m] & 0xFFu) << (8 * m);
+    t.hi0 |= ((uint32_t)lut[4 + m] >> 8) << (8 * m);
+  }
+  return t;
+}
+
 // 2-bit codes: the four levels by code; low bytes in lo0, high bytes in hi0.
 __device__ __forceinline__ Tab make_tab_v2(const uint16_t *lut) {
   Tab t{0, 0, 0, 0};
@@ -177,6 +188,46 @@ __device__ __forceinline__ half8_t lut_k4(uint32_t w, const Tab &T) {
   const uint32_t he = perm(T.hi1, T.hi0, me) | (~(w << 4) & 0x80808080u);
   const uint32_t lo = perm(T.lo1, T.lo0, mo);
   const uint32_t ho = perm(T.hi1, T.hi0, mo) | (~w & 0x80808080u);
+  return from_dwords(perm(he, le, 0x05010400u), perm(he, le, 0x07030602u), perm(ho, lo, 0x05010400u),
+                     perm(ho, lo, 0x07030602u));
+}
+
+// The 24 bits of 3-bit codes of 32-coordinate block kb (8 coordinates) from the lane's run of codes.
+template <int KW>
+__device__ __forceinline__ uint32_t k3_field(const uint32_t (&w)[KW], int kb) {
+  if (kb == 0) return w[0];
+  if (kb == 1) return __builtin_amdgcn_alignbit(w[1], w[0], 24);
+  if constexpr (KW > 2) {
+    if (kb == 2) return __builtin_amdgcn_alignbit(w[2], w[1], 16);
+    return w[2] >> 8;
+  }
+  return 0u;
+}
+
+// Eight 3-bit codes at bits 3e..3e+2 of g -> the pair (2k, 2k + 1) in bits 0-5 of byte k.
+__device__ __forceinline__ uint32_t spread3(uint32_t g) {
+  return (g & 0x3Fu) | ((g << 2) & 0x3F00u) | ((g << 4) & 0x3F0000u) | ((g << 6) & 0x3F000000u);
+}
+
+// 3-bit codes in bits 0-2 of each byte of x -> the four fp16 levels as two dwords (bytes 0, 1 and 2, 3).
+__device__ __forceinline__ void lut3_bytes(uint32_t x, const Tab &T, uint32_t &d01, uint32_t &d23) {
+  const uint32_t m = x & 0x03030303u;
+  const uint32_t lb = perm(T.lo0, T.lo0, m);
+  const uint32_t hb = perm(T.hi0, T.hi0, m) | (~(x << 5) & 0x80808080u);
+  d01 = perm(hb, lb, 0x05010400u);
+  d23 = perm(hb, lb, 0x07030602u);
+}
+
+// Eight 3-bit sign-magnitude codes (coordinate e at bits 3e..3e+2 of g) -> fp16 levels in MFMA order
+// e = 0,2,4,6,1,3,5,7: the code pairs spread one per byte, then byte-table lookups of the magnitudes, sign bit set
+// when the code's top bit is clear.
+__device__ __forceinline__ half8_t lut_k3(uint32_t g, const Tab &T) {
+  const uint32_t P = spread3(g);
+  const uint32_t me = P & 0x03030303u, mo = (P >> 3) & 0x03030303u;
+  const uint32_t le = perm(T.lo0, T.lo0, me);
+  const uint32_t he = perm(T.hi0, T.hi0, me) | (~(P << 5) & 0x80808080u);
+  const uint32_t lo = perm(T.lo0, T.lo0, mo);
+  const uint32_t ho = perm(T.hi0, T.hi0, mo) | (~(P << 2) & 0x80808080u);
   return from_dwords(perm(he, le, 0x05010400u), perm(he, le, 0x07030602u), perm(ho, lo, 0x05010400u),
                      perm(ho, lo, 0x07030602u));
 }
@@ -671,7 +722,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   }
   Tab tk{0, 0, 0, 0}, tv{0, 0, 0, 0};
   if constexpr (KB == 4) tk = make_tab_k4(s_lutk);
+  if constexpr (KB == 3) tk = make_tab_k3(s_lutk);
   if constexpr (VB == 2) tv = make_tab_v2(s_lutv);
+  if constexpr (VB == 3 && D == 128) tv = make_tab_k3(s_lutv);
   uint32_t negpair1 = 0;  // 1-bit levels: fp16 pattern of the negative level in both halves
   if constexpr (KB == 1) negpair1 = (uint32_t)s_lutk[0] * 0x00010001u;
 
@@ -726,7 +779,31 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   // fp16 V levels of one page pair as MFMA operands: Bop[nb] holds, for lane (c, g4), the level of
   // coordinate (D / 16) * c + nb for the 8 tokens of contraction rows 8 * g4 .. 8 * g4 + 7.
   auto v_operands = [&](const F &cur, half8_t *Bop) {
-    if constexpr (VB == 2 && D == 128) {
+    if constexpr (VB == 3 && D == 128) {
+      // each token's 24-bit group (code nb = coordinate nb of the lane's group) spread one code pair per byte;
+      // then per byte k and page, the four tokens' pair k gathered into one dword
+      uint32_t X[2][4];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        uint32_t Pt[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Pt[j] = spread3(k3_field(cur.vw[q2], j));
+#pragma unroll
+        for (int k = 0; k < 4; k += 2) {
+          const uint32_t sel = k == 0 ? 0x05010400u : 0x07030602u;  // bytes k, k + 1 of two tokens
+          const uint32_t a01 = perm(Pt[1], Pt[0], sel), a23 = perm(Pt[3], Pt[2], sel);
+          X[q2][k] = perm(a23, a01, 0x05040100u);
+          X[q2][k + 1] = perm(a23, a01, 0x07060302u);
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        uint32_t d[4];
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) lut3_bytes(X[q2][nb >> 1] >> (3 * (nb & 1)), tv, d[2 * q2], d[2 * q2 + 1]);
+        Bop[nb] = from_dwords(d[0], d[1], d[2], d[3]);
+      }
+    } else if constexpr (VB == 2 && D == 128) {
       // code blocks nb and nb + 4 of a token sit one byte apart: one mask yields both selector sets
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -783,6 +860,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         half8_t A;
         if constexpr (KB == 4) {
           A = lut_k4(cur.kw[q2][kb], tk);
+        } else if constexpr (KB == 3) {
+          A = lut_k3(k3_field(cur.kw[q2], kb), tk);
         } else if constexpr (KB == 1) {
           const uint32_t z = cur.kw[q2][0] >> (8 * kb);
           A = from_dwords(negpair1 ^ ((z & 1u) << 15) ^ ((z & 2u) << 30), negpair1 ^ ((z & 4u) << 13) ^ ((z & 8u) << 28),
