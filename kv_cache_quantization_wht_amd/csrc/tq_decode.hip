@@ -76,6 +76,11 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// p | (~s & 0x80808080): the sign bit of every byte set where bit 7 of s is clear (one v_bitop3).
+__device__ __forceinline__ uint32_t or_signs(uint32_t p, uint32_t s) {
+  return __builtin_amdgcn_bitop3_b32(p, s, 0x80808080u, 0xF2);
+}
+
 // NBYTES bytes from p (aligned to ALIGN bytes) into dwords (little-endian).
 template <int NBYTES, int ALIGN>
 __device__ __forceinline__ void load_bytes(const unsigned char *p, uint32_t *w) {
@@ -185,9 +190,9 @@ __device__ __forceinline__ Tab make_tab_v2(const uint16_t *lut) {
 __device__ __forceinline__ half8_t lut_k4(uint32_t w, const Tab &T) {
   const uint32_t me = w & 0x07070707u, mo = (w >> 4) & 0x07070707u;
   const uint32_t le = perm(T.lo1, T.lo0, me);
-  const uint32_t he = perm(T.hi1, T.hi0, me) | (~(w << 4) & 0x80808080u);
+  const uint32_t he = or_signs(perm(T.hi1, T.hi0, me), w << 4);
   const uint32_t lo = perm(T.lo1, T.lo0, mo);
-  const uint32_t ho = perm(T.hi1, T.hi0, mo) | (~w & 0x80808080u);
+  const uint32_t ho = or_signs(perm(T.hi1, T.hi0, mo), w);
   return from_dwords(perm(he, le, 0x05010400u), perm(he, le, 0x07030602u), perm(ho, lo, 0x05010400u),
                      perm(ho, lo, 0x07030602u));
 }
@@ -213,7 +218,7 @@ __device__ __forceinline__ uint32_t spread3(uint32_t g) {
 __device__ __forceinline__ void lut3_bytes(uint32_t x, const Tab &T, uint32_t &d01, uint32_t &d23) {
   const uint32_t m = x & 0x03030303u;
   const uint32_t lb = perm(T.lo0, T.lo0, m);
-  const uint32_t hb = perm(T.hi0, T.hi0, m) | (~(x << 5) & 0x80808080u);
+  const uint32_t hb = or_signs(perm(T.hi0, T.hi0, m), x << 5);
   d01 = perm(hb, lb, 0x05010400u);
   d23 = perm(hb, lb, 0x07030602u);
 }
@@ -225,9 +230,9 @@ __device__ __forceinline__ half8_t lut_k3(uint32_t g, const Tab &T) {
   const uint32_t P = spread3(g);
   const uint32_t me = P & 0x03030303u, mo = (P >> 3) & 0x03030303u;
   const uint32_t le = perm(T.lo0, T.lo0, me);
-  const uint32_t he = perm(T.hi0, T.hi0, me) | (~(P << 5) & 0x80808080u);
+  const uint32_t he = or_signs(perm(T.hi0, T.hi0, me), P << 5);
   const uint32_t lo = perm(T.lo0, T.lo0, mo);
-  const uint32_t ho = perm(T.hi0, T.hi0, mo) | (~(P << 2) & 0x80808080u);
+  const uint32_t ho = or_signs(perm(T.hi0, T.hi0, mo), P << 2);
   return from_dwords(perm(he, le, 0x05010400u), perm(he, le, 0x07030602u), perm(ho, lo, 0x05010400u),
                      perm(ho, lo, 0x07030602u));
 }
