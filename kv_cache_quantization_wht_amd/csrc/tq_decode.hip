@@ -809,16 +809,17 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         Bop[nb] = from_dwords(d[0], d[1], d[2], d[3]);
       }
     } else if constexpr (VB == 2 && D == 128) {
-      // code blocks nb and nb + 4 of a token sit one byte apart: one mask yields both selector sets
+      // code blocks nb and nb + 4 of a token sit one byte apart: one mask yields four codes, whose low and
+      // high level bytes are looked up at once and then paired into fp16 values
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         uint32_t lo_[4], hi_[4];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const uint32_t y = (cur.vw[w >> 1][w & 1] >> (2 * k)) & 0x03030303u;
-          const uint32_t y4 = y | 0x04040404u;
-          lo_[w] = perm(tv.hi0, tv.lo0, perm(y4, y, 0x06020400u));  // code block k
-          hi_[w] = perm(tv.hi0, tv.lo0, perm(y4, y, 0x07030501u));  // code block k + 4
+          const uint32_t lb = perm(tv.lo0, tv.lo0, y), hb = perm(tv.hi0, tv.hi0, y);
+          lo_[w] = perm(hb, lb, 0x06020400u);  // code block k
+          hi_[w] = perm(hb, lb, 0x07030501u);  // code block k + 4
         }
         Bop[k] = from_dwords(lo_[0], lo_[1], lo_[2], lo_[3]);
         Bop[k + 4] = from_dwords(hi_[0], hi_[1], hi_[2], hi_[3]);
