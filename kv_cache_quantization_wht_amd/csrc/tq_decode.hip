@@ -197,6 +197,19 @@ __device__ __forceinline__ half8_t lut_k4(uint32_t w, const Tab &T) {
                      perm(ho, lo, 0x07030602u));
 }
 
+// Eight sign bits at bits off..off+7 of w (bit p set: +level, clear: -level) -> fp16 operand of the eight
+// values in order p. hitab: the high byte of -level in byte 0 and of +level in byte 1; lo4: the low byte of the
+// level in all four bytes. Each nibble's bits are spread to bit 0 of bytes 0..3 by one 24-bit multiply (the copies
+// of bit j land 7 apart; only its own lands on 8j), which then select the high bytes from hitab; a last permute
+// pairs them with the low byte.
+__device__ __forceinline__ half8_t signs_to_half8(uint32_t w, int off, uint32_t hitab, uint32_t lo4) {
+  const uint32_t n0 = __builtin_amdgcn_ubfe(w, off, 4), n1 = __builtin_amdgcn_ubfe(w, off + 4, 4);
+  const uint32_t h0 = perm(hitab, hitab, (n0 * 0x00204081u) & 0x01010101u);
+  const uint32_t h1 = perm(hitab, hitab, (n1 * 0x00204081u) & 0x01010101u);
+  return from_dwords(perm(h0, lo4, 0x05000400u), perm(h0, lo4, 0x07000600u), perm(h1, lo4, 0x05000400u),
+                     perm(h1, lo4, 0x07000600u));
+}
+
 // The 24 bits of 3-bit codes of 32-coordinate block kb (8 coordinates) from the lane's run of codes.
 template <int KW>
 __device__ __forceinline__ uint32_t k3_field(const uint32_t (&w)[KW], int kb) {
@@ -730,8 +743,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   if constexpr (KB == 3) tk = make_tab_k3(s_lutk);
   if constexpr (VB == 2) tv = make_tab_v2(s_lutv);
   if constexpr (VB == 3 && D == 128) tv = make_tab_k3(s_lutv);
-  uint32_t negpair1 = 0;  // 1-bit levels: fp16 pattern of the negative level in both halves
-  if constexpr (KB == 1) negpair1 = (uint32_t)s_lutk[0] * 0x00010001u;
+  // 1-bit levels: the high byte of the negative and the positive level, and the low byte in all four bytes
+  uint32_t lev1_hitab = 0, lev1_lo4 = 0;
+  if constexpr (KB == 1) {
+    lev1_hitab = ((uint32_t)s_lutk[0] >> 8) | ((uint32_t)s_lutk[1] & 0xFF00u);
+    lev1_lo4 = ((uint32_t)s_lutk[0] & 0xFFu) * 0x01010101u;
+  }
 
   // ---- 3. stream the page pairs
   float m_run = -INFINITY;
@@ -869,9 +886,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         } else if constexpr (KB == 3) {
           A = lut_k3(k3_field(cur.kw[q2], kb), tk);
         } else if constexpr (KB == 1) {
-          const uint32_t z = cur.kw[q2][0] >> (8 * kb);
-          A = from_dwords(negpair1 ^ ((z & 1u) << 15) ^ ((z & 2u) << 30), negpair1 ^ ((z & 4u) << 13) ^ ((z & 8u) << 28),
-                          negpair1 ^ ((z & 16u) << 11) ^ ((z & 32u) << 26), negpair1 ^ ((z & 64u) << 9) ^ ((z & 128u) << 24));
+          A = signs_to_half8(cur.kw[q2][0], 8 * kb, lev1_hitab, lev1_lo4);
         } else {
           uint16_t hv[8];
 #pragma unroll
@@ -886,10 +901,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         floatx4_t acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KBLK; ++kb) {
-          const uint32_t z = cur.zb[q2] >> (8 * kb);
-          const uint32_t NEG = 0xBC00BC00u;  // -1, -1; a set bit flips to +1
-          const half8_t A = from_dwords(NEG ^ ((z & 1u) << 15) ^ ((z & 2u) << 30), NEG ^ ((z & 4u) << 13) ^ ((z & 8u) << 28),
-                                        NEG ^ ((z & 16u) << 11) ^ ((z & 32u) << 26), NEG ^ ((z & 64u) << 9) ^ ((z & 128u) << 24));
+          const half8_t A = signs_to_half8(cur.zb[q2], 8 * kb, 0x3CBCu, 0u);  // -1 (0xBC00); a set bit: +1 (0x3C00)
           acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, shi[kb], acc2, 0, 0, 0);
           if constexpr (!PK) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, slo[kb], acc2, 0, 0, 0);
         }
