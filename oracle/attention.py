@@ -17,7 +17,9 @@ zero output. ``decode_attention`` dequantizes every cached vector back to the
 original domain and applies softmax(scale * q . k) v exactly as defined.
 ``decode_attention_rotated`` forms the same quantity in the rotated domain (query
 rotated once, values accumulated rotated, one inverse rotation at the end) and is
-used to check the first against a second route.
+used to check the first against a second route. ``prefill_attention`` is the
+causal attention of a chunk of new tokens over the same cache (a causal mask
+in place of the sequence length; its reading is stated on the function).
 """
 from __future__ import annotations
 
@@ -93,6 +95,49 @@ def decode_attention_rotated(pool, L, cb_k, cb_v, q, page_table, seq_lens, scale
             Vr = codec.dequantize_rotated(rv["codes"], rv["norm16"], cb_v, rv.get("gamma16"), rv.get("qjl"))
             w = _softmax_weights(scale * (q_rot[b, hs] @ Kr.T))
             out[b, hs] = cb_v.unrotate(w @ Vr)
+    return out
+
+
+def prefill_attention(pool, L, cb_k, cb_v, q, page_table, prefix_lens, scale, rows=None):
+    """Causal attention of a chunk of new tokens over the packed cache (fp64).
+
+    Sources: "Where This Fits in the Inference Stack", "Decode Throughput vs. Time to
+    First Token" (prefill attention over long contexts is the bandwidth-bound regime
+    the compressed cache also relieves); "Why the KV Cache Exists", "The KV Cache
+    Solution" and "Prefix Caching" (the prompt's keys and values are computed once,
+    stored, and later tokens attend to the stored prefix).
+
+    Reading adopted: the chunk's own keys and values are written to the cache first
+    (quantize-on-write), and every query reads them back quantized, like the prefix.
+    q[b, i] is the query of the chunk's token i of sequence b, at position
+    prefix_lens[b] + i; it attends to positions 0 .. prefix_lens[b] + i, itself
+    included:
+        out[b, i, h] = sum_{t <= P_b + i} softmax_t(scale <q[b,i,h], khat_t>) vhat_t
+    with khat, vhat of KV head floor(h / G). ``rows`` optionally restricts the
+    computation to a list of (b, i) pairs; other rows are left as NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, C, Hq, d = q.shape
+    Hkv = L["H"]
+    G = Hq // Hkv
+    out = np.full((B, C, Hq, d), np.nan)
+    for b in range(B):
+        P = int(prefix_lens[b])
+        want = list(range(C)) if rows is None else sorted({int(i) for bb, i in rows if int(bb) == b})
+        if not want:
+            continue
+        pos = P + np.asarray(want)                       # position of each wanted query
+        T = int(pos.max()) + 1                           # cached tokens any of them may see
+        allowed = np.arange(T)[None, :] <= pos[:, None]  # [query, key]: causal, own token included
+        for g in range(Hkv):
+            hs = slice(g * G, (g + 1) * G)
+            rk = gather(pool, L, "k", page_table[b], T, g)
+            rv = gather(pool, L, "v", page_table[b], T, g)
+            K = codec.dequantize(rk["codes"], rk["norm16"], cb_k, rk.get("gamma16"), rk.get("qjl"))
+            V = codec.dequantize(rv["codes"], rv["norm16"], cb_v, rv.get("gamma16"), rv.get("qjl"))
+            logits = scale * (q[b][want][:, hs] @ K.T)   # [query, head, key]
+            logits = np.where(allowed[:, None, :], logits, -np.inf)
+            out[b, want, hs] = _softmax_weights(logits) @ V
     return out
 
 

@@ -487,6 +487,76 @@ def check_attention_special_cases():
     assert np.all(out == 0)
 
 
+def _prefill_cache(H, d, Hq, B, prefix, C, kb, km, vb, vm, seed):
+    """A cache holding prefix + chunk tokens per sequence, and chunk queries [B, C, Hq, d]."""
+    c = build_cache(H, d, Hq, B, [p + C for p in prefix], kb, km, vb, vm, seed=seed)
+    rng = np.random.Generator(np.random.Philox(seed + 100))
+    c["qc"] = rng.standard_normal((B, C, Hq, d))
+    c["prefix"] = np.asarray(prefix)
+    return c
+
+
+def check_prefill_vs_torch_sdpa():
+    """Chunk attention against torch's scaled_dot_product_attention (fp64, CPU) on the dequantized cache with
+    an explicit boolean mask (query i sees keys 0 .. P + i), GQA expanded with repeat_interleave."""
+    import torch
+
+    H, d, Hq, B, C = 2, 64, 8, 2, 21
+    prefix = [0, 35]
+    for (kb, km, vb, vm) in ((4, 0, 2, 0), (2, 1, 3, 0)):
+        c = _prefill_cache(H, d, Hq, B, prefix, C, kb, km, vb, vm, seed=70 + kb)
+        out = attention.prefill_attention(c["pool"], c["L"], c["cbk"], c["cbv"], c["qc"], c["pt"], c["prefix"], 0.15)
+        for b in range(B):
+            T = prefix[b] + C
+            Ks, Vs = [], []
+            for h in range(H):
+                rk = attention.gather(c["pool"], c["L"], "k", c["pt"][b], T, h)
+                rv = attention.gather(c["pool"], c["L"], "v", c["pt"][b], T, h)
+                Ks.append(codec.dequantize(rk["codes"], rk["norm16"], c["cbk"], rk.get("gamma16"), rk.get("qjl")))
+                Vs.append(codec.dequantize(rv["codes"], rv["norm16"], c["cbv"]))
+            Kt = torch.tensor(np.stack(Ks)).repeat_interleave(Hq // H, dim=0)  # [Hq, T, d]
+            Vt = torch.tensor(np.stack(Vs)).repeat_interleave(Hq // H, dim=0)
+            qt = torch.tensor(c["qc"][b]).transpose(0, 1)                     # [Hq, C, d]
+            mask = torch.ones(C, T, dtype=torch.bool).tril(diagonal=prefix[b])
+            ref = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, attn_mask=mask, scale=0.15)
+            assert np.allclose(out[b], ref.transpose(0, 1).numpy(), rtol=1e-10, atol=1e-12), (kb, b)
+
+
+def check_prefill_special_cases():
+    """Zero queries weigh every visible token equally: row i is the mean of the dequantized values of tokens
+    0 .. P + i; with no prefix the first row is token 0's value whatever its query; a restricted row set gives
+    the same rows."""
+    H, d, Hq, C = 1, 64, 2, 19
+    for P in (0, 16, 29):
+        c = _prefill_cache(H, d, Hq, 1, [P], C, 3, 0, 2, 0, seed=80 + P)
+        rv = attention.gather(c["pool"], c["L"], "v", c["pt"][0], P + C, 0)
+        V = codec.dequantize(rv["codes"], rv["norm16"], c["cbv"])
+        zero = attention.prefill_attention(c["pool"], c["L"], c["cbk"], c["cbv"], np.zeros_like(c["qc"]), c["pt"],
+                                           [P], 0.3)
+        for i in range(C):
+            assert np.allclose(zero[0, i], V[: P + i + 1].mean(axis=0)[None, :], atol=1e-13), (P, i)
+        full = attention.prefill_attention(c["pool"], c["L"], c["cbk"], c["cbv"], c["qc"], c["pt"], [P], 0.3)
+        if P == 0:
+            assert np.allclose(full[0, 0], V[0][None, :], atol=1e-13)
+        some = attention.prefill_attention(c["pool"], c["L"], c["cbk"], c["cbv"], c["qc"], c["pt"], [P], 0.3,
+                                           rows=[(0, 3), (0, C - 1)])
+        assert np.array_equal(some[0, [3, C - 1]], full[0, [3, C - 1]])
+        assert np.isnan(some[0, 0]).all()
+
+
+def check_prefill_rows_are_decode_steps():
+    """Row i of a chunk is the decode attention of its query at sequence length P + i + 1 (a second route: the
+    decode oracle's own gather and softmax at each length)."""
+    H, d, Hq, B, C = 2, 64, 4, 2, 18
+    prefix = [5, 40]
+    c = _prefill_cache(H, d, Hq, B, prefix, C, 4, 0, 3, 0, seed=90)
+    out = attention.prefill_attention(c["pool"], c["L"], c["cbk"], c["cbv"], c["qc"], c["pt"], c["prefix"], 0.2)
+    for i in range(C):
+        ref = attention.decode_attention(c["pool"], c["L"], c["cbk"], c["cbv"], c["qc"][:, i], c["pt"],
+                                         c["prefix"] + i + 1, 0.2)
+        assert attention.relative_error(out[:, i], ref) < 1e-12, i
+
+
 def check_page_table_invariance():
     """The same tokens stored through a shuffled or an identity page table give identical outputs."""
     outs = []

@@ -256,3 +256,44 @@ def test_mutant_dense_unrotate_transposed(monkeypatch):
     monkeypatch.setattr(codec.Codebook, "unrotate", lambda self, y: np.asarray(y, dtype=np.float64) @ self.R.T
                         if self.dense is not None else rotation.unrotate(y, self.sign_words))
     assert _caught(pins.check_dense_rotation_reduces_to_known_paths) and _caught(pins.check_dense_rotation_mse)
+
+
+def _prefill_with_mask(rule):
+    """The prefill oracle with its causal rule replaced: rule(t, P, i) -> allowed."""
+    def prefill(pool, L, cb_k, cb_v, q, page_table, prefix_lens, scale, rows=None):
+        q = np.asarray(q, dtype=np.float64)
+        B, C, Hq, d = q.shape
+        G = Hq // L["H"]
+        out = np.full((B, C, Hq, d), np.nan)
+        for b in range(B):
+            P = int(prefix_lens[b])
+            want = list(range(C)) if rows is None else sorted({i for bb, i in rows if bb == b})
+            T = P + max(want) + 1
+            allowed = np.array([[rule(t, P, i) for t in range(T)] for i in want])
+            for g in range(L["H"]):
+                rk = attention.gather(pool, L, "k", page_table[b], T, g)
+                rv = attention.gather(pool, L, "v", page_table[b], T, g)
+                K = codec.dequantize(rk["codes"], rk["norm16"], cb_k, rk.get("gamma16"), rk.get("qjl"))
+                V = codec.dequantize(rv["codes"], rv["norm16"], cb_v)
+                lg = scale * (q[b][want][:, g * G:(g + 1) * G] @ K.T)
+                lg = np.where(allowed[:, None, :], lg, -np.inf)
+                out[b, want, g * G:(g + 1) * G] = attention._softmax_weights(lg) @ V
+        return out
+    return prefill
+
+
+@pytest.mark.parametrize("rule", [
+    lambda t, P, i: t < P + i or t == 0,  # own token excluded
+    lambda t, P, i: t <= i,               # prefix ignored
+    lambda t, P, i: True,                 # no mask: the whole chunk visible
+    lambda t, P, i: t <= P + i + 1,       # one token of look-ahead
+], ids=["own-token-excluded", "prefix-ignored", "unmasked", "lookahead"])
+def test_mutant_prefill_mask(monkeypatch, rule):
+    monkeypatch.setattr(attention, "prefill_attention", _prefill_with_mask(rule))
+    assert _caught(pins.check_prefill_vs_torch_sdpa, pins.check_prefill_special_cases)
+
+
+def test_mutant_prefill_mask_control(monkeypatch):
+    """The mutant scaffold with the true rule passes the pins (so the cases above fail for their rule)."""
+    monkeypatch.setattr(attention, "prefill_attention", _prefill_with_mask(lambda t, P, i: t <= P + i))
+    assert not _caught(pins.check_prefill_vs_torch_sdpa, pins.check_prefill_special_cases)
