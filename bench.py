@@ -69,6 +69,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the uncompressed bf16 and FP8 comparators")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
     ap.add_argument("--eager", action="store_true", help="launch steps from Python instead of a captured graph")
     ap.add_argument("--workload", default=None,
                     help="another synthetic workload by name or index (default: the Llama-3.1-8B single layer); "
@@ -296,6 +297,8 @@ def main():
         result["dense_bf16"] = dense_comparator(wl, k_pre, v_pre, k_new, v_new, qs, W, K, ms_per_step, step_bytes)
         result["dense_fp8"] = dense_comparator(wl, k_pre, v_pre, k_new, v_new, qs, W, K, ms_per_step, step_bytes,
                                                fmt="fp8")
+    if not args.no_prefill:
+        result["prefill"] = prefill_leg(wl, layout, pages, page_tables[0], k_pre, v_pre, kcb, vcb)
     if not args.no_cpu_baseline:
         first = int(page_tables[0][0, 0].item())
         npg = (T + 15) // 16
@@ -303,6 +306,74 @@ def main():
         result["cpu_baseline"] = cpu_baseline(H, d, bits, pool, T, qs.double().cpu().numpy(), scale, sw, None,
                                               args.cpu_seconds, rec_bytes, "copy 0")
     print(json.dumps(result), flush=True)
+
+
+def prefill_leg(wl, layout, pages, page_table, k_pre, v_pre, kcb, vcb, chunk=2048, reps=8):
+    """The last ``chunk`` tokens of the layer's prompt as one prefill chunk over the packed cache of copy 0
+    (prefix T - chunk cached tokens): tq_prefill_attention alone (its kernel, from HIP events around a graph of
+    ``reps`` launches) and tq_prefill_chunk (quantize of the chunk's K/V into their slots, which rewrites the
+    same bytes, plus the attention). Algorithmic work: 4 * d flops per (query head, visible key) pair - the
+    q.k and p.v products - over the causal pairs; the kernel runs each product as fp16 hi + lo MFMA pairs,
+    so the matrix cores issue twice these flops."""
+    import torch
+
+    import kv_cache_quantization_wht_amd as tq
+
+    dev = "cuda"
+    H, Hq, d, T = wl.kv_heads, wl.q_heads, wl.head_dim, wl.seq_len
+    P = T - chunk
+    g = torch.Generator(device=dev).manual_seed(kvsynth_seed_q())
+    q = torch.randn(1, chunk, Hq, d, generator=g, device=dev).to(torch.bfloat16)
+    prefix = torch.tensor([P], dtype=torch.int32, device=dev)
+    first = int(page_table[0, 0].item())
+    slots = (first * 16 + torch.arange(P, T, dtype=torch.int64, device=dev))
+    kc, vc = k_pre[P:T].unsqueeze(0).contiguous(), v_pre[P:T].unsqueeze(0).contiguous()
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+
+    def attn():
+        tq.prefill_attention(layout, pages, q, page_table, prefix, wl.softmax_scale, kcb, vcb, out=out)
+
+    def fused():
+        tq.prefill_chunk(layout, pages, kc, vc, slots, q, page_table, prefix, wl.softmax_scale, kcb, vcb, out=out)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gph):
+            for _ in range(reps):
+                fn()
+        gph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    t_attn = timed(attn)
+    t_fused = timed(fused)
+    pairs = chunk * P + chunk * (chunk + 1) // 2  # (query token, visible key) pairs per query head
+    flops = 4.0 * d * Hq * pairs
+    tflops = flops / t_attn / 1e12
+    peak = 2500.0
+    log(f"prefill: chunk {chunk} after {P} cached tokens: attention kernel {t_attn * 1e6:.1f} us "
+        f"({tflops:.0f} TFLOP/s algorithmic, {100 * tflops / peak:.1f}% of fp16 MFMA peak); with the chunk's "
+        f"quantize {t_fused * 1e6:.1f} us -> {chunk / t_fused:.0f} tokens/s")
+    return {"chunk": chunk, "prefix": P, "attn_us": round(t_attn * 1e6, 2), "chunk_us": round(t_fused * 1e6, 2),
+            "tokens_per_s": round(chunk / t_fused, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                         "frac": round(tflops / peak, 4), "traffic": None, "flops_per_launch": flops,
+                         "kernel": "prefill_kernel<128,4,2> (tq_prefill_attention)", "mfma_issue_factor": 2},
+            "what": "tq_prefill_attention / tq_prefill_chunk of the last 2048 prompt tokens of the 8B layer, "
+                    "HIP events around a graph of 8 launches"}
+
+
+def kvsynth_seed_q():
+    import kvsynth
+
+    return kvsynth.data_seed(WORKLOAD_INDEX, 0, "q") + 17
 
 
 def dense_comparator(wl, k_pre, v_pre, k_new, v_new, qs, W, K, ms_compressed, step_bytes, fmt="bf16"):

@@ -28,6 +28,9 @@
  *   tq_qr_rotation, tq_rotate_rows, tq_quantize_kv_qr, tq_decode_attention_qr
  *                       the dense random (QR) rotation in place of the WHT: the same codes and
  *                       attention with a d x d orthogonal matrix, for the comparison of the two.
+ *   tq_prefill_attention, tq_prefill_chunk
+ *                       chunked prefill: a chunk of new tokens attends causally to the packed cache
+ *                       (its own keys and values written there first), on the matrix cores.
  *   tq_dense_*          the uncompressed comparators: the same paged decode attention over a bf16
  *                       cache and (tq_dense_fp8_*) over an FP8 E4M3 cache with per-tensor scales, to
  *                       measure the compressed path against the bytes it saves.
@@ -251,6 +254,45 @@ int tq_decode_combine(const tq_layout *layout, const void *pages, int64_t num_pa
                       int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
                       int pages_per_split, const void *k_cb, const void *v_cb, void *workspace,
                       size_t workspace_bytes, float *out, void *stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * Chunked prefill over the packed cache ("Where This Fits in the Inference Stack", "Decode Throughput
+ * vs. Time to First Token": over long inputs the attention of prefill reads the cache too, and a cache
+ * 4x smaller shortens it; "Why the KV Cache Exists", "The KV Cache Solution" and "Prefix Caching": the
+ * prompt's keys and values are stored once and later tokens attend to the stored prefix).
+ *
+ * A chunk of chunk_len new tokens of each of `batch` sequences: token i of sequence b sits at position
+ * prefix_lens[b] + i and attends causally to positions 0 .. prefix_lens[b] + i of its sequence, itself
+ * included. Every key and value is read from the packed pages, the chunk's own included (they must have
+ * been written there first: tq_prefill_chunk does both), so row i equals tq_decode_attention of its
+ * query at sequence length prefix_lens[b] + i + 1 up to fp32 rounding.
+ *   q            device [batch][chunk_len][num_q_heads][head_dim], dtype q_dtype, contiguous
+ *   page_table   device int32 [batch][max_pages_per_seq]; entries < 0 or >= num_pages are empty pages
+ *                (their tokens get no weight), as are positions >= max_pages_per_seq * 16
+ *   prefix_lens  device int32 [batch]: cached tokens ahead of the chunk (negative values count as 0)
+ *   out          device fp32 [batch][chunk_len][num_q_heads][head_dim] (written); a row that sees no
+ *                key (every visible page empty) is zero
+ * K and V must be in MSE mode (prod mode: TQ_ENOTSUP) and num_q_heads / num_kv_heads <= 16.
+ * Errors: TQ_EINVAL (layout, dtype, shapes, null or misaligned pointers: pages and the codebooks
+ * 16-byte aligned, q and out element-aligned), TQ_ENOTSUP, TQ_EHIP. batch or chunk_len 0 launches
+ * nothing. */
+int tq_prefill_attention(const tq_layout *layout, const void *pages, int64_t num_pages, const void *q,
+                         int q_dtype, int batch, int chunk_len, int num_q_heads, const int32_t *page_table,
+                         int max_pages_per_seq, const int32_t *prefix_lens, float softmax_scale,
+                         const void *k_cb, const void *v_cb, float *out, void *stream);
+
+/* One prefill chunk: quantize its keys and values into the pages (tq_quantize_kv of the batch * chunk_len
+ * tokens), then tq_prefill_attention, on `stream` in that order.
+ *   k, v   device [batch][chunk_len][num_kv_heads][head_dim], dtype kv_dtype, contiguous, 16-byte aligned
+ *   slots  device int64 [batch * chunk_len]: the global slot of each token, which must be the one the
+ *          page table gives its position (page_table[b][t / 16] * 16 + t % 16 for t = prefix_lens[b] + i)
+ * Every argument is checked before the first launch. Errors as for tq_quantize_kv and
+ * tq_prefill_attention. */
+int tq_prefill_chunk(const tq_layout *layout, void *pages, int64_t num_pages, const void *k, const void *v,
+                     int kv_dtype, const int64_t *slots, const void *q, int q_dtype, int batch, int chunk_len,
+                     int num_q_heads, const int32_t *page_table, int max_pages_per_seq,
+                     const int32_t *prefix_lens, float softmax_scale, const void *k_cb, const void *v_cb,
+                     float *out, void *stream);
 
 /* ------------------------------------------------------------------------------------------------
  * Uncompressed comparator ("Where This Fits in the Inference Stack", "What Changes When KV Cache Is

@@ -31,6 +31,7 @@ C_SYMBOLS = (
     "tq_dense_fp8_page_bytes", "tq_dense_fp8_write_kv", "tq_dense_fp8_decode_attention",
     "tq_qr_rotation", "tq_rotate_rows", "tq_quantize_kv_qr_workspace_bytes", "tq_quantize_kv_qr",
     "tq_decode_qr_workspace_bytes", "tq_decode_attention_qr",
+    "tq_prefill_attention", "tq_prefill_chunk",
 )
 
 
@@ -91,6 +92,9 @@ def _lib():
         lib.tq_decode_qr_workspace_bytes.argtypes = [lay, i32, i32, i32, i32, ctypes.POINTER(sz)]
         lib.tq_decode_attention_qr.argtypes = [lay, vp, i64, vp, i32, i32, i32, vp, i32, vp, f32, i32, vp, vp, vp,
                                                vp, vp, sz, vp, vp]
+        lib.tq_prefill_attention.argtypes = [lay, vp, i64, vp, i32, i32, i32, i32, vp, i32, vp, f32, vp, vp, vp, vp]
+        lib.tq_prefill_chunk.argtypes = [lay, vp, i64, vp, vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, vp, f32, vp,
+                                         vp, vp, vp]
         for name in C_SYMBOLS:
             getattr(lib, name).restype = ctypes.c_char_p if name == "tq_strerror" else ctypes.c_int
         _LIB = lib
@@ -526,4 +530,63 @@ def decode_attention_qr(layout: Layout, pages, q, page_table, seq_lens, softmax_
                                          float(softmax_scale), pages_per_split, k_cb.data_ptr(), v_cb.data_ptr(),
                                          k_rot.data_ptr(), v_inv.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                          out.data_ptr(), _stream(stream)), "tq_decode_attention_qr")
+    return out
+
+
+def _prefill_args(layout: Layout, pages, q, page_table, prefix_lens, out):
+    import torch
+
+    _need(pages, "pages", torch.uint8)
+    _need(q, "q")
+    _need(page_table, "page_table", torch.int32)
+    _need(prefix_lens, "prefix_lens", torch.int32)
+    if q.dim() != 4 or q.shape[3] != layout.head_dim or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [batch, chunk_len, num_q_heads, head_dim] tensor")
+    B, C, Hq, _ = q.shape
+    if page_table.dim() != 2 or page_table.shape[0] != B or not page_table.is_contiguous():
+        raise ValueError("page_table must be a contiguous [batch, max_pages_per_seq] int32 tensor")
+    if prefix_lens.numel() != B or not prefix_lens.is_contiguous():
+        raise ValueError("prefix_lens must hold one int32 per sequence")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32)
+    if out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor shaped like q")
+    num_pages = pages.numel() // page_layout(layout)["page_bytes"]
+    return B, C, Hq, num_pages, out
+
+
+def prefill_attention(layout: Layout, pages, q, page_table, prefix_lens, softmax_scale, k_cb, v_cb, out=None,
+                      stream=None):
+    """Causal attention of a chunk q [batch, chunk_len, num_q_heads, head_dim] at positions prefix_lens[b] + i
+    over the packed cache (the chunk's own keys and values already in it); returns fp32 out shaped like q."""
+    B, C, Hq, num_pages, out = _prefill_args(layout, pages, q, page_table, prefix_lens, out)
+    _check(_lib().tq_prefill_attention(ctypes.byref(layout.c()), pages.data_ptr(), num_pages, q.data_ptr(),
+                                       _dtype_code(q), B, C, Hq, page_table.data_ptr(), page_table.shape[1],
+                                       prefix_lens.data_ptr(), float(softmax_scale), k_cb.data_ptr(), v_cb.data_ptr(),
+                                       out.data_ptr(), _stream(stream)), "tq_prefill_attention")
+    return out
+
+
+def prefill_chunk(layout: Layout, pages, k, v, slots, q, page_table, prefix_lens, softmax_scale, k_cb, v_cb, out=None,
+                  stream=None):
+    """Quantize the chunk's k, v [batch, chunk_len, num_kv_heads, head_dim] into ``slots`` (int64, one per token),
+    then prefill_attention of q over the cache; returns fp32 out shaped like q."""
+    import torch
+
+    B, C, Hq, num_pages, out = _prefill_args(layout, pages, q, page_table, prefix_lens, out)
+    _need(slots, "slots", torch.int64)
+    for name, t in (("k", k), ("v", v)):
+        _need(t, name)
+        if t.shape != (B, C, layout.num_kv_heads, layout.head_dim) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [batch, chunk_len, num_kv_heads, head_dim] tensor")
+    if k.dtype != v.dtype:
+        raise TypeError("k and v must share a dtype")
+    if not slots.is_contiguous() or slots.numel() != B * C:
+        raise ValueError("slots must be a contiguous int64 vector with one entry per chunk token")
+    _check(_lib().tq_prefill_chunk(ctypes.byref(layout.c()), pages.data_ptr(), num_pages, k.data_ptr(), v.data_ptr(),
+                                   _dtype_code(k), slots.data_ptr(), q.data_ptr(), _dtype_code(q), B, C, Hq,
+                                   page_table.data_ptr(), page_table.shape[1], prefix_lens.data_ptr(),
+                                   float(softmax_scale), k_cb.data_ptr(), v_cb.data_ptr(), out.data_ptr(),
+                                   _stream(stream)), "tq_prefill_chunk")
     return out

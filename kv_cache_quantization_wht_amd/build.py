@@ -36,6 +36,7 @@ SOURCES = [
     ("tq_dense.hip", "tq_dense.o", ["-fno-honor-nans"]),
     ("tq_rotate.hip", "tq_rotate.o", []),
     ("tq_qr.cpp", "tq_qr.o", []),
+    ("tq_prefill.hip", "tq_prefill.o", ["-fno-honor-nans"]),
     ("tq_decode.hip", "tq_decode_d128_pk.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=1"]),
     ("tq_decode.hip", "tq_decode_d128.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=2"]),
     ("tq_decode.hip", "tq_decode_d64_pk.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=3"]),

@@ -464,6 +464,60 @@ int tq_decode_combine(const tq_layout *layout, const void *pages, int64_t num_pa
                        tq::kPassCombine, stream);
 }
 
+// Every check of tq_prefill_attention, before anything is launched (tq_prefill_chunk runs them ahead of its
+// quantize launch too).
+static int prefill_check(const tq_layout *layout, tq::PageGeom *g, const void *pages, int64_t num_pages,
+                         const void *q, int q_dtype, int batch, int chunk_len, int num_q_heads,
+                         const int32_t *page_table, int max_pages_per_seq, const int32_t *prefix_lens,
+                         float softmax_scale, const void *k_cb, const void *v_cb, const float *out) {
+  int st = tq::make_geom(layout, g);
+  if (st) return st;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return TQ_EINVAL;
+  if (batch < 0 || chunk_len < 0 || num_q_heads < 1 || num_q_heads % g->num_kv_heads) return TQ_EINVAL;
+  if (num_q_heads / g->num_kv_heads > 16) return TQ_ENOTSUP;
+  if (g->k_mode != TQ_MSE || g->v_mode != TQ_MSE) return TQ_ENOTSUP;
+  if (max_pages_per_seq < 1 || max_pages_per_seq > (1 << 26) || num_pages < 1) return TQ_EINVAL;
+  if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return TQ_EINVAL;
+  if (batch == 0 || chunk_len == 0) return TQ_OK;
+  if (!pages || !q || !page_table || !prefix_lens || !k_cb || !v_cb || !out) return TQ_EINVAL;
+  if (((uintptr_t)pages | (uintptr_t)k_cb | (uintptr_t)v_cb) & 15) return TQ_EINVAL;
+  if (((uintptr_t)q & (q_dtype == TQ_F32 ? 3 : 1)) || ((uintptr_t)out & 3)) return TQ_EINVAL;
+  const int64_t tiles = ((int64_t)chunk_len * (num_q_heads / g->num_kv_heads) + 127) / 128 + 1;
+  if (tiles * g->num_kv_heads * batch > 0x7FFFFFFF) return TQ_EINVAL;
+  return TQ_OK;
+}
+
+int tq_prefill_attention(const tq_layout *layout, const void *pages, int64_t num_pages, const void *q, int q_dtype,
+                         int batch, int chunk_len, int num_q_heads, const int32_t *page_table,
+                         int max_pages_per_seq, const int32_t *prefix_lens, float softmax_scale, const void *k_cb,
+                         const void *v_cb, float *out, void *stream) {
+  tq::PageGeom g;
+  const int st = prefill_check(layout, &g, pages, num_pages, q, q_dtype, batch, chunk_len, num_q_heads, page_table,
+                               max_pages_per_seq, prefix_lens, softmax_scale, k_cb, v_cb, out);
+  if (st || batch == 0 || chunk_len == 0) return st;
+  return tq::launch_prefill(g, pages, num_pages, q, q_dtype, batch, chunk_len, num_q_heads, page_table,
+                            max_pages_per_seq, prefix_lens, softmax_scale, k_cb, v_cb, out, (hipStream_t)stream);
+}
+
+int tq_prefill_chunk(const tq_layout *layout, void *pages, int64_t num_pages, const void *k, const void *v,
+                     int kv_dtype, const int64_t *slots, const void *q, int q_dtype, int batch, int chunk_len,
+                     int num_q_heads, const int32_t *page_table, int max_pages_per_seq, const int32_t *prefix_lens,
+                     float softmax_scale, const void *k_cb, const void *v_cb, float *out, void *stream) {
+  tq::PageGeom g;
+  int st = prefill_check(layout, &g, pages, num_pages, q, q_dtype, batch, chunk_len, num_q_heads, page_table,
+                         max_pages_per_seq, prefix_lens, softmax_scale, k_cb, v_cb, out);
+  if (st || batch == 0 || chunk_len == 0) return st;
+  // the quantize call's own checks, ahead of its launch, so that a failure launches nothing
+  if (kv_dtype != TQ_F32 && kv_dtype != TQ_BF16 && kv_dtype != TQ_F16) return TQ_EINVAL;
+  if (!k || !v || !slots || (((uintptr_t)k | (uintptr_t)v) & 15)) return TQ_EINVAL;
+  const int64_t row = (int64_t)g.num_kv_heads * g.head_dim;
+  const int64_t n_tok = (int64_t)batch * chunk_len;
+  if ((st = tq_quantize_kv(layout, pages, num_pages, k, v, kv_dtype, n_tok, row, row, slots, k_cb, v_cb, stream)))
+    return st;
+  return tq::launch_prefill(g, pages, num_pages, q, q_dtype, batch, chunk_len, num_q_heads, page_table,
+                            max_pages_per_seq, prefix_lens, softmax_scale, k_cb, v_cb, out, (hipStream_t)stream);
+}
+
 static int dense_geom(int head_dim, int num_kv_heads, bool fp8, tq::PageGeom *g) {
   if ((head_dim != 64 && head_dim != 128) || num_kv_heads < 1 || num_kv_heads > 4096) return TQ_EINVAL;
   *g = tq::PageGeom{};

@@ -91,4 +91,11 @@ int launch_quantize_qr(const PageGeom &g, void *pages, int64_t num_pages, const 
 int launch_rotate_rows(int head_dim, const float *mat, const void *x, int x_dtype, int64_t rows, float *y,
                        hipStream_t stream);
 
+// Causal attention of a chunk of chunk_len new tokens per sequence over the packed cache (K and V in MSE
+// mode; TQ_ENOTSUP otherwise): q [batch][chunk_len][num_q_heads][head_dim], out fp32 of the same shape.
+int launch_prefill(const PageGeom &g, const void *pages, int64_t num_pages, const void *q, int q_dtype, int batch,
+                   int chunk_len, int num_q_heads, const int32_t *page_table, int max_pages_per_seq,
+                   const int32_t *prefix_lens, float softmax_scale, const void *k_cb, const void *v_cb, float *out,
+                   hipStream_t stream);
+
 }  // namespace tq

@@ -1,0 +1,585 @@
+// Chunked prefill attention over the packed cache ("Where This Fits in the Inference Stack", "Decode Throughput
+// vs. Time to First Token": over long contexts the attention of prefill reads the cache too, and its traffic
+// shrinks with it; "Why the KV Cache Exists", "The KV Cache Solution" and "Prefix Caching": the prompt's keys
+// and values are stored once and later tokens attend to the stored prefix).
+//
+// A chunk of C new tokens of each sequence, at positions P_b .. P_b + C - 1, attends causally to the cached
+// tokens 0 .. its own position (its own keys and values already written to the pages, quantized). Where the
+// decode kernel gives every byte of a page to G query heads, here a work-group owns 128 query columns - the
+// (token, head) pairs of 128 / G consecutive tokens of one KV head - so one dequantization serves 128 columns
+// and the contraction runs on the matrix cores:
+//   1. Query rotation as in decode (signs, Walsh-Hadamard butterflies, 1/d, a power-of-two range factor per
+//      column), the fp16 hi and lo parts of each column kept in registers as MFMA operands.
+//   2. Steps of 32 keys (two pages). All 256 threads load the next step's codes and norms while the
+//      wavefronts compute this one, then look the codes up in the level tables and store fp16 levels in a
+//      double-buffered LDS tile: K as [key][coordinate], V as [coordinate][key] in the key order of the
+//      softmax operand. One barrier per step.
+//        scores  S^T[16 keys, 16 columns] = Khat Q on MFMA 16x16x32 f16 (hi and lo query parts), times the
+//                key norms; causal mask per column where the step reaches past a column's position;
+//        softmax running maximum per column (base 2), sums per lane;
+//        values  O^T[coordinates, columns] += Vhat^T P'^T with P' = p * ||v|| as fp16 hi + lo.
+//   3. Each column's sums divided by its total weight, the inverse rotation by butterflies, fp32 rows out.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <type_traits>
+
+#include "tq_common.h"
+#include "tq_internal.h"
+#include "tq_lanes.h"
+
+namespace tq {
+
+struct PrefillArgs {
+  const unsigned char *pages;
+  int num_pages32;  // min(num_pages, INT32_MAX)
+  int64_t page_bytes;
+  int64_t k_codes, k_norms, v_codes, v_norms;
+  const void *q;  // [B][C][Hq][D]
+  int q_dtype;
+  int B, C, Hq, Hkv, G, TQ;  // TQ: query tokens per work-group (128 / G)
+  int tiles;                 // work-groups along the chunk (ceil(C / TQ))
+  const int32_t *page_table;
+  int max_pages;
+  const int32_t *prefix_lens;
+  float scale_log2;
+  const unsigned char *kcb, *vcb;
+  BlobOffsets ko, vo;
+  float *out;  // [B][C][Hq][D]
+};
+
+namespace {
+
+constexpr int kWavesP = 4;
+constexpr int kThreadsP = 64 * kWavesP;
+constexpr int kColsP = 32 * kWavesP;  // query columns per work-group: two 16-column blocks per wavefront
+constexpr int kStepKeys = 32;         // keys per step: two pages
+constexpr float kLog2eP = 1.4426950408889634f;
+constexpr float kHeadroomP = 4.0f;    // log2 units between a column's running maximum and its weight reference
+
+typedef _Float16 half4p_t __attribute__((ext_vector_type(4)));
+
+// Largest power of two sigma with max|x| * sigma < 256 (1 if x is all zero).
+__device__ __forceinline__ float range_factor_p(float maxabs) {
+  if (!(maxabs > 0.f)) return 1.0f;
+  int e;
+  frexpf(maxabs, &e);
+  return ldexpf(1.0f, 8 - e);
+}
+
+__device__ __forceinline__ void split_hi_lo_p(float x, _Float16 &hi, _Float16 &lo) {
+  hi = (_Float16)x;
+  lo = (_Float16)(x - (float)hi);
+}
+
+// LDS of one work-group: the double-buffered level tiles of a step, or (prologue, epilogue) one
+// [16][D + 4] fp32 staging block per wavefront.
+template <int D>
+struct Tiles {
+  _Float16 k[2][kStepKeys][D + 8];  // K levels [key][coordinate]; rows padded so 16 keys hit distinct banks
+  _Float16 v[2][D][kStepKeys + 8];  // V levels [coordinate][k'], k' = 8 g + 4 q2 + j <-> key 16 q2 + 4 g + j
+  uint16_t nk[2][kStepKeys], nv[2][kStepKeys];  // fp16 norms of the step's keys
+};
+template <int D>
+union PrefillLds {
+  Tiles<D> t;
+  float stage[kWavesP][16][D + 4];
+};
+
+// Per-thread registers of one step's loads: K codes of 8 keys' coordinate chunk, V codes of 4 slots of one
+// piece, one norm.
+template <int D, int KB, int VB>
+struct StepRegs {
+  static constexpr int KBYTES = KB * D / 64;              // bytes of the thread's D/8 K codes
+  static constexpr int KW = (KBYTES % 4 == 0) ? KBYTES / 4 : (KBYTES + 3) / 4 + 1;  // dwords covering them
+  uint32_t kw[KW];
+  uint32_t vw[VB];  // 4 slots x VB bytes
+  uint32_t norm;
+};
+
+// Dwords [off / 4, off / 4 + N) of a page through a buffer resource (zero-size for a missing page).
+template <int N>
+__device__ __forceinline__ void load_dwords(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t *w) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const uint4 t = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, 0));
+      w[4 * i] = t.x;
+      w[4 * i + 1] = t.y;
+      w[4 * i + 2] = t.z;
+      w[4 * i + 3] = t.w;
+    }
+  } else if constexpr (N % 2 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const uint2 t = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off + 8 * i, 0, 0));
+      w[2 * i] = t.x;
+      w[2 * i + 1] = t.y;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * i, 0, 0);
+  }
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const PrefillArgs &a, int pg) {
+  const bool ok = pg >= 0 && pg < a.num_pages32;
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(a.pages + (int64_t)(ok ? pg : 0) * a.page_bytes), (short)0,
+                                           ok ? (int)a.page_bytes : 0, 0x00020000);
+}
+
+// NB bits at bit offset `bit` of a little-endian dword array (NB <= 8, the field may straddle two dwords).
+template <int NB, int NW>
+__device__ __forceinline__ uint32_t field(const uint32_t (&w)[NW], int bit) {
+  const int i = bit >> 5, s = bit & 31;
+  const uint32_t lo = w[i];
+  const uint32_t hi = (i + 1 < NW) ? w[i + 1] : 0u;
+  return __builtin_amdgcn_alignbit(hi, lo, s) & ((1u << NB) - 1u);
+}
+
+template <int D, int KB, int VB>
+__global__ __launch_bounds__(kThreadsP, D == 128 ? 1 : 2) void prefill_kernel(PrefillArgs a) {
+  constexpr int KBLK = D / 32;  // 32-coordinate blocks of the score contraction
+  constexpr int NB = D / 16;    // 16-coordinate blocks of the value contraction
+  constexpr int KREC = D * KB / 8;
+  constexpr int CPT = D / 32;   // V coordinates per thread and step
+  constexpr int NH = 8 / CPT;   // threads per (piece, group) of one page
+  using R = StepRegs<D, KB, VB>;
+
+  __shared__ __align__(16) PrefillLds<D> lds;
+  __shared__ uint16_t s_lutk[1 << KB], s_lutv[1 << VB];
+  __shared__ float s_sig[kWavesP][16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15;
+  const int g4 = lane >> 4;
+
+  // work item: consecutive items (tiles of one KV head) go to one XCD when the grid divides evenly
+  int item = blockIdx.x;
+  {
+    const int total = gridDim.x;
+    if ((total & 7) == 0) item = (item & 7) * (total >> 3) + (item >> 3);
+  }
+  const int tile = item % a.tiles;
+  const int kvh = (item / a.tiles) % a.Hkv;
+  const int b = item / (a.tiles * a.Hkv);
+  const int G = a.G;
+  const int i0 = tile * a.TQ;
+  const int ntok = min(a.TQ, a.C - i0);
+  const int kmax = a.max_pages * TQ_PAGE_TOKENS;
+  int P = a.prefix_lens[b];
+  P = P < 0 ? 0 : P;
+  const int kend = min(P + i0 + ntok, kmax);  // keys [0, kend) are visible to some column of this work-group
+  const int nsteps = kend > 0 ? (kend + kStepKeys - 1) / kStepKeys : 0;
+  const int32_t *ptab = a.page_table + (int64_t)b * a.max_pages;
+
+  // level tables (code-indexed: code c -> ascending level c in the upper half, half - 1 - c in the lower)
+  {
+    const int nk = 1 << KB, nv = 1 << VB;
+    for (int i = tid; i < nk; i += kThreadsP)
+      s_lutk[i] = ((const uint16_t *)(a.kcb + a.ko.levels))[i >= nk / 2 ? i : nk / 2 - 1 - i];
+    for (int i = tid; i < nv; i += kThreadsP)
+      s_lutv[i] = ((const uint16_t *)(a.vcb + a.vo.levels))[i >= nv / 2 ? i : nv / 2 - 1 - i];
+  }
+
+  // ---- 1. query columns: column j = 32 wave + 16 nq + c is token i0 + j / G, head kvh * G + j % G
+  half8_t qhi[2][KBLK], qlo[2][KBLK];
+  float colscale[2];
+  int lim[2];  // last visible key of the lane's column (-1: a column with no query)
+  {
+    const uint32_t *ksw = (const uint32_t *)(a.kcb + a.ko.signs);
+    const bool neg0 = (ksw[lane >> 5] >> (lane & 31)) & 1u;
+    const bool neg1 = D == 128 ? ((ksw[(lane + 64) >> 5] >> (lane & 31)) & 1u) : false;
+    float(*st)[D + 4] = lds.stage[wave];
+#pragma unroll
+    for (int nq = 0; nq < 2; ++nq) {
+      // the 16 rows of this block, raw bits, into registers first (independent loads in flight; the dtype
+      // is the same for every row, so one branch)
+      uint32_t x0[16], x1[16];
+      auto row_base = [&](int r, bool &real) {
+        const int j = 32 * wave + 16 * nq + r;
+        const int i = i0 + j / G;
+        real = j < a.TQ * G && i < a.C;
+        return (((int64_t)b * a.C + (real ? i : 0)) * a.Hq + kvh * G + j % G) * D;
+      };
+      if (a.q_dtype == TQ_F32) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          bool real;
+          const uint32_t *row = (const uint32_t *)a.q + row_base(r, real);
+          x0[r] = real ? row[lane] : 0u;
+          x1[r] = (real && D == 128) ? row[lane + 64] : 0u;
+        }
+      } else {
+        const bool bf = a.q_dtype == TQ_BF16;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          bool real;
+          const uint16_t *row = (const uint16_t *)a.q + row_base(r, real);
+          const uint32_t u0 = real ? row[lane] : 0u;
+          const uint32_t u1 = (real && D == 128) ? row[lane + 64] : 0u;
+          x0[r] = bf ? u0 << 16 : __float_as_uint(half_bits_to_float((uint16_t)u0));
+          x1[r] = bf ? u1 << 16 : __float_as_uint(half_bits_to_float((uint16_t)u1));
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float y0 = __uint_as_float(x0[r] ^ (neg0 ? 0x80000000u : 0u));
+        float y1 = __uint_as_float(x1[r] ^ (neg1 ? 0x80000000u : 0u));
+        y0 = wht_stage<1>(y0, lane);
+        y1 = wht_stage<1>(y1, lane);
+        y0 = wht_stage<2>(y0, lane);
+        y1 = wht_stage<2>(y1, lane);
+        y0 = wht_stage<4>(y0, lane);
+        y1 = wht_stage<4>(y1, lane);
+        y0 = wht_stage<8>(y0, lane);
+        y1 = wht_stage<8>(y1, lane);
+        y0 = wht_stage<16>(y0, lane);
+        y1 = wht_stage<16>(y1, lane);
+        y0 = wht_stage<32>(y0, lane);
+        y1 = wht_stage<32>(y1, lane);
+        if (D == 128) {
+          const float u = y0;
+          y0 = u + y1;
+          y1 = u - y1;
+        }
+        y0 *= (1.0f / D);
+        y1 *= (1.0f / D);
+        const float mx = wave_max(fmaxf(fabsf(y0), D == 128 ? fabsf(y1) : 0.f), lane);
+        st[r][lane] = y0;
+        if (D == 128) st[r][lane + 64] = y1;
+        if (lane == 0) s_sig[wave][r] = range_factor_p(mx);
+      }
+      __syncthreads();
+      {
+        const int j = 32 * wave + 16 * nq + c;
+        const int i = i0 + j / G;
+        const bool real = j < a.TQ * G && i < a.C;
+        const float sig = s_sig[wave][c];
+        colscale[nq] = real ? a.scale_log2 / sig : 0.f;
+        lim[nq] = real ? min(P + i, kmax - 1) : -1;
+#pragma unroll
+        for (int kb = 0; kb < KBLK; ++kb) {
+          const float4 u0 = *(const float4 *)&st[c][32 * kb + 8 * g4];
+          const float4 u1 = *(const float4 *)&st[c][32 * kb + 8 * g4 + 4];
+          const float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+          for (int p = 0; p < 8; ++p) {
+            _Float16 h, l;
+            split_hi_lo_p(real ? v[p] * sig : 0.f, h, l);
+            qhi[nq][kb][p] = h;
+            qlo[nq][kb][p] = l;
+          }
+        }
+      }
+      __syncthreads();  // the staging block is rewritten by the next block (and then by the level tiles)
+    }
+  }
+  // the smallest position of the work-group: steps whose keys all precede it need no causal mask
+  const int first_pos = P + i0;
+
+  // ---- 2. the key steps
+  // thread roles of the loads: K codes of key kk (page kq = wave / 2), coordinate chunk kc; V codes of
+  // piece vp, slot group vg, coordinates 8 vp + CPT vh .. of page vq = wave / 2; norms (waves 0 and 2,
+  // lanes 0..31): K (lanes < 16) or V norm of slot lane % 16 of page wave / 2
+  const int kk = tid >> 3, kc = tid & 7;
+  const int pq = wave >> 1;  // page of the step this wavefront loads
+  const int vt = tid & 127;
+  const int vp = vt / (4 * NH), vg = (vt / NH) & 3, vh = vt % NH;
+  const uint32_t k_off = (uint32_t)(a.k_codes + (int64_t)(kvh * TQ_PAGE_TOKENS + (kk & 15)) * KREC) +
+                         (uint32_t)(kc * R::KBYTES);
+  const uint32_t k_off_al = k_off & ~3u;
+  const int k_bit0 = 8 * (int)(k_off & 3u);
+  const uint32_t v_off = (uint32_t)(a.v_codes + ((int64_t)(kvh * (D / 8) + vp) * TQ_PAGE_TOKENS + 4 * vg) * VB);
+  const bool norm_lane = (wave & 1) == 0 && lane < 32;
+  const uint32_t n_off = (uint32_t)((lane < 16 ? a.k_norms : a.v_norms) +
+                                    (int64_t)(kvh * TQ_PAGE_TOKENS + (lane & 15)) * 2);
+
+  auto page_id = [&](int pi) { return pi < a.max_pages ? ptab[pi] : -1; };
+  auto page_ok = [&](int pg) { return pg >= 0 && pg < a.num_pages32; };
+
+  auto load_step = [&](int pg_this, R &rg) {
+    const __amdgpu_buffer_rsrc_t r = page_rsrc(a, pg_this);
+    load_dwords<R::KW>(r, k_off_al, rg.kw);
+    load_dwords<VB>(r, v_off, rg.vw);
+    rg.norm = norm_lane ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, n_off & ~1u, 0, 0) : 0u;
+  };
+  auto store_step = [&](int buf, const R &rg) {
+    // K: D / 8 levels of key kk (the codes first shifted down to bit 0, so every field offset is fixed)
+    {
+      uint32_t kw[R::KW];
+#pragma unroll
+      for (int i = 0; i < R::KW; ++i)
+        kw[i] = __builtin_amdgcn_alignbit(i + 1 < R::KW ? rg.kw[i + 1] : 0u, rg.kw[i], k_bit0);
+      _Float16 h[D / 8];
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        const uint16_t bits = s_lutk[field<KB, R::KW>(kw, KB * i)];
+        h[i] = __builtin_bit_cast(_Float16, bits);
+      }
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) {
+        half8_t t;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) t[p] = h[8 * i + p];
+        *(half8_t *)&lds.t.k[buf][kk][kc * (D / 8) + 8 * i] = t;
+      }
+    }
+    // V: CPT coordinates of piece vp for slots 4 vg .. 4 vg + 3 of page pq
+    {
+      uint32_t w[VB];
+#pragma unroll
+      for (int i = 0; i < VB; ++i) w[i] = rg.vw[i];
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) {
+        const int ci = CPT * vh + e;
+        half4p_t t;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint16_t bits = s_lutv[field<VB, VB>(w, 8 * VB * s + VB * ci)];
+          t[s] = __builtin_bit_cast(_Float16, bits);
+        }
+        *(half4p_t *)&lds.t.v[buf][8 * vp + ci][8 * vg + 4 * pq] = t;
+      }
+    }
+    if (norm_lane) {
+      const int key = 16 * pq + (lane & 15);
+      if (lane < 16) lds.t.nk[buf][key] = (uint16_t)rg.norm;
+      else lds.t.nv[buf][key] = (uint16_t)rg.norm;
+    }
+  };
+
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_part[2] = {0.f, 0.f};
+  floatx4_t O[2][NB];
+#pragma unroll
+  for (int nq = 0; nq < 2; ++nq)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) O[nq][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  // one step of 32 keys from buffer buf: FULL = every key visible to every column and in a valid page
+  auto compute = [&](int buf, int s, bool ok0, bool ok1, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    floatx4_t acc[2][2];
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+      for (int nq = 0; nq < 2; ++nq) acc[q2][nq] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+      for (int kb = 0; kb < KBLK; ++kb) {
+        const half8_t A = *(const half8_t *)&lds.t.k[buf][16 * q2 + c][32 * kb + 8 * g4];
+#pragma unroll
+        for (int nq = 0; nq < 2; ++nq) {
+          acc[q2][nq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qhi[nq][kb], acc[q2][nq], 0, 0, 0);
+          acc[q2][nq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qlo[nq][kb], acc[q2][nq], 0, 0, 0);
+        }
+      }
+    half4p_t nk[2], nv[2];
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      nk[q2] = *(const half4p_t *)&lds.t.nk[buf][16 * q2 + 4 * g4];
+      nv[q2] = *(const half4p_t *)&lds.t.nv[buf][16 * q2 + 4 * g4];
+    }
+    half8_t phi[2], plo[2];
+#pragma unroll
+    for (int nq = 0; nq < 2; ++nq) {
+      float sc[2][4];
+      bool okm[2][4];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sc[q2][j] = fmaf((float)nk[q2][j], acc[q2][nq][j], 0.f);  // score / (softmax scale * log2 e)
+          if constexpr (!FULL) {
+            const int t = kStepKeys * s + 16 * q2 + 4 * g4 + j;
+            okm[q2][j] = (q2 ? ok1 : ok0) && t <= lim[nq];
+            sc[q2][j] = okm[q2][j] ? sc[q2][j] : -3.0e38f;
+          }
+        }
+      float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+      mx = max_xor32(max_xor16(mx));
+      const float m_new = colscale[nq] * mx;
+      if (__any(m_new > m_run[nq])) {
+        const bool up = m_new > m_run[nq];
+        const float m_ref = up ? m_new + kHeadroomP : m_run[nq];
+        const float alpha = up ? ((m_run[nq] == -INFINITY) ? 0.f : fast_exp2(m_run[nq] - m_ref)) : 1.f;
+        l_part[nq] *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) O[nq][nb] *= alpha;
+        m_run[nq] = m_ref;
+      }
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+          float p0 = fast_exp2(fmaf(sc[q2][j], colscale[nq], -m_run[nq]));
+          float p1 = fast_exp2(fmaf(sc[q2][j + 1], colscale[nq], -m_run[nq]));
+          if constexpr (!FULL) {
+            p0 = okm[q2][j] ? p0 : 0.f;
+            p1 = okm[q2][j + 1] ? p1 : 0.f;
+          }
+          l_part[nq] += p0 + p1;
+          const float2_t pv = {fmaf((float)nv[q2][j], p0, 0.f), fmaf((float)nv[q2][j + 1], p1, 0.f)};
+          const half2_t h = __builtin_convertvector(pv, half2_t);
+          const half2_t l = __builtin_convertvector(pv - __builtin_convertvector(h, float2_t), half2_t);
+          phi[nq][4 * q2 + j] = h[0];
+          phi[nq][4 * q2 + j + 1] = h[1];
+          plo[nq][4 * q2 + j] = l[0];
+          plo[nq][4 * q2 + j + 1] = l[1];
+        }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const half8_t Vop = *(const half8_t *)&lds.t.v[buf][16 * nb + c][8 * g4];
+#pragma unroll
+      for (int nq = 0; nq < 2; ++nq) {
+        O[nq][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Vop, phi[nq], O[nq][nb], 0, 0, 0);
+        O[nq][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Vop, plo[nq], O[nq][nb], 0, 0, 0);
+      }
+    }
+  };
+
+  if (nsteps > 0) {
+    // page ids of steps 0 and 1 (scalar), step 0's codes into buffer 0
+    int pid_cur[2] = {page_id(0), page_id(1)};
+    int pid_nxt[2] = {page_id(2), page_id(3)};
+    R rg;
+    load_step(pid_cur[pq], rg);
+    store_step(0, rg);
+    __syncthreads();
+    for (int s = 0; s < nsteps; ++s) {
+      const bool more = s + 1 < nsteps;
+      const bool ok0 = page_ok(pid_cur[0]), ok1 = page_ok(pid_cur[1]);
+      if (more) load_step(pid_nxt[pq], rg);
+      const int pid_after[2] = {page_id(2 * s + 4), page_id(2 * s + 5)};
+      const bool full = ok0 && ok1 && kStepKeys * (s + 1) <= first_pos + 1;
+      if (full) compute(s & 1, s, ok0, ok1, std::true_type{});
+      else compute(s & 1, s, ok0, ok1, std::false_type{});
+      if (more) store_step((s + 1) & 1, rg);
+      __syncthreads();
+      pid_cur[0] = pid_nxt[0];
+      pid_cur[1] = pid_nxt[1];
+      pid_nxt[0] = pid_after[0];
+      pid_nxt[1] = pid_after[1];
+    }
+  }
+
+  // ---- 3. normalise, inverse rotation, fp32 rows
+  const uint32_t *vsw = (const uint32_t *)(a.vcb + a.vo.signs);
+  const bool vneg0 = (vsw[lane >> 5] >> (lane & 31)) & 1u;
+  const bool vneg1 = D == 128 ? ((vsw[(lane + 64) >> 5] >> (lane & 31)) & 1u) : false;
+  float(*st)[D + 4] = lds.stage[wave];
+#pragma unroll
+  for (int nq = 0; nq < 2; ++nq) {
+    const float L = sum_xor16_32(l_part[nq]);
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      *(float4 *)&st[c][16 * nb + 4 * g4] =
+          float4{O[nq][nb][0] * inv, O[nq][nb][1] * inv, O[nq][nb][2] * inv, O[nq][nb][3] * inv};
+    __syncthreads();
+    for (int r = 0; r < 16; ++r) {
+      const int j = 32 * wave + 16 * nq + r;
+      const int i = i0 + j / G;
+      if (!(j < a.TQ * G && i < a.C)) continue;  // wavefront-uniform
+      float y0 = st[r][lane];
+      float y1 = D == 128 ? st[r][lane + 64] : 0.f;
+      y0 = wht_stage<1>(y0, lane);
+      y1 = wht_stage<1>(y1, lane);
+      y0 = wht_stage<2>(y0, lane);
+      y1 = wht_stage<2>(y1, lane);
+      y0 = wht_stage<4>(y0, lane);
+      y1 = wht_stage<4>(y1, lane);
+      y0 = wht_stage<8>(y0, lane);
+      y1 = wht_stage<8>(y1, lane);
+      y0 = wht_stage<16>(y0, lane);
+      y1 = wht_stage<16>(y1, lane);
+      y0 = wht_stage<32>(y0, lane);
+      y1 = wht_stage<32>(y1, lane);
+      if (D == 128) {
+        const float u = y0;
+        y0 = u + y1;
+        y1 = u - y1;
+      }
+      y0 *= (1.0f / D);
+      y1 *= (1.0f / D);
+      float *orow = a.out + (((int64_t)b * a.C + i) * a.Hq + kvh * G + j % G) * D;
+      orow[lane] = vneg0 ? -y0 : y0;
+      if (D == 128) orow[lane + 64] = vneg1 ? -y1 : y1;
+    }
+    __syncthreads();
+  }
+}
+
+template <int D, int KB>
+bool prefill_dispatch_v(int vb, const PrefillArgs &a, dim3 grid, hipStream_t s) {
+  switch (vb) {
+    case 1: hipLaunchKernelGGL((prefill_kernel<D, KB, 1>), grid, dim3(kThreadsP), 0, s, a); return true;
+    case 2: hipLaunchKernelGGL((prefill_kernel<D, KB, 2>), grid, dim3(kThreadsP), 0, s, a); return true;
+    case 3: hipLaunchKernelGGL((prefill_kernel<D, KB, 3>), grid, dim3(kThreadsP), 0, s, a); return true;
+    case 4: hipLaunchKernelGGL((prefill_kernel<D, KB, 4>), grid, dim3(kThreadsP), 0, s, a); return true;
+    case 8: hipLaunchKernelGGL((prefill_kernel<D, KB, 8>), grid, dim3(kThreadsP), 0, s, a); return true;
+    default: return false;
+  }
+}
+
+template <int D>
+bool prefill_dispatch(int kb, int vb, const PrefillArgs &a, dim3 grid, hipStream_t s) {
+  switch (kb) {
+    case 1: return prefill_dispatch_v<D, 1>(vb, a, grid, s);
+    case 2: return prefill_dispatch_v<D, 2>(vb, a, grid, s);
+    case 3: return prefill_dispatch_v<D, 3>(vb, a, grid, s);
+    case 4: return prefill_dispatch_v<D, 4>(vb, a, grid, s);
+    case 8: return prefill_dispatch_v<D, 8>(vb, a, grid, s);
+    default: return false;
+  }
+}
+
+}  // namespace
+
+int launch_prefill(const PageGeom &g, const void *pages, int64_t num_pages, const void *q, int q_dtype, int batch,
+                   int chunk_len, int num_q_heads, const int32_t *page_table, int max_pages_per_seq,
+                   const int32_t *prefix_lens, float softmax_scale, const void *k_cb, const void *v_cb, float *out,
+                   hipStream_t stream) {
+  if (g.k_mode != TQ_MSE || g.v_mode != TQ_MSE) return TQ_ENOTSUP;
+  PrefillArgs a;
+  a.pages = (const unsigned char *)pages;
+  a.num_pages32 = (int)std::min<int64_t>(num_pages, 0x7FFFFFFF);
+  a.page_bytes = g.page_bytes;
+  a.k_codes = g.k_codes;
+  a.k_norms = g.k_norms;
+  a.v_codes = g.v_codes;
+  a.v_norms = g.v_norms;
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.B = batch;
+  a.C = chunk_len;
+  a.Hq = num_q_heads;
+  a.Hkv = g.num_kv_heads;
+  a.G = num_q_heads / g.num_kv_heads;
+  a.TQ = kColsP / a.G;
+  a.tiles = (chunk_len + a.TQ - 1) / a.TQ;
+  a.page_table = page_table;
+  a.max_pages = max_pages_per_seq;
+  a.prefix_lens = prefix_lens;
+  a.scale_log2 = softmax_scale * kLog2eP;
+  a.kcb = (const unsigned char *)k_cb;
+  a.vcb = (const unsigned char *)v_cb;
+  a.ko = g.kcb;
+  a.vo = g.vcb;
+  a.out = out;
+  const int64_t items = (int64_t)a.tiles * a.Hkv * batch;
+  if (items > 0x7FFFFFFF) return TQ_EINVAL;
+  const dim3 grid((unsigned)items);
+  const bool ok = g.head_dim == 128 ? prefill_dispatch<128>(g.k_mse_bits, g.v_mse_bits, a, grid, stream)
+                                    : prefill_dispatch<64>(g.k_mse_bits, g.v_mse_bits, a, grid, stream);
+  if (!ok) return TQ_ENOTSUP;
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+}  // namespace tq

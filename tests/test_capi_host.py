@@ -279,3 +279,31 @@ def test_qr_argument_errors_need_no_gpu():
         bad = list(a)
         bad[i] = val
         assert lib.tq_decode_attention_qr(*bad) == want, (i, val)
+
+
+def test_prefill_argument_errors_need_no_gpu():
+    lib = tq._lib()
+    L = tq.Layout(128, 8, 4, 0, 2, 0).c()
+    # (layout, pages, num_pages, q, q_dtype, B, C, Hq, pt, maxp, prefix_lens, scale, k_cb, v_cb, out, stream)
+    a = [ctypes.byref(L), 16, 4, 16, 1, 2, 64, 32, 16, 100, 16, 0.1, 16, 16, 16, None]
+    for i, val, want in ((4, 9, -1), (5, -1, -1), (6, -1, -1), (7, 30, -1), (7, 8 * 17, -3), (9, 0, -1), (2, 0, -1),
+                         (11, float("nan"), -1), (11, -1.0, -1), (1, None, -1), (3, None, -1), (8, None, -1),
+                         (10, None, -1), (12, None, -1), (13, None, -1), (14, None, -1), (1, 24, -1), (12, 24, -1),
+                         (3, 17, -1), (14, 18, -1)):
+        bad = list(a)
+        bad[i] = val
+        assert lib.tq_prefill_attention(*bad) == want, (i, val)
+    for i in (5, 6):  # an empty batch or chunk launches nothing
+        empty = list(a)
+        empty[i] = 0
+        assert lib.tq_prefill_attention(*empty) == 0
+    prod = tq.Layout(128, 8, 2, 1, 2, 0).c()
+    assert lib.tq_prefill_attention(ctypes.byref(prod), *a[1:]) == -3
+    # (layout, pages, num_pages, k, v, kv_dtype, slots, q, q_dtype, B, C, Hq, pt, maxp, prefix_lens, scale, k_cb,
+    #  v_cb, out, stream): the quantize arguments are checked before anything is launched too
+    c = [ctypes.byref(L), 16, 4, 16, 16, 1, 16, 16, 1, 2, 64, 32, 16, 100, 16, 0.1, 16, 16, 16, None]
+    for i, val, want in ((5, 9, -1), (3, None, -1), (4, 24, -1), (6, None, -1), (8, 9, -1), (11, 30, -1),
+                         (18, None, -1)):
+        bad = list(c)
+        bad[i] = val
+        assert lib.tq_prefill_chunk(*bad) == want, (i, val)

@@ -1,0 +1,181 @@
+"""Chunked prefill through the C ABI against the oracle's causal chunk attention.
+
+  tq_prefill_chunk      the chunk's records byte-identical to tq_quantize_kv of the same tokens, and its
+                        attention output against the oracle run on the GPU's own pool (max relative error
+                        per row <= 2e-3, the decode bar)
+  tq_prefill_attention  the same attention over a cache written beforehand; ragged chunks (several
+                        work-groups and a partial last one), prefixes that end inside a page or a page pair,
+                        no prefix, GQA group sizes 1 to 16, d = 64 and 128, code widths 1 to 8, f32 / bf16 /
+                        f16 queries, a shuffled page table, and the 8B layer at full length (sampled rows)
+"""
+import math
+
+import numpy as np
+import pytest
+
+import kvsynth
+from oracle import attention
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(H, d, Hq, B, prefix, C, fmt, seed, q_dtype="bf16", recipe="lognormal"):
+    """A device pool holding each sequence's prefix, the chunk's K/V/q and the oracle's codebooks. The default
+    recipe plants a zero key, a zero value and a 300x key among the first tokens."""
+    import torch
+    import kv_cache_quantization_wht_amd as tq
+
+    kb, km, vb, vm = fmt
+    layout, Lo = parity.make_layout(H, d, kb, km, vb, vm)
+    kcb, cbk = parity.device_codebook(d, kb, km, seed)
+    vcb, cbv = parity.device_codebook(d, vb, vm, seed + 1)
+    npp = max(1, max((p + C + 15) // 16 for p in prefix))
+    pt, npages = kvsynth.page_table(B, npp, True, seed=seed + 4, extra_pages=1)
+    pages = torch.full((npages * Lo["page_bytes"],), 0x5A, dtype=torch.uint8, device="cuda")
+    for b in range(B):
+        if prefix[b]:
+            k, v = parity.seeded_kv(prefix[b], H, d, seed=seed * 10 + b, recipe=recipe)
+            tq.quantize_kv(layout, pages, k.cuda(), v.cuda(), torch.from_numpy(kvsynth.slots_for(pt, b, 0, prefix[b])).cuda(),
+                           kcb, vcb)
+    kc, vc = parity.seeded_kv(B * C, H, d, seed=seed * 10 + 9, recipe=recipe)
+    kc, vc = kc.reshape(B, C, H, d).contiguous(), vc.reshape(B, C, H, d).contiguous()
+    slots = np.concatenate([kvsynth.slots_for(pt, b, prefix[b], prefix[b] + C) for b in range(B)])
+    g = torch.Generator().manual_seed(seed + 5)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[q_dtype]
+    q = torch.randn(B, C, Hq, d, generator=g).to(tdt)
+    return dict(layout=layout, Lo=Lo, kcb=kcb, vcb=vcb, cbk=cbk, cbv=cbv, pt=pt, pages=pages, kc=kc, vc=vc,
+                slots=slots, q=q, prefix=np.array(prefix, np.int32))
+
+
+def _oracle_error(st, out, scale, rows=None):
+    pool = st["pages"].cpu().numpy()
+    ref = attention.prefill_attention(pool, st["Lo"], st["cbk"], st["cbv"], st["q"].double().numpy(), st["pt"],
+                                      st["prefix"], scale, rows=rows)
+    got = out.cpu().numpy().astype(np.float64)
+    if rows is not None:
+        sel = tuple(np.array(rows).T)
+        got, ref = got[sel], ref[sel]
+    return parity.attention_error(got, ref)
+
+
+CASES = [  # name, H, d, Hq, B, prefix, C
+    ("d128-gqa4", 2, 128, 8, 2, [0, 37], 150),
+    ("d128-gqa8-long", 1, 128, 8, 1, [333], 40),
+    ("d64-gqa4", 2, 64, 8, 2, [16, 31], 70),
+    ("d128-mha", 3, 128, 3, 1, [50], 300),
+    ("d64-gqa16", 1, 64, 16, 2, [5, 64], 21),
+    ("d128-gqa2-onetoken", 2, 128, 4, 3, [0, 1, 90], 1),
+]
+FORMATS = [(4, 0, 2, 0), (3, 0, 3, 0), (8, 0, 8, 0), (1, 0, 4, 0), (2, 0, 1, 0)]
+
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=[f"k{f[0]}v{f[2]}" for f in FORMATS])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_prefill_chunk_matches_oracle(case, fmt):
+    import torch
+    import kv_cache_quantization_wht_amd as tq
+
+    name, H, d, Hq, B, prefix, C = case
+    print(f"prefill {name} fmt {fmt}", flush=True)
+    st = _setup(H, d, Hq, B, prefix, C, fmt, seed=len(name) + 3 * fmt[0] + fmt[2])
+    scale = 1.0 / math.sqrt(d)
+    two = st["pages"].clone()  # the same prefix; the chunk written by tq_quantize_kv alone
+    out = tq.prefill_chunk(st["layout"], st["pages"], st["kc"].cuda(), st["vc"].cuda(),
+                           torch.from_numpy(st["slots"]).cuda(), st["q"].cuda(), torch.from_numpy(st["pt"]).cuda(),
+                           torch.from_numpy(st["prefix"]).cuda(), scale, st["kcb"], st["vcb"])
+    tq.quantize_kv(st["layout"], two, st["kc"].reshape(B * C, H, d).cuda(), st["vc"].reshape(B * C, H, d).cuda(),
+                   torch.from_numpy(st["slots"]).cuda(), st["kcb"], st["vcb"])
+    torch.cuda.synchronize()
+    assert torch.equal(st["pages"], two), "the chunk's records differ from tq_quantize_kv's"
+    assert torch.isfinite(out).all()
+    err = _oracle_error(st, out, scale)
+    print(f"  max relative error {err:.2e}", flush=True)
+    assert err <= parity.ATTN_TOL
+
+
+@pytest.mark.parametrize("q_dtype", ["f32", "f16"])
+def test_prefill_attention_query_dtypes(q_dtype):
+    """tq_prefill_attention over a cache written beforehand, f32 and f16 queries, a softmax scale of 0
+    (uniform weights over every visible token) and a large one. No planted zero value here: with a large
+    scale a row whose winning key has a zero value has an output of ~1e-9 of the values' size, made of weights
+    below the fp16 range of the value operand (flushed in the kernel, as in decode), and a relative error of
+    such a row measures nothing."""
+    import torch
+    import kv_cache_quantization_wht_amd as tq
+
+    st = _setup(2, 128, 8, 2, [20, 47], 97, (4, 0, 2, 0), seed=31, q_dtype=q_dtype, recipe="plain")
+    B, C, H, d = st["kc"].shape
+    tq.quantize_kv(st["layout"], st["pages"], st["kc"].reshape(B * C, H, d).cuda(),
+                   st["vc"].reshape(B * C, H, d).cuda(), torch.from_numpy(st["slots"]).cuda(), st["kcb"], st["vcb"])
+    for scale in (0.0, 1.0 / math.sqrt(d), 0.5):
+        print(f"prefill q {q_dtype} scale {scale}", flush=True)
+        out = tq.prefill_attention(st["layout"], st["pages"], st["q"].cuda(), torch.from_numpy(st["pt"]).cuda(),
+                                   torch.from_numpy(st["prefix"]).cuda(), scale, st["kcb"], st["vcb"])
+        torch.cuda.synchronize()
+        err = _oracle_error(st, out, scale)
+        print(f"  max relative error {err:.2e}", flush=True)
+        assert err <= parity.ATTN_TOL
+
+
+def test_prefill_rows_match_decode():
+    """Row i of a chunk against tq_decode_attention of the same query at length P + i + 1 (both from the same
+    pool; the two kernels order their sums differently, so the bar is the oracle's)."""
+    import torch
+    import kv_cache_quantization_wht_amd as tq
+
+    st = _setup(2, 128, 8, 1, [61], 40, (4, 0, 2, 0), seed=41)
+    B, C, H, d = st["kc"].shape
+    tq.quantize_kv(st["layout"], st["pages"], st["kc"].reshape(B * C, H, d).cuda(),
+                   st["vc"].reshape(B * C, H, d).cuda(), torch.from_numpy(st["slots"]).cuda(), st["kcb"], st["vcb"])
+    scale = 1.0 / math.sqrt(d)
+    pt = torch.from_numpy(st["pt"]).cuda()
+    out = tq.prefill_attention(st["layout"], st["pages"], st["q"].cuda(), pt, torch.from_numpy(st["prefix"]).cuda(),
+                               scale, st["kcb"], st["vcb"])
+    qd = st["q"][0].cuda().contiguous()  # [C, Hq, d]: one decode row per chunk token
+    lens = torch.tensor(61 + 1 + np.arange(C), dtype=torch.int32, device="cuda")
+    dec = tq.decode_attention(st["layout"], st["pages"], qd, pt.expand(C, -1).contiguous(), lens, scale, st["kcb"],
+                              st["vcb"])
+    torch.cuda.synchronize()
+    err = parity.attention_error(out[0].cpu().numpy(), dec.cpu().numpy().astype(np.float64))
+    print(f"prefill vs decode rows: max relative difference {err:.2e}", flush=True)
+    assert err <= parity.ATTN_TOL
+
+
+def test_prefill_full_size_8b_layer():
+    """The 8B layer (8 KV heads, 32 query heads, d = 128, K4/V2): the last 2048-token chunk of a 32768-token
+    prompt after a 30720-token cached prefix, through tq_prefill_chunk; sampled rows of two KV heads' query
+    heads against the oracle."""
+    import torch
+    import kv_cache_quantization_wht_amd as tq
+
+    wl = kvsynth.workloads()[1]
+    H, Hq, d, T = wl.kv_heads, wl.q_heads, wl.head_dim, wl.seq_len
+    C = 2048
+    P = T - C
+    layout, Lo = parity.make_layout(H, d, 4, 0, 2, 0)
+    kcb, cbk = parity.device_codebook(d, 4, 0, 11)
+    vcb, cbv = parity.device_codebook(d, 2, 0, 12)
+    pt, npages = kvsynth.page_table(1, T // 16, False)
+    pages = torch.zeros(npages * Lo["page_bytes"], dtype=torch.uint8, device="cuda")
+    k, v = kvsynth.make_kv(wl, 1, 0, T, device="cuda")
+    tq.quantize_kv(layout, pages, k[:P], v[:P], torch.from_numpy(kvsynth.slots_for(pt, 0, 0, P)).cuda(), kcb, vcb)
+    g = torch.Generator(device="cuda").manual_seed(9)
+    q = torch.randn(1, C, Hq, d, generator=g, device="cuda").to(torch.bfloat16)
+    print("prefill full size: chunk of 2048 after 30720 cached tokens", flush=True)
+    out = tq.prefill_chunk(layout, pages, k[P:].unsqueeze(0).contiguous(), v[P:].unsqueeze(0).contiguous(),
+                           torch.from_numpy(kvsynth.slots_for(pt, 0, P, T)).cuda(), q, torch.from_numpy(pt).cuda(),
+                           torch.tensor([P], dtype=torch.int32, device="cuda"), wl.softmax_scale, kcb, vcb)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    pool = pages.cpu().numpy()
+    rng = np.random.default_rng(4)
+    rows = sorted(set([0, 1, 31, 32, C - 1] + rng.integers(0, C, 6).tolist()))
+    qn = q.double().cpu().numpy()
+    G = Hq // H
+    ref = attention.prefill_attention(pool, Lo, cbk, cbv, qn, pt, [P], wl.softmax_scale, rows=[(0, i) for i in rows])
+    for kvh in (0, 5):
+        hs = slice(kvh * G, (kvh + 1) * G)
+        err = parity.attention_error(out.cpu().numpy()[0, rows, hs].astype(np.float64), ref[0, rows, hs])
+        print(f"  KV head {kvh}: rows {rows}: max relative error {err:.2e}", flush=True)
+        assert err <= parity.ATTN_TOL, (kvh, err)
