@@ -27,6 +27,7 @@
 #include "tq_common.h"
 #include "tq_internal.h"
 #include "tq_lanes.h"
+#include "tq_operands.h"
 
 namespace tq {
 
@@ -58,19 +59,6 @@ constexpr float kLog2eP = 1.4426950408889634f;
 constexpr float kHeadroomP = 4.0f;    // log2 units between a column's running maximum and its weight reference
 
 typedef _Float16 half4p_t __attribute__((ext_vector_type(4)));
-
-// Largest power of two sigma with max|x| * sigma < 256 (1 if x is all zero).
-__device__ __forceinline__ float range_factor_p(float maxabs) {
-  if (!(maxabs > 0.f)) return 1.0f;
-  int e;
-  frexpf(maxabs, &e);
-  return ldexpf(1.0f, 8 - e);
-}
-
-__device__ __forceinline__ void split_hi_lo_p(float x, _Float16 &hi, _Float16 &lo) {
-  hi = (_Float16)x;
-  lo = (_Float16)(x - (float)hi);
-}
 
 // LDS of one work-group: the double-buffered level tiles of a step, or (prologue, epilogue) one
 // [16][D + 4] fp32 staging block per wavefront.
@@ -137,8 +125,15 @@ __device__ __forceinline__ uint32_t field(const uint32_t (&w)[NW], int bit) {
   return __builtin_amdgcn_alignbit(hi, lo, s) & ((1u << NB) - 1u);
 }
 
+// Coordinate (inside its 8-coordinate group) of K-tile position p: 4-bit codes are looked up eight at a time
+// in the MFMA order of lut_k4, the other widths are stored in coordinate order.
+template <int KB>
+__device__ __forceinline__ constexpr int kpos(int p) {
+  return KB == 4 ? k_order<4>(p) : p;
+}
+
 template <int D, int KB, int VB>
-__global__ __launch_bounds__(kThreadsP, D == 128 ? 1 : 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreadsP, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int KBLK = D / 32;  // 32-coordinate blocks of the score contraction
   constexpr int NB = D / 16;    // 16-coordinate blocks of the value contraction
   constexpr int KREC = D * KB / 8;
@@ -250,7 +245,7 @@ __global__ __launch_bounds__(kThreadsP, D == 128 ? 1 : 2) void prefill_kernel(Pr
         const float mx = wave_max(fmaxf(fabsf(y0), D == 128 ? fabsf(y1) : 0.f), lane);
         st[r][lane] = y0;
         if (D == 128) st[r][lane + 64] = y1;
-        if (lane == 0) s_sig[wave][r] = range_factor_p(mx);
+        if (lane == 0) s_sig[wave][r] = range_factor(mx);
       }
       __syncthreads();
       {
@@ -265,13 +260,15 @@ __global__ __launch_bounds__(kThreadsP, D == 128 ? 1 : 2) void prefill_kernel(Pr
           const float4 u0 = *(const float4 *)&st[c][32 * kb + 8 * g4];
           const float4 u1 = *(const float4 *)&st[c][32 * kb + 8 * g4 + 4];
           const float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+          half8_t lo8;
 #pragma unroll
           for (int p = 0; p < 8; ++p) {
             _Float16 h, l;
-            split_hi_lo_p(real ? v[p] * sig : 0.f, h, l);
+            split_hi_lo(real ? v[kpos<KB>(p)] * sig : 0.f, h, l);
             qhi[nq][kb][p] = h;
-            qlo[nq][kb][p] = l;
+            lo8[p] = l;
           }
+          qlo[nq][kb] = lo8;
         }
       }
       __syncthreads();  // the staging block is rewritten by the next block (and then by the level tiles)
@@ -281,6 +278,9 @@ __global__ __launch_bounds__(kThreadsP, D == 128 ? 1 : 2) void prefill_kernel(Pr
   const int first_pos = P + i0;
 
   // ---- 2. the key steps
+  Tab tk{0, 0, 0, 0}, tv{0, 0, 0, 0};
+  if constexpr (KB == 4) tk = make_tab_k4(s_lutk);
+  if constexpr (VB == 2) tv = make_tab_v2(s_lutv);
   // thread roles of the loads: K codes of key kk (page kq = wave / 2), coordinate chunk kc; V codes of
   // piece vp, slot group vg, coordinates 8 vp + CPT vh .. of page vq = wave / 2; norms (waves 0 and 2,
   // lanes 0..31): K (lanes < 16) or V norm of slot lane % 16 of page wave / 2
@@ -307,8 +307,12 @@ __global__ __launch_bounds__(kThreadsP, D == 128 ? 1 : 2) void prefill_kernel(Pr
     rg.norm = norm_lane ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, n_off & ~1u, 0, 0) : 0u;
   };
   auto store_step = [&](int buf, const R &rg) {
-    // K: D / 8 levels of key kk (the codes first shifted down to bit 0, so every field offset is fixed)
-    {
+    // K: D / 8 levels of key kk (4-bit codes: byte-table lookups, eight at a time; other widths: the codes
+    // shifted down to bit 0, so every field offset is fixed, and one table read each)
+    if constexpr (KB == 4) {
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) *(half8_t *)&lds.t.k[buf][kk][kc * (D / 8) + 8 * i] = lut_k4(rg.kw[i], tk);
+    } else {
       uint32_t kw[R::KW];
 #pragma unroll
       for (int i = 0; i < R::KW; ++i)
@@ -327,8 +331,16 @@ __global__ __launch_bounds__(kThreadsP, D == 128 ? 1 : 2) void prefill_kernel(Pr
         *(half8_t *)&lds.t.k[buf][kk][kc * (D / 8) + 8 * i] = t;
       }
     }
-    // V: CPT coordinates of piece vp for slots 4 vg .. 4 vg + 3 of page pq
-    {
+    // V: CPT coordinates of piece vp for slots 4 vg .. 4 vg + 3 of page pq (2-bit codes: slots 0, 1 and 2, 3
+    // of a coordinate looked up as pairs)
+    if constexpr (VB == 2) {
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) {
+        const int ci = CPT * vh + e;
+        *(uint2 *)&lds.t.v[buf][8 * vp + ci][8 * vg + 4 * pq] =
+            uint2{lut_v2_pair(rg.vw[0] >> (2 * ci), tv), lut_v2_pair(rg.vw[1] >> (2 * ci), tv)};
+      }
+    } else {
       uint32_t w[VB];
 #pragma unroll
       for (int i = 0; i < VB; ++i) w[i] = rg.vw[i];
@@ -359,9 +371,9 @@ __global__ __launch_bounds__(kThreadsP, D == 128 ? 1 : 2) void prefill_kernel(Pr
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) O[nq][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  // one step of 32 keys from buffer buf: FULL = every key visible to every column and in a valid page
-  auto compute = [&](int buf, int s, bool ok0, bool ok1, auto full_tag) {
-    constexpr bool FULL = decltype(full_tag)::value;
+  // one step of 32 keys from buffer buf (full: every key visible to every column and in a valid page). One
+  // body for both cases: a second, unmasked copy raises the register pressure past two work-groups per CU.
+  auto compute = [&](int buf, int s, bool ok0, bool ok1, bool full) {
     floatx4_t acc[2][2];
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2)
@@ -394,7 +406,8 @@ __global__ __launch_bounds__(kThreadsP, D == 128 ? 1 : 2) void prefill_kernel(Pr
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           sc[q2][j] = fmaf((float)nk[q2][j], acc[q2][nq][j], 0.f);  // score / (softmax scale * log2 e)
-          if constexpr (!FULL) {
+          okm[q2][j] = true;
+          if (!full) {
             const int t = kStepKeys * s + 16 * q2 + 4 * g4 + j;
             okm[q2][j] = (q2 ? ok1 : ok0) && t <= lim[nq];
             sc[q2][j] = okm[q2][j] ? sc[q2][j] : -3.0e38f;
@@ -419,7 +432,7 @@ __global__ __launch_bounds__(kThreadsP, D == 128 ? 1 : 2) void prefill_kernel(Pr
         for (int j = 0; j < 4; j += 2) {
           float p0 = fast_exp2(fmaf(sc[q2][j], colscale[nq], -m_run[nq]));
           float p1 = fast_exp2(fmaf(sc[q2][j + 1], colscale[nq], -m_run[nq]));
-          if constexpr (!FULL) {
+          if (!full) {
             p0 = okm[q2][j] ? p0 : 0.f;
             p1 = okm[q2][j + 1] ? p1 : 0.f;
           }
@@ -458,8 +471,7 @@ __global__ __launch_bounds__(kThreadsP, D == 128 ? 1 : 2) void prefill_kernel(Pr
       if (more) load_step(pid_nxt[pq], rg);
       const int pid_after[2] = {page_id(2 * s + 4), page_id(2 * s + 5)};
       const bool full = ok0 && ok1 && kStepKeys * (s + 1) <= first_pos + 1;
-      if (full) compute(s & 1, s, ok0, ok1, std::true_type{});
-      else compute(s & 1, s, ok0, ok1, std::false_type{});
+      compute(s & 1, s, ok0, ok1, full);
       if (more) store_step((s + 1) & 1, rg);
       __syncthreads();
       pid_cur[0] = pid_nxt[0];
