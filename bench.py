@@ -365,7 +365,7 @@ def prefill_leg(wl, layout, pages, page_table, k_pre, v_pre, kcb, vcb, chunk=204
             "tokens_per_s": round(chunk / t_fused, 1),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
                          "frac": round(tflops / peak, 4), "traffic": None, "flops_per_launch": flops,
-                         "kernel": "prefill_kernel<128,4,2> (tq_prefill_attention)", "mfma_issue_factor": 2},
+                         "kernel": "prefill_kernel<128,4,false,2> (tq_prefill_attention)", "mfma_issue_factor": 2},
             "what": "tq_prefill_attention / tq_prefill_chunk of the last 2048 prompt tokens of the 8B layer, "
                     "HIP events around a graph of 8 launches"}
 

@@ -272,7 +272,8 @@ int tq_decode_combine(const tq_layout *layout, const void *pages, int64_t num_pa
  *   prefix_lens  device int32 [batch]: cached tokens ahead of the chunk (negative values count as 0)
  *   out          device fp32 [batch][chunk_len][num_q_heads][head_dim] (written); a row that sees no
  *                key (every visible page empty) is zero
- * K and V must be in MSE mode (prod mode: TQ_ENOTSUP) and num_q_heads / num_kv_heads <= 16.
+ * K may be in either mode (a sketched K adds the QJL term to every score, as in decode); V must be in MSE
+ * mode (prod-mode V: TQ_ENOTSUP, as in decode); num_q_heads / num_kv_heads <= 16.
  * Errors: TQ_EINVAL (layout, dtype, shapes, null or misaligned pointers: pages and the codebooks
  * 16-byte aligned, q and out element-aligned), TQ_ENOTSUP, TQ_EHIP. batch or chunk_len 0 launches
  * nothing. */

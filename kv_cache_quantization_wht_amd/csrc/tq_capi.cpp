@@ -475,14 +475,14 @@ static int prefill_check(const tq_layout *layout, tq::PageGeom *g, const void *p
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return TQ_EINVAL;
   if (batch < 0 || chunk_len < 0 || num_q_heads < 1 || num_q_heads % g->num_kv_heads) return TQ_EINVAL;
   if (num_q_heads / g->num_kv_heads > 16) return TQ_ENOTSUP;
-  if (g->k_mode != TQ_MSE || g->v_mode != TQ_MSE) return TQ_ENOTSUP;
+  if (g->v_mode != TQ_MSE) return TQ_ENOTSUP;
   if (max_pages_per_seq < 1 || max_pages_per_seq > (1 << 26) || num_pages < 1) return TQ_EINVAL;
   if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return TQ_EINVAL;
   if (batch == 0 || chunk_len == 0) return TQ_OK;
   if (!pages || !q || !page_table || !prefix_lens || !k_cb || !v_cb || !out) return TQ_EINVAL;
   if (((uintptr_t)pages | (uintptr_t)k_cb | (uintptr_t)v_cb) & 15) return TQ_EINVAL;
   if (((uintptr_t)q & (q_dtype == TQ_F32 ? 3 : 1)) || ((uintptr_t)out & 3)) return TQ_EINVAL;
-  const int64_t tiles = ((int64_t)chunk_len * (num_q_heads / g->num_kv_heads) + 127) / 128 + 1;
+  const int64_t tiles = ((int64_t)chunk_len * (num_q_heads / g->num_kv_heads) + 63) / 64 + 1;  // 64 or 128 columns
   if (tiles * g->num_kv_heads * batch > 0x7FFFFFFF) return TQ_EINVAL;
   return TQ_OK;
 }

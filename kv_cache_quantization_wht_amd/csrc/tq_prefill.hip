@@ -5,17 +5,18 @@
 //
 // A chunk of C new tokens of each sequence, at positions P_b .. P_b + C - 1, attends causally to the cached
 // tokens 0 .. its own position (its own keys and values already written to the pages, quantized). Where the
-// decode kernel gives every byte of a page to G query heads, here a work-group owns 128 query columns - the
-// (token, head) pairs of 128 / G consecutive tokens of one KV head - so one dequantization serves 128 columns
-// and the contraction runs on the matrix cores:
+// decode kernel gives every byte of a page to G query heads, here a work-group owns 128 query columns (64 with a
+// sketched K) - the (token, head) pairs of 128 / G consecutive tokens of one KV head - so one dequantization
+// serves all of them and the contraction runs on the matrix cores:
 //   1. Query rotation as in decode (signs, Walsh-Hadamard butterflies, 1/d, a power-of-two range factor per
 //      column), the fp16 hi and lo parts of each column kept in registers as MFMA operands.
 //   2. Steps of 32 keys (two pages). All 256 threads load the next step's codes and norms while the
 //      wavefronts compute this one, then look the codes up in the level tables and store fp16 levels in a
 //      double-buffered LDS tile: K as [key][coordinate], V as [coordinate][key] in the key order of the
 //      softmax operand. One barrier per step.
-//        scores  S^T[16 keys, 16 columns] = Khat Q on MFMA 16x16x32 f16 (hi and lo query parts), times the
-//                key norms; causal mask per column where the step reaches past a column's position;
+//        scores  S^T[16 keys, 16 columns] = Khat Q on MFMA 16x16x32 f16 (hi and lo query parts), plus for a
+//                sketched K gamma * <q_s, z> from a second tile of the keys' sketch signs, times the key norms;
+//                causal mask per column where the step reaches past a column's position;
 //        softmax running maximum per column (base 2), sums per lane;
 //        values  O^T[coordinates, columns] += Vhat^T P'^T with P' = p * ||v|| as fp16 hi + lo.
 //   3. Each column's sums divided by its total weight, the inverse rotation by butterflies, fp32 rows out.
@@ -36,9 +37,10 @@ struct PrefillArgs {
   int num_pages32;  // min(num_pages, INT32_MAX)
   int64_t page_bytes;
   int64_t k_codes, k_norms, v_codes, v_norms;
+  int64_t k_qjl, k_gamma;  // prod-mode K: sketch bits and residual norms
   const void *q;  // [B][C][Hq][D]
   int q_dtype;
-  int B, C, Hq, Hkv, G, TQ;  // TQ: query tokens per work-group (128 / G)
+  int B, C, Hq, Hkv, G, TQ;  // TQ: query tokens per work-group (query columns per work-group / G)
   int tiles;                 // work-groups along the chunk (ceil(C / TQ))
   const int32_t *page_table;
   int max_pages;
@@ -53,7 +55,12 @@ namespace {
 
 constexpr int kWavesP = 4;
 constexpr int kThreadsP = 64 * kWavesP;
-constexpr int kColsP = 32 * kWavesP;  // query columns per work-group: two 16-column blocks per wavefront
+constexpr int kBlocksPerCU = 2;       // work-groups per CU the register budget is set for
+
+// 16-column MFMA blocks of query columns per wavefront: two, or one with a sketched K (whose second query
+// operand takes the registers of the second block)
+__host__ __device__ constexpr int col_blocks(bool kprod) { return kprod ? 1 : 2; }
+__host__ __device__ constexpr int cols_per_group(bool kprod) { return 16 * col_blocks(kprod) * kWavesP; }
 constexpr int kStepKeys = 32;         // keys per step: two pages
 constexpr float kLog2eP = 1.4426950408889634f;
 constexpr float kHeadroomP = 4.0f;    // log2 units between a column's running maximum and its weight reference
@@ -62,15 +69,18 @@ typedef _Float16 half4p_t __attribute__((ext_vector_type(4)));
 
 // LDS of one work-group: the double-buffered level tiles of a step, or (prologue, epilogue) one
 // [16][D + 4] fp32 staging block per wavefront.
-template <int D>
+template <int D, bool KPROD>
 struct Tiles {
   _Float16 k[2][kStepKeys][D + 8];  // K levels [key][coordinate]; rows padded so 16 keys hit distinct banks
   _Float16 v[2][D][kStepKeys + 8];  // V levels [coordinate][k'], k' = 8 g + 4 q2 + j <-> key 16 q2 + 4 g + j
   uint16_t nk[2][kStepKeys], nv[2][kStepKeys];  // fp16 norms of the step's keys
+  // sketched K: the sketch as fp16 -1 / +1 [key][coordinate], and the fp16 residual norms
+  _Float16 z[KPROD ? 2 : 1][KPROD ? kStepKeys : 1][D + 8];
+  uint16_t gm[2][kStepKeys];
 };
-template <int D>
+template <int D, bool KPROD>
 union PrefillLds {
-  Tiles<D> t;
+  Tiles<D, KPROD> t;
   float stage[kWavesP][16][D + 4];
 };
 
@@ -83,6 +93,7 @@ struct StepRegs {
   uint32_t kw[KW];
   uint32_t vw[VB];  // 4 slots x VB bytes
   uint32_t norm;
+  uint32_t zb;  // sketched K: the D / 8 sketch bits of the K chunk
 };
 
 // Dwords [off / 4, off / 4 + N) of a page through a buffer resource (zero-size for a missing page).
@@ -132,8 +143,9 @@ __device__ __forceinline__ constexpr int kpos(int p) {
   return KB == 4 ? k_order<4>(p) : p;
 }
 
-template <int D, int KB, int VB>
-__global__ __launch_bounds__(kThreadsP, 2) void prefill_kernel(PrefillArgs a) {
+template <int D, int KB, bool KPROD, int VB>
+__global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(PrefillArgs a) {
+  constexpr int kNQ = col_blocks(KPROD);
   constexpr int KBLK = D / 32;  // 32-coordinate blocks of the score contraction
   constexpr int NB = D / 16;    // 16-coordinate blocks of the value contraction
   constexpr int KREC = D * KB / 8;
@@ -141,7 +153,7 @@ __global__ __launch_bounds__(kThreadsP, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int NH = 8 / CPT;   // threads per (piece, group) of one page
   using R = StepRegs<D, KB, VB>;
 
-  __shared__ __align__(16) PrefillLds<D> lds;
+  __shared__ __align__(16) PrefillLds<D, KPROD> lds;
   __shared__ uint16_t s_lutk[1 << KB], s_lutv[1 << VB];
   __shared__ float s_sig[kWavesP][16];
 
@@ -158,6 +170,7 @@ __global__ __launch_bounds__(kThreadsP, 2) void prefill_kernel(PrefillArgs a) {
     if ((total & 7) == 0) item = (item & 7) * (total >> 3) + (item >> 3);
   }
   const int tile = item % a.tiles;
+  static_assert(!KPROD || D == 128 || D == 64, "head dims");
   const int kvh = (item / a.tiles) % a.Hkv;
   const int b = item / (a.tiles * a.Hkv);
   const int G = a.G;
@@ -179,22 +192,26 @@ __global__ __launch_bounds__(kThreadsP, 2) void prefill_kernel(PrefillArgs a) {
       s_lutv[i] = ((const uint16_t *)(a.vcb + a.vo.levels))[i >= nv / 2 ? i : nv / 2 - 1 - i];
   }
 
-  // ---- 1. query columns: column j = 32 wave + 16 nq + c is token i0 + j / G, head kvh * G + j % G
-  half8_t qhi[2][KBLK], qlo[2][KBLK];
-  float colscale[2];
-  int lim[2];  // last visible key of the lane's column (-1: a column with no query)
+  // ---- 1. query columns: column j = 16 kNQ wave + 16 nq + c is token i0 + j / G, head kvh * G + j % G
+  half8_t qhi[kNQ][KBLK], qlo[kNQ][KBLK];
+  // sketched K: q_s = S (R q) sqrt(pi/2) / m as a second operand, with its own range factor (skratio = the
+  // ratio of the two factors)
+  half8_t shi[KPROD ? kNQ : 1][KPROD ? KBLK : 1], slo[KPROD ? kNQ : 1][KPROD ? KBLK : 1];
+  float skratio[kNQ];
+  float colscale[kNQ];
+  int lim[kNQ];  // last visible key of the lane's column (-1: a column with no query)
   {
     const uint32_t *ksw = (const uint32_t *)(a.kcb + a.ko.signs);
     const bool neg0 = (ksw[lane >> 5] >> (lane & 31)) & 1u;
     const bool neg1 = D == 128 ? ((ksw[(lane + 64) >> 5] >> (lane & 31)) & 1u) : false;
     float(*st)[D + 4] = lds.stage[wave];
 #pragma unroll
-    for (int nq = 0; nq < 2; ++nq) {
+    for (int nq = 0; nq < kNQ; ++nq) {
       // the 16 rows of this block, raw bits, into registers first (independent loads in flight; the dtype
       // is the same for every row, so one branch)
       uint32_t x0[16], x1[16];
       auto row_base = [&](int r, bool &real) {
-        const int j = 32 * wave + 16 * nq + r;
+        const int j = 16 * kNQ * wave + 16 * nq + r;
         const int i = i0 + j / G;
         real = j < a.TQ * G && i < a.C;
         return (((int64_t)b * a.C + (real ? i : 0)) * a.Hq + kvh * G + j % G) * D;
@@ -249,7 +266,7 @@ __global__ __launch_bounds__(kThreadsP, 2) void prefill_kernel(PrefillArgs a) {
       }
       __syncthreads();
       {
-        const int j = 32 * wave + 16 * nq + c;
+        const int j = 16 * kNQ * wave + 16 * nq + c;
         const int i = i0 + j / G;
         const bool real = j < a.TQ * G && i < a.C;
         const float sig = s_sig[wave][c];
@@ -269,6 +286,46 @@ __global__ __launch_bounds__(kThreadsP, 2) void prefill_kernel(PrefillArgs a) {
             lo8[p] = l;
           }
           qlo[nq][kb] = lo8;
+        }
+        skratio[nq] = 0.f;
+        if constexpr (KPROD) {
+          // the lane's 8 * KBLK coordinates j = 32 kb + 8 g4 + p of column c: rows j of S times the column
+          const float *S = (const float *)(a.kcb + a.ko.proj);
+          const float cq = 1.2533141373155003f / (float)a.ko.qjl_rows * (float)D *
+                           (D == 128 ? 0.088388347648318440f : 0.125f);
+          float qs[KBLK][8];
+          float mx = 0.f;
+#pragma unroll
+          for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+              const float4 *srow = (const float4 *)(S + (int64_t)(32 * kb + 8 * g4 + p) * D);
+              float acc = 0.f;
+#pragma unroll 8
+              for (int k4 = 0; k4 < D / 4; ++k4) {
+                const float4 sv = srow[k4];
+                const float4 xv = *(const float4 *)&st[c][4 * k4];
+                acc = fmaf(sv.x, xv.x, fmaf(sv.y, xv.y, fmaf(sv.z, xv.z, fmaf(sv.w, xv.w, acc))));
+              }
+              qs[kb][p] = acc * cq;
+              mx = fmaxf(mx, fabsf(qs[kb][p]));
+            }
+          mx = max_xor32(max_xor16(mx));  // over the four lanes of column c
+          const float sig2 = range_factor(mx);
+          skratio[nq] = real ? sig / sig2 : 0.f;
+#pragma unroll
+          for (int kb = 0; kb < KBLK; ++kb) {
+            half8_t h8, l8;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+              _Float16 h, l;
+              split_hi_lo(real ? qs[kb][p] * sig2 : 0.f, h, l);
+              h8[p] = h;
+              l8[p] = l;
+            }
+            shi[nq][kb] = h8;
+            slo[nq][kb] = l8;
+          }
         }
       }
       __syncthreads();  // the staging block is rewritten by the next block (and then by the level tiles)
@@ -293,9 +350,12 @@ __global__ __launch_bounds__(kThreadsP, 2) void prefill_kernel(PrefillArgs a) {
   const uint32_t k_off_al = k_off & ~3u;
   const int k_bit0 = 8 * (int)(k_off & 3u);
   const uint32_t v_off = (uint32_t)(a.v_codes + ((int64_t)(kvh * (D / 8) + vp) * TQ_PAGE_TOKENS + 4 * vg) * VB);
-  const bool norm_lane = (wave & 1) == 0 && lane < 32;
-  const uint32_t n_off = (uint32_t)((lane < 16 ? a.k_norms : a.v_norms) +
+  // lanes 32..47 of the same wavefronts: the residual norms of a sketched K
+  const bool norm_lane = (wave & 1) == 0 && lane < (KPROD ? 48 : 32);
+  const uint32_t n_off = (uint32_t)((lane < 16 ? a.k_norms : (lane < 32 ? a.v_norms : a.k_gamma)) +
                                     (int64_t)(kvh * TQ_PAGE_TOKENS + (lane & 15)) * 2);
+  const uint32_t z_off = (uint32_t)(a.k_qjl + (int64_t)(kvh * TQ_PAGE_TOKENS + (kk & 15)) * (D / 8)) +
+                         (uint32_t)(kc * (D / 64));
 
   auto page_id = [&](int pi) { return pi < a.max_pages ? ptab[pi] : -1; };
   auto page_ok = [&](int pg) { return pg >= 0 && pg < a.num_pages32; };
@@ -305,6 +365,11 @@ __global__ __launch_bounds__(kThreadsP, 2) void prefill_kernel(PrefillArgs a) {
     load_dwords<R::KW>(r, k_off_al, rg.kw);
     load_dwords<VB>(r, v_off, rg.vw);
     rg.norm = norm_lane ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, n_off & ~1u, 0, 0) : 0u;
+    rg.zb = 0u;
+    if constexpr (KPROD) {
+      if constexpr (D == 128) rg.zb = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, z_off, 0, 0);
+      else rg.zb = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, z_off, 0, 0);
+    }
   };
   auto store_step = [&](int buf, const R &rg) {
     // K: D / 8 levels of key kk (4-bit codes: byte-table lookups, eight at a time; other widths: the codes
@@ -359,33 +424,47 @@ __global__ __launch_bounds__(kThreadsP, 2) void prefill_kernel(PrefillArgs a) {
     if (norm_lane) {
       const int key = 16 * pq + (lane & 15);
       if (lane < 16) lds.t.nk[buf][key] = (uint16_t)rg.norm;
-      else lds.t.nv[buf][key] = (uint16_t)rg.norm;
+      else if (lane < 32) lds.t.nv[buf][key] = (uint16_t)rg.norm;
+      else lds.t.gm[buf][key] = (uint16_t)rg.norm;
+    }
+    if constexpr (KPROD) {
+      // sketch bit set: +1 (0x3C00), clear: -1 (0xBC00), coordinate order
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) {
+        half8_t t;
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+          t[p] = __builtin_bit_cast(_Float16, (uint16_t)(((rg.zb >> (8 * i + p)) & 1u) ? 0x3C00u : 0xBC00u));
+        *(half8_t *)&lds.t.z[buf][kk][kc * (D / 8) + 8 * i] = t;
+      }
     }
   };
 
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_part[2] = {0.f, 0.f};
-  floatx4_t O[2][NB];
+  float m_run[kNQ], l_part[kNQ];
+  floatx4_t O[kNQ][NB];
 #pragma unroll
-  for (int nq = 0; nq < 2; ++nq)
+  for (int nq = 0; nq < kNQ; ++nq) {
+    m_run[nq] = -INFINITY;
+    l_part[nq] = 0.f;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) O[nq][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   // one step of 32 keys from buffer buf (full: every key visible to every column and in a valid page). One
   // body for both cases: a second, unmasked copy raises the register pressure past two work-groups per CU.
   auto compute = [&](int buf, int s, bool ok0, bool ok1, bool full) {
-    floatx4_t acc[2][2];
+    floatx4_t acc[2][kNQ];
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
-      for (int nq = 0; nq < 2; ++nq) acc[q2][nq] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      for (int nq = 0; nq < kNQ; ++nq) acc[q2][nq] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
       for (int kb = 0; kb < KBLK; ++kb) {
         const half8_t A = *(const half8_t *)&lds.t.k[buf][16 * q2 + c][32 * kb + 8 * g4];
 #pragma unroll
-        for (int nq = 0; nq < 2; ++nq) {
+        for (int nq = 0; nq < kNQ; ++nq) {
           acc[q2][nq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qhi[nq][kb], acc[q2][nq], 0, 0, 0);
           acc[q2][nq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qlo[nq][kb], acc[q2][nq], 0, 0, 0);
         }
@@ -396,9 +475,33 @@ __global__ __launch_bounds__(kThreadsP, 2) void prefill_kernel(PrefillArgs a) {
       nk[q2] = *(const half4p_t *)&lds.t.nk[buf][16 * q2 + 4 * g4];
       nv[q2] = *(const half4p_t *)&lds.t.nv[buf][16 * q2 + 4 * g4];
     }
-    half8_t phi[2], plo[2];
+    if constexpr (KPROD) {
+      // the sketch term: <q_s, z> for every key, times gamma and the ratio of the two range factors, joins the
+      // level term before the key norm
 #pragma unroll
-    for (int nq = 0; nq < 2; ++nq) {
+      for (int q2 = 0; q2 < 2; ++q2) {
+        floatx4_t acc2[kNQ];
+#pragma unroll
+        for (int nq = 0; nq < kNQ; ++nq) acc2[nq] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KBLK; ++kb) {
+          const half8_t Z = *(const half8_t *)&lds.t.z[buf][16 * q2 + c][32 * kb + 8 * g4];
+#pragma unroll
+          for (int nq = 0; nq < kNQ; ++nq) {
+            acc2[nq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Z, shi[nq][kb], acc2[nq], 0, 0, 0);
+            acc2[nq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Z, slo[nq][kb], acc2[nq], 0, 0, 0);
+          }
+        }
+        const half4p_t gm = *(const half4p_t *)&lds.t.gm[buf][16 * q2 + 4 * g4];
+#pragma unroll
+        for (int nq = 0; nq < kNQ; ++nq)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[q2][nq][j] = fmaf((float)gm[j] * skratio[nq], acc2[nq][j], acc[q2][nq][j]);
+      }
+    }
+    half8_t phi[kNQ], plo[kNQ];
+#pragma unroll
+    for (int nq = 0; nq < kNQ; ++nq) {
       float sc[2][4];
       bool okm[2][4];
 #pragma unroll
@@ -450,7 +553,7 @@ __global__ __launch_bounds__(kThreadsP, 2) void prefill_kernel(PrefillArgs a) {
     for (int nb = 0; nb < NB; ++nb) {
       const half8_t Vop = *(const half8_t *)&lds.t.v[buf][16 * nb + c][8 * g4];
 #pragma unroll
-      for (int nq = 0; nq < 2; ++nq) {
+      for (int nq = 0; nq < kNQ; ++nq) {
         O[nq][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Vop, phi[nq], O[nq][nb], 0, 0, 0);
         O[nq][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Vop, plo[nq], O[nq][nb], 0, 0, 0);
       }
@@ -487,7 +590,7 @@ __global__ __launch_bounds__(kThreadsP, 2) void prefill_kernel(PrefillArgs a) {
   const bool vneg1 = D == 128 ? ((vsw[(lane + 64) >> 5] >> (lane & 31)) & 1u) : false;
   float(*st)[D + 4] = lds.stage[wave];
 #pragma unroll
-  for (int nq = 0; nq < 2; ++nq) {
+  for (int nq = 0; nq < kNQ; ++nq) {
     const float L = sum_xor16_32(l_part[nq]);
     const float inv = L > 0.f ? 1.0f / L : 0.f;
 #pragma unroll
@@ -496,7 +599,7 @@ __global__ __launch_bounds__(kThreadsP, 2) void prefill_kernel(PrefillArgs a) {
           float4{O[nq][nb][0] * inv, O[nq][nb][1] * inv, O[nq][nb][2] * inv, O[nq][nb][3] * inv};
     __syncthreads();
     for (int r = 0; r < 16; ++r) {
-      const int j = 32 * wave + 16 * nq + r;
+      const int j = 16 * kNQ * wave + 16 * nq + r;
       const int i = i0 + j / G;
       if (!(j < a.TQ * G && i < a.C)) continue;  // wavefront-uniform
       float y0 = st[r][lane];
@@ -528,26 +631,34 @@ __global__ __launch_bounds__(kThreadsP, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <int D, int KB>
+template <int D, int KB, bool KPROD>
 bool prefill_dispatch_v(int vb, const PrefillArgs &a, dim3 grid, hipStream_t s) {
   switch (vb) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<D, KB, 1>), grid, dim3(kThreadsP), 0, s, a); return true;
-    case 2: hipLaunchKernelGGL((prefill_kernel<D, KB, 2>), grid, dim3(kThreadsP), 0, s, a); return true;
-    case 3: hipLaunchKernelGGL((prefill_kernel<D, KB, 3>), grid, dim3(kThreadsP), 0, s, a); return true;
-    case 4: hipLaunchKernelGGL((prefill_kernel<D, KB, 4>), grid, dim3(kThreadsP), 0, s, a); return true;
-    case 8: hipLaunchKernelGGL((prefill_kernel<D, KB, 8>), grid, dim3(kThreadsP), 0, s, a); return true;
+    case 1: hipLaunchKernelGGL((prefill_kernel<D, KB, KPROD, 1>), grid, dim3(kThreadsP), 0, s, a); return true;
+    case 2: hipLaunchKernelGGL((prefill_kernel<D, KB, KPROD, 2>), grid, dim3(kThreadsP), 0, s, a); return true;
+    case 3: hipLaunchKernelGGL((prefill_kernel<D, KB, KPROD, 3>), grid, dim3(kThreadsP), 0, s, a); return true;
+    case 4: hipLaunchKernelGGL((prefill_kernel<D, KB, KPROD, 4>), grid, dim3(kThreadsP), 0, s, a); return true;
+    case 8: hipLaunchKernelGGL((prefill_kernel<D, KB, KPROD, 8>), grid, dim3(kThreadsP), 0, s, a); return true;
     default: return false;
   }
 }
 
 template <int D>
-bool prefill_dispatch(int kb, int vb, const PrefillArgs &a, dim3 grid, hipStream_t s) {
+bool prefill_dispatch(int kb, bool kprod, int vb, const PrefillArgs &a, dim3 grid, hipStream_t s) {
+  if (kprod) {  // MSE parts of a sketched K: 1 to 3 bits
+    switch (kb) {
+      case 1: return prefill_dispatch_v<D, 1, true>(vb, a, grid, s);
+      case 2: return prefill_dispatch_v<D, 2, true>(vb, a, grid, s);
+      case 3: return prefill_dispatch_v<D, 3, true>(vb, a, grid, s);
+      default: return false;
+    }
+  }
   switch (kb) {
-    case 1: return prefill_dispatch_v<D, 1>(vb, a, grid, s);
-    case 2: return prefill_dispatch_v<D, 2>(vb, a, grid, s);
-    case 3: return prefill_dispatch_v<D, 3>(vb, a, grid, s);
-    case 4: return prefill_dispatch_v<D, 4>(vb, a, grid, s);
-    case 8: return prefill_dispatch_v<D, 8>(vb, a, grid, s);
+    case 1: return prefill_dispatch_v<D, 1, false>(vb, a, grid, s);
+    case 2: return prefill_dispatch_v<D, 2, false>(vb, a, grid, s);
+    case 3: return prefill_dispatch_v<D, 3, false>(vb, a, grid, s);
+    case 4: return prefill_dispatch_v<D, 4, false>(vb, a, grid, s);
+    case 8: return prefill_dispatch_v<D, 8, false>(vb, a, grid, s);
     default: return false;
   }
 }
@@ -558,7 +669,8 @@ int launch_prefill(const PageGeom &g, const void *pages, int64_t num_pages, cons
                    int chunk_len, int num_q_heads, const int32_t *page_table, int max_pages_per_seq,
                    const int32_t *prefix_lens, float softmax_scale, const void *k_cb, const void *v_cb, float *out,
                    hipStream_t stream) {
-  if (g.k_mode != TQ_MSE || g.v_mode != TQ_MSE) return TQ_ENOTSUP;
+  if (g.v_mode != TQ_MSE) return TQ_ENOTSUP;
+  const bool kprod = g.k_mode == TQ_PROD;
   PrefillArgs a;
   a.pages = (const unsigned char *)pages;
   a.num_pages32 = (int)std::min<int64_t>(num_pages, 0x7FFFFFFF);
@@ -567,6 +679,8 @@ int launch_prefill(const PageGeom &g, const void *pages, int64_t num_pages, cons
   a.k_norms = g.k_norms;
   a.v_codes = g.v_codes;
   a.v_norms = g.v_norms;
+  a.k_qjl = g.k_qjl;
+  a.k_gamma = g.k_gamma;
   a.q = q;
   a.q_dtype = q_dtype;
   a.B = batch;
@@ -574,7 +688,7 @@ int launch_prefill(const PageGeom &g, const void *pages, int64_t num_pages, cons
   a.Hq = num_q_heads;
   a.Hkv = g.num_kv_heads;
   a.G = num_q_heads / g.num_kv_heads;
-  a.TQ = kColsP / a.G;
+  a.TQ = cols_per_group(kprod) / a.G;
   a.tiles = (chunk_len + a.TQ - 1) / a.TQ;
   a.page_table = page_table;
   a.max_pages = max_pages_per_seq;
@@ -588,8 +702,8 @@ int launch_prefill(const PageGeom &g, const void *pages, int64_t num_pages, cons
   const int64_t items = (int64_t)a.tiles * a.Hkv * batch;
   if (items > 0x7FFFFFFF) return TQ_EINVAL;
   const dim3 grid((unsigned)items);
-  const bool ok = g.head_dim == 128 ? prefill_dispatch<128>(g.k_mse_bits, g.v_mse_bits, a, grid, stream)
-                                    : prefill_dispatch<64>(g.k_mse_bits, g.v_mse_bits, a, grid, stream);
+  const bool ok = g.head_dim == 128 ? prefill_dispatch<128>(g.k_mse_bits, kprod, g.v_mse_bits, a, grid, stream)
+                                    : prefill_dispatch<64>(g.k_mse_bits, kprod, g.v_mse_bits, a, grid, stream);
   if (!ok) return TQ_ENOTSUP;
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP;
 }

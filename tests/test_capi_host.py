@@ -297,8 +297,8 @@ def test_prefill_argument_errors_need_no_gpu():
         empty = list(a)
         empty[i] = 0
         assert lib.tq_prefill_attention(*empty) == 0
-    prod = tq.Layout(128, 8, 2, 1, 2, 0).c()
-    assert lib.tq_prefill_attention(ctypes.byref(prod), *a[1:]) == -3
+    vprod = tq.Layout(128, 8, 4, 0, 3, 1).c()  # a sketched V is not supported (as in decode)
+    assert lib.tq_prefill_attention(ctypes.byref(vprod), *a[1:]) == -3
     # (layout, pages, num_pages, k, v, kv_dtype, slots, q, q_dtype, B, C, Hq, pt, maxp, prefix_lens, scale, k_cb,
     #  v_cb, out, stream): the quantize arguments are checked before anything is launched too
     c = [ctypes.byref(L), 16, 4, 16, 16, 1, 16, 16, 1, 2, 64, 32, 16, 100, 16, 0.1, 16, 16, 16, None]
