@@ -299,6 +299,7 @@ def main():
                                                fmt="fp8")
     if not args.no_prefill:
         result["prefill"] = prefill_leg(wl, layout, pages, page_tables[0], k_pre, v_pre, kcb, vcb)
+        result["prefill_k2qjl"] = prefill_sketched(wl, k_pre, v_pre, sw)
     if not args.no_cpu_baseline:
         first = int(page_tables[0][0, 0].item())
         npg = (T + 15) // 16
@@ -367,6 +368,57 @@ def prefill_leg(wl, layout, pages, page_table, k_pre, v_pre, kcb, vcb, chunk=204
                          "frac": round(tflops / peak, 4), "traffic": None, "flops_per_launch": flops,
                          "kernel": "prefill_kernel<128,4,false,2> (tq_prefill_attention)", "mfma_issue_factor": 2},
             "what": "tq_prefill_attention / tq_prefill_chunk of the last 2048 prompt tokens of the 8B layer, "
+                    "HIP events around a graph of 8 launches"}
+
+
+def prefill_sketched(wl, k_pre, v_pre, sw, chunk=2048, reps=8):
+    """The same chunk over a cache of the layer's K/V with a sketched K (K2 + QJL / V2, prod mode: 1-bit levels and
+    the 1-bit residual sketch): one cache, prefilled by tq_quantize_kv, tq_prefill_attention timed as in
+    prefill_leg. Algorithmic flops: 6 d per (query head, visible key) pair (q.k, the sketch term q_s.z, p.v)."""
+    import torch
+
+    import kvsynth
+    import kv_cache_quantization_wht_amd as tq
+
+    dev = "cuda"
+    H, Hq, d, T = wl.kv_heads, wl.q_heads, wl.head_dim, wl.seq_len
+    P = T - chunk
+    layout = tq.Layout(d, H, 2, 1, 2, 0)
+    S = kvsynth.qjl_projection(kvsynth.rotation_seed(0), d)
+    kcb = torch.from_numpy(tq.build_codebook(d, 2, 1, sw, S)).to(dev)
+    vcb = torch.from_numpy(tq.build_codebook(d, 2, 0, sw)).to(dev)
+    pages = torch.zeros((T // 16) * tq.page_layout(layout)["page_bytes"], dtype=torch.uint8, device=dev)
+    tq.quantize_kv(layout, pages, k_pre, v_pre, torch.arange(T, dtype=torch.int64, device=dev), kcb, vcb)
+    pt = torch.arange(T // 16, dtype=torch.int32, device=dev)[None]
+    g = torch.Generator(device=dev).manual_seed(kvsynth_seed_q())
+    q = torch.randn(1, chunk, Hq, d, generator=g, device=dev).to(torch.bfloat16)
+    prefix = torch.tensor([P], dtype=torch.int32, device=dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+
+    def attn():
+        tq.prefill_attention(layout, pages, q, pt, prefix, wl.softmax_scale, kcb, vcb, out=out)
+
+    attn()
+    torch.cuda.synchronize()
+    gph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gph):
+        for _ in range(reps):
+            attn()
+    gph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    gph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    pairs = chunk * P + chunk * (chunk + 1) // 2
+    flops = 6.0 * d * Hq * pairs
+    log(f"prefill, sketched K (K2+QJL/V2): attention kernel {t * 1e6:.1f} us ({flops / t / 1e12:.0f} TFLOP/s "
+        f"algorithmic)")
+    return {"chunk": chunk, "prefix": P, "attn_us": round(t * 1e6, 2), "tflops": round(flops / t / 1e12, 1),
+            "kernel": "prefill_kernel<128,1,true,2> (tq_prefill_attention)",
+            "what": "tq_prefill_attention of the last 2048 prompt tokens over a K2+QJL/V2 cache of the 8B layer, "
                     "HIP events around a graph of 8 launches"}
 
 
