@@ -48,6 +48,26 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def prefill_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("tq_prefill.hip", "tq_common.h", "tq_lanes.h", "tq_operands.h"):
+        with open(os.path.join(ROOT, "kv_cache_quantization_wht_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_prefill_traffic():
+    """HBM traffic of the K4/V2 prefill kernel from committed rocprofv3 counter runs, if taken on this source."""
+    path = os.path.join(ROOT, "profiles", "prefill_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != prefill_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
 def load_traffic(bytes_per_launch_alg):
     """HBM traffic of the decode kernel from committed rocprofv3 counter runs, if taken on this source."""
     path = os.path.join(ROOT, "profiles", "decode_traffic.json")
@@ -365,7 +385,7 @@ def prefill_leg(wl, layout, pages, page_table, k_pre, v_pre, kcb, vcb, chunk=204
     return {"chunk": chunk, "prefix": P, "attn_us": round(t_attn * 1e6, 2), "chunk_us": round(t_fused * 1e6, 2),
             "tokens_per_s": round(chunk / t_fused, 1),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
-                         "frac": round(tflops / peak, 4), "traffic": None, "flops_per_launch": flops,
+                         "frac": round(tflops / peak, 4), "traffic": load_prefill_traffic(), "flops_per_launch": flops,
                          "kernel": "prefill_kernel<128,4,false,2> (tq_prefill_attention)", "mfma_issue_factor": 2},
             "what": "tq_prefill_attention / tq_prefill_chunk of the last 2048 prompt tokens of the 8B layer, "
                     "HIP events around a graph of 8 launches"}
