@@ -6,8 +6,8 @@
 // A chunk of C new tokens of each sequence, at positions P_b .. P_b + C - 1, attends causally to the cached
 // tokens 0 .. its own position (its own keys and values already written to the pages, quantized). Where the
 // decode kernel gives every byte of a page to G query heads, here a work-group owns 128 query columns (64 with a
-// sketched K) - the (token, head) pairs of 128 / G consecutive tokens of one KV head - so one dequantization
-// serves all of them and the contraction runs on the matrix cores:
+// sketched K) - the (token, head) pairs of 128 / G (64 / G) consecutive tokens of one KV head - so one
+// dequantization serves all of them and the contraction runs on the matrix cores:
 //   1. Query rotation as in decode (signs, Walsh-Hadamard butterflies, 1/d, a power-of-two range factor per
 //      column), the fp16 hi and lo parts of each column kept in registers as MFMA operands.
 //   2. Steps of 32 keys (two pages). All 256 threads load the next step's codes and norms while the
@@ -170,7 +170,6 @@ __global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(Prefil
     if ((total & 7) == 0) item = (item & 7) * (total >> 3) + (item >> 3);
   }
   const int tile = item % a.tiles;
-  static_assert(!KPROD || D == 128 || D == 64, "head dims");
   const int kvh = (item / a.tiles) % a.Hkv;
   const int b = item / (a.tiles * a.Hkv);
   const int G = a.G;
