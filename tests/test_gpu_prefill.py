@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import kvsynth
-from oracle import attention
+from oracle import attention, codec
 from tests import parity
 
 pytestmark = pytest.mark.gpu
@@ -195,3 +195,55 @@ def test_prefill_full_size_8b_layer(kfmt):
         err = parity.attention_error(out.cpu().numpy()[0, rows, hs].astype(np.float64), ref[0, rows, hs])
         print(f"  KV head {kvh}: rows {rows}: max relative error {err:.2e}", flush=True)
         assert err <= parity.ATTN_TOL, (kvh, err)
+
+
+def test_prefill_empty_pages():
+    """Page-table entries < 0 or >= num_pages inside a sequence are empty pages: their tokens get no weight (and
+    the chunk's tokens that fall in them are not written). Reference: the oracle's dequantized records of the tokens
+    of valid pages only, causal, through attention.reference_attention; decode on the same table agrees."""
+    import torch
+    import kv_cache_quantization_wht_amd as tq
+
+    H, d, Hq, P, C = 2, 128, 8, 70, 40
+    fmt = (4, 0, 2, 0)
+    st = _setup(H, d, Hq, 1, [P], C, fmt, seed=61, recipe="plain")
+    npages = st["pages"].numel() // st["Lo"]["page_bytes"]
+    pt = st["pt"].copy()
+    pt[0, 2] = -1       # inside the prefix
+    pt[0, 5] = npages   # inside the chunk (positions 80 .. 95)
+    # rebuild the pool through the edited table: the prefix, then the chunk with tq_prefill_chunk
+    pages = torch.full_like(st["pages"], 0x5A)
+    k, v = parity.seeded_kv(P, H, d, seed=61 * 10, recipe="plain")
+    tq.quantize_kv(st["layout"], pages, k.cuda(), v.cuda(), torch.from_numpy(kvsynth.slots_for(pt, 0, 0, P)).cuda(),
+                   st["kcb"], st["vcb"])
+    slots = kvsynth.slots_for(pt, 0, P, P + C)
+    scale = 1.0 / math.sqrt(d)
+    ptd = torch.from_numpy(pt).cuda()
+    out = tq.prefill_chunk(st["layout"], pages, st["kc"].cuda(), st["vc"].cuda(), torch.from_numpy(slots).cuda(),
+                           st["q"].cuda(), ptd, torch.tensor([P], dtype=torch.int32, device="cuda"), scale, st["kcb"],
+                           st["vcb"])
+    qd = st["q"][0].cuda().contiguous()
+    lens = torch.tensor(P + 1 + np.arange(C), dtype=torch.int32, device="cuda")
+    dec = tq.decode_attention(st["layout"], pages, qd, ptd.expand(C, -1).contiguous(), lens, scale, st["kcb"],
+                              st["vcb"])
+    torch.cuda.synchronize()
+    pool = pages.cpu().numpy()
+    T = P + C
+    t = np.arange(T)
+    valid = (pt[0, t // 16] >= 0) & (pt[0, t // 16] < npages)
+    G = Hq // H
+    q = st["q"][0].double().numpy()
+    ref = np.zeros((C, Hq, d))
+    for g in range(H):
+        tv = t[valid]
+        rk = codec.read_records(pool, st["Lo"], "k", pt[0, tv // 16], tv % 16, g)
+        rv = codec.read_records(pool, st["Lo"], "v", pt[0, tv // 16], tv % 16, g)
+        K = codec.dequantize(rk["codes"], rk["norm16"], st["cbk"])
+        V = codec.dequantize(rv["codes"], rv["norm16"], st["cbv"])
+        for i in range(C):
+            n = int(np.sum(tv <= P + i))
+            ref[i, g * G:(g + 1) * G] = attention.reference_attention(q[i, g * G:(g + 1) * G], K[:n], V[:n], scale)
+    err = floored_error(out[0].cpu().numpy(), ref)
+    err_dec = floored_error(dec.cpu().numpy(), ref)
+    print(f"prefill with empty pages: max relative error {err:.2e} (decode {err_dec:.2e})", flush=True)
+    assert err <= parity.ATTN_TOL and err_dec <= parity.ATTN_TOL
