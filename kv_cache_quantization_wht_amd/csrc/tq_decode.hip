@@ -13,7 +13,8 @@
 //                levels looked up from the codes (v_perm byte tables for 4-bit codes), the Q operand the
 //                hi and lo parts of the G rotated queries (two MFMAs per 32 coordinates);
 //        softmax running max per head (base-2), sums kept per lane;
-//        values  O[rows, d] += P'[rows, 32 tok] Vhat[32 tok, d] with P' = p * ||v|| as fp16 hi + lo and
+//        values  O[rows, d] += P'[rows, 32 tok] Vhat[32 tok, d] with P' = p * ||v|| as fp16 hi + lo (each
+//                column's weights shifted by a power of two that keeps them in the fp16 range) and
 //                Vhat the fp16 V levels (v_perm table for 2-bit codes).
 //   3. The wavefronts merge in LDS (fixed-order tree). With one run per (sequence, KV head) the work-group
 //      applies R_V^T once per output (butterflies in LDS) and writes fp32 out; with several runs it writes
@@ -667,6 +668,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   // ---- 3. stream the page pairs
   float m_run = -INFINITY;
   float l_part = 0.f;
+  float ev = 0.f;    // the column's weight shift (power of two), see weight_shift
+  float wmax = 0.f;  // the largest value weight the lane has seen, in the current units
   floatx4_t O[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) O[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -698,6 +701,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         const float p = fast_exp2(-kHeadroom);
         l_part = g4 == 0 ? p : 0.f;
         const float pv = lo_part ? 0.f : p * s_newnorm[1];  // PK: the value enters once, in the high column
+        wmax = p * s_newnorm[1];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -854,47 +858,66 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 
     // online softmax in base 2 (m_run is in units of scale * log2 e); this lane holds head column c,
     // tokens 4*g4 .. 4*g4+3 of both pages
-    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    // m_run is the reference the weights are taken against; it only has to bound the scores seen so
-    // far. When a score passes it, the new reference is set kHeadroom above the new maximum, so the
-    // rescale (which any reference allows: it cancels between the sums and the weights) runs only on
-    // real jumps of the maximum. Weights stay <= 1, the largest >= 2^-kHeadroom.
-    mx = max_xor32(max_xor16(mx));
-    const float m_new = colscale * mx;
-    if (__any(m_new > m_run)) {
+    const float mxl = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                            fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    // m_run bounds the scores seen so far. When a score passes it, the new reference is set kHeadroom above
+    // the new maximum, so the rescale (which any reference allows: it cancels between the sums and the
+    // weights) runs only on real jumps of the maximum. The test is taken on the lane's own scores; the
+    // column's maximum (over its four lanes) only when some lane passes.
+    if (__any(colscale * mxl > m_run)) {
       // O holds head column c in this lane, as do m_run and l_part: the rescale stays in the lane
+      const float m_new = colscale * max_xor32(max_xor16(mxl));
       const bool up = m_new > m_run;
       const float m_ref = up ? m_new + kHeadroom : m_run;
       const float alpha = up ? ((m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_ref)) : 1.f;
       l_part *= alpha;
+      wmax *= alpha;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) O[nb] *= alpha;
       m_run = m_ref;
+    }
+    // weights against the effective reference m_run - ev: p <= 2^ev, value weights P' = p ||v||
+    const float m_eff = m_run - ev;
+    float pv[2][4];
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float p = fast_exp2(fmaf(s[q2][j], colscale, -m_eff));
+        if constexpr (!FULL) p = okm[q2][j] ? p : 0.f;
+        l_part += p;
+        pv[q2][j] = fmaf((float)nv[q2][j], p, 0.f);
+      }
+    }
+    const float pvl = fmaxf(fmaxf(fmaxf(pv[0][0], pv[0][1]), fmaxf(pv[0][2], pv[0][3])),
+                            fmaxf(fmaxf(pv[1][0], pv[1][1]), fmaxf(pv[1][2], pv[1][3])));
+    wmax = fmaxf(wmax, pvl);
+    if (__any(pvl > kWeightHigh || (wmax < kWeightLow && pvl > 0.f))) {
+      const float f = weight_shift(max_xor32(max_xor16(wmax)), ev, wmax);
+      l_part *= f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) O[nb] *= f;
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pv[q2][j] *= f;
     }
     half8_t phi, plo;
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
 #pragma unroll
       for (int j = 0; j < 4; j += 2) {
-        float p0 = fast_exp2(fmaf(s[q2][j], colscale, -m_run));
-        float p1 = fast_exp2(fmaf(s[q2][j + 1], colscale, -m_run));
-        if constexpr (!FULL) {
-          p0 = okm[q2][j] ? p0 : 0.f;
-          p1 = okm[q2][j + 1] ? p1 : 0.f;
-        }
-        l_part += p0 + p1;
-        const float2_t pv = {fmaf((float)nv[q2][j], p0, 0.f), fmaf((float)nv[q2][j + 1], p1, 0.f)};
-        const half2_t h = __builtin_convertvector(pv, half2_t);
+        const float2_t pw = {pv[q2][j], pv[q2][j + 1]};
+        const half2_t h = __builtin_convertvector(pw, half2_t);
         if constexpr (PK) {
           // high column: P' rounded to fp16; low column: what that rounding left out
           const float2_t hf = __builtin_convertvector(h, float2_t);
-          const float2_t t = {fmaf(lo_neg, hf[0], pv[0]), fmaf(lo_neg, hf[1], pv[1])};
+          const float2_t t = {fmaf(lo_neg, hf[0], pw[0]), fmaf(lo_neg, hf[1], pw[1])};
           const half2_t u = __builtin_convertvector(t, half2_t);
           phi[4 * q2 + j] = u[0];
           phi[4 * q2 + j + 1] = u[1];
         } else {
-          const half2_t l = __builtin_convertvector(pv - __builtin_convertvector(h, float2_t), half2_t);
+          const half2_t l = __builtin_convertvector(pw - __builtin_convertvector(h, float2_t), half2_t);
           phi[4 * q2 + j] = h[0];
           phi[4 * q2 + j + 1] = h[1];
           plo[4 * q2 + j] = l[0];
@@ -937,10 +960,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) O[nb][j] += xor_lane<8>(O[nb][j]);
   }
+  // the sums are in units of the effective reference m_run - ev
+  const float m_eff = m_run - ev;
   {
     const float l_tot = sum_xor16_32(l_part);
     if (g4 == 0) {
-      s_m[wave][c] = m_run;
+      s_m[wave][c] = m_eff;
       s_l[wave][c] = l_tot;
     }
   }
@@ -949,7 +974,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][c]);
-    const float e = (M == -INFINITY || m_run == -INFINITY) ? 0.f : fast_exp2(m_run - M);
+    const float e = (M == -INFINITY || m_eff == -INFINITY) ? 0.f : fast_exp2(m_eff - M);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) O[nb] *= e;
   }

@@ -17,6 +17,36 @@ __device__ __forceinline__ float range_factor(float maxabs) {
   return ldexpf(1.0f, 8 - e);
 }
 
+// Range control of the value weights P' = p * ||v||, which enter the value MFMAs as fp16 hi + lo parts. The softmax
+// reference keeps every p <= 1, but a value norm far from 1 (a cache of tiny or huge values, or a winning key whose
+// value is zero, so that the weights that matter are far below 1) would put P' outside the fp16 range. Each column
+// therefore carries a power-of-two shift 2^ev applied to its weights, its softmax sum and its value sums alike (the
+// ratio, the output, does not see it): the effective reference is m_run - ev. A column whose largest weight so far
+// passes 2^14 (fp16 ends below 2^16) or stays under 2^-2 is shifted so that it lies in [2^6, 2^7); hi + lo then
+// carry ~22 bits of every weight within 2^-16 of the column's largest. The upward shift is capped so that
+// 2^ev times the softmax sum stays finite in fp32.
+constexpr float kWeightHigh = 16384.0f;
+constexpr float kWeightLow = 0.25f;
+constexpr int kWeightTopExp = 7;
+constexpr float kWeightShiftCap = 80.0f;
+
+// wcol: the column's largest value weight so far (> 0, the same in every lane of the column). Returns the factor
+// that the column's weights and sums are multiplied by (1 when it is in range), adds its exponent to ev, and sets
+// wmax to the column's largest weight after the shift (at least kWeightLow, so that a column held down by the cap
+// does not ask again on every step).
+__device__ __forceinline__ float weight_shift(float wcol, float &ev, float &wmax) {
+  float f = 1.0f;
+  if (wcol > kWeightHigh || wcol < kWeightLow) {
+    int e;
+    frexpf(wcol, &e);  // wcol in [2^(e-1), 2^e)
+    const float sh = fminf((float)(kWeightTopExp - e), kWeightShiftCap - ev);
+    f = ldexpf(1.0f, (int)sh);
+    ev += sh;
+  }
+  wmax = fmaxf(wcol * f, kWeightLow);
+  return f;
+}
+
 __device__ __forceinline__ void split_hi_lo(float x, _Float16 &hi, _Float16 &lo) {
   hi = (_Float16)x;
   lo = (_Float16)(x - (float)hi);

@@ -18,7 +18,8 @@
 //                sketched K gamma * <q_s, z> from a second tile of the keys' sketch signs, times the key norms;
 //                causal mask per column where the step reaches past a column's position;
 //        softmax running maximum per column (base 2), sums per lane;
-//        values  O^T[coordinates, columns] += Vhat^T P'^T with P' = p * ||v|| as fp16 hi + lo.
+//        values  O^T[coordinates, columns] += Vhat^T P'^T with P' = p * ||v|| as fp16 hi + lo (each column's
+//                weights shifted by a power of two that keeps them in the fp16 range).
 //   3. Each column's sums divided by its total weight, the inverse rotation by butterflies, fp32 rows out.
 #include <hip/hip_runtime.h>
 
@@ -440,11 +441,14 @@ __global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(Prefil
   };
 
   float m_run[kNQ], l_part[kNQ];
+  float ev[kNQ], wmax[kNQ];  // each column's weight shift and largest value weight (see weight_shift)
   floatx4_t O[kNQ][NB];
 #pragma unroll
   for (int nq = 0; nq < kNQ; ++nq) {
     m_run[nq] = -INFINITY;
     l_part[nq] = 0.f;
+    ev[nq] = 0.f;
+    wmax[nq] = 0.f;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) O[nq][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
@@ -515,33 +519,52 @@ __global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(Prefil
             sc[q2][j] = okm[q2][j] ? sc[q2][j] : -3.0e38f;
           }
         }
-      float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-      mx = max_xor32(max_xor16(mx));
-      const float m_new = colscale[nq] * mx;
-      if (__any(m_new > m_run[nq])) {
+      // the lane's own maximum first; the column's (over its four lanes) only when some lane passes m_run
+      const float mxl = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                              fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+      if (__any(colscale[nq] * mxl > m_run[nq])) {
+        const float m_new = colscale[nq] * max_xor32(max_xor16(mxl));
         const bool up = m_new > m_run[nq];
         const float m_ref = up ? m_new + kHeadroomP : m_run[nq];
         const float alpha = up ? ((m_run[nq] == -INFINITY) ? 0.f : fast_exp2(m_run[nq] - m_ref)) : 1.f;
         l_part[nq] *= alpha;
+        wmax[nq] *= alpha;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) O[nq][nb] *= alpha;
         m_run[nq] = m_ref;
+      }
+      // weights against the effective reference m_run - ev, value weights P' = p ||v|| kept in the fp16 range
+      const float m_eff = m_run[nq] - ev[nq];
+      float pv[2][4];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float p = fast_exp2(fmaf(sc[q2][j], colscale[nq], -m_eff));
+          if (!full) p = okm[q2][j] ? p : 0.f;
+          l_part[nq] += p;
+          pv[q2][j] = fmaf((float)nv[q2][j], p, 0.f);
+        }
+      const float pvl = fmaxf(fmaxf(fmaxf(pv[0][0], pv[0][1]), fmaxf(pv[0][2], pv[0][3])),
+                              fmaxf(fmaxf(pv[1][0], pv[1][1]), fmaxf(pv[1][2], pv[1][3])));
+      wmax[nq] = fmaxf(wmax[nq], pvl);
+      if (__any(pvl > kWeightHigh || (wmax[nq] < kWeightLow && pvl > 0.f))) {
+        const float f = weight_shift(max_xor32(max_xor16(wmax[nq])), ev[nq], wmax[nq]);
+        l_part[nq] *= f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) O[nq][nb] *= f;
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pv[q2][j] *= f;
       }
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
         for (int j = 0; j < 4; j += 2) {
-          float p0 = fast_exp2(fmaf(sc[q2][j], colscale[nq], -m_run[nq]));
-          float p1 = fast_exp2(fmaf(sc[q2][j + 1], colscale[nq], -m_run[nq]));
-          if (!full) {
-            p0 = okm[q2][j] ? p0 : 0.f;
-            p1 = okm[q2][j + 1] ? p1 : 0.f;
-          }
-          l_part[nq] += p0 + p1;
-          const float2_t pv = {fmaf((float)nv[q2][j], p0, 0.f), fmaf((float)nv[q2][j + 1], p1, 0.f)};
-          const half2_t h = __builtin_convertvector(pv, half2_t);
-          const half2_t l = __builtin_convertvector(pv - __builtin_convertvector(h, float2_t), half2_t);
+          const float2_t pw = {pv[q2][j], pv[q2][j + 1]};
+          const half2_t h = __builtin_convertvector(pw, half2_t);
+          const half2_t l = __builtin_convertvector(pw - __builtin_convertvector(h, float2_t), half2_t);
           phi[nq][4 * q2 + j] = h[0];
           phi[nq][4 * q2 + j + 1] = h[1];
           plo[nq][4 * q2 + j] = l[0];

@@ -97,18 +97,27 @@ def attention_error(out_gpu, out_ref):
     return attention.relative_error(np.asarray(out_gpu, dtype=np.float64), out_ref)
 
 
-def seeded_kv(n_tok, H, d, seed, recipe="lognormal", dtype="bf16"):
-    """K/V test tensors: log-normal channel scales, a few zero and huge vectors."""
+def seeded_kv(n_tok, H, d, seed, recipe="lognormal", dtype="bf16", v_mult=1.0):
+    """K/V test tensors: K with log-normal channel scales, V unit normal, and by recipe
+      plain      nothing planted
+      zeros      token 3 a zero key, token 4 a zero value
+      lognormal  zeros, and token 5 a key 300x larger
+      vrange     lognormal, and every token's value scaled by its own power of two 2^u, u uniform in [-14, 6]
+    v_mult scales every value (a power of two keeps the inputs exact)."""
     import torch
 
     g = torch.Generator().manual_seed(seed)
     k = torch.randn(n_tok, H, d, generator=g) * torch.exp(torch.randn(H, d, generator=g))
     v = torch.randn(n_tok, H, d, generator=g)
-    if recipe == "lognormal":
+    if recipe in ("zeros", "lognormal", "vrange"):
         if n_tok > 5:
             k[3] = 0.0
             v[4] = 0.0
-            k[5] *= 300.0
+            if recipe != "zeros":
+                k[5] *= 300.0
+    if recipe == "vrange":
+        v *= torch.pow(2.0, torch.randint(-14, 7, (n_tok, 1, 1), generator=g).float())
+    v *= v_mult
     dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
     return k.to(dt), v.to(dt)
 

@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 
 
 def build(H, d, Hq, B, lens, kb, km, vb, vm, seed=0, shuffled=True, dtype="bf16", q_scale=1.0,
-          extra_pages=3, k_mult=1.0, min_pages=0):
+          extra_pages=3, k_mult=1.0, min_pages=0, recipe="lognormal", v_mult=1.0):
     import torch
     import kv_cache_quantization_wht_amd as tq
 
@@ -26,7 +26,7 @@ def build(H, d, Hq, B, lens, kb, km, vb, vm, seed=0, shuffled=True, dtype="bf16"
     for b in range(B):
         if lens[b] == 0:
             continue
-        k, v = parity.seeded_kv(lens[b], H, d, seed=seed * 100 + b, recipe="plain", dtype=dtype)
+        k, v = parity.seeded_kv(lens[b], H, d, seed=seed * 100 + b, recipe=recipe, dtype=dtype, v_mult=v_mult)
         slots = torch.from_numpy(kvsynth.slots_for(pt, b, 0, lens[b])).cuda()
         tq.quantize_kv(layout, pages, (k.float() * k_mult).to(k.dtype).cuda(), v.cuda(), slots, kcb, vcb)
     g = torch.Generator().manual_seed(seed + 77)
@@ -110,11 +110,83 @@ def test_page_table_shuffle_invariance():
 
 
 def test_large_key_norms():
-    """K ~ N(0, 100^2) with V ~ N(0, 1) (norm ratio ~100): very peaked softmax stays within tolerance."""
-    c = build(2, 128, 16, 1, [400], 4, 0, 2, 0, seed=21, k_mult=100.0)
+    """K ~ N(0, 100^2) with V ~ N(0, 1) (norm ratio ~100): very peaked softmax stays within tolerance. (The zero
+    vectors are planted, the 300x key is not: 300 times these keys would pass the fp16 range of the stored norm.)"""
+    c = build(2, 128, 16, 1, [400], 4, 0, 2, 0, seed=21, k_mult=100.0, recipe="zeros")
     scale = 1 / math.sqrt(128)
     out = run_gpu(c, scale)
     assert parity.attention_error(out, run_ref(c, scale)) <= parity.ATTN_TOL
+
+
+VALUE_CASES = [
+    # name, H, d, Hq, B, lens, kb, km, vb, vm, q_scale, recipe, v_mult, pages_per_split
+    ("v-tiny-k4v2", 2, 128, 8, 2, [300, 77], 4, 0, 2, 0, 1.0, "lognormal", 2.0 ** -16, 0),
+    ("v-huge-k4v2", 2, 128, 8, 2, [300, 77], 4, 0, 2, 0, 1.0, "lognormal", 2.0 ** 8, 0),
+    ("v-tiny-k3v3-splits", 2, 128, 8, 1, [700], 3, 0, 3, 0, 1.0, "lognormal", 2.0 ** -16, 4),
+    ("v-tiny-gqa16", 1, 128, 16, 1, [260], 4, 0, 2, 0, 1.0, "lognormal", 2.0 ** -16, 0),
+    ("v-tiny-prod-d64", 2, 64, 8, 2, [90, 200], 2, 1, 2, 0, 1.0, "lognormal", 2.0 ** -16, 0),
+    ("v-range-k4v2", 2, 128, 8, 2, [600, 129], 4, 0, 2, 0, 1.0, "vrange", 1.0, 0),
+    ("v-range-k8v8-peaked", 2, 128, 8, 1, [333], 8, 0, 8, 0, 4.0, "vrange", 1.0, 2),
+    ("v-range-k4v4-gqa16", 1, 128, 16, 1, [400], 4, 0, 4, 0, 1.0, "vrange", 1.0, 0),
+]
+
+
+@pytest.mark.parametrize("case", VALUE_CASES, ids=[c[0] for c in VALUE_CASES])
+def test_value_norm_range(case):
+    """Values uniformly tiny (2^-16) or large (2^8), or of norms spread over 2^-14 .. 2^6 token by token: the value
+    weights p * ||v|| enter the matrix cores as fp16, and each column's power-of-two shift keeps them in range, so
+    every row is within the bar of the oracle and the output scales with V."""
+    name, H, d, Hq, B, lens, kb, km, vb, vm, qs, recipe, vmul, pps = case
+    print(f"value-range case {name}", flush=True)
+    scale = 1.0 / math.sqrt(d)
+    c = build(H, d, Hq, B, lens, kb, km, vb, vm, seed=len(name) + 5, q_scale=qs, recipe=recipe, v_mult=vmul)
+    out = run_gpu(c, scale, pps)
+    ref = run_ref(c, scale)
+    err = parity.attention_error(out, ref)
+    print(f"{name}: max rel err {err:.3e}", flush=True)
+    assert np.all(np.isfinite(out))
+    assert err <= parity.ATTN_TOL
+    if vmul != 1.0:
+        # the same keys and values at scale 1 (a power of two scales the fp16 norms exactly, the codes not at all)
+        one = run_gpu(build(H, d, Hq, B, lens, kb, km, vb, vm, seed=len(name) + 5, q_scale=qs, recipe=recipe), scale,
+                      pps)
+        rel = parity.attention_error(out / vmul, one)
+        print(f"{name}: output / {vmul:g} against the unscaled run {rel:.3e}", flush=True)
+        assert rel <= 1e-5
+
+
+def test_zero_value_winner():
+    """A key far ahead of the others whose value is zero: the output is made of weights ~2^-30 .. 2^-50 of the winner's,
+    which the value shift brings into the fp16 range of the value operand."""
+    import torch
+    import kv_cache_quantization_wht_amd as tq
+
+    H, d, Hq = 2, 128, 8
+    scale = 1 / math.sqrt(d)
+    for lead in (30.0, 50.0):
+        c = build(H, d, Hq, 1, [400], 4, 0, 2, 0, seed=91, recipe="plain")
+        # rewrite token 200 of both KV heads: a key along the mean query direction of its group whose logit is about
+        # `lead` log2 units above the others' largest (~12), value zero; the oracle reads the GPU's own records of it
+        q = c["q"].float()
+        k = torch.zeros(1, H, d)
+        for g in range(H):
+            qm = q[0, g * (Hq // H):(g + 1) * (Hq // H)].mean(0)
+            k[0, g] = qm / qm.norm() * ((lead + 12.0) * math.log(2) / (scale * qm.norm()))
+        v = torch.zeros(1, H, d)
+        slot = int(c["pt"][0, 200 // 16]) * 16 + 200 % 16
+        tq.quantize_kv(c["layout"], c["pages"], k.to(torch.bfloat16).cuda(), v.to(torch.bfloat16).cuda(),
+                       torch.tensor([slot], dtype=torch.int64, device="cuda"), c["kcb"], c["vcb"])
+        torch.cuda.synchronize()
+        c["pool"] = c["pages"].cpu().numpy()
+        for pps in (0, 4):
+            out = run_gpu(c, scale, pps)
+            ref = run_ref(c, scale)
+            err = parity.attention_error(out, ref)
+            size = float(np.abs(ref).max(axis=-1).min())
+            print(f"zero-value winner lead {lead}: smallest row max |o| {size:.2e}, max rel err {err:.3e} (pps {pps})",
+                  flush=True)
+            assert size < 1e-6  # the rows really are made of far-behind weights
+            assert err <= parity.ATTN_TOL
 
 
 def test_zero_softmax_scale_is_uniform_average():

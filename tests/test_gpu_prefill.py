@@ -2,8 +2,8 @@
 
   tq_prefill_chunk      the chunk's records byte-identical to tq_quantize_kv of the same tokens, and its
                         attention output against the oracle run on the GPU's own pool (max relative error
-                        per row <= 2e-3, the decode bar, with a floor of 1e-3 of the case's output scale
-                        under a row's own norm: see floored_error)
+                        per row <= 2e-3, the decode bar), on inputs with a zero key, a zero value and a 300x key
+                        planted, and values tiny, large or spread over 2^-14 .. 2^6 token by token
   tq_prefill_attention  the same attention over a cache written beforehand; ragged chunks (several
                         work-groups and a partial last one), prefixes that end inside a page or a page pair,
                         no prefix, GQA group sizes 1 to 16, d = 64 and 128, code widths 1 to 8, sketched (prod)
@@ -22,7 +22,7 @@ from tests import parity
 pytestmark = pytest.mark.gpu
 
 
-def _setup(H, d, Hq, B, prefix, C, fmt, seed, q_dtype="bf16", recipe="lognormal"):
+def _setup(H, d, Hq, B, prefix, C, fmt, seed, q_dtype="bf16", recipe="lognormal", v_mult=1.0):
     """A device pool holding each sequence's prefix, the chunk's K/V/q and the oracle's codebooks. The default
     recipe plants a zero key, a zero value and a 300x key among the first tokens."""
     import torch
@@ -37,10 +37,10 @@ def _setup(H, d, Hq, B, prefix, C, fmt, seed, q_dtype="bf16", recipe="lognormal"
     pages = torch.full((npages * Lo["page_bytes"],), 0x5A, dtype=torch.uint8, device="cuda")
     for b in range(B):
         if prefix[b]:
-            k, v = parity.seeded_kv(prefix[b], H, d, seed=seed * 10 + b, recipe=recipe)
+            k, v = parity.seeded_kv(prefix[b], H, d, seed=seed * 10 + b, recipe=recipe, v_mult=v_mult)
             tq.quantize_kv(layout, pages, k.cuda(), v.cuda(), torch.from_numpy(kvsynth.slots_for(pt, b, 0, prefix[b])).cuda(),
                            kcb, vcb)
-    kc, vc = parity.seeded_kv(B * C, H, d, seed=seed * 10 + 9, recipe=recipe)
+    kc, vc = parity.seeded_kv(B * C, H, d, seed=seed * 10 + 9, recipe=recipe, v_mult=v_mult)
     kc, vc = kc.reshape(B, C, H, d).contiguous(), vc.reshape(B, C, H, d).contiguous()
     slots = np.concatenate([kvsynth.slots_for(pt, b, prefix[b], prefix[b] + C) for b in range(B)])
     g = torch.Generator().manual_seed(seed + 5)
@@ -48,18 +48,6 @@ def _setup(H, d, Hq, B, prefix, C, fmt, seed, q_dtype="bf16", recipe="lognormal"
     q = torch.randn(B, C, Hq, d, generator=g).to(tdt)
     return dict(layout=layout, Lo=Lo, kcb=kcb, vcb=vcb, cbk=cbk, cbv=cbv, pt=pt, pages=pages, kc=kc, vc=vc,
                 slots=slots, q=q, prefix=np.array(prefix, np.int32))
-
-
-def floored_error(got, ref):
-    """max over rows of ||got - ref||_inf / max(||ref||_inf, 1e-3 * the largest ||ref||_inf of the case): the decode
-    bar, except that a row whose exact output is below a thousandth of the case's output scale - a row whose
-    winning key has a zero value, where the result is made of weights under the fp16 range of the value operand
-    (dropped, in decode as here) - is held to the bar against that floor instead of its own tiny norm."""
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    num = np.abs(got - ref).max(axis=-1)
-    den = np.abs(ref).max(axis=-1)
-    return float(np.max(num / np.maximum(den, 1e-3 * den.max())))
 
 
 def _oracle_error(st, out, scale, rows=None):
@@ -70,7 +58,7 @@ def _oracle_error(st, out, scale, rows=None):
     if rows is not None:
         sel = tuple(np.array(rows).T)
         got, ref = got[sel], ref[sel]
-    return floored_error(got, ref)
+    return parity.attention_error(got, ref)
 
 
 CASES = [  # name, H, d, Hq, B, prefix, C
@@ -111,14 +99,13 @@ def test_prefill_chunk_matches_oracle(case, fmt):
 @pytest.mark.parametrize("q_dtype", ["f32", "f16"])
 def test_prefill_attention_query_dtypes(q_dtype):
     """tq_prefill_attention over a cache written beforehand, f32 and f16 queries, a softmax scale of 0
-    (uniform weights over every visible token) and a large one. No planted zero value here: with a large
-    scale a row whose winning key has a zero value has an output of ~1e-9 of the values' size, made of weights
-    below the fp16 range of the value operand (flushed in the kernel, as in decode), and a relative error of
-    such a row measures nothing."""
+    (uniform weights over every visible token) and a large one, on the planted inputs: with the large scale some
+    rows' winning key has the zero value, and their output (~1e-9 of the values' size) is made of weights far
+    below the winner's, which the value shift keeps in the fp16 range of the value operand."""
     import torch
     import kv_cache_quantization_wht_amd as tq
 
-    st = _setup(2, 128, 8, 2, [20, 47], 97, (4, 0, 2, 0), seed=31, q_dtype=q_dtype, recipe="plain")
+    st = _setup(2, 128, 8, 2, [20, 47], 97, (4, 0, 2, 0), seed=31, q_dtype=q_dtype)
     B, C, H, d = st["kc"].shape
     tq.quantize_kv(st["layout"], st["pages"], st["kc"].reshape(B * C, H, d).cuda(),
                    st["vc"].reshape(B * C, H, d).cuda(), torch.from_numpy(st["slots"]).cuda(), st["kcb"], st["vcb"])
@@ -130,6 +117,47 @@ def test_prefill_attention_query_dtypes(q_dtype):
         err = _oracle_error(st, out, scale)
         print(f"  max relative error {err:.2e}", flush=True)
         assert err <= parity.ATTN_TOL
+
+
+VALUE_CASES = [  # name, fmt, recipe, v_mult
+    ("v-tiny-k4v2", (4, 0, 2, 0), "lognormal", 2.0 ** -16),
+    ("v-huge-k4v2", (4, 0, 2, 0), "lognormal", 2.0 ** 8),
+    ("v-tiny-k2pv2", (2, 1, 2, 0), "lognormal", 2.0 ** -16),
+    ("v-range-k4v2", (4, 0, 2, 0), "vrange", 1.0),
+    ("v-range-k8v8", (8, 0, 8, 0), "vrange", 1.0),
+    ("v-range-k4pv3", (4, 1, 3, 0), "vrange", 1.0),
+]
+
+
+@pytest.mark.parametrize("case", VALUE_CASES, ids=[c[0] for c in VALUE_CASES])
+def test_prefill_value_norm_range(case):
+    """Values uniformly tiny (2^-16) or large (2^8), or of norms spread over 2^-14 .. 2^6 token by token, through
+    tq_prefill_chunk: every row within the bar of the oracle, and a uniform power-of-two scale of V scales the output."""
+    import torch
+    import kv_cache_quantization_wht_amd as tq
+
+    name, fmt, recipe, vmul = case
+    print(f"prefill value-range case {name}", flush=True)
+
+    def run(vm):
+        st = _setup(2, 128, 8, 2, [45, 130], 70, fmt, seed=17, recipe=recipe, v_mult=vm)
+        out = tq.prefill_chunk(st["layout"], st["pages"], st["kc"].cuda(), st["vc"].cuda(),
+                               torch.from_numpy(st["slots"]).cuda(), st["q"].cuda(), torch.from_numpy(st["pt"]).cuda(),
+                               torch.from_numpy(st["prefix"]).cuda(), 1.0 / math.sqrt(128), st["kcb"], st["vcb"])
+        torch.cuda.synchronize()
+        return st, out
+
+    st, out = run(vmul)
+    assert torch.isfinite(out).all()
+    err = _oracle_error(st, out, 1.0 / math.sqrt(128))
+    print(f"  max relative error {err:.2e}", flush=True)
+    assert err <= parity.ATTN_TOL
+    if vmul != 1.0:
+        _, one = run(1.0)
+        rel = parity.attention_error(out.cpu().numpy().astype(np.float64) / vmul,
+                                     one.cpu().numpy().astype(np.float64))
+        print(f"  output / {vmul:g} against the unscaled run {rel:.2e}", flush=True)
+        assert rel <= 1e-5
 
 
 def test_prefill_rows_match_decode():
@@ -206,14 +234,14 @@ def test_prefill_empty_pages():
 
     H, d, Hq, P, C = 2, 128, 8, 70, 40
     fmt = (4, 0, 2, 0)
-    st = _setup(H, d, Hq, 1, [P], C, fmt, seed=61, recipe="plain")
+    st = _setup(H, d, Hq, 1, [P], C, fmt, seed=61)
     npages = st["pages"].numel() // st["Lo"]["page_bytes"]
     pt = st["pt"].copy()
     pt[0, 2] = -1       # inside the prefix
     pt[0, 5] = npages   # inside the chunk (positions 80 .. 95)
     # rebuild the pool through the edited table: the prefix, then the chunk with tq_prefill_chunk
     pages = torch.full_like(st["pages"], 0x5A)
-    k, v = parity.seeded_kv(P, H, d, seed=61 * 10, recipe="plain")
+    k, v = parity.seeded_kv(P, H, d, seed=61 * 10)
     tq.quantize_kv(st["layout"], pages, k.cuda(), v.cuda(), torch.from_numpy(kvsynth.slots_for(pt, 0, 0, P)).cuda(),
                    st["kcb"], st["vcb"])
     slots = kvsynth.slots_for(pt, 0, P, P + C)
@@ -243,7 +271,7 @@ def test_prefill_empty_pages():
         for i in range(C):
             n = int(np.sum(tv <= P + i))
             ref[i, g * G:(g + 1) * G] = attention.reference_attention(q[i, g * G:(g + 1) * G], K[:n], V[:n], scale)
-    err = floored_error(out[0].cpu().numpy(), ref)
-    err_dec = floored_error(dec.cpu().numpy(), ref)
+    err = parity.attention_error(out[0].cpu().numpy(), ref)
+    err_dec = parity.attention_error(dec.cpu().numpy(), ref)
     print(f"prefill with empty pages: max relative error {err:.2e} (decode {err_dec:.2e})", flush=True)
     assert err <= parity.ATTN_TOL and err_dec <= parity.ATTN_TOL
