@@ -205,6 +205,27 @@ int tq_decode_attention(const tq_layout *layout, const void *pages, int64_t num_
                         const void *v_cb, void *workspace, size_t workspace_bytes, float *out,
                         void *stream);
 
+/* Largest split-partial buffer tq_decode_attention_noalloc can use: the bytes of the fixed device array it keeps
+ * them in (compare with tq_decode_workspace_bytes for the same arguments). */
+#define TQ_DECODE_NOALLOC_MAX_BYTES ((size_t)4 << 20)
+
+/* tq_decode_attention for callers that cannot allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. Same arguments, layout, result and errors as
+ * tq_decode_attention without `workspace` / `workspace_bytes`; the split partials live in a fixed device array
+ * of TQ_DECODE_NOALLOC_MAX_BYTES bytes that the library's code object holds on each device it runs on until the
+ * process ends. Allocates nothing: no hipMalloc, no hipFree, no allocating library call. The array's address on
+ * the current device is looked up on the first call on that device (thread-safe).
+ * Every call on one device shares that device's array and leaves the last call's partials in it (no initial
+ * contents are needed): calls that overlap in time on one device (two streams, two threads) race and must be
+ * ordered by the caller.
+ * Errors: those of tq_decode_attention; TQ_ENOSPC when the plan's partials (tq_decode_workspace_bytes for the
+ * same arguments) exceed TQ_DECODE_NOALLOC_MAX_BYTES - a larger pages_per_split needs fewer;
+ * TQ_ENOTSUP on a device index >= 64. */
+int tq_decode_attention_noalloc(const tq_layout *layout, const void *pages, int64_t num_pages, const void *q,
+                                int q_dtype, int batch, int num_q_heads, const int32_t *page_table,
+                                int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
+                                int pages_per_split, const void *k_cb, const void *v_cb, float *out, void *stream);
+
 /* One decode step ("Where This Fits in the Inference Stack", "Production Deployment: Tensor Parallelism":
  * quantize the new K/V before it reaches HBM; "Why the KV Cache Exists", "The KV Cache Solution": the new
  * query attends over every cached token including its own): appends the new token of each sequence and

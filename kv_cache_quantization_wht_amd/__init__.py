@@ -26,7 +26,7 @@ _LIB = None
 C_SYMBOLS = (
     "tq_strerror", "tq_codebook_bytes", "tq_build_codebook", "tq_page_layout", "tq_quantize_kv",
     "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_partial", "tq_decode_combine",
-    "tq_decode_step", "tq_decode_step_partial",
+    "tq_decode_step", "tq_decode_step_partial", "tq_decode_attention_noalloc",
     "tq_dense_page_bytes", "tq_dense_write_kv", "tq_dense_decode_workspace_bytes", "tq_dense_decode_attention",
     "tq_dense_fp8_page_bytes", "tq_dense_fp8_write_kv", "tq_dense_fp8_decode_attention",
     "tq_qr_rotation", "tq_rotate_rows", "tq_quantize_kv_qr_workspace_bytes", "tq_quantize_kv_qr",
@@ -71,6 +71,8 @@ def _lib():
                                             ctypes.c_float, i32, vp, vp, vp, sz, vp, vp]
         lib.tq_decode_combine.argtypes = [ctypes.POINTER(_Layout), vp, i64, vp, i32, i32, i32, vp, i32, vp,
                                             ctypes.c_float, i32, vp, vp, vp, sz, vp, vp]
+        lib.tq_decode_attention_noalloc.argtypes = [ctypes.POINTER(_Layout), vp, i64, vp, i32, i32, i32, vp, i32,
+                                                    vp, ctypes.c_float, i32, vp, vp, vp, vp]
         for nm in ("tq_decode_step", "tq_decode_step_partial"):
             getattr(lib, nm).argtypes = [ctypes.POINTER(_Layout), vp, i64, vp, vp, i32, vp, i32, i32, i32, vp, i32,
                                          vp, ctypes.c_float, i32, vp, vp, vp, sz, vp, vp]
@@ -248,6 +250,38 @@ def decode_attention(layout: Layout, pages, q, page_table, seq_lens, softmax_sca
     """Decode attention for q [batch, num_q_heads, head_dim]; returns fp32 out of the same shape."""
     return _decode_call("tq_decode_attention", layout, pages, q, page_table, seq_lens, softmax_scale, k_cb, v_cb,
                         workspace, out, pages_per_split, stream)
+
+
+NOALLOC_MAX_BYTES = 4 << 20  # TQ_DECODE_NOALLOC_MAX_BYTES
+
+
+def decode_attention_noalloc(layout: Layout, pages, q, page_table, seq_lens, softmax_scale, k_cb, v_cb, out,
+                             pages_per_split: int = 0, stream=None):
+    """decode_attention with the split partials in the library's fixed device array (tq_decode_attention_noalloc):
+    no workspace, and ``out`` (fp32, shaped like q) is the caller's. Calls on one device must not overlap."""
+    import torch
+
+    _need(pages, "pages", torch.uint8)
+    _need(q, "q")
+    _need(page_table, "page_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(out, "out", torch.float32)
+    if q.dim() != 3 or q.shape[2] != layout.head_dim or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [batch, num_q_heads, head_dim] tensor")
+    B, Hq, _ = q.shape
+    if page_table.dim() != 2 or page_table.shape[0] != B or not page_table.is_contiguous():
+        raise ValueError("page_table must be a contiguous [batch, max_pages_per_seq] int32 tensor")
+    if seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must hold one int32 per sequence")
+    if out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor shaped like q")
+    num_pages = pages.numel() // page_layout(layout)["page_bytes"]
+    _check(_lib().tq_decode_attention_noalloc(ctypes.byref(layout.c()), pages.data_ptr(), num_pages, q.data_ptr(),
+                                              _dtype_code(q), B, Hq, page_table.data_ptr(), page_table.shape[1],
+                                              seq_lens.data_ptr(), float(softmax_scale), pages_per_split,
+                                              k_cb.data_ptr(), v_cb.data_ptr(), out.data_ptr(), _stream(stream)),
+           "tq_decode_attention_noalloc")
+    return out
 
 
 def decode_partial(layout: Layout, pages, q, page_table, seq_lens, softmax_scale, k_cb, v_cb, workspace,

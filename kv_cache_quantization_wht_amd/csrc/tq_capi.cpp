@@ -369,6 +369,29 @@ int tq_decode_workspace_bytes(const tq_layout *layout, int batch, int num_q_head
   return TQ_OK;
 }
 
+// Every check of a decode call but the workspace's, and its plan. Returns TQ_OK with *launch = false when there is
+// nothing to launch (batch 0).
+static int decode_prepare(const tq_layout *layout, const void *pages, int64_t num_pages, const void *q, int q_dtype,
+                          int batch, int num_q_heads, const int32_t *page_table, int max_pages_per_seq,
+                          const int32_t *seq_lens, float softmax_scale, int pages_per_split, const void *k_cb,
+                          const void *v_cb, float *out, tq::PageGeom *g, tq::DecodeWs *ws, bool *launch) {
+  *launch = false;
+  int st = tq::make_geom(layout, g);
+  if (st) return st;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return TQ_EINVAL;
+  if (batch < 0 || num_q_heads < 1 || num_q_heads % g->num_kv_heads) return TQ_EINVAL;
+  if (num_q_heads / g->num_kv_heads > 16) return TQ_ENOTSUP;  // one MFMA column block of query heads
+  if (g->v_mode == TQ_PROD) return TQ_ENOTSUP;
+  if (max_pages_per_seq < 1 || num_pages < 1 || !std::isfinite(softmax_scale) || softmax_scale < 0.f) return TQ_EINVAL;
+  if (batch == 0) return TQ_OK;
+  if (!pages || !q || !page_table || !seq_lens || !k_cb || !v_cb || !out) return TQ_EINVAL;
+  if (((uintptr_t)pages | (uintptr_t)k_cb | (uintptr_t)v_cb) & 15) return TQ_EINVAL;
+  st = tq::plan_decode(*g, batch, num_q_heads, max_pages_per_seq, pages_per_split, ws);
+  if (st) return st;
+  *launch = true;
+  return TQ_OK;
+}
+
 static int decode_passes(const tq_layout *layout, const void *pages, int64_t num_pages, const void *q,
                          int q_dtype, int batch, int num_q_heads, const int32_t *page_table,
                          int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
@@ -376,19 +399,12 @@ static int decode_passes(const tq_layout *layout, const void *pages, int64_t num
                          size_t workspace_bytes, float *out, int passes, void *stream,
                          const void *k_new = nullptr, const void *v_new = nullptr, int kv_dtype = TQ_BF16) {
   tq::PageGeom g;
-  int st = tq::make_geom(layout, &g);
-  if (st) return st;
-  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return TQ_EINVAL;
-  if (batch < 0 || num_q_heads < 1 || num_q_heads % g.num_kv_heads) return TQ_EINVAL;
-  if (num_q_heads / g.num_kv_heads > 16) return TQ_ENOTSUP;  // one MFMA column block of query heads
-  if (g.v_mode == TQ_PROD) return TQ_ENOTSUP;
-  if (max_pages_per_seq < 1 || num_pages < 1 || !std::isfinite(softmax_scale) || softmax_scale < 0.f) return TQ_EINVAL;
-  if (batch == 0) return TQ_OK;
-  if (!pages || !q || !page_table || !seq_lens || !k_cb || !v_cb || !workspace || !out) return TQ_EINVAL;
-  if (((uintptr_t)pages | (uintptr_t)k_cb | (uintptr_t)v_cb | (uintptr_t)workspace) & 15) return TQ_EINVAL;
   tq::DecodeWs ws;
-  st = tq::plan_decode(g, batch, num_q_heads, max_pages_per_seq, pages_per_split, &ws);
-  if (st) return st;
+  bool launch = false;
+  int st = decode_prepare(layout, pages, num_pages, q, q_dtype, batch, num_q_heads, page_table, max_pages_per_seq,
+                          seq_lens, softmax_scale, pages_per_split, k_cb, v_cb, out, &g, &ws, &launch);
+  if (st || !launch) return st;
+  if (!workspace || ((uintptr_t)workspace & 15)) return TQ_EINVAL;
   if (workspace_bytes < ws.total) return TQ_ENOSPC;
   return tq::launch_decode(g, ws, pages, num_pages, q, q_dtype, batch, num_q_heads, page_table,
                            max_pages_per_seq, seq_lens, softmax_scale, k_cb, v_cb, workspace, out, passes,
@@ -404,6 +420,25 @@ int tq_decode_attention(const tq_layout *layout, const void *pages, int64_t num_
   return decode_passes(layout, pages, num_pages, q, q_dtype, batch, num_q_heads, page_table, max_pages_per_seq,
                        seq_lens, softmax_scale, pages_per_split, k_cb, v_cb, workspace, workspace_bytes, out,
                        tq::kPassScan | tq::kPassCombine, stream);
+}
+
+int tq_decode_attention_noalloc(const tq_layout *layout, const void *pages, int64_t num_pages, const void *q,
+                                int q_dtype, int batch, int num_q_heads, const int32_t *page_table,
+                                int max_pages_per_seq, const int32_t *seq_lens, float softmax_scale,
+                                int pages_per_split, const void *k_cb, const void *v_cb, float *out, void *stream) {
+  tq::PageGeom g;
+  tq::DecodeWs ws;
+  bool launch = false;
+  int st = decode_prepare(layout, pages, num_pages, q, q_dtype, batch, num_q_heads, page_table, max_pages_per_seq,
+                          seq_lens, softmax_scale, pages_per_split, k_cb, v_cb, out, &g, &ws, &launch);
+  if (st || !launch) return st;
+  if (ws.total > tq::kDecodeScratchBytes) return TQ_ENOSPC;  // the plan's partials do not fit the fixed array
+  void *scratch = nullptr;
+  st = tq::decode_scratch(&scratch);
+  if (st) return st;
+  return tq::launch_decode(g, ws, pages, num_pages, q, q_dtype, batch, num_q_heads, page_table, max_pages_per_seq,
+                           seq_lens, softmax_scale, k_cb, v_cb, scratch, out, tq::kPassScan | tq::kPassCombine,
+                           nullptr, nullptr, TQ_BF16, (hipStream_t)stream);
 }
 
 static int decode_step_passes(const tq_layout *layout, void *pages, int64_t num_pages, const void *k_new,

@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "tq_common.h"
@@ -1280,6 +1282,31 @@ bool decode_dispatch_d64(int kb, bool kprod, int vb, const DecodeArgs &a, hipStr
 #endif
 
 #if !defined(TQ_DECODE_PART) || TQ_DECODE_PART == 1
+// Split partials of tq_decode_attention_noalloc: a fixed array in the library's code object, one copy per device.
+// Host code never uses this name as an address (on the host it is only a handle of the device symbol): the
+// address comes from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+int decode_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void *> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TQ_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return TQ_ENOTSUP;
+  void *p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TQ_EHIP;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return TQ_OK;
+}
+
 int launch_combine_plain(const float *part_o, const float *part_ml, int n_splits, int64_t rows, int head_dim,
                          float *out, hipStream_t stream) {
   DecodeArgs a{};

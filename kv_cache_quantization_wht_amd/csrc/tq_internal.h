@@ -46,6 +46,11 @@ constexpr int kDecodeMaxSplits = 2048;
 int plan_decode(const PageGeom &g, int batch, int num_q_heads, int max_pages_per_seq,
                 int pages_per_split, DecodeWs *ws);
 
+// The allocation-free decode entry point keeps its split partials in one fixed device array of this many
+// bytes (per device, for the life of the process); decode_scratch gives its address on the current device.
+constexpr size_t kDecodeScratchBytes = TQ_DECODE_NOALLOC_MAX_BYTES;
+int decode_scratch(void **ptr);
+
 int launch_quantize(const PageGeom &g, void *pages, int64_t num_pages, const void *k, const void *v,
                     int dtype, int64_t n_tok, int64_t k_stride, int64_t v_stride,
                     const int64_t *slots, const void *k_cb, const void *v_cb, hipStream_t stream);

@@ -169,6 +169,30 @@ def test_decode_step_argument_errors_need_no_gpu():
     assert lib.tq_decode_step(ctypes.byref(L), *bad) == -1
 
 
+def test_decode_noalloc_argument_errors_need_no_gpu():
+    """tq_decode_attention_noalloc runs tq_decode_attention's checks, and refuses a plan whose partials pass the
+    fixed array, before it looks the array up or launches anything."""
+    lib = tq._lib()
+    L = tq.Layout(128, 8, 4, 0, 2, 0).c()
+    # (pages, num_pages, q, q_dtype, B, Hq, page_table, maxp, seq_lens, scale, pps, k_cb, v_cb, out, stream)
+    a = (16, 4, 16, 1, 1, 32, 16, 10, 16, 0.1, 2, 16, 16, 16, None)
+    for i, val, want in ((3, 9, -1), (5, 30, -1), (5, 8 * 17, -3), (9, -1.0, -1), (9, float("nan"), -1), (7, 0, -1),
+                         (0, None, -1), (13, None, -1), (11, 24, -1)):
+        bad = list(a)
+        bad[i] = val
+        assert lib.tq_decode_attention_noalloc(ctypes.byref(L), *bad) == want, (i, val)
+    bad = list(a)
+    bad[4] = 0  # empty batch: nothing to do
+    assert lib.tq_decode_attention_noalloc(ctypes.byref(L), *bad) == 0
+    # 64 sequences x 64 query heads x 2048 runs of partials: far past the fixed array
+    big = list(a)
+    big[4], big[5], big[7], big[10] = 64, 64, 4096, 2
+    need = ctypes.c_size_t()
+    assert lib.tq_decode_workspace_bytes(ctypes.byref(L), 64, 64, 4096, 2, ctypes.byref(need)) == 0
+    assert need.value > tq.NOALLOC_MAX_BYTES
+    assert lib.tq_decode_attention_noalloc(ctypes.byref(L), *big) == -2
+
+
 def test_dense_argument_errors_need_no_gpu():
     lib = tq._lib()
     sz = ctypes.c_size_t()
