@@ -152,6 +152,19 @@ int tq_codebook_bytes(int head_dim, int bits, int mode, size_t *out);
 int tq_build_codebook(int head_dim, int bits, int mode, const uint32_t *sign_words,
                       const float *qjl_proj, void *blob, size_t blob_bytes);
 
+/* tq_build_codebook with the random objects drawn by the library from one 64-bit seed ("Why the KV Cache Exists",
+ * "Prefix Caching": the rotation is fixed per model load; "What the Paper Doesn't Tell You", Finding 4: the WHT
+ * rotation is one random sign vector, 16 bytes at head_dim 128). Use one seed per layer (the same for its K and V
+ * blobs, so that they share a rotation). Host only, synchronous, deterministic.
+ *   signs  bit i of the sign vector is bit i % 64 of output i / 64 of SplitMix64 (Steele, Lea, Flood 2014)
+ *          started from state seed ^ 0x5349474E ("SIGN"); set = coordinate negated
+ *   S      (prod mode) head_dim x head_dim, row-major: outputs 2k, 2k + 1 of SplitMix64 from seed ^ 0x514A4C53
+ *          ("QJLS") give u = ((x >> 11) + 0.5) * 2^-53, and the Box-Muller pair sqrt(-2 ln u1) * (cos, sin)(2 pi u2)
+ *          fills entries 2k, 2k + 1 (fp64, rounded to fp32)
+ * The blob equals tq_build_codebook's for those signs and S.
+ * Errors: those of tq_build_codebook. */
+int tq_build_codebook_seeded(int head_dim, int bits, int mode, uint64_t seed, void *blob, size_t blob_bytes);
+
 /* Page layout of one layer. Host only. Errors: TQ_EINVAL for an invalid layout or null pointer. */
 int tq_page_layout(const tq_layout *layout, tq_page_offsets *out);
 

@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(_HERE, "libtq.so")
 _LIB = None
 
 C_SYMBOLS = (
-    "tq_strerror", "tq_codebook_bytes", "tq_build_codebook", "tq_page_layout", "tq_quantize_kv",
+    "tq_strerror", "tq_codebook_bytes", "tq_build_codebook", "tq_build_codebook_seeded", "tq_page_layout",
+    "tq_quantize_kv",
     "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_partial", "tq_decode_combine",
     "tq_decode_step", "tq_decode_step_partial", "tq_decode_attention_noalloc",
     "tq_dense_page_bytes", "tq_dense_write_kv", "tq_dense_decode_workspace_bytes", "tq_dense_decode_attention",
@@ -62,6 +63,7 @@ def _lib():
         lib.tq_strerror.argtypes = [i32]
         lib.tq_codebook_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         lib.tq_build_codebook.argtypes = [i32, i32, i32, vp, vp, vp, sz]
+        lib.tq_build_codebook_seeded.argtypes = [i32, i32, i32, ctypes.c_uint64, vp, sz]
         lib.tq_page_layout.argtypes = [ctypes.POINTER(_Layout), ctypes.POINTER(_Offsets)]
         lib.tq_quantize_kv.argtypes = [ctypes.POINTER(_Layout), vp, i64, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp]
         lib.tq_decode_workspace_bytes.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32, i32, ctypes.POINTER(sz)]
@@ -142,6 +144,15 @@ def build_codebook(head_dim: int, bits: int, mode: int, sign_words, qjl_proj=Non
     _check(_lib().tq_build_codebook(head_dim, bits, mode, sw.ctypes.data,
                                     None if pj is None else pj.ctypes.data, blob.ctypes.data, n),
            "tq_build_codebook")
+    return blob
+
+
+def build_codebook_seeded(head_dim: int, bits: int, mode: int, seed: int) -> np.ndarray:
+    """Host codebook blob (uint8) with the signs (and in prod mode S) drawn by the library from ``seed``."""
+    n = codebook_bytes(head_dim, bits, mode)
+    blob = np.zeros(n, dtype=np.uint8)
+    _check(_lib().tq_build_codebook_seeded(head_dim, bits, mode, ctypes.c_uint64(seed & (2 ** 64 - 1)),
+                                           blob.ctypes.data, n), "tq_build_codebook_seeded")
     return blob
 
 

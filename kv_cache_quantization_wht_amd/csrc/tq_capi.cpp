@@ -318,6 +318,68 @@ int tq_build_codebook(int head_dim, int bits, int mode, const uint32_t *sign_wor
   return TQ_OK;
 }
 
+namespace {
+
+// SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number generators", OOPSLA 2014): the state
+// advances by the golden-ratio increment and each output is the state through Stafford's variant-13 mix.
+struct SplitMix64 {
+  uint64_t state;
+  uint64_t next() {
+    state += 0x9E3779B97F4A7C15ull;
+    uint64_t z = state;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+  }
+};
+
+constexpr uint64_t kSignStream = 0x5349474Eull;  // "SIGN"
+constexpr uint64_t kQjlStream = 0x514A4C53ull;   // "QJLS"
+
+// The rotation's signs: the bits of consecutive outputs of stream seed ^ "SIGN", low to high (bit i of the vector
+// is bit i % 64 of output i / 64; set = coordinate negated).
+void draw_signs(uint64_t seed, int head_dim, uint32_t *words) {
+  SplitMix64 g{seed ^ kSignStream};
+  for (int w = 0; w < head_dim / 32; w += 2) {
+    const uint64_t x = g.next();
+    words[w] = (uint32_t)x;
+    if (w + 1 < head_dim / 32) words[w + 1] = (uint32_t)(x >> 32);
+  }
+}
+
+// The QJL projection, rows x head_dim row-major: Box-Muller ("A Note on the Generation of Random Normal Deviates",
+// 1958) on output pairs of stream seed ^ "QJLS": u = ((x >> 11) + 1/2) 2^-53 in (0, 1], r = sqrt(-2 ln u1), the
+// pair r cos(2 pi u2), r sin(2 pi u2) into entries 2k, 2k + 1 (fp64, then rounded to fp32).
+void draw_projection(uint64_t seed, int rows, int head_dim, float *S) {
+  SplitMix64 g{seed ^ kQjlStream};
+  const int n = rows * head_dim;
+  const double two_pi = 2.0 * 3.141592653589793;
+  for (int k = 0; k < n; k += 2) {
+    const double u1 = ((double)(g.next() >> 11) + 0.5) * 0x1p-53;
+    const double u2 = ((double)(g.next() >> 11) + 0.5) * 0x1p-53;
+    const double r = std::sqrt(-2.0 * std::log(u1));
+    const double t = two_pi * u2;
+    const double c = std::cos(t);
+    const double sn = std::sin(t);
+    S[k] = (float)(r * c);
+    if (k + 1 < n) S[k + 1] = (float)(r * sn);
+  }
+}
+
+}  // namespace
+
+int tq_build_codebook_seeded(int head_dim, int bits, int mode, uint64_t seed, void *blob, size_t blob_bytes) {
+  if (!valid_head_dim(head_dim) || !valid_bits(bits, mode) || !blob) return TQ_EINVAL;
+  std::vector<uint32_t> signs((size_t)head_dim / 32);
+  draw_signs(seed, head_dim, signs.data());
+  std::vector<float> S;
+  if (mode == TQ_PROD) {
+    S.resize((size_t)head_dim * head_dim);
+    draw_projection(seed, head_dim, head_dim, S.data());
+  }
+  return tq_build_codebook(head_dim, bits, mode, signs.data(), S.empty() ? nullptr : S.data(), blob, blob_bytes);
+}
+
 int tq_page_layout(const tq_layout *layout, tq_page_offsets *out) {
   if (!out) return TQ_EINVAL;
   tq::PageGeom g;

@@ -13,10 +13,13 @@ receive what it produces as plain inputs:
   Finding 1 and Finding 4);
 * page tables (optionally shuffled) and write slots for 16-token pages.
 
-Sign bits come from SplitMix64 (Steele, Lea, Flood: "Fast splittable
-pseudorandom number generators", OOPSLA 2014) so that they are identical on
-every platform; Gaussian draws come from torch generators and are copied, never
-re-drawn, when both sides need them.
+Sign bits and the QJL projection come from SplitMix64 (Steele, Lea, Flood: "Fast
+splittable pseudorandom number generators", OOPSLA 2014), the projection's normals
+by the Box-Muller transform (Box and Muller, "A Note on the Generation of Random
+Normal Deviates", 1958), so that a seed alone fixes them on every platform (the
+library's seeded codebook build draws the same streams from its own code). The
+other Gaussian draws (the dense rotation's matrix, bulk K/V/q data) come from
+torch generators and are copied, never re-drawn, when both sides need them.
 """
 from __future__ import annotations
 
@@ -66,12 +69,26 @@ def rotation_signs(seed: int, head_dim: int) -> np.ndarray:
 
 
 def qjl_projection(seed: int, head_dim: int, rows: int | None = None) -> np.ndarray:
-    """Gaussian projection for the QJL residual sketch: ``rows x head_dim`` fp32, iid N(0,1)."""
-    import torch
+    """Gaussian projection for the QJL residual sketch: ``rows x head_dim`` fp32, iid N(0,1).
 
+    Outputs 2k and 2k + 1 of SplitMix64 stream ``seed ^ "QJLS"`` give u1, u2 = ((x >> 11) + 0.5) * 2^-53 in (0, 1],
+    and the Box-Muller pair r cos(2 pi u2), r sin(2 pi u2) with r = sqrt(-2 ln u1) fills entries 2k and 2k + 1 in
+    row-major order (fp64, then rounded to fp32, nearest even). Scalar libm calls, in this order, so that the
+    library's C++ draw of the same stream gives the same bits.
+    """
     rows = head_dim if rows is None else rows
-    g = torch.Generator(device="cpu").manual_seed((seed ^ QJL_STREAM) & 0x7FFFFFFFFFFFFFFF)
-    return torch.randn(rows, head_dim, generator=g, dtype=torch.float64).to(torch.float32).numpy()
+    n = rows * head_dim
+    xs = [int(x) for x in splitmix64(seed ^ QJL_STREAM, n + (n & 1))]
+    out = np.empty(n + (n & 1), dtype=np.float64)
+    two_pi = 2.0 * math.pi
+    for k in range(0, len(xs), 2):
+        u1 = (float(xs[k] >> 11) + 0.5) * 2.0 ** -53
+        u2 = (float(xs[k + 1] >> 11) + 0.5) * 2.0 ** -53
+        r = math.sqrt(-2.0 * math.log(u1))
+        t = two_pi * u2
+        out[k] = r * math.cos(t)
+        out[k + 1] = r * math.sin(t)
+    return out[:n].astype(np.float32).reshape(rows, head_dim)
 
 
 def qr_gaussian(seed: int, head_dim: int) -> np.ndarray:

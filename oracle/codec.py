@@ -154,8 +154,8 @@ def encode(x, cb: Codebook) -> Encoded:
     safe = np.where(n > 0, n, 1.0)
     u = np.where(n[:, None] > 0, x / safe[:, None], 0.0)
     y = cb.rotate(u)
-    y32 = (y * math.sqrt(d)).astype(np.float32).astype(np.float64)
-    index = np.searchsorted(cb.thresholds, y32, side="right").astype(np.int64)
+    # the decision on the exact (fp64) value y' = sqrt(d) y: index = #{j : y' >= t_j}, a tie going to the upper cell
+    index = np.searchsorted(cb.thresholds, y * math.sqrt(d), side="right").astype(np.int64)
     enc = Encoded(codes=stored_code(index, cb.mse_bits), norm16=fp16_round(n), norm=n, y=y)
     if cb.mode == PROD:
         yhat = cb.levels16[index] / math.sqrt(d)

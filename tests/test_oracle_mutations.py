@@ -63,8 +63,7 @@ def test_mutant_ties_go_down(monkeypatch):
 
     def ties_down(x, cb):
         e = orig(x, cb)
-        y32 = (e.y * math.sqrt(cb.head_dim)).astype(np.float32).astype(np.float64)
-        e.codes = e.codes - np.isin(y32, cb.thresholds)
+        e.codes = e.codes - np.isin(e.y * math.sqrt(cb.head_dim), cb.thresholds)
         return e
 
     monkeypatch.setattr(codec, "encode", ties_down)
