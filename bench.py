@@ -1,23 +1,25 @@
 #!/usr/bin/env python3
 """Benchmark of the TurboQuant hot path on one MI355X.
 
-Workload: the Llama-3.1-8B single-layer cache (8 KV heads, 32 query heads, head_dim 128, batch 1,
-32768 cached tokens, K 4-bit / V 2-bit MSE, bf16 inputs). One step is one decode step of that workload:
-quantize-on-write of the new token's K and V (8 heads each) into its page slot and decode attention of the
-new query over all cached tokens (rotation of q, split-K scores/softmax/value sums on the packed pages,
-merge and inverse rotation), as tq_decode_step: the work-group owning the new token's page quantizes it,
-so the step is one split-K launch plus the merge launch.
+Default workload: the Llama-70B-shaped cache (80 layers, 8 KV heads, 64 query heads, head_dim 128, batch 4,
+131072 cached tokens per sequence; layers 0, 1, 78 and 79 with K and V at 8 bits, the others K 4-bit / V 2-bit,
+MSE; 16-token pages with a shuffled page table; bf16 inputs). Every layer has its own page pool (36 GB in all),
+filled by a 131072-token prefill quantize-on-write per sequence; one step is one decode step of the whole model:
+for every layer, the new token of every sequence is quantized into its slot and the new queries attend over every
+cached token (tq_decode_step: the split-K launch with the append fused, plus the merge; 8-bit layers:
+tq_quantize_kv + tq_decode_attention). The timed region replays the K steps as one HIP graph.
 
-The cache of one layer is 26 MB, which would stay in the 256 MB Infinity Cache if the same layer were
-read step after step. A real model reads every other layer's cache before it comes back to this one, so
-the benchmark cycles through ``--copies`` independent copies of the layer cache (16 x 26 MB by default,
-more than the Infinity Cache) and each step works on the next copy: every step's bytes come from HBM.
-
-Prints one JSON line. ``value`` is the step's algorithmic bytes (compressed-KV records of every cached token,
-the new token's K/V input, page ids) divided by the wall time of the whole step (both launches), in GB/s;
-``roofline`` reports the split-K launch alone (algorithmic bytes per launch / its average launch duration
-from HIP events); ``quantize_vectors_per_s`` is the quantize kernel's rate on the 32768-token prefill of the
-layer (524288 vectors); ``cpu_baseline`` times the CPU oracle on a bounded sample of the same cache.
+Prints one JSON line. ``value`` is the step's algorithmic bytes (the compressed records of every cached token of
+every layer and KV head, the new tokens' K/V input, page ids) divided by the wall time of the K steps, in GB/s;
+``roofline`` is the split-K launch of the K4/V2 layers (algorithmic bytes per launch / its average duration from
+HIP events around a graph of those launches alone), with its HBM traffic from committed rocprofv3 counter runs
+while the kernel source is unchanged; ``quantize`` reports the prefill's quantize-on-write (a K4/V2 layer and an
+8-bit layer: vectors/s and bytes in + out against the HBM peak); ``stream_read`` is a plain streaming read of a
+large buffer, the practical ceiling; ``step_breakdown`` sums the launches of one step timed by kind;
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same cache. ``secondary`` holds the Llama-3.1-8B
+single-layer line (``--workload 1`` prints it as the main line): one layer, batch 1, 32768 tokens, cycled through
+16 cache copies so that every step's bytes come from HBM, with the uncompressed comparators and the chunked
+prefill leg.
 """
 from __future__ import annotations
 
@@ -33,7 +35,8 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
-WORKLOAD_INDEX = 1
+WORKLOAD_INDEX = 4         # the headline workload: the largest one that fits one GPU (Llama-70B shape)
+SINGLE_LAYER_INDEX = 1     # the Llama-3.1-8B single layer (secondary line)
 
 
 def log(msg):
@@ -56,53 +59,47 @@ def prefill_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_prefill_traffic():
-    """HBM traffic of the K4/V2 prefill kernel from committed rocprofv3 counter runs, if taken on this source."""
-    path = os.path.join(ROOT, "profiles", "prefill_traffic.json")
+def quantize_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("tq_quantize.hip", "tq_common.h", "tq_quant_common.h"):
+        with open(os.path.join(ROOT, "kv_cache_quantization_wht_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name, source_hash, key="hbm_bytes_per_launch"):
+    """HBM traffic of a kernel from committed rocprofv3 counter runs (``profiles/<name>``), if they were taken on
+    the current source of that kernel; else None."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != prefill_source_hash():
+    if t.get("kernel_source_hash") != source_hash:
         return None
-    return t.get("hbm_bytes_per_launch")
-
-
-def load_traffic(bytes_per_launch_alg):
-    """HBM traffic of the decode kernel from committed rocprofv3 counter runs, if taken on this source."""
-    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    return t.get("hbm_bytes_per_launch")
+    return t.get(key)
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 128; another workload: its own)")
-    ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (default 16; another workload: 2)")
-    ap.add_argument("--copies", type=int, default=16, help="independent layer caches cycled per step")
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: the workload's own, 64 for the 70B shape, 128 for the 8B layer)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (default 2; 8B layer: 16)")
+    ap.add_argument("--copies", type=int, default=16, help="8B single layer: independent layer caches cycled per step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the uncompressed bf16 and FP8 comparators")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
-    ap.add_argument("--eager", action="store_true", help="launch steps from Python instead of a captured graph")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the 8B single-layer line after the headline")
+    ap.add_argument("--eager", action="store_true", help="8B layer: launch steps from Python instead of a graph")
     ap.add_argument("--workload", default=None,
-                    help="another synthetic workload by name or index (default: the Llama-3.1-8B single layer); "
-                         "its steps run every layer of the workload, each layer its own cache")
+                    help="workload by name or index (default: the Llama-70B shape, index 4); index 1, the 8B "
+                         "single layer, prints that line as the main one")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="only run a plain device-to-device copy of MB megabytes (5 times), to scale the HBM "
                          "byte counters of rocprofv3")
     args = ap.parse_args()
-    args.steps_given, args.warmup_given = args.steps is not None, args.warmup is not None
-    if args.steps is None:
-        args.steps = 128
-    if args.warmup is None:
-        args.warmup = 16
     if args.calibrate_copy:
         import torch
 
@@ -124,25 +121,42 @@ def main():
     import torch
 
     import kvsynth
-    import kv_cache_quantization_wht_amd as tq
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    wi = WORKLOAD_INDEX
     if args.workload is not None:
         names = [w.name for w in kvsynth.workloads()]
         wi = int(args.workload) if args.workload.isdigit() else names.index(args.workload)
-        if wi != WORKLOAD_INDEX:
-            run_workload(args, wi)
-            return
+    if wi == SINGLE_LAYER_INDEX:
+        result = single_layer(args, args.steps if args.steps is not None else 128,
+                              args.warmup if args.warmup is not None else 16, cpu=not args.no_cpu_baseline)
+    else:
+        result = run_workload(args, wi)
+        torch.cuda.empty_cache()
+        if not args.no_secondary:
+            sec = single_layer(args, 128, 16, cpu=False)
+            result["secondary"] = {sec["config"]["workload"]: sec}
+    print(json.dumps(result), flush=True)
+
+
+def single_layer(args, K, W, cpu=True):
+    """The Llama-3.1-8B single-layer line: one decode step = tq_decode_step of the new token over 32768 cached
+    tokens of one layer (batch 1), the layer cycled through ``--copies`` independent caches."""
+    import torch
+
+    import kvsynth
+    import kv_cache_quantization_wht_amd as tq
+
     dev = "cuda"
-    wl = kvsynth.workloads()[WORKLOAD_INDEX]
+    wl = kvsynth.workloads()[SINGLE_LAYER_INDEX]
     H, Hq, d, T = wl.kv_heads, wl.q_heads, wl.head_dim, wl.seq_len
     bits = wl.bits[0]
     layout = tq.Layout(d, H, bits.k_bits, bits.k_mode, bits.v_bits, bits.v_mode)
     offs = tq.page_layout(layout)
     page_bytes = offs["page_bytes"]
-    K, W, C = args.steps, args.warmup, args.copies
+    C = args.copies
     total_steps = W + K
     max_len = T + (total_steps + C - 1) // C + 1
     pages_per_copy = (max_len + 15) // 16
@@ -158,7 +172,7 @@ def main():
                    for c in range(C)]
 
     # ---- prefill: quantize T tokens into every copy (timed on copy 0 for the quantize rate)
-    k_pre, v_pre = kvsynth.make_kv(wl, WORKLOAD_INDEX, 0, T, device=dev)
+    k_pre, v_pre = kvsynth.make_kv(wl, SINGLE_LAYER_INDEX, 0, T, device=dev)
     slots0 = torch.arange(T, dtype=torch.int64, device=dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     qtimes = []
@@ -178,8 +192,8 @@ def main():
     log(f"prefill quantize: {n_vec} vectors in {q_time * 1e6:.1f} us -> {quant_vps / 1e9:.2f} G vectors/s")
 
     # ---- per-step inputs: new token K/V, query, slot, sequence length (all resident before timing)
-    k_new, v_new = kvsynth.make_kv(wl, WORKLOAD_INDEX, 0, total_steps, device=dev, token_offset_seed=1)
-    g = torch.Generator(device=dev).manual_seed(kvsynth.data_seed(WORKLOAD_INDEX, 0, "q"))
+    k_new, v_new = kvsynth.make_kv(wl, SINGLE_LAYER_INDEX, 0, total_steps, device=dev, token_offset_seed=1)
+    g = torch.Generator(device=dev).manual_seed(kvsynth.data_seed(SINGLE_LAYER_INDEX, 0, "q"))
     qs = torch.randn(total_steps, 1, Hq, d, generator=g, device=dev).to(torch.bfloat16)
     lens = [T] * C
     step_slots, step_lens, step_copy, step_bytes = [], [], [], []
@@ -212,15 +226,11 @@ def main():
     mode = "eager" if args.eager else "graph"
     graph = None
     if not args.eager:
-        try:
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                for i in range(W, total_steps):
-                    step(i)
-            torch.cuda.synchronize()
-        except Exception as e:  # noqa: BLE001
-            log(f"graph capture unavailable ({e!r}); timing eagerly")
-            graph, mode = None, "eager"
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(W, total_steps):
+                step(i)
+        torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps
     torch.cuda.synchronize()
@@ -236,24 +246,7 @@ def main():
     bytes_timed = float(np.sum(step_bytes[W:]))
     value = bytes_timed / elapsed / 1e9
 
-    # ---- split-K kernel duration from HIP events on the launch stream. Events recorded inside a captured
-    #      graph are not timed on this platform, so the K tq_decode_partial launches of the timed steps are
-    #      captured on their own (no other kernel between them) and one event pair brackets the replay:
-    #      average duration = elapsed / K. The same is done for the K tq_decode_combine launches.
-    def replay_avg(fn):
-        gph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gph):
-            for i in range(W, total_steps):
-                fn(i)
-        gph.replay()  # warm
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        gph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3 / K
-
+    # ---- split-K kernel and merge durations: HIP events on the launch stream around a graph of the K launches
     def partial_only(i):
         tq.decode_step(layout, pages, k_new[i:i + 1], v_new[i:i + 1], qs[i], page_tables[step_copy[i]], step_lens[i],
                        scale, kcb, vcb, workspace=ws, out=out, first_pass_only=True)
@@ -262,30 +255,13 @@ def main():
         tq.decode_combine(layout, pages, qs[i], page_tables[step_copy[i]], step_lens[i], scale, kcb, vcb, ws, out=out)
 
     kmode = "graph of the K launches, one event pair"
-    try:
-        durs = np.array([replay_avg(partial_only)])
-        comb = np.array([replay_avg(combine_only)])
-    except Exception as e:  # noqa: BLE001
-        log(f"graph timing unavailable ({e!r}); events around eager launches")
-        kmode = "eager+sleep"
-        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)]
-        if hasattr(torch.cuda, "_sleep"):
-            torch.cuda._sleep(50_000_000)  # keep the GPU busy while every launch is queued
-        for j, i in enumerate(range(W, total_steps)):
-            evs[j][0].record()
-            partial_only(i)
-            evs[j][1].record()
-            combine_only(i)
-            evs[j][2].record()
-        torch.cuda.synchronize()
-        durs = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
-        comb = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
-    kern_s = float(np.mean(durs))
+    kern_s = graph_avg(lambda: [partial_only(i) for i in range(W, total_steps)], K)
+    comb_s = graph_avg(lambda: [combine_only(i) for i in range(W, total_steps)], K)
     alg_per_launch = float(np.mean(step_bytes[W:]))
     achieved = alg_per_launch / kern_s / 1e9
-    traffic = load_traffic(alg_per_launch)
+    traffic = load_traffic("decode_traffic.json", kernel_source_hash())
     log(f"step {ms_per_step * 1e3:.2f} us ({mode}); split-K decode kernel {kern_s * 1e6:.2f} us, combine "
-        f"{float(np.mean(comb)) * 1e6:.2f} us ({kmode}); {alg_per_launch / 1e6:.2f} MB/launch -> {achieved:.0f} GB/s")
+        f"{comb_s * 1e6:.2f} us ({kmode}); {alg_per_launch / 1e6:.2f} MB/launch -> {achieved:.0f} GB/s")
 
     result = {
         "metric": "decode-attn compressed-KV GB/s (% of HBM peak); KV quantize vectors/s",
@@ -309,7 +285,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_kernel<128,4,false,2,true,true> (tq_decode_step_partial)",
                      "bytes_per_launch": round(alg_per_launch), "avg_launch_us": round(kern_s * 1e6, 3),
-                     "combine_avg_us": round(float(np.mean(comb)) * 1e6, 3), "timing": kmode},
+                     "combine_avg_us": round(comb_s * 1e6, 3), "timing": kmode},
         "cpu_baseline": None,
     }
 
@@ -320,13 +296,32 @@ def main():
     if not args.no_prefill:
         result["prefill"] = prefill_leg(wl, layout, pages, page_tables[0], k_pre, v_pre, kcb, vcb)
         result["prefill_k2qjl"] = prefill_sketched(wl, k_pre, v_pre, sw)
-    if not args.no_cpu_baseline:
+    if cpu:
         first = int(page_tables[0][0, 0].item())
         npg = (T + 15) // 16
         pool = pages[first * page_bytes:(first + npg) * page_bytes].cpu().numpy()
         result["cpu_baseline"] = cpu_baseline(H, d, bits, pool, T, qs.double().cpu().numpy(), scale, sw, None,
                                               args.cpu_seconds, rec_bytes, "copy 0")
-    print(json.dumps(result), flush=True)
+    return result
+
+
+def graph_avg(launch_all, n):
+    """Average duration of ``n`` launches: they are captured into one graph (no other kernel between them),
+    replayed once to warm up, then once between two HIP events on the launch stream (events recorded inside a
+    captured graph are not timed on this platform)."""
+    import torch
+
+    gph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gph):
+        launch_all()
+    gph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    gph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / n
 
 
 def prefill_leg(wl, layout, pages, page_table, k_pre, v_pre, kcb, vcb, chunk=2048, reps=8):
@@ -385,7 +380,8 @@ def prefill_leg(wl, layout, pages, page_table, k_pre, v_pre, kcb, vcb, chunk=204
     return {"chunk": chunk, "prefix": P, "attn_us": round(t_attn * 1e6, 2), "chunk_us": round(t_fused * 1e6, 2),
             "tokens_per_s": round(chunk / t_fused, 1),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
-                         "frac": round(tflops / peak, 4), "traffic": load_prefill_traffic(), "flops_per_launch": flops,
+                         "frac": round(tflops / peak, 4), "traffic": load_traffic("prefill_traffic.json", prefill_source_hash()),
+                         "flops_per_launch": flops,
                          "kernel": "prefill_kernel<128,4,false,2> (tq_prefill_attention)", "mfma_issue_factor": 2},
             "what": "tq_prefill_attention / tq_prefill_chunk of the last 2048 prompt tokens of the 8B layer, "
                     "HIP events around a graph of 8 launches"}
@@ -445,7 +441,7 @@ def prefill_sketched(wl, k_pre, v_pre, sw, chunk=2048, reps=8):
 def kvsynth_seed_q():
     import kvsynth
 
-    return kvsynth.data_seed(WORKLOAD_INDEX, 0, "q") + 17
+    return kvsynth.data_seed(SINGLE_LAYER_INDEX, 0, "q") + 17
 
 
 def dense_comparator(wl, k_pre, v_pre, k_new, v_new, qs, W, K, ms_compressed, step_bytes, fmt="bf16"):
@@ -583,8 +579,8 @@ def run_workload(args, wi):
     dev = "cuda"
     wl = kvsynth.workloads()[wi]
     L, H, Hq, d, B, T = wl.layers, wl.kv_heads, wl.q_heads, wl.head_dim, wl.batch, wl.seq_len
-    K = args.steps if args.steps_given else wl.decode_steps
-    W = args.warmup if args.warmup_given else 2
+    K = args.steps if args.steps is not None else wl.decode_steps
+    W = args.warmup if args.warmup is not None else 2
     total = W + K
     pps = (T + total + 15) // 16
     layers = []
@@ -603,30 +599,49 @@ def run_workload(args, wi):
     total_mb = sum(x["pages"].numel() for x in layers) / 1e6
     log(f"workload {wl.name}: {L} layers, batch {B}, {T} cached tokens, {total_mb:.0f} MB of pages")
 
-    # ---- prefill every layer (all sequences of a layer in one launch); the largest launch is timed
-    slots_all = torch.from_numpy(np.concatenate([kvsynth.slots_for(layers[0]["pt"], b, 0, T) for b in range(B)])).to(dev)
-    quant_vps, qn = 0.0, 0
+    def fmt_of(x):
+        b0 = x["bits"]
+        return f"K{b0.k_bits}{'qjl' if b0.k_mode else ''}/V{b0.v_bits}{'qjl' if b0.v_mode else ''}"
+
+    # ---- prefill every layer (all sequences of a layer in one launch). The first layer of each format is timed
+    #      (median of 3 launches, HIP events on the launch stream): the quantize-on-write rate and its bytes
+    prefill_t = {}
     for l, x in enumerate(layers):
         k, v = kvsynth.make_kv(wl, wi, l, B * T, device=dev)
-        sl_all = slots_all if l == 0 else torch.from_numpy(
-            np.concatenate([kvsynth.slots_for(x["pt"], b, 0, T) for b in range(B)])).to(dev)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        reps = 3 if l == 0 else 1
+        sl_all = torch.from_numpy(np.concatenate([kvsynth.slots_for(x["pt"], b, 0, T) for b in range(B)])).to(dev)
+        f = fmt_of(x)
+        reps = 3 if f not in prefill_t else 1
         times = []
         for _ in range(reps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             ev[0].record()
             tq.quantize_kv(x["layout"], x["pages"], k, v, sl_all, x["kcb"], x["vcb"])
             ev[1].record()
             torch.cuda.synchronize()
             times.append(ev[0].elapsed_time(ev[1]) * 1e-3)
-        if l == 0:
-            qn = B * T * H * 2
-            quant_vps = qn / float(np.median(times))
-        del k, v
+        if f not in prefill_t:
+            prefill_t[f] = (l, float(np.median(times)))
+        del k, v, sl_all
         if l % 16 == 15:
             log(f"  prefilled {l + 1} layers")
     torch.cuda.synchronize()
-    log(f"prefill quantize (layer 0, {qn} vectors): {quant_vps / 1e9:.2f} G vectors/s")
+    quantize = {}
+    n_vec = B * T * H * 2
+    for f, (l, t) in prefill_t.items():
+        x = layers[l]
+        rec = record_bytes(x["offs"], H)  # K + V record bytes of one token of one KV head
+        bytes_io = B * T * H * (2 * d * 2 + rec)
+        gbs = bytes_io / t / 1e9
+        quantize[f] = {"layer": l, "vectors": n_vec, "avg_launch_us": round(t * 1e6, 2),
+                       "vectors_per_s": round(n_vec / t, 1),
+                       "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": bytes_io,
+                                    "traffic": load_traffic("quantize_traffic.json", quantize_source_hash(),
+                                                            key=f"hbm_bytes_per_launch_{f.replace('/', '')}"),
+                                    "kernel": "quantize_kernel (tq_quantize_kv)",
+                                    "bytes": "bf16 K and V in (2 x 256 B per token and KV head) + their records out"}}
+        log(f"prefill quantize {f} (layer {l}, {n_vec} vectors): {t * 1e6:.0f} us -> {n_vec / t / 1e9:.2f} G vectors/s, "
+            f"{gbs:.0f} GB/s in + out ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak)")
 
     # ---- per-step inputs, resident before timing
     news = [kvsynth.make_kv(wl, wi, l, total * B, device=dev, token_offset_seed=1) for l in range(L)]
@@ -642,25 +657,33 @@ def run_workload(args, wi):
         x["ws"] = wss[key]
     out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
     scale = wl.softmax_scale
-    step_bytes = []
-    for i in range(total):
-        tot = 0
-        for x in layers:
-            tot += B * H * (T + i + 1) * record_bytes(x["offs"], H) + B * H * 2 * d * 2 + 4 * B * ((T + i + 1 + 15) // 16)
-        step_bytes.append(tot)
 
-    def layer_step(l, i, first_pass_only=False):
+    def layer_bytes(x, i):
+        """Algorithmic bytes of layer x at step i: records of the T + i + 1 cached tokens (the new one written),
+        the new tokens' K/V input, page ids."""
+        return B * H * (T + i + 1) * record_bytes(x["offs"], H) + B * H * 2 * d * 2 + 4 * B * ((T + i + 1 + 15) // 16)
+
+    step_bytes = [sum(layer_bytes(x, i) for x in layers) for i in range(total)]
+
+    def layer_step(l, i, part="all"):
+        """part: all (the layer's whole step), scan (its split-K launch alone), combine (its merge launch alone),
+        append (the separate quantize launch of a layer outside the fused step)."""
         x = layers[l]
         kn, vn = news[l][0][i * B:(i + 1) * B], news[l][1][i * B:(i + 1) * B]
-        if x["fused"]:
-            tq.decode_step(x["layout"], x["pages"], kn, vn, qs[l][i], x["ptd"], lens[i], scale, x["kcb"], x["vcb"],
-                           workspace=x["ws"], out=out, first_pass_only=first_pass_only)
+        if part == "combine":
+            tq.decode_combine(x["layout"], x["pages"], qs[l][i], x["ptd"], lens[i], scale, x["kcb"], x["vcb"],
+                              x["ws"], out=out)
+        elif x["fused"]:
+            if part in ("all", "scan"):
+                tq.decode_step(x["layout"], x["pages"], kn, vn, qs[l][i], x["ptd"], lens[i], scale, x["kcb"],
+                               x["vcb"], workspace=x["ws"], out=out, first_pass_only=part == "scan")
         else:
-            if not first_pass_only:
+            if part in ("all", "append"):
                 tq.quantize_kv(x["layout"], x["pages"], kn, vn, step_slots[l][i], x["kcb"], x["vcb"])
+            if part == "all":
                 tq.decode_attention(x["layout"], x["pages"], qs[l][i], x["ptd"], lens[i], scale, x["kcb"], x["vcb"],
                                     workspace=x["ws"], out=out)
-            else:
+            elif part == "scan":
                 tq.decode_partial(x["layout"], x["pages"], qs[l][i], x["ptd"], lens[i], scale, x["kcb"], x["vcb"],
                                   x["ws"], out=out)
 
@@ -682,56 +705,114 @@ def run_workload(args, wi):
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / K
     value = float(np.sum(step_bytes[W:])) / elapsed / 1e9
+    del graph
 
-    # ---- the split-K launch of the most common layer format, alone: graph of its K launches, one event pair
-    fmt = max(set((x["bits"].k_bits, x["bits"].v_bits) for x in layers),
-              key=lambda f: sum(1 for x in layers if (x["bits"].k_bits, x["bits"].v_bits) == f))
-    lr = next(l for l, x in enumerate(layers) if (x["bits"].k_bits, x["bits"].v_bits) == fmt)
-    gph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gph):
-        for i in range(W, total):
-            layer_step(lr, i, first_pass_only=True)
-    gph.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    gph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    kern_s = e0.elapsed_time(e1) * 1e-3 / K
-    xr = layers[lr]
-    alg = float(np.mean([B * H * (T + i + 1) * record_bytes(xr["offs"], H) + 4 * B * ((T + i + 1 + 15) // 16)
-                         + (B * H * 2 * d * 2 if xr["fused"] else 0) for i in range(W, total)]))
+    # ---- the launches of one step timed by kind (graphs of that kind alone, every layer of the kind in step order,
+    #      HIP events around one replay): the split-K launch of each format, the merges, the 8-bit layers' appends.
+    #      The K4/V2 split-K launch is the roofline kernel.
+    fmts = sorted(set(fmt_of(x) for x in layers), key=lambda f: -sum(fmt_of(x) == f for x in layers))
+    breakdown = {}
+    for f in fmts:
+        ls = [l for l, x in enumerate(layers) if fmt_of(x) == f]
+        n = len(ls) * K
+        t_scan = graph_avg(lambda: [layer_step(l, i, "scan") for i in range(W, total) for l in ls], n)
+        t_comb = graph_avg(lambda: [layer_step(l, i, "combine") for i in range(W, total) for l in ls], n)
+        ent = {"layers": len(ls), "scan_avg_us": round(t_scan * 1e6, 3), "combine_avg_us": round(t_comb * 1e6, 3),
+               "scan_bytes_avg": round(float(np.mean([layer_bytes(layers[l], i) if layers[l]["fused"] else
+                                                      layer_bytes(layers[l], i) - B * H * 2 * d * 2
+                                                      for i in range(W, total) for l in ls])))}
+        if not layers[ls[0]]["fused"]:
+            ent["append_avg_us"] = round(graph_avg(lambda: [layer_step(l, i, "append") for i in range(W, total)
+                                                          for l in ls], n) * 1e6, 3)
+        ent["scan_gbs"] = round(ent["scan_bytes_avg"] / t_scan / 1e9, 1)
+        breakdown[f] = ent
+        log(f"  {f}: {len(ls)} layers, split-K launch {t_scan * 1e6:.2f} us ({ent['scan_gbs']:.0f} GB/s), merge "
+            f"{t_comb * 1e6:.2f} us" + (f", append {ent['append_avg_us']:.2f} us" if "append_avg_us" in ent else ""))
+    parts_us = sum(e["layers"] * (e["scan_avg_us"] + e["combine_avg_us"] + e.get("append_avg_us", 0.0))
+                   for e in breakdown.values())
+    step_breakdown = {"by_format": breakdown, "sum_of_launches_us": round(parts_us, 1),
+                      "step_us": round(ms_per_step * 1e3, 1),
+                      "what": "per format: the average of its launches, each kind timed as a graph of that kind "
+                              "alone over every layer of the format and every timed step; the sum is the "
+                              "step's launches end to end"}
+
+    main_f = fmts[0]
+    xr = layers[next(l for l, x in enumerate(layers) if fmt_of(x) == main_f)]
+    lr = next(l for l, x in enumerate(layers) if fmt_of(x) == main_f)
+    kern_s = breakdown[main_f]["scan_avg_us"] * 1e-6
+    alg = breakdown[main_f]["scan_bytes_avg"]
     achieved = alg / kern_s / 1e9
     b0 = xr["bits"]
     kname = (f"decode_kernel<{d},{b0.k_bits - b0.k_mode},{'true' if b0.k_mode else 'false'},{b0.v_bits},"
              f"{'true' if xr['fused'] else 'false'},{'true' if Hq // H <= 8 else 'false'}> "
              f"({'tq_decode_step_partial' if xr['fused'] else 'tq_decode_partial'})")
-    log(f"step {ms_per_step * 1e3:.1f} us -> {value:.0f} GB/s; layer {lr} split-K kernel {kern_s * 1e6:.2f} us, "
-        f"{alg / 1e6:.1f} MB/launch -> {achieved:.0f} GB/s")
+    log(f"step {ms_per_step * 1e3:.1f} us -> {value:.0f} GB/s; {main_f} split-K kernel {kern_s * 1e6:.2f} us, "
+        f"{alg / 1e6:.1f} MB/launch -> {achieved:.0f} GB/s; launches of a step end to end {parts_us:.0f} us")
+
+    # ---- the practical ceiling: a plain streaming read of a buffer the size of a few layers
+    ceiling = stream_ceiling()
+
+    main_q = quantize.get(main_f)
     result = {
         "metric": "decode-attn compressed-KV GB/s (% of HBM peak); KV quantize vectors/s",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp16-mfma+fp32", "data": "synthetic",
         "config": {"workload": wl.name, "layers": L, "kv_heads": H, "q_heads": Hq, "head_dim": d, "batch": B,
-                   "seq_len": T, "bits": sorted(set(f"K{x['bits'].k_bits}{'qjl' if x['bits'].k_mode else ''}"
-                                                    f"/V{x['bits'].v_bits}" for x in layers)),
+                   "seq_len": T, "bits": {f: sum(fmt_of(x) == f for x in layers) for f in fmts},
                    "page_tokens": 16, "shuffled_pages": wl.shuffled_pages, "launch": "graph"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "quantize_vectors_per_s": round(quant_vps, 1),
+        "quantize_vectors_per_s": main_q["vectors_per_s"] if main_q else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kname,
-                     "bytes_per_launch": round(alg), "avg_launch_us": round(kern_s * 1e6, 3),
-                     "timing": "graph of the K launches, one event pair"},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(f"decode_traffic_{wl.name}.json", kernel_source_hash()),
+                     "kernel": kname, "bytes_per_launch": round(alg), "avg_launch_us": round(kern_s * 1e6, 3),
+                     "frac_of_stream_read": round(achieved / ceiling["gbs"], 4) if ceiling else None,
+                     "timing": f"graph of the {main_f} layers' split-K launches of the timed steps "
+                               f"({breakdown[main_f]['layers']} x {K}), one event pair"},
+        "quantize": quantize,
+        "stream_read": ceiling,
+        "step_breakdown": step_breakdown,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         pool = _seq_pages(xr["pages"], xr["offs"]["page_bytes"], xr["pt"][0, :(T + 15) // 16])
         result["cpu_baseline"] = cpu_baseline(H, d, b0, pool, T, qs[lr].double().cpu().numpy(), scale, xr["sw"],
                                               xr["S"], args.cpu_seconds, record_bytes(xr["offs"], H),
-                                              f"layer {lr}, sequence 0")
-    print(json.dumps(result), flush=True)
+                                              f"layer {lr} ({main_f}), sequence 0")
+    del layers, news, qs, wss
+    return result
+
+
+def stream_ceiling(mb=2048, reps=5):
+    """A plain streaming read (tq_stream_read) of an ``mb`` MB buffer, larger than the Infinity Cache: the best of
+    a few launch sizes, each timed by HIP events around ``reps`` launches; GB/s."""
+    import torch
+
+    import kv_cache_quantization_wht_amd as tq
+
+    buf = torch.ones(mb * 1000 * 1000 // 16 * 16, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    best = None
+    for per_cu in (2, 4, 8, 16):
+        blocks = cus * per_cu
+        tq.stream_read(buf, blocks, sink)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            tq.stream_read(buf, blocks, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = buf.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = {"gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": buf.numel(),
+                    "blocks": blocks, "kernel": "stream_read_kernel (tq_stream_read)",
+                    "what": f"plain streaming read of {mb} MB, 16-byte loads, best of 2-16 work-groups per CU"}
+    log(f"streaming-read ceiling: {best['gbs']:.0f} GB/s ({100 * best['frac_of_peak']:.1f}% of 8 TB/s)")
+    del buf
+    return best
 
 
 def _seq_pages(pages, page_bytes, ids):

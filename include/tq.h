@@ -218,6 +218,15 @@ int tq_decode_attention(const tq_layout *layout, const void *pages, int64_t num_
                         const void *v_cb, void *workspace, size_t workspace_bytes, float *out,
                         void *stream);
 
+/* A plain streaming read of `bytes` bytes of device memory at `buf` (16-byte aligned, a multiple of 16) by
+ * `blocks` work-groups of 512 threads, each lane four 16-byte loads in flight with a grid stride: the practical
+ * HBM ceiling the decode kernels are measured against ("Where This Fits in the Inference Stack", "What Changes
+ * When KV Cache Is 4x Smaller": decode reads the whole cache from HBM, so its bound is the streaming rate).
+ * `sink`: device uint32, written only for one data value that keeps the loads live (contents unspecified).
+ * Asynchronous on `stream`. Errors: TQ_EINVAL (null, misaligned or empty buffer, blocks outside
+ * 1 .. 2^20), TQ_EHIP. */
+int tq_stream_read(const void *buf, size_t bytes, int blocks, uint32_t *sink, void *stream);
+
 /* Largest split-partial buffer tq_decode_attention_noalloc can use: the bytes of the fixed device array it keeps
  * them in (compare with tq_decode_workspace_bytes for the same arguments). */
 #define TQ_DECODE_NOALLOC_MAX_BYTES ((size_t)4 << 20)

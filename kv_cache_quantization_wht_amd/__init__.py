@@ -32,7 +32,7 @@ C_SYMBOLS = (
     "tq_dense_fp8_page_bytes", "tq_dense_fp8_write_kv", "tq_dense_fp8_decode_attention",
     "tq_qr_rotation", "tq_rotate_rows", "tq_quantize_kv_qr_workspace_bytes", "tq_quantize_kv_qr",
     "tq_decode_qr_workspace_bytes", "tq_decode_attention_qr",
-    "tq_prefill_attention", "tq_prefill_chunk",
+    "tq_prefill_attention", "tq_prefill_chunk", "tq_stream_read",
 )
 
 
@@ -64,6 +64,7 @@ def _lib():
         lib.tq_codebook_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         lib.tq_build_codebook.argtypes = [i32, i32, i32, vp, vp, vp, sz]
         lib.tq_build_codebook_seeded.argtypes = [i32, i32, i32, ctypes.c_uint64, vp, sz]
+        lib.tq_stream_read.argtypes = [vp, sz, i32, vp, vp]
         lib.tq_page_layout.argtypes = [ctypes.POINTER(_Layout), ctypes.POINTER(_Offsets)]
         lib.tq_quantize_kv.argtypes = [ctypes.POINTER(_Layout), vp, i64, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp]
         lib.tq_decode_workspace_bytes.argtypes = [ctypes.POINTER(_Layout), i32, i32, i32, i32, ctypes.POINTER(sz)]
@@ -154,6 +155,12 @@ def build_codebook_seeded(head_dim: int, bits: int, mode: int, seed: int) -> np.
     _check(_lib().tq_build_codebook_seeded(head_dim, bits, mode, ctypes.c_uint64(seed & (2 ** 64 - 1)),
                                            blob.ctypes.data, n), "tq_build_codebook_seeded")
     return blob
+
+
+def stream_read(buf, blocks: int, sink, stream=None) -> None:
+    """Plain streaming read of the device tensor ``buf`` (tq_stream_read); ``sink``: a device uint32/int32 tensor."""
+    _check(_lib().tq_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), blocks, sink.data_ptr(),
+                                 _stream(stream)), "tq_stream_read")
 
 
 def page_layout(layout: Layout) -> dict:

@@ -35,6 +35,7 @@ SOURCES = [
     ("tq_quantize.hip", "tq_quantize.o", []),
     ("tq_dense.hip", "tq_dense.o", ["-fno-honor-nans"]),
     ("tq_rotate.hip", "tq_rotate.o", []),
+    ("tq_stream.hip", "tq_stream.o", []),
     ("tq_qr.cpp", "tq_qr.o", []),
     ("tq_prefill.hip", "tq_prefill.o", ["-fno-honor-nans"]),
     ("tq_decode.hip", "tq_decode_d128_pk.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=1"]),

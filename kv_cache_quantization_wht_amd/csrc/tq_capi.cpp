@@ -380,6 +380,12 @@ int tq_build_codebook_seeded(int head_dim, int bits, int mode, uint64_t seed, vo
   return tq_build_codebook(head_dim, bits, mode, signs.data(), S.empty() ? nullptr : S.data(), blob, blob_bytes);
 }
 
+int tq_stream_read(const void *buf, size_t bytes, int blocks, uint32_t *sink, void *stream) {
+  if (!buf || !sink || bytes == 0 || bytes % 16 || ((uintptr_t)buf & 15) || blocks < 1 || blocks > (1 << 20))
+    return TQ_EINVAL;
+  return tq::launch_stream_read(buf, (int64_t)bytes, blocks, sink, (hipStream_t)stream);
+}
+
 int tq_page_layout(const tq_layout *layout, tq_page_offsets *out) {
   if (!out) return TQ_EINVAL;
   tq::PageGeom g;

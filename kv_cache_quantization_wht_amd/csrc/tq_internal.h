@@ -46,6 +46,9 @@ constexpr int kDecodeMaxSplits = 2048;
 int plan_decode(const PageGeom &g, int batch, int num_q_heads, int max_pages_per_seq,
                 int pages_per_split, DecodeWs *ws);
 
+// Plain streaming read of `bytes` (a multiple of 16) bytes at `buf` by `blocks` work-groups.
+int launch_stream_read(const void *buf, int64_t bytes, int blocks, uint32_t *sink, hipStream_t stream);
+
 // The allocation-free decode entry point keeps its split partials in one fixed device array of this many
 // bytes (per device, for the life of the process); decode_scratch gives its address on the current device.
 constexpr size_t kDecodeScratchBytes = TQ_DECODE_NOALLOC_MAX_BYTES;

@@ -97,6 +97,17 @@ def attention_error(out_gpu, out_ref):
     return attention.relative_error(np.asarray(out_gpu, dtype=np.float64), out_ref)
 
 
+def end_to_end_reference(q, k_raw, v_raw, cb_k, cb_v, scale):
+    """The oracle's attention of the query rows q [G, d] over its own encoding of the raw keys and values
+    [T, d] (fp64): the end-to-end figure, which includes any allowed code flip of the GPU's encoding, next to
+    the gated one (the oracle run on the GPU's own records)."""
+    ek = codec.encode(np.asarray(k_raw, dtype=np.float64), cb_k)
+    ev = codec.encode(np.asarray(v_raw, dtype=np.float64), cb_v)
+    K = codec.dequantize(ek.codes, ek.norm16, cb_k, ek.gamma16, ek.qjl)
+    V = codec.dequantize(ev.codes, ev.norm16, cb_v, ev.gamma16, ev.qjl)
+    return attention.reference_attention(np.asarray(q, dtype=np.float64), K, V, scale)
+
+
 def seeded_kv(n_tok, H, d, seed, recipe="lognormal", dtype="bf16", v_mult=1.0):
     """K/V test tensors: K with log-normal channel scales, V unit normal, and by recipe
       plain      nothing planted

@@ -8,7 +8,9 @@ are checked against the oracle one by one.
              every KV head, K and V: the oracle's encoding of the same input vectors, under the code /
              norm / sketch rules of the other quantize tests
   attention  sampled (sequence, KV head) pairs: all G query heads against the oracle run on the GPU's
-             own pages of that sequence, max relative error <= 2e-3
+             own pages of that sequence, max relative error <= 2e-3; and, reported (not gated), the end-to-end
+             figure of the first and last pair: against the oracle's attention over its own encoding of the raw
+             K/V of the whole sequence
 """
 import numpy as np
 import pytest
@@ -59,8 +61,11 @@ def test_full_size_layer(case):
 
     # prefill, sequence by sequence; keep the input vectors of the sampled tokens
     samples = []  # (b, token positions, k [n, H, d], v [n, H, d]) as fp64 host arrays
+    raw = {}  # (b, KV head) -> raw K, V [T, d] of the end-to-end pairs
     for b in range(B):
         k, v = kvsynth.make_kv(wl, wi, layer, T, device="cuda", token_offset_seed=2 + b)
+        for g in {0: [0], B - 1: [H - 1]}.get(b, []) if B > 1 else [0, H - 1]:
+            raw[(b, g)] = (k[:, g].double().cpu().numpy(), v[:, g].double().cpu().numpy())
         slots = torch.from_numpy(kvsynth.slots_for(pt, b, 0, T)).cuda()
         tq.quantize_kv(layout, pages, k, v, slots, kcb, vcb)
         if b in (0, B - 1) or b % 7 == 3:
@@ -117,5 +122,11 @@ def test_full_size_layer(case):
         worst = max(worst, err)
         assert err <= parity.ATTN_TOL, (b, g, err)
     print(f"  attention: {len(picks)} (sequence, KV head) pairs, max relative error {worst:.2e}", flush=True)
+    for (b, g), (kr, vr) in sorted(raw.items()):
+        kr = np.concatenate([kr, kn[b:b + 1, g]])
+        vr = np.concatenate([vr, vn[b:b + 1, g]])
+        e2e = parity.end_to_end_reference(qh[b, g * G:(g + 1) * G], kr, vr, cbk, cbv, wl.softmax_scale)
+        print(f"  end to end (the oracle's own codes of the raw K/V), sequence {b} KV head {g}: relative error "
+              f"{parity.attention_error(out[b, g * G:(g + 1) * G], e2e):.2e}", flush=True)
     del pages
     torch.cuda.empty_cache()
