@@ -394,6 +394,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   constexpr int KBLK = D / 32;  // 32-coordinate blocks of the score contraction
   constexpr int NB = D / 16;    // 16-coordinate blocks of the value contraction
   constexpr int QF = 16 * D;    // floats in one [16][D] block
+  constexpr bool LUT = KB == 4 && VB == 2 && D == 128 && !KPROD;
   using F = Frag<D, KB, KPROD, VB>;
 
   // Every argument the prologue needs, fetched from the argument segment in one round trip (left to
@@ -426,6 +427,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   __shared__ float s_m[kWaves][16], s_l[kWaves][16];
   __shared__ float s_rowm[16], s_rowl[16];
   __shared__ __align__(16) float s_newlev[APPEND ? 2 : 1][APPEND ? D : 4];  // appended token: K and V levels
+  // LUT (4-bit K, 2-bit V, head_dim 128): codes become fp16 levels through LDS lookups. Row x (256 bytes) of the
+  // table holds, for the code byte x, the K entry (levels of its two 4-bit codes, one dword) 32 times in bytes
+  // 0..127 and the V entry (levels of its four 2-bit codes, two dwords) 16 times in bytes 128..255: lane l reads
+  // copy l % 32 (K) or l % 16 (V), so the 32 lanes of a 4-byte read or the 16 lanes of an 8-byte read fall in
+  // distinct banks. The row address is the code byte itself shifted up by 8 bits, so one v_perm of the code word
+  // and the lane's copy offset forms each address.
+  __shared__ __align__(16) uint32_t s_lut[LUT ? 256 * 64 : 4];
+  auto lut_read = [&](uint32_t byte_addr) { return *(const uint32_t *)((const unsigned char *)s_lut + byte_addr); };
+  auto lut_read2 = [&](uint32_t byte_addr) { return *(const uint2 *)((const unsigned char *)s_lut + byte_addr); };
   __shared__ float s_newnorm[2];
   float(*s_q)[QS] = (float(*)[QS])arena;              // rotated queries / d
   float(*s_qs)[QS] = (float(*)[QS])(arena + 16 * QS);  // sketch-domain queries
@@ -584,6 +594,23 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   // level tables and rotated queries
   // pairs [0, n_full) of the run hold only cached tokens of valid pages: they need no masking
   const bool all_ok = __syncthreads_and(pids_ok);
+  if constexpr (LUT) {
+    // thread pair (2x, 2x + 1) writes row x: the even thread the K copies, the odd one the V copies, 16 bytes at a
+    // time starting at a chunk that rotates with the lane, so the 8 lanes of a 16-byte store cycle hit all banks
+    const int x = tid >> 1;
+    uint4 val;
+    if ((tid & 1) == 0) {
+      const uint32_t e = (uint32_t)s_lutk[x & 15] | ((uint32_t)s_lutk[x >> 4] << 16);
+      val = uint4{e, e, e, e};
+    } else {
+      const uint32_t e0 = (uint32_t)s_lutv[x & 3] | ((uint32_t)s_lutv[(x >> 2) & 3] << 16);
+      const uint32_t e1 = (uint32_t)s_lutv[(x >> 4) & 3] | ((uint32_t)s_lutv[x >> 6] << 16);
+      val = uint4{e0, e1, e0, e1};
+    }
+    uint4 *row = (uint4 *)&s_lut[x * 64 + (tid & 1) * 32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) row[(i + lane) & 7] = val;
+  }
   const int full_end = min(p_end, seq_mem / TQ_PAGE_TOKENS);
   const int n_full = (all_ok && full_end > p_begin) ? (full_end - p_begin) / 2 : 0;
   if constexpr (KPROD) {
@@ -626,7 +653,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       const float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
-        const float x = real ? v[k_order<KB>(p)] * sig : 0.f;
+        const float x = real ? v[LUT ? p : k_order<KB>(p)] * sig : 0.f;
         _Float16 h, l;
         split_hi_lo(x, h, l);
         if constexpr (PK) {
@@ -656,9 +683,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     }
   }
   Tab tk{0, 0, 0, 0}, tv{0, 0, 0, 0};
-  if constexpr (KB == 4) tk = make_tab_k4(s_lutk);
+  // LUT: byte 0 of these words is the lane's copy offset inside a table row (K: bytes 0..127, V: 128..255)
+  const uint32_t lut_kb = (uint32_t)(lane & 31) * 4u, lut_vb = 128u + (uint32_t)(lane & 15) * 8u;
+  if constexpr (LUT) __syncthreads();  // the table is complete
+  if constexpr (KB == 4 && !LUT) tk = make_tab_k4(s_lutk);
   if constexpr (KB == 3) tk = make_tab_k3(s_lutk);
-  if constexpr (VB == 2) tv = make_tab_v2(s_lutv);
+  if constexpr (VB == 2 && !LUT) tv = make_tab_v2(s_lutv);
   if constexpr (VB == 3 && D == 128) tv = make_tab_k3(s_lutv);
   // 1-bit levels: the high byte of the negative and the positive level, and the low byte in all four bytes
   uint32_t lev1_hitab = 0, lev1_lo4 = 0;
@@ -721,7 +751,27 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   // fp16 V levels of one page pair as MFMA operands: Bop[nb] holds, for lane (c, g4), the level of
   // coordinate (D / 16) * c + nb for the 8 tokens of contraction rows 8 * g4 .. 8 * g4 + 7.
   auto v_operands = [&](const F &cur, half8_t *Bop) {
-    if constexpr (VB == 3 && D == 128) {
+    if constexpr (LUT) {
+      // each code byte (four coordinates of one token) looked up once; the levels of a coordinate for a token pair
+      // are then paired into one dword (two fp16 halves)
+      uint32_t pairs[8][4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t vw = cur.vw[w >> 1][w & 1];  // tokens 2(w&1), 2(w&1) + 1 of the page: bytes a0, a1, b0, b1
+        const uint2 a0 = lut_read2(perm(vw, lut_vb, 0x0C0C0400u)), a1 = lut_read2(perm(vw, lut_vb, 0x0C0C0500u));
+        const uint2 b0 = lut_read2(perm(vw, lut_vb, 0x0C0C0600u)), b1 = lut_read2(perm(vw, lut_vb, 0x0C0C0700u));
+        pairs[0][w] = perm(b0.x, a0.x, 0x05040100u);
+        pairs[1][w] = perm(b0.x, a0.x, 0x07060302u);
+        pairs[2][w] = perm(b0.y, a0.y, 0x05040100u);
+        pairs[3][w] = perm(b0.y, a0.y, 0x07060302u);
+        pairs[4][w] = perm(b1.x, a1.x, 0x05040100u);
+        pairs[5][w] = perm(b1.x, a1.x, 0x07060302u);
+        pairs[6][w] = perm(b1.y, a1.y, 0x05040100u);
+        pairs[7][w] = perm(b1.y, a1.y, 0x07060302u);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) Bop[nb] = from_dwords(pairs[nb][0], pairs[nb][1], pairs[nb][2], pairs[nb][3]);
+    } else if constexpr (VB == 3 && D == 128) {
       // each token's 24-bit group (code nb = coordinate nb of the lane's group) spread one code pair per byte;
       // then per byte k and page, the four tokens' pair k gathered into one dword
       uint32_t X[2][4];
@@ -801,7 +851,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int kb = 0; kb < KBLK; ++kb) {
         half8_t A;
-        if constexpr (KB == 4) {
+        if constexpr (LUT) {
+          // dword j of the operand: the levels of coordinates 2j, 2j + 1 (code byte j) from table row byte j
+          const uint32_t w = cur.kw[q2][kb];
+          A = from_dwords(lut_read(perm(w, lut_kb, 0x0C0C0400u)), lut_read(perm(w, lut_kb, 0x0C0C0500u)),
+                          lut_read(perm(w, lut_kb, 0x0C0C0600u)), lut_read(perm(w, lut_kb, 0x0C0C0700u)));
+        } else if constexpr (KB == 4) {
           A = lut_k4(cur.kw[q2][kb], tk);
         } else if constexpr (KB == 3) {
           A = lut_k3(k3_field(cur.kw[q2], kb), tk);
