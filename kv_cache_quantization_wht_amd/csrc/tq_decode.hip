@@ -337,8 +337,8 @@ __device__ __forceinline__ void append_quantize(const DecodeArgs &a, bool is_v, 
 #pragma unroll
   for (int k = 0; k < 8; ++k) ss = fmaf(x[k], x[k], ss);
   ss = group_sum<D / 8>(ss);
-  const float n = sqrtf(ss);
-  const float inv = n > 0.f ? 1.0f / n : 0.f;
+  float n, inv;
+  norm_and_inverse(ss, n, inv);
   const uint32_t sbits = (in.sword >> ((8 * lq) & 31)) & 0xFFu;
 #pragma unroll
   for (int k = 0; k < 8; ++k)
@@ -361,9 +361,8 @@ __device__ __forceinline__ void append_quantize(const DecodeArgs &a, bool is_v, 
   uint32_t packed = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const float y = x[k] * inv;
-    const bool neg = y < 0.f;
-    const int z = (int)(__float_as_uint(y) & 0x7FFFFFFFu) - (neg ? 1 : 0);
+    const bool neg = x[k] < 0.f;
+    const int z = __float_as_int(fabsf(x[k]) * inv);
     const int mag = magnitude_count<4>(z, in.P);  // thresholds past the code's own are +inf
     const int code = neg ? mag : (half | mag);
     packed |= (uint32_t)code << (nbits * k);

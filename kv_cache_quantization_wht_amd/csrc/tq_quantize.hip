@@ -3,15 +3,21 @@
 //   idx_i = #{j : y'_i >= t_j}      (Gaussian Lloyd-Max thresholds, midpoints of the fp16 levels),
 //   code_i = sign-magnitude form of idx_i, pack the b-bit codes, store n as fp16, and in prod mode also
 //   r = (y' - level[code]) / sqrt(d), gamma = ||r||, z_j = [(S r)_j >= 0].
+// The kernels decide in fp32: the code's top bit is set unless the rotated coordinate is negative, and its
+// magnitude is the number of positive thresholds at or below |y| (the thresholds are symmetric about 0, so this
+// is idx_i except where |y| falls exactly on a threshold, which it then takes to the larger magnitude).
 // MSE mode: one vector is handled by d/32 lanes that each own 32 consecutive coordinates: the five lowest
-// Walsh-Hadamard stages run in registers, the others exchange values between lanes with DPP moves. A lane's
-// 32 codes are 4b whole bytes of the vector's bit stream (four whole V pieces), so each lane writes its own
-// bytes. The vectors of a work-group are consecutive tokens of one head, so the records they write are
+// Walsh-Hadamard stages run in registers, the others combine values across lanes with one DPP fmac per value.
+// A lane's 32 codes are 4b whole bytes of the vector's bit stream (four whole V pieces), so each lane writes
+// its own bytes. The vectors of a work-group are consecutive tokens of one head, so the records they write are
 // neighbours in a page. The code width is a compile-time parameter (one uniform switch per work-group).
+// The kernel is bound by its vector ALU work, so each step is shaped for instruction count: the signs are
+// applied to the packed bf16 input (one xor per two coordinates), the code bits are shifted into the packed
+// stream by add-with-carry, and a lane group quantizes several vectors with the next one's input in flight.
 // Prod mode runs in its own kernel: the MSE steps with d/8 lanes of 8 coordinates per vector, then the
 // residual sketch S r, a dense d x d product per vector, on MFMA for 16 vectors at a time (Z^T = R S^T) with
 // S held in registers for a long run of tokens. Both layouts (and the decode step's append) take the norm's
-// partial sums and the butterflies in the same order, so they write the same bytes.
+// partial sums, the butterflies and the code rule in the same order, so they write the same bytes.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -43,6 +49,7 @@ struct QuantArgs {
 };
 
 constexpr int kProdChunk = 1024;  // tokens per work-group of the prod kernel (S is loaded once per work-group)
+constexpr int kQuantPasses = 4;   // vectors per lane group of one MSE work-group
 
 // One vector: norm, signs, rotation, codes, record write. Leaves the rotated unit vector y (N(0,1)/sqrt(d)
 // units), the stored codes, whether the slot is valid and the byte offset of the record's page for the
@@ -64,8 +71,8 @@ __device__ __forceinline__ void quantize_vector(const QuantArgs &a, int which, f
 #pragma unroll
   for (int k = 0; k < 8; ++k) ss = fmaf(x[k], x[k], ss);
   ss = group_sum<LANES>(ss);
-  const float n = sqrtf(ss);
-  const float inv = n > 0.f ? 1.0f / n : 0.f;
+  float n, inv;
+  norm_and_inverse(ss, n, inv);
 
   const uint32_t sbits = (sword >> ((8 * lane) & 31)) & 0xFFu;
 #pragma unroll
@@ -88,24 +95,21 @@ __device__ __forceinline__ void quantize_vector(const QuantArgs &a, int which, f
   wht_lanes<4>(x, lane);
   if constexpr (LANES == 16) wht_lanes<8>(x, lane);
 
-  // Lloyd-Max index (ties to the upper cell) in its stored sign-magnitude form: the top bit marks the
-  // non-negative half, the low bits count the rank away from zero. For y < 0 the rank counts thresholds
-  // strictly below |y|, i.e. thresholds at or below the next float under |y|.
+  // the stored sign-magnitude code: the top bit set unless the coordinate is negative, the low bits the number
+  // of positive thresholds at or below |y| (the rule of the 32-coordinate layout's push_code)
   const PosThresholdsV PV = thresholds_in_vgprs(P);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     y[k] = x[k] * inv;
-    const bool neg = y[k] < 0.f;
-    const int z = (int)(__float_as_uint(y[k]) & 0x7FFFFFFFu) - (neg ? 1 : 0);
+    const bool neg = x[k] < 0.f;
+    const int z = __float_as_int(fabsf(x[k]) * inv);
     int mag;
     if constexpr (BT >= 1) {
       mag = magnitude_v<BT>(z, PV);
-    } else {
-      // wide codes: binary search over all thresholds in LDS, then the sign-magnitude form
-      int c = 0;
-      for (int st = half; st > 0; st >>= 1)
-        if (y[k] >= s_th[c + st - 1]) c += st;
-      mag = c >= half ? c - half : half - 1 - c;
+    } else {  // wide codes: binary search over the positive thresholds in LDS
+      mag = 0;
+      for (int st = half >> 1; st > 0; st >>= 1)
+        if (z >= __float_as_int(s_th[half - 1 + mag + st])) mag += st;
     }
     code[k] = neg ? mag : (half | mag);
   }
@@ -143,11 +147,11 @@ __device__ __forceinline__ void quantize_vector(const QuantArgs &a, int which, f
 // (norm, reciprocal, record addresses) is shared by fewer lanes and a lane writes 4b bytes of a K record or
 // four b-byte V pieces. The norm's partial sums (8 coordinates, then pairs, then lanes) and the butterflies
 // (ascending strides) are taken in the same order as the 8-coordinate layout of the prod kernel and of the
-// decode step's append, so every layout writes the same bytes.
+// decode step's append, so every layout writes the same bytes. x: the lane's 32 coordinates with the
+// codebook's signs applied.
 template <int D, int BT>
 __device__ __forceinline__ void quantize_vector32(const QuantArgs &a, int which, float *x, int64_t slot, bool active,
-                                                  int h, int lane, uint32_t sword, const PosThresholds &P,
-                                                  const float *s_th) {
+                                                  int h, int lane, const PosThresholdsV &PV, const float *s_th) {
   constexpr int LANES = D / 32;
   static_assert(BT >= 1 && BT <= 8 && BT != 5 && BT != 6 && BT != 7, "MSE code widths 1, 2, 3, 4, 8");
   constexpr int half = (1 << BT) >> 1;
@@ -164,12 +168,9 @@ __device__ __forceinline__ void quantize_vector32(const QuantArgs &a, int which,
   float ss = (s8[0] + s8[1]) + (s8[2] + s8[3]);
   ss += xor_lane<1>(ss);
   if constexpr (LANES == 4) ss += xor_lane<2>(ss);
-  const float n = sqrtf(ss);
-  const float inv = n > 0.f ? 1.0f / n : 0.f;
+  float n, inv;
+  norm_and_inverse(ss, n, inv);
 
-#pragma unroll
-  for (int k = 0; k < 32; ++k)
-    if ((sword >> k) & 1u) x[k] = -x[k];
 #pragma unroll
   for (int hs = 1; hs < 32; hs <<= 1) {
 #pragma unroll
@@ -181,84 +182,115 @@ __device__ __forceinline__ void quantize_vector32(const QuantArgs &a, int which,
       }
     }
   }
+  // the lane stages leave every value times the lane's factor (-1)^(number of set lane bits)
+  const float f1 = (lane & 1) ? -1.f : 1.f;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const float p = xor_lane<1>(x[k]);
-    x[k] = (lane & 1) ? (p - x[k]) : (x[k] + p);
-  }
+  for (int k = 0; k < 32; k += 8) wht_lane_signed8<1>(x + k, f1);
+  bool flip = (lane & 1) != 0;
   if constexpr (LANES == 4) {
+    const float f2 = (lane & 2) ? -1.f : 1.f;
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      const float p = xor_lane<2>(x[k]);
-      x[k] = (lane & 2) ? (p - x[k]) : (x[k] + p);
-    }
+    for (int k = 0; k < 32; k += 8) wht_lane_signed8<2>(x + k, f2);
+    flip = flip != ((lane & 2) != 0);
   }
+  // v_cmp_class mask of the values that are not negative coordinates (the lane may hold them negated)
+  const int nn_class = flip ? 0x07F : 0x3E3;
 
-  // codes (sign-magnitude, ties to the upper cell), packed into the lane's 32 * b bits as they come
+  // codes (sign-magnitude), packed into the lane's 32 * b bits: for 1, 2 and 4 bits each dword's codes are
+  // shifted in from its highest coordinate down; 3-bit codes straddle dwords and are placed by shifts
   constexpr int BW = BT;  // dwords of the lane's 32 * BT bit stream
-  const PosThresholdsV PV = thresholds_in_vgprs(P);
   uint32_t w[BW];
+  if constexpr (BT == 1 || BT == 2 || BT == 4) {
+    constexpr int PER = 32 / BT;
 #pragma unroll
-  for (int i = 0; i < BW; ++i) w[i] = 0u;
+    for (int i = 0; i < BW; ++i) {
+      uint32_t wi = 0u;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const float y = x[k] * inv;
-    const bool neg = y < 0.f;
-    const int z = (int)(__float_as_uint(y) & 0x7FFFFFFFu) - (neg ? 1 : 0);
-    int mag;
-    if constexpr (BT <= 4) {
-      mag = magnitude_v<BT>(z, PV);
-    } else {  // 8-bit codes: binary search over all thresholds in LDS
-      int c = 0;
-      for (int st = half; st > 0; st >>= 1)
-        if (y >= s_th[c + st - 1]) c += st;
-      mag = c >= half ? c - half : half - 1 - c;
-    }
-    const uint32_t code = (uint32_t)(neg ? mag : (half | mag));
-    const int bit = BT * k;
-    w[bit >> 5] |= code << (bit & 31);
-    if ((bit & 31) + BT > 32) w[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
-  }
-  if (!valid) return;
-  const int64_t page = slot / TQ_PAGE_TOKENS;
-  const int off = (int)(slot % TQ_PAGE_TOKENS);
-  unsigned char *pg = a.pages + page * a.page_bytes;
-  if (which == 0) {
-    uint32_t *dst = (uint32_t *)(pg + a.codes_off[0] + (int64_t)(h * TQ_PAGE_TOKENS + off) * (D * BT / 8) + lane * 4 * BT);
-    if constexpr (BT == 8) {
-      ((uint4 *)dst)[0] = uint4{w[0], w[1], w[2], w[3]};
-      ((uint4 *)dst)[1] = uint4{w[4], w[5], w[6], w[7]};
-    } else if constexpr (BT == 4) {
-      *(uint4 *)dst = uint4{w[0], w[1], w[2], w[3]};
-    } else if constexpr (BT == 2) {
-      *(uint2 *)dst = uint2{w[0], w[1]};
-    } else {
-#pragma unroll
-      for (int i = 0; i < BT; ++i) dst[i] = w[i];
+      for (int j = PER - 1; j >= 0; --j) push_code<BT>(wi, x[PER * i + j], inv, nn_class, PV);
+      w[i] = wi;
     }
   } else {
-    // piece i (codes 8i .. 8i + 7 of the lane) = bits 8 * BT * i .. of the lane's stream
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      unsigned char *dst = pg + a.codes_off[1] + ((int64_t)(h * (D / 8) + 4 * lane + i) * TQ_PAGE_TOKENS + off) * BT;
-      const int bit = 8 * BT * i;
-      const uint64_t two = (uint64_t)w[bit >> 5] | ((bit >> 5) + 1 < BW ? (uint64_t)w[(bit >> 5) + 1] << 32 : 0ull);
-      const uint64_t piece = two >> (bit & 31);
-      if constexpr (BT == 1) *dst = (unsigned char)piece;
-      else if constexpr (BT == 2) *(uint16_t *)dst = (uint16_t)piece;
-      else if constexpr (BT == 4) *(uint32_t *)dst = (uint32_t)piece;
-      else if constexpr (BT == 8) *(uint64_t *)dst = piece;
-      else {
+    for (int i = 0; i < BW; ++i) w[i] = 0u;
 #pragma unroll
-        for (int q = 0; q < BT; ++q) dst[q] = (unsigned char)(piece >> (8 * q));
+    for (int k = 0; k < 32; ++k) {
+      uint32_t code;
+      if constexpr (BT == 3) {
+        code = 0u;
+        push_code<3>(code, x[k], inv, nn_class, PV);
+      } else {  // 8-bit codes: binary search over the positive thresholds in LDS
+        const int z = __float_as_int(fabsf(x[k]) * inv);
+        int c = 0;
+#pragma unroll
+        for (int st = half >> 1; st > 0; st >>= 1)
+          if (z >= __float_as_int(s_th[half - 1 + c + st])) c += st;
+        code = (uint32_t)(__builtin_amdgcn_classf(x[k], nn_class) ? (half | c) : c);
       }
+      const int bit = BT * k;
+      w[bit >> 5] |= code << (bit & 31);
+      if ((bit & 31) + BT > 32) w[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
     }
   }
-  if (lane == 0)
-    *(uint16_t *)(pg + a.norms_off[which] + (int64_t)(h * TQ_PAGE_TOKENS + off) * 2) = float_to_half_bits(n);
+  if (valid) {
+    const int64_t page = slot / TQ_PAGE_TOKENS;
+    const int off = (int)(slot % TQ_PAGE_TOKENS);
+    unsigned char *pg = a.pages + page * a.page_bytes;
+    if (which == 0) {
+      uint32_t *dst = (uint32_t *)(pg + a.codes_off[0] + (int64_t)(h * TQ_PAGE_TOKENS + off) * (D * BT / 8) + lane * 4 * BT);
+      if constexpr (BT == 8) {
+        ((uint4 *)dst)[0] = uint4{w[0], w[1], w[2], w[3]};
+        ((uint4 *)dst)[1] = uint4{w[4], w[5], w[6], w[7]};
+      } else if constexpr (BT == 4) {
+        *(uint4 *)dst = uint4{w[0], w[1], w[2], w[3]};
+      } else if constexpr (BT == 2) {
+        *(uint2 *)dst = uint2{w[0], w[1]};
+      } else {
+#pragma unroll
+        for (int i = 0; i < BT; ++i) dst[i] = w[i];
+      }
+    } else {
+      // piece i (codes 8i .. 8i + 7 of the lane) = bits 8 * BT * i .. of the lane's stream
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        unsigned char *dst = pg + a.codes_off[1] + ((int64_t)(h * (D / 8) + 4 * lane + i) * TQ_PAGE_TOKENS + off) * BT;
+        const int bit = 8 * BT * i;
+        const uint64_t two = (uint64_t)w[bit >> 5] | ((bit >> 5) + 1 < BW ? (uint64_t)w[(bit >> 5) + 1] << 32 : 0ull);
+        const uint64_t piece = two >> (bit & 31);
+        if constexpr (BT == 1) *dst = (unsigned char)piece;
+        else if constexpr (BT == 2) *(uint16_t *)dst = (uint16_t)piece;
+        else if constexpr (BT == 4) *(uint32_t *)dst = (uint32_t)piece;
+        else if constexpr (BT == 8) *(uint64_t *)dst = piece;
+        else {
+#pragma unroll
+          for (int q = 0; q < BT; ++q) dst[q] = (unsigned char)(piece >> (8 * q));
+        }
+      }
+    }
+    if (lane == 0)
+      *(uint16_t *)(pg + a.norms_off[which] + (int64_t)(h * TQ_PAGE_TOKENS + off) * 2) = float_to_half_bits(n);
+  }
 }
 
-// A work-group holds VPB consecutive tokens of one head (K or V, MSE mode), one vector per D / 32 lanes.
+// The sign word of coordinates 32 * lane .. 32 * lane + 31, and its deinterleaved form (unshuffle_bits), from the
+// D / 32 words read through the scalar cache (the deinterleave runs once per wavefront on the scalar unit).
+template <int D>
+__device__ __forceinline__ void lane_sign_words(const unsigned char *signs, int lane, uint32_t &sword, uint32_t &W) {
+  const const_i32 sw = (const_i32)signs;
+  const uint32_t s0 = (uint32_t)sw[0], s1 = (uint32_t)sw[1];
+  if constexpr (D == 128) {
+    const uint32_t s2 = (uint32_t)sw[2], s3 = (uint32_t)sw[3];
+    const uint32_t u0 = unshuffle_bits(s0), u1 = unshuffle_bits(s1), u2 = unshuffle_bits(s2), u3 = unshuffle_bits(s3);
+    sword = (lane & 2) ? ((lane & 1) ? s3 : s2) : ((lane & 1) ? s1 : s0);
+    W = (lane & 2) ? ((lane & 1) ? u3 : u2) : ((lane & 1) ? u1 : u0);
+  } else {
+    static_assert(D == 64, "head_dim 64 or 128");
+    sword = (lane & 1) ? s1 : s0;
+    W = (lane & 1) ? unshuffle_bits(s1) : unshuffle_bits(s0);
+  }
+}
+
+// A work-group holds kQuantPasses * VPB consecutive tokens of one head (K or V, MSE mode): in each pass one
+// vector per D / 32 lanes, the next pass's input rows already in flight (bf16 inputs).
 template <int D, int BT>
 __device__ __forceinline__ void quantize_tokens(const QuantArgs &a, int which, float *s_th) {
   constexpr int LANES = D / 32;
@@ -271,23 +303,67 @@ __device__ __forceinline__ void quantize_tokens(const QuantArgs &a, int which, f
   const int lane = threadIdx.x % LANES;
   const int vl = threadIdx.x / LANES;
   const int h = blockIdx.x % a.H;
-  const int64_t t = (int64_t)(blockIdx.x / a.H) * VPB + vl;
-  const int64_t tc = t < a.n_tok ? t : 0;
+  const int64_t t0 = (int64_t)(blockIdx.x / a.H) * (VPB * kQuantPasses);  // first token of the work-group
 
-  const uint32_t sword = ((const uint32_t *)(cb + bo.signs))[lane];
+  uint32_t sword, W;
+  lane_sign_words<D>(cb + bo.signs, lane, sword, W);
   // positive thresholds (t[half-1] is 0 by symmetry), as integer bit patterns
-  PosThresholds P{};
+  PosThresholdsV PV{};
   if constexpr (BT <= 4) {
-    P = pos_thresholds((const_i32)(cb + bo.thresholds), half);
+    PV = thresholds_in_vgprs(pos_thresholds((const_i32)(cb + bo.thresholds), half));
   } else {
     for (int i = threadIdx.x; i < nl - 1; i += 256) s_th[i] = ((const float *)(cb + bo.thresholds))[i];
     __syncthreads();
   }
-  const int64_t slot = a.slots[tc];
-  float x[32];
+  const void *in = a.in[which];
+  const int64_t stride = a.stride[which];
+  const int64_t col = (int64_t)h * D + 32 * lane;
+  if (a.dtype == TQ_BF16) {
+    // the signs of coordinate pairs 2j, 2j + 1 at bits 15 and 31: one xor negates both bf16 values of a dword
+    uint32_t sm[16];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) load8(a.in[which], tc * a.stride[which] + (int64_t)h * D + 32 * lane + 8 * g, a.dtype, x + 8 * g);
-  quantize_vector32<D, BT>(a, which, x, slot, t < a.n_tok, h, lane, sword, P, s_th);
+    for (int j = 0; j < 16; ++j) sm[j] = (W << (15 - j)) & 0x80008000u;
+    auto fetch = [&](int64_t t, uint32_t *d, int64_t &slot) {
+      const int64_t tc = t < a.n_tok ? t : 0;
+      const uint4 *src = (const uint4 *)((const uint16_t *)in + tc * stride + col);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint4 u = src[g];
+        d[4 * g] = u.x; d[4 * g + 1] = u.y; d[4 * g + 2] = u.z; d[4 * g + 3] = u.w;
+      }
+      slot = a.slots[tc];
+    };
+    uint32_t d[2][16];
+    int64_t slot[2];
+    fetch(t0 + vl, d[0], slot[0]);
+#pragma unroll
+    for (int v = 0; v < kQuantPasses; ++v) {
+      const int64_t tp = t0 + (int64_t)v * VPB;  // first token of the pass
+      if (tp >= a.n_tok) break;
+      if (v + 1 < kQuantPasses && tp + VPB < a.n_tok) fetch(tp + VPB + vl, d[(v + 1) & 1], slot[(v + 1) & 1]);
+      float x[32];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t u = d[v & 1][j] ^ sm[j];
+        x[2 * j] = __uint_as_float(u << 16);
+        x[2 * j + 1] = __uint_as_float(u & 0xFFFF0000u);
+      }
+      quantize_vector32<D, BT>(a, which, x, slot[v & 1], tp + vl < a.n_tok, h, lane, PV, s_th);
+    }
+  } else {
+#pragma unroll 1
+    for (int v = 0; v < kQuantPasses; ++v) {
+      const int64_t tp = t0 + (int64_t)v * VPB;
+      if (tp >= a.n_tok) break;
+      const int64_t t = tp + vl;
+      const int64_t tc = t < a.n_tok ? t : 0;
+      float x[32];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) load8(in, tc * stride + col + 8 * g, a.dtype, x + 8 * g);
+      apply_signs32(x, sword);
+      quantize_vector32<D, BT>(a, which, x, a.slots[tc], t < a.n_tok, h, lane, PV, s_th);
+    }
+  }
 }
 
 template <int D>
@@ -355,9 +431,9 @@ __device__ __forceinline__ void quantize_qr_tiles(const QuantArgs &a, int which,
       }
   }
   const uint32_t sword = ((const uint32_t *)(cb + bo.signs))[ln];
-  PosThresholds P{};
+  PosThresholdsV PV{};
   if constexpr (BT <= 4) {
-    P = pos_thresholds((const_i32)(cb + bo.thresholds), half);
+    PV = thresholds_in_vgprs(pos_thresholds((const_i32)(cb + bo.thresholds), half));
   } else {
     for (int i = tid; i < (1 << BT) - 1; i += 256) s_th[i] = ((const float *)(cb + bo.thresholds))[i];
     __syncthreads();
@@ -451,7 +527,8 @@ __device__ __forceinline__ void quantize_qr_tiles(const QuantArgs &a, int which,
         x[4 * k + 2] = u.z;
         x[4 * k + 3] = u.w;
       }
-      quantize_vector32<D, BT>(a, which, x, slot, t < a.n_tok, h, ln, sword, P, s_th);
+      apply_signs32(x, sword);
+      quantize_vector32<D, BT>(a, which, x, slot, t < a.n_tok, h, ln, PV, s_th);
     }
     __syncthreads();
   }
@@ -707,7 +784,7 @@ int launch_quantize(const PageGeom &g, void *pages, int64_t num_pages, const voi
     QuantArgs m = a;
     m.which_of_y[0] = mse_of[0];
     m.which_of_y[1] = mse_of[1];
-    const int vpb = 256 / (g.head_dim / 32);  // vectors per work-group: one per D / 32 lanes
+    const int vpb = 256 / (g.head_dim / 32) * kQuantPasses;  // vectors per work-group
     const int64_t blocks = (n_tok + vpb - 1) / vpb * g.num_kv_heads;
     if (blocks > 0x7FFFFFFF) return TQ_EINVAL;
     const dim3 grid((unsigned)blocks, n_mse);
