@@ -49,7 +49,7 @@ struct QuantArgs {
 };
 
 constexpr int kProdChunk = 1024;  // tokens per work-group of the prod kernel (S is loaded once per work-group)
-constexpr int kQuantPasses = 4;   // vectors per lane group of one MSE work-group
+constexpr int kQuantPasses = 2;   // vectors per lane group of one MSE work-group
 
 // One vector: norm, signs, rotation, codes, record write. Leaves the rotated unit vector y (N(0,1)/sqrt(d)
 // units), the stored codes, whether the slot is valid and the byte offset of the record's page for the
