@@ -51,6 +51,44 @@ struct QuantArgs {
 constexpr int kProdChunk = 1024;  // tokens per work-group of the prod kernel (S is loaded once per work-group)
 constexpr int kQuantPasses = 2;   // vectors per lane group of one MSE work-group
 
+// 8-bit codes: a bucket table over the bit patterns of |y| (non-negative floats order like their patterns). Bucket
+// b covers the patterns [(z0 + b) << kBucketShift, (z0 + b + 1) << kBucketShift); its entry holds the pattern of the
+// threshold inside it (INT_MAX if none) and the number of thresholds below it, so that the magnitude
+// #{m : P_m <= |y|} is base + [pattern(|y|) >= T] as long as no bucket holds two thresholds. That is checked while
+// the table is built (a bucket spans 1/64 of an octave; the Gaussian Lloyd-Max thresholds of 8-bit codes lie at
+// least 1.6% apart); otherwise the binary search over the thresholds is used.
+constexpr int kBucketShift = 17;
+constexpr int kMaxBuckets = 1024;
+struct CodeBuckets {
+  const uint2 *e;
+  int z0, nb;  // nb == 0: no table
+};
+
+// Every thread of the work-group calls this after s_th (the full threshold table) is in LDS.
+__device__ __forceinline__ CodeBuckets build_code_buckets(const float *s_th, int half, uint2 *s_bkt) {
+  const int npos = half - 1;  // positive thresholds P_m = s_th[half - 1 + m], m = 1 .. npos, ascending
+  auto P = [&](int m) { return __float_as_int(s_th[half - 1 + m]); };
+  const int z0 = P(1) >> kBucketShift;
+  const int nb = (P(npos) >> kBucketShift) - z0 + 2;
+  bool bad = nb > kMaxBuckets;
+  if (!bad) {
+    for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+      const int lo = (z0 + b) << kBucketShift, hi = lo + (1 << kBucketShift);
+      int base = 0;  // #{m : P_m < lo}
+      for (int st = half >> 1; st > 0; st >>= 1)
+        if (base + st <= npos && P(base + st) < lo) base += st;
+      int t = 0x7FFFFFFF;
+      if (base < npos && P(base + 1) < hi) {
+        t = P(base + 1);
+        if (base + 1 < npos && P(base + 2) < hi) bad = true;
+      }
+      s_bkt[b] = uint2{(uint32_t)t, (uint32_t)base};
+    }
+  }
+  bad = __syncthreads_or(bad);
+  return CodeBuckets{s_bkt, z0, bad ? 0 : nb};
+}
+
 // One vector: norm, signs, rotation, codes, record write. Leaves the rotated unit vector y (N(0,1)/sqrt(d)
 // units), the stored codes, whether the slot is valid and the byte offset of the record's page for the
 // prod kernel's residual. BT: the code width when it is 1..4 (then every shift, search and store is fixed
@@ -151,7 +189,8 @@ __device__ __forceinline__ void quantize_vector(const QuantArgs &a, int which, f
 // codebook's signs applied.
 template <int D, int BT>
 __device__ __forceinline__ void quantize_vector32(const QuantArgs &a, int which, float *x, int64_t slot, bool active,
-                                                  int h, int lane, const PosThresholdsV &PV, const float *s_th) {
+                                                  int h, int lane, const PosThresholdsV &PV, const float *s_th,
+                                                  const CodeBuckets &cbk) {
   constexpr int LANES = D / 32;
   static_assert(BT >= 1 && BT <= 8 && BT != 5 && BT != 6 && BT != 7, "MSE code widths 1, 2, 3, 4, 8");
   constexpr int half = (1 << BT) >> 1;
@@ -212,23 +251,44 @@ __device__ __forceinline__ void quantize_vector32(const QuantArgs &a, int which,
   } else {
 #pragma unroll
     for (int i = 0; i < BW; ++i) w[i] = 0u;
+    auto put = [&](int k, uint32_t code) {
+      const int bit = BT * k;
+      w[bit >> 5] |= code << (bit & 31);
+      if ((bit & 31) + BT > 32) w[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
+    };
+    if constexpr (BT == 3) {
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      uint32_t code;
-      if constexpr (BT == 3) {
-        code = 0u;
+      for (int k = 0; k < 32; ++k) {
+        uint32_t code = 0u;
         push_code<3>(code, x[k], inv, nn_class, PV);
-      } else {  // 8-bit codes: binary search over the positive thresholds in LDS
+        put(k, code);
+      }
+    } else if (cbk.nb) {  // 8-bit codes by the bucket table: eight lookups in flight at a time
+#pragma unroll
+      for (int k0 = 0; k0 < 32; k0 += 8) {
+        int z[8];
+        uint2 e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          z[j] = __float_as_int(fabsf(x[k0 + j]) * inv);
+          e[j] = cbk.e[min(max((z[j] >> kBucketShift) - cbk.z0, 0), cbk.nb - 1)];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = (int)e[j].y + (z[j] >= (int)e[j].x ? 1 : 0);
+          put(k0 + j, (uint32_t)(__builtin_amdgcn_classf(x[k0 + j], nn_class) ? (half | c) : c));
+        }
+      }
+    } else {  // 8-bit codes: binary search over the positive thresholds in LDS
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
         const int z = __float_as_int(fabsf(x[k]) * inv);
         int c = 0;
 #pragma unroll
         for (int st = half >> 1; st > 0; st >>= 1)
           if (z >= __float_as_int(s_th[half - 1 + c + st])) c += st;
-        code = (uint32_t)(__builtin_amdgcn_classf(x[k], nn_class) ? (half | c) : c);
+        put(k, (uint32_t)(__builtin_amdgcn_classf(x[k], nn_class) ? (half | c) : c));
       }
-      const int bit = BT * k;
-      w[bit >> 5] |= code << (bit & 31);
-      if ((bit & 31) + BT > 32) w[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
     }
   }
   if (valid) {
@@ -309,11 +369,14 @@ __device__ __forceinline__ void quantize_tokens(const QuantArgs &a, int which, f
   lane_sign_words<D>(cb + bo.signs, lane, sword, W);
   // positive thresholds (t[half-1] is 0 by symmetry), as integer bit patterns
   PosThresholdsV PV{};
+  CodeBuckets cbk{nullptr, 0, 0};
   if constexpr (BT <= 4) {
     PV = thresholds_in_vgprs(pos_thresholds((const_i32)(cb + bo.thresholds), half));
   } else {
+    __shared__ uint2 s_bkt[kMaxBuckets];
     for (int i = threadIdx.x; i < nl - 1; i += 256) s_th[i] = ((const float *)(cb + bo.thresholds))[i];
     __syncthreads();
+    cbk = build_code_buckets(s_th, half, s_bkt);
   }
   const void *in = a.in[which];
   const int64_t stride = a.stride[which];
@@ -348,7 +411,7 @@ __device__ __forceinline__ void quantize_tokens(const QuantArgs &a, int which, f
         x[2 * j] = __uint_as_float(u << 16);
         x[2 * j + 1] = __uint_as_float(u & 0xFFFF0000u);
       }
-      quantize_vector32<D, BT>(a, which, x, slot[v & 1], tp + vl < a.n_tok, h, lane, PV, s_th);
+      quantize_vector32<D, BT>(a, which, x, slot[v & 1], tp + vl < a.n_tok, h, lane, PV, s_th, cbk);
     }
   } else {
 #pragma unroll 1
@@ -361,7 +424,7 @@ __device__ __forceinline__ void quantize_tokens(const QuantArgs &a, int which, f
 #pragma unroll
       for (int g = 0; g < 4; ++g) load8(in, tc * stride + col + 8 * g, a.dtype, x + 8 * g);
       apply_signs32(x, sword);
-      quantize_vector32<D, BT>(a, which, x, a.slots[tc], t < a.n_tok, h, lane, PV, s_th);
+      quantize_vector32<D, BT>(a, which, x, a.slots[tc], t < a.n_tok, h, lane, PV, s_th, cbk);
     }
   }
 }
@@ -528,7 +591,7 @@ __device__ __forceinline__ void quantize_qr_tiles(const QuantArgs &a, int which,
         x[4 * k + 3] = u.w;
       }
       apply_signs32(x, sword);
-      quantize_vector32<D, BT>(a, which, x, slot, t < a.n_tok, h, ln, PV, s_th);
+      quantize_vector32<D, BT>(a, which, x, slot, t < a.n_tok, h, ln, PV, s_th, CodeBuckets{nullptr, 0, 0});
     }
     __syncthreads();
   }
