@@ -585,7 +585,8 @@ static int prefill_check(const tq_layout *layout, tq::PageGeom *g, const void *p
   if (!pages || !q || !page_table || !prefix_lens || !k_cb || !v_cb || !out) return TQ_EINVAL;
   if (((uintptr_t)pages | (uintptr_t)k_cb | (uintptr_t)v_cb) & 15) return TQ_EINVAL;
   if (((uintptr_t)q & (q_dtype == TQ_F32 ? 3 : 1)) || ((uintptr_t)out & 3)) return TQ_EINVAL;
-  const int64_t tiles = ((int64_t)chunk_len * (num_q_heads / g->num_kv_heads) + 63) / 64 + 1;  // 64 or 128 columns
+  // work-groups own 64 columns or more; this bound covers every column count
+  const int64_t tiles = ((int64_t)chunk_len * (num_q_heads / g->num_kv_heads) + 63) / 64 + 1;
   if (tiles * g->num_kv_heads * batch > 0x7FFFFFFF) return TQ_EINVAL;
   return TQ_OK;
 }

@@ -5,21 +5,23 @@
 //
 // A chunk of C new tokens of each sequence, at positions P_b .. P_b + C - 1, attends causally to the cached
 // tokens 0 .. its own position (its own keys and values already written to the pages, quantized). Where the
-// decode kernel gives every byte of a page to G query heads, here a work-group owns 128 query columns (64 with a
-// sketched K) - the (token, head) pairs of 128 / G (64 / G) consecutive tokens of one KV head - so one
+// decode kernel gives every byte of a page to G query heads, here a work-group of eight wavefronts owns 256 query
+// columns (128 with a sketched K) - the (token, head) pairs of 256 / G consecutive tokens of one KV head - so one
 // dequantization serves all of them and the contraction runs on the matrix cores:
 //   1. Query rotation as in decode (signs, Walsh-Hadamard butterflies, 1/d, a power-of-two range factor per
 //      column), the fp16 hi and lo parts of each column kept in registers as MFMA operands.
-//   2. Steps of 32 keys (two pages). All 256 threads load the next step's codes and norms while the
-//      wavefronts compute this one, then look the codes up in the level tables and store fp16 levels in a
-//      double-buffered LDS tile: K as [key][coordinate], V as [coordinate][key] in the key order of the
-//      softmax operand. One barrier per step.
-//        scores  S^T[16 keys, 16 columns] = Khat Q on MFMA 16x16x32 f16 (hi and lo query parts), plus for a
-//                sketched K gamma * <q_s, z> from a second tile of the keys' sketch signs, times the key norms;
-//                causal mask per column where the step reaches past a column's position;
-//        softmax running maximum per column (base 2), sums per lane;
-//        values  O^T[coordinates, columns] += Vhat^T P'^T with P' = p * ||v|| as fp16 hi + lo (each column's
-//                weights shifted by a power of two that keeps them in the fp16 range).
+//   2. Steps of 32 keys (two pages), in two groups of four wavefronts half a step apart: while one group's
+//      wavefronts run a matrix phase the other's run the softmax, on the same SIMDs, with a barrier between phases.
+//        matrix phase M_j: values O^T[coordinates, columns] += Vhat^T P'^T of step j - 1 (P' = p * ||v|| as fp16
+//                hi + lo, each column's weights shifted by a power of two that keeps them in the fp16 range);
+//                scores S^T[16 keys, 16 columns] = Khat Q of step j on MFMA 16x16x32 f16 (hi and lo query parts),
+//                plus for a sketched K gamma * <q_s, z> from a tile of the keys' sketch signs; and the group's
+//                share of the table lookups: group 0 stores step j's V levels, group 1 step j + 1's K levels
+//                and norms, into double-buffered LDS tiles (K as [key][coordinate], V as [coordinate][key] in
+//                the key order of the softmax operand), from codes loaded one matrix phase earlier;
+//        vector phase V_j: the scores times the key norms, the causal mask (only on steps that reach past a
+//                column's position), the running maximum per column (base 2), the weights, their sums and the
+//                value weights P' for the next matrix phase.
 //   3. Each column's sums divided by its total weight, the inverse rotation by butterflies, fp32 rows out.
 #include <hip/hip_runtime.h>
 
@@ -54,9 +56,9 @@ struct PrefillArgs {
 
 namespace {
 
-constexpr int kWavesP = 4;
+constexpr int kWavesP = 8;
 constexpr int kThreadsP = 64 * kWavesP;
-constexpr int kBlocksPerCU = 2;       // work-groups per CU the register budget is set for
+constexpr int kBlocksPerCU = 1;       // work-groups per CU the register budget is set for
 
 // 16-column MFMA blocks of query columns per wavefront: two, or one with a sketched K (whose second query
 // operand takes the registers of the second block)
@@ -65,8 +67,20 @@ __host__ __device__ constexpr int cols_per_group(bool kprod) { return 16 * col_b
 constexpr int kStepKeys = 32;         // keys per step: two pages
 constexpr float kLog2eP = 1.4426950408889634f;
 constexpr float kHeadroomP = 4.0f;    // log2 units between a column's running maximum and its weight reference
+// a column's running maximum before its first visible key: finite, so that a masked score (-inf) weighs
+// exp2(-inf) = 0 and the first rescale factor exp2(kNoMaxP - m) underflows to 0
+constexpr float kNoMaxP = -1.0e30f;
 
 typedef _Float16 half4p_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float f4at(const float4 &v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+// largest of eight values as three 3-input maxima and one 2-input
+__device__ __forceinline__ float max8(const float (&v)[2][4]) {
+  const float a = fmaxf(fmaxf(v[0][0], v[0][1]), v[0][2]);
+  const float b = fmaxf(fmaxf(a, v[0][3]), v[1][0]);
+  const float c = fmaxf(fmaxf(b, v[1][1]), v[1][2]);
+  return fmaxf(c, v[1][3]);
+}
 
 // LDS of one work-group: the double-buffered level tiles of a step, or (prologue, epilogue) one
 // [16][D + 4] fp32 staging block per wavefront.
@@ -74,10 +88,10 @@ template <int D, bool KPROD>
 struct Tiles {
   _Float16 k[2][kStepKeys][D + 8];  // K levels [key][coordinate]; rows padded so 16 keys hit distinct banks
   _Float16 v[2][D][kStepKeys + 8];  // V levels [coordinate][k'], k' = 8 g + 4 q2 + j <-> key 16 q2 + 4 g + j
-  uint16_t nk[2][kStepKeys], nv[2][kStepKeys];  // fp16 norms of the step's keys
+  float nk[2][kStepKeys], nv[2][kStepKeys];  // the step's fp16 norms, widened once by the lane that stores them
   // sketched K: the sketch as fp16 -1 / +1 [key][coordinate], and the fp16 residual norms
   _Float16 z[KPROD ? 2 : 1][KPROD ? kStepKeys : 1][D + 8];
-  uint16_t gm[2][kStepKeys];
+  float gm[2][kStepKeys];
 };
 template <int D, bool KPROD>
 union PrefillLds {
@@ -270,7 +284,9 @@ __global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(Prefil
         const int i = i0 + j / G;
         const bool real = j < a.TQ * G && i < a.C;
         const float sig = s_sig[wave][c];
-        colscale[nq] = real ? a.scale_log2 / sig : 0.f;
+        // at least the smallest normal float: a masked score (-inf) times the factor stays -inf, never NaN; with a
+        // softmax scale of 0 the factor times any score is far below an ulp of the weight reference
+        colscale[nq] = fmaxf(real ? a.scale_log2 / sig : 0.f, 1.17549435e-38f);
         lim[nq] = real ? min(P + i, kmax - 1) : -1;
 #pragma unroll
         for (int kb = 0; kb < KBLK; ++kb) {
@@ -331,27 +347,32 @@ __global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(Prefil
       __syncthreads();  // the staging block is rewritten by the next block (and then by the level tiles)
     }
   }
-  // the smallest position of the work-group: steps whose keys all precede it need no causal mask
-  const int first_pos = P + i0;
-
-  // ---- 2. the key steps
+  // ---- 2. the key steps, in two wavefront groups half a step apart. Each group alternates between a matrix
+  // phase M_j (the value sums of step j - 1, the scores of step j, and the group's share of the tile lookups) and
+  // a vector phase V_j (the softmax of step j); group 1 runs one phase behind group 0, so on every SIMD one
+  // wavefront issues MFMAs and table lookups while the other runs the softmax, and a barrier between phases keeps
+  // the offset. In M_j group 0 builds the V tile of step j, group 1 the K tile and the norms of step j + 1; tile j
+  // (K, V, norms) lives in buffer j & 1, which is rewritten only after both groups have read its previous content.
+  const int grp = wave >> 2;
+  const int lw = wave & 3;
+  const int t = tid & 255;
   Tab tk{0, 0, 0, 0}, tv{0, 0, 0, 0};
   if constexpr (KB == 4) tk = make_tab_k4(s_lutk);
   if constexpr (VB == 2) tv = make_tab_v2(s_lutv);
-  // thread roles of the loads: K codes of key kk (page kq = wave / 2), coordinate chunk kc; V codes of
-  // piece vp, slot group vg, coordinates 8 vp + CPT vh .. of page vq = wave / 2; norms (waves 0 and 2,
-  // lanes 0..31): K (lanes < 16) or V norm of slot lane % 16 of page wave / 2
-  const int kk = tid >> 3, kc = tid & 7;
-  const int pq = wave >> 1;  // page of the step this wavefront loads
-  const int vt = tid & 127;
+  // thread roles of the loads. Group 1: K codes of key kk (page kk / 16 = lw / 2), coordinate chunk kc;
+  // norms (its wavefronts 0 and 2, lanes 0..31, 0..47 with a sketched K): K (lanes < 16), V (16..31) or
+  // residual (32..47) norm of slot lane % 16 of page lw / 2. Group 0: V codes of piece vp, slot group vg,
+  // coordinates CPT vh .. of page lw / 2.
+  const int kk = t >> 3, kc = t & 7;
+  const int pq = lw >> 1;
+  const int vt = t & 127;
   const int vp = vt / (4 * NH), vg = (vt / NH) & 3, vh = vt % NH;
   const uint32_t k_off = (uint32_t)(a.k_codes + (int64_t)(kvh * TQ_PAGE_TOKENS + (kk & 15)) * KREC) +
                          (uint32_t)(kc * R::KBYTES);
   const uint32_t k_off_al = k_off & ~3u;
   const int k_bit0 = 8 * (int)(k_off & 3u);
   const uint32_t v_off = (uint32_t)(a.v_codes + ((int64_t)(kvh * (D / 8) + vp) * TQ_PAGE_TOKENS + 4 * vg) * VB);
-  // lanes 32..47 of the same wavefronts: the residual norms of a sketched K
-  const bool norm_lane = (wave & 1) == 0 && lane < (KPROD ? 48 : 32);
+  const bool norm_lane = (lw & 1) == 0 && lane < (KPROD ? 48 : 32);
   const uint32_t n_off = (uint32_t)((lane < 16 ? a.k_norms : (lane < 32 ? a.v_norms : a.k_gamma)) +
                                     (int64_t)(kvh * TQ_PAGE_TOKENS + (lane & 15)) * 2);
   const uint32_t z_off = (uint32_t)(a.k_qjl + (int64_t)(kvh * TQ_PAGE_TOKENS + (kk & 15)) * (D / 8)) +
@@ -360,10 +381,10 @@ __global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(Prefil
   auto page_id = [&](int pi) { return pi < a.max_pages ? ptab[pi] : -1; };
   auto page_ok = [&](int pg) { return pg >= 0 && pg < a.num_pages32; };
 
-  auto load_step = [&](int pg_this, R &rg) {
-    const __amdgpu_buffer_rsrc_t r = page_rsrc(a, pg_this);
+  R rg;
+  auto load_k = [&](int st) __attribute__((always_inline)) {  // group 1: step st's K codes, norms (and sketch bits)
+    const __amdgpu_buffer_rsrc_t r = page_rsrc(a, page_id(2 * st + pq));
     load_dwords<R::KW>(r, k_off_al, rg.kw);
-    load_dwords<VB>(r, v_off, rg.vw);
     rg.norm = norm_lane ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, n_off & ~1u, 0, 0) : 0u;
     rg.zb = 0u;
     if constexpr (KPROD) {
@@ -371,8 +392,12 @@ __global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(Prefil
       else rg.zb = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, z_off, 0, 0);
     }
   };
-  auto store_step = [&](int buf, const R &rg) {
-    // K: D / 8 levels of key kk (4-bit codes: byte-table lookups, eight at a time; other widths: the codes
+  auto load_v = [&](int st) __attribute__((always_inline)) {  // group 0: step st's V codes
+    const __amdgpu_buffer_rsrc_t r = page_rsrc(a, page_id(2 * st + pq));
+    load_dwords<VB>(r, v_off, rg.vw);
+  };
+  auto store_k = [&](int buf) __attribute__((always_inline)) {
+    // D / 8 levels of key kk (4-bit codes: byte-table lookups, eight at a time; other widths: the codes
     // shifted down to bit 0, so every field offset is fixed, and one table read each)
     if constexpr (KB == 4) {
 #pragma unroll
@@ -390,14 +415,34 @@ __global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(Prefil
       }
 #pragma unroll
       for (int i = 0; i < D / 64; ++i) {
-        half8_t t;
+        half8_t t8;
 #pragma unroll
-        for (int p = 0; p < 8; ++p) t[p] = h[8 * i + p];
-        *(half8_t *)&lds.t.k[buf][kk][kc * (D / 8) + 8 * i] = t;
+        for (int p = 0; p < 8; ++p) t8[p] = h[8 * i + p];
+        *(half8_t *)&lds.t.k[buf][kk][kc * (D / 8) + 8 * i] = t8;
       }
     }
-    // V: CPT coordinates of piece vp for slots 4 vg .. 4 vg + 3 of page pq (2-bit codes: slots 0, 1 and 2, 3
-    // of a coordinate looked up as pairs)
+    if (norm_lane) {
+      const int key = 16 * pq + (lane & 15);
+      const float nf = half_bits_to_float((uint16_t)rg.norm);
+      if (lane < 16) lds.t.nk[buf][key] = nf;
+      else if (lane < 32) lds.t.nv[buf][key] = nf;
+      else lds.t.gm[buf][key] = nf;
+    }
+    if constexpr (KPROD) {
+      // sketch bit set: +1 (0x3C00), clear: -1 (0xBC00), coordinate order
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) {
+        half8_t t8;
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+          t8[p] = __builtin_bit_cast(_Float16, (uint16_t)(((rg.zb >> (8 * i + p)) & 1u) ? 0x3C00u : 0xBC00u));
+        *(half8_t *)&lds.t.z[buf][kk][kc * (D / 8) + 8 * i] = t8;
+      }
+    }
+  };
+  auto store_v = [&](int buf) __attribute__((always_inline)) {
+    // CPT coordinates of piece vp for slots 4 vg .. 4 vg + 3 of page pq (2-bit codes: slots 0, 1 and 2, 3 of a
+    // coordinate looked up as pairs)
     if constexpr (VB == 2) {
 #pragma unroll
       for (int e = 0; e < CPT; ++e) {
@@ -412,30 +457,13 @@ __global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(Prefil
 #pragma unroll
       for (int e = 0; e < CPT; ++e) {
         const int ci = CPT * vh + e;
-        half4p_t t;
+        half4p_t t4;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const uint16_t bits = s_lutv[field<VB, VB>(w, 8 * VB * s + VB * ci)];
-          t[s] = __builtin_bit_cast(_Float16, bits);
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const uint16_t bits = s_lutv[field<VB, VB>(w, 8 * VB * s4 + VB * ci)];
+          t4[s4] = __builtin_bit_cast(_Float16, bits);
         }
-        *(half4p_t *)&lds.t.v[buf][8 * vp + ci][8 * vg + 4 * pq] = t;
-      }
-    }
-    if (norm_lane) {
-      const int key = 16 * pq + (lane & 15);
-      if (lane < 16) lds.t.nk[buf][key] = (uint16_t)rg.norm;
-      else if (lane < 32) lds.t.nv[buf][key] = (uint16_t)rg.norm;
-      else lds.t.gm[buf][key] = (uint16_t)rg.norm;
-    }
-    if constexpr (KPROD) {
-      // sketch bit set: +1 (0x3C00), clear: -1 (0xBC00), coordinate order
-#pragma unroll
-      for (int i = 0; i < D / 64; ++i) {
-        half8_t t;
-#pragma unroll
-        for (int p = 0; p < 8; ++p)
-          t[p] = __builtin_bit_cast(_Float16, (uint16_t)(((rg.zb >> (8 * i + p)) & 1u) ? 0x3C00u : 0xBC00u));
-        *(half8_t *)&lds.t.z[buf][kk][kc * (D / 8) + 8 * i] = t;
+        *(half4p_t *)&lds.t.v[buf][8 * vp + ci][8 * vg + 4 * pq] = t4;
       }
     }
   };
@@ -445,88 +473,119 @@ __global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(Prefil
   floatx4_t O[kNQ][NB];
 #pragma unroll
   for (int nq = 0; nq < kNQ; ++nq) {
-    m_run[nq] = -INFINITY;
+    m_run[nq] = kNoMaxP;
     l_part[nq] = 0.f;
     ev[nq] = 0.f;
     wmax[nq] = 0.f;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) O[nq][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
+  // carried from M_j to V_j: the scores (and the sketch contraction); from V_j to M_{j+1}:
+  // the value weights as fp16 hi + lo operands
+  floatx4_t acc[2][kNQ], acc2[KPROD ? 2 : 1][kNQ];
 
-  // one step of 32 keys from buffer buf (full: every key visible to every column and in a valid page). One
-  // body for both cases: a second, unmasked copy raises the register pressure past two work-groups per CU.
-  auto compute = [&](int buf, int s, bool ok0, bool ok1, bool full) {
-    floatx4_t acc[2][kNQ];
+  half8_t phi[kNQ], plo[kNQ];
+  // the smallest position of the wavefront's columns: steps whose keys all precede it need no causal mask
+  const int first_pos = P + i0 + (16 * kNQ * wave) / G;
+
+  auto mphase = [&](int j) __attribute__((always_inline)) {
+    if (j >= 1) {  // O^T += Vhat^T P'^T of step j - 1
+      const int buf = (j - 1) & 1;
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-      for (int nq = 0; nq < kNQ; ++nq) acc[q2][nq] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-      for (int kb = 0; kb < KBLK; ++kb) {
-        const half8_t A = *(const half8_t *)&lds.t.k[buf][16 * q2 + c][32 * kb + 8 * g4];
+      for (int nb = 0; nb < NB; ++nb) {
+        const half8_t Vop = *(const half8_t *)&lds.t.v[buf][16 * nb + c][8 * g4];
 #pragma unroll
         for (int nq = 0; nq < kNQ; ++nq) {
-          acc[q2][nq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qhi[nq][kb], acc[q2][nq], 0, 0, 0);
-          acc[q2][nq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qlo[nq][kb], acc[q2][nq], 0, 0, 0);
+          O[nq][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Vop, phi[nq], O[nq][nb], 0, 0, 0);
+          O[nq][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Vop, plo[nq], O[nq][nb], 0, 0, 0);
         }
       }
-    half4p_t nk[2], nv[2];
-#pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
-      nk[q2] = *(const half4p_t *)&lds.t.nk[buf][16 * q2 + 4 * g4];
-      nv[q2] = *(const half4p_t *)&lds.t.nv[buf][16 * q2 + 4 * g4];
     }
-    if constexpr (KPROD) {
-      // the sketch term: <q_s, z> for every key, times gamma and the ratio of the two range factors, joins the
-      // level term before the key norm
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        floatx4_t acc2[kNQ];
-#pragma unroll
-        for (int nq = 0; nq < kNQ; ++nq) acc2[nq] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KBLK; ++kb) {
-          const half8_t Z = *(const half8_t *)&lds.t.z[buf][16 * q2 + c][32 * kb + 8 * g4];
-#pragma unroll
-          for (int nq = 0; nq < kNQ; ++nq) {
-            acc2[nq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Z, shi[nq][kb], acc2[nq], 0, 0, 0);
-            acc2[nq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Z, slo[nq][kb], acc2[nq], 0, 0, 0);
-          }
-        }
-        const half4p_t gm = *(const half4p_t *)&lds.t.gm[buf][16 * q2 + 4 * g4];
-#pragma unroll
-        for (int nq = 0; nq < kNQ; ++nq)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[q2][nq][j] = fmaf((float)gm[j] * skratio[nq], acc2[nq][j], acc[q2][nq][j]);
-      }
-    }
-    half8_t phi[kNQ], plo[kNQ];
-#pragma unroll
-    for (int nq = 0; nq < kNQ; ++nq) {
-      float sc[2][4];
-      bool okm[2][4];
+    __builtin_amdgcn_sched_barrier(0);  // the value operands' registers are free before the key operands load
+    if (j < nsteps) {  // S^T = Khat Q of step j (hi and lo query parts), the step's norms into registers
+      const int buf = j & 1;
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sc[q2][j] = fmaf((float)nk[q2][j], acc[q2][nq][j], 0.f);  // score / (softmax scale * log2 e)
-          okm[q2][j] = true;
-          if (!full) {
-            const int t = kStepKeys * s + 16 * q2 + 4 * g4 + j;
-            okm[q2][j] = (q2 ? ok1 : ok0) && t <= lim[nq];
-            sc[q2][j] = okm[q2][j] ? sc[q2][j] : -3.0e38f;
+        for (int nq = 0; nq < kNQ; ++nq) acc[q2][nq] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int kb = 0; kb < KBLK; ++kb) {
+          const half8_t A = *(const half8_t *)&lds.t.k[buf][16 * q2 + c][32 * kb + 8 * g4];
+#pragma unroll
+          for (int nq = 0; nq < kNQ; ++nq) {
+            acc[q2][nq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qhi[nq][kb], acc[q2][nq], 0, 0, 0);
+            acc[q2][nq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qlo[nq][kb], acc[q2][nq], 0, 0, 0);
           }
         }
+      if constexpr (KPROD) {  // <q_s, z> for every key
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+#pragma unroll
+          for (int nq = 0; nq < kNQ; ++nq) acc2[q2][nq] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < KBLK; ++kb) {
+            const half8_t Z = *(const half8_t *)&lds.t.z[buf][16 * q2 + c][32 * kb + 8 * g4];
+#pragma unroll
+            for (int nq = 0; nq < kNQ; ++nq) {
+              acc2[q2][nq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Z, shi[nq][kb], acc2[q2][nq], 0, 0, 0);
+              acc2[q2][nq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Z, slo[nq][kb], acc2[q2][nq], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+  };
+
+  // the online softmax of step j: running maximum, weights, value weights P' = p ||v|| as fp16 hi + lo. One body
+  // for masked and unmasked steps (full: every key of the step is visible to every column of the wavefront and
+  // lies in a valid page); a second copy raises the register pressure past the budget.
+  auto softmax = [&](int j) __attribute__((always_inline)) {
+    const bool ok0 = page_ok(page_id(2 * j)), ok1 = page_ok(page_id(2 * j + 1));
+    const bool full = ok0 && ok1 && kStepKeys * (j + 1) <= first_pos + 1;
+    const int nbuf = j & 1;
+    float4 nkr[2], nvr[2], gmr[KPROD ? 2 : 1];
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      nkr[q2] = *(const float4 *)&lds.t.nk[nbuf][16 * q2 + 4 * g4];
+      nvr[q2] = *(const float4 *)&lds.t.nv[nbuf][16 * q2 + 4 * g4];
+      if constexpr (KPROD) gmr[q2] = *(const float4 *)&lds.t.gm[nbuf][16 * q2 + 4 * g4];
+    }
+    if constexpr (KPROD) {
+      // the sketch term, times gamma and the ratio of the two range factors, joins the level term before the
+      // key norm
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int nq = 0; nq < kNQ; ++nq)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            acc[q2][nq][jj] = fmaf(f4at(gmr[q2], jj) * skratio[nq], acc2[q2][nq][jj], acc[q2][nq][jj]);
+    }
+#pragma unroll
+    for (int nq = 0; nq < kNQ; ++nq) {
+      float sc[2][4];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) sc[q2][jj] = f4at(nkr[q2], jj) * acc[q2][nq][jj];  // score / (scale log2 e)
+      if (!full) {  // keys past a column's position or in a missing page weigh exp2(-inf) = 0
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int key = kStepKeys * j + 16 * q2 + 4 * g4 + jj;
+            if (!((q2 ? ok1 : ok0) && key <= lim[nq])) sc[q2][jj] = -INFINITY;
+          }
+      }
       // the lane's own maximum first; the column's (over its four lanes) only when some lane passes m_run
-      const float mxl = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                              fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+      const float mxl = max8(sc);
       if (__any(colscale[nq] * mxl > m_run[nq])) {
         const float m_new = colscale[nq] * max_xor32(max_xor16(mxl));
         const bool up = m_new > m_run[nq];
         const float m_ref = up ? m_new + kHeadroomP : m_run[nq];
-        const float alpha = up ? ((m_run[nq] == -INFINITY) ? 0.f : fast_exp2(m_run[nq] - m_ref)) : 1.f;
+        const float alpha = up ? fast_exp2(m_run[nq] - m_ref) : 1.f;
         l_part[nq] *= alpha;
         wmax[nq] *= alpha;
 #pragma unroll
@@ -539,14 +598,12 @@ __global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(Prefil
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float p = fast_exp2(fmaf(sc[q2][j], colscale[nq], -m_eff));
-          if (!full) p = okm[q2][j] ? p : 0.f;
+        for (int jj = 0; jj < 4; ++jj) {
+          float p = fast_exp2(fmaf(sc[q2][jj], colscale[nq], -m_eff));
           l_part[nq] += p;
-          pv[q2][j] = fmaf((float)nv[q2][j], p, 0.f);
+          pv[q2][jj] = f4at(nvr[q2], jj) * p;
         }
-      const float pvl = fmaxf(fmaxf(fmaxf(pv[0][0], pv[0][1]), fmaxf(pv[0][2], pv[0][3])),
-                              fmaxf(fmaxf(pv[1][0], pv[1][1]), fmaxf(pv[1][2], pv[1][3])));
+      const float pvl = max8(pv);
       wmax[nq] = fmaxf(wmax[nq], pvl);
       if (__any(pvl > kWeightHigh || (wmax[nq] < kWeightLow && pvl > 0.f))) {
         const float f = weight_shift(max_xor32(max_xor16(wmax[nq])), ev[nq], wmax[nq]);
@@ -556,53 +613,59 @@ __global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(Prefil
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) pv[q2][j] *= f;
+          for (int jj = 0; jj < 4; ++jj) pv[q2][jj] *= f;
       }
+      // hi = fp16(P'), lo = fp16(P' - hi) with the difference taken in fp32 from the fp16 hi (one mixed fma)
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
-        for (int j = 0; j < 4; j += 2) {
-          const float2_t pw = {pv[q2][j], pv[q2][j + 1]};
+        for (int jj = 0; jj < 4; jj += 2) {
+          const float2_t pw = {pv[q2][jj], pv[q2][jj + 1]};
           const half2_t h = __builtin_convertvector(pw, half2_t);
-          const half2_t l = __builtin_convertvector(pw - __builtin_convertvector(h, float2_t), half2_t);
-          phi[nq][4 * q2 + j] = h[0];
-          phi[nq][4 * q2 + j + 1] = h[1];
-          plo[nq][4 * q2 + j] = l[0];
-          plo[nq][4 * q2 + j + 1] = l[1];
+          const float2_t r = {fmaf((float)h[0], -1.0f, pw[0]), fmaf((float)h[1], -1.0f, pw[1])};
+          const half2_t l = __builtin_convertvector(r, half2_t);
+          phi[nq][4 * q2 + jj] = h[0];
+          phi[nq][4 * q2 + jj + 1] = h[1];
+          plo[nq][4 * q2 + jj] = l[0];
+          plo[nq][4 * q2 + jj + 1] = l[1];
         }
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const half8_t Vop = *(const half8_t *)&lds.t.v[buf][16 * nb + c][8 * g4];
-#pragma unroll
-      for (int nq = 0; nq < kNQ; ++nq) {
-        O[nq][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Vop, phi[nq], O[nq][nb], 0, 0, 0);
-        O[nq][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Vop, plo[nq], O[nq][nb], 0, 0, 0);
-      }
     }
   };
 
   if (nsteps > 0) {
-    // page ids of steps 0 and 1 (scalar), step 0's codes into buffer 0
-    int pid_cur[2] = {page_id(0), page_id(1)};
-    int pid_nxt[2] = {page_id(2), page_id(3)};
-    R rg;
-    load_step(pid_cur[pq], rg);
-    store_step(0, rg);
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-      const bool more = s + 1 < nsteps;
-      const bool ok0 = page_ok(pid_cur[0]), ok1 = page_ok(pid_cur[1]);
-      if (more) load_step(pid_nxt[pq], rg);
-      const int pid_after[2] = {page_id(2 * s + 4), page_id(2 * s + 5)};
-      const bool full = ok0 && ok1 && kStepKeys * (s + 1) <= first_pos + 1;
-      compute(s & 1, s, ok0, ok1, full);
-      if (more) store_step((s + 1) & 1, rg);
+    // Phases 0 .. 2 nsteps + 1, one barrier after each; each group runs its own loop (the two execute the
+    // same sequence of barriers). Group 0: M_0, V_0, M_1, .., V_{nsteps-1}, M_nsteps, then one idle phase;
+    // group 1: one idle phase, then the same sequence. Codes are loaded one matrix phase ahead of their lookup.
+    if (grp == 0) {
+      load_v(0);
+      __syncthreads();  // step 0's K tile and norms
+      for (int j = 0; j < nsteps; ++j) {
+        mphase(j);
+        store_v(j & 1);
+        if (j + 1 < nsteps) load_v(j + 1);
+        __syncthreads();
+        softmax(j);
+        __syncthreads();
+      }
+      mphase(nsteps);
       __syncthreads();
-      pid_cur[0] = pid_nxt[0];
-      pid_cur[1] = pid_nxt[1];
-      pid_nxt[0] = pid_after[0];
-      pid_nxt[1] = pid_after[1];
+      __syncthreads();
+    } else {
+      load_k(0);
+      store_k(0);
+      if (nsteps > 1) load_k(1);
+      __syncthreads();
+      __syncthreads();
+      for (int j = 0; j < nsteps; ++j) {
+        mphase(j);
+        if (j + 1 < nsteps) store_k((j + 1) & 1);
+        if (j + 2 < nsteps) load_k(j + 2);
+        __syncthreads();
+        softmax(j);
+        __syncthreads();
+      }
+      mphase(nsteps);
+      __syncthreads();
     }
   }
 
