@@ -88,10 +88,12 @@ template <int D, bool KPROD>
 struct Tiles {
   _Float16 k[2][kStepKeys][D + 8];  // K levels [key][coordinate]; rows padded so 16 keys hit distinct banks
   _Float16 v[2][D][kStepKeys + 8];  // V levels [coordinate][k'], k' = 8 g + 4 q2 + j <-> key 16 q2 + 4 g + j
-  float nk[2][kStepKeys], nv[2][kStepKeys];  // the step's fp16 norms, widened once by the lane that stores them
+  // the step's fp16 norms, widened once by the lane that stores them; buffer step % 2, or step % 3 with a sketched
+  // K (whose norms are stored two steps ahead)
+  float nk[3][kStepKeys], nv[3][kStepKeys];
   // sketched K: the sketch as fp16 -1 / +1 [key][coordinate], and the fp16 residual norms
   _Float16 z[KPROD ? 2 : 1][KPROD ? kStepKeys : 1][D + 8];
-  float gm[2][kStepKeys];
+  float gm[3][kStepKeys];
 };
 template <int D, bool KPROD>
 union PrefillLds {
@@ -396,7 +398,8 @@ __global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(Prefil
     const __amdgpu_buffer_rsrc_t r = page_rsrc(a, page_id(2 * st + pq));
     load_dwords<VB>(r, v_off, rg.vw);
   };
-  auto store_k = [&](int buf) __attribute__((always_inline)) {
+  auto store_k = [&](int st) __attribute__((always_inline)) {  // step st's K tile and norms
+    const int buf = st & 1, nbuf = KPROD ? st % 3 : st & 1;
     // D / 8 levels of key kk (4-bit codes: byte-table lookups, eight at a time; other widths: the codes
     // shifted down to bit 0, so every field offset is fixed, and one table read each)
     if constexpr (KB == 4) {
@@ -424,9 +427,9 @@ __global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(Prefil
     if (norm_lane) {
       const int key = 16 * pq + (lane & 15);
       const float nf = half_bits_to_float((uint16_t)rg.norm);
-      if (lane < 16) lds.t.nk[buf][key] = nf;
-      else if (lane < 32) lds.t.nv[buf][key] = nf;
-      else lds.t.gm[buf][key] = nf;
+      if (lane < 16) lds.t.nk[nbuf][key] = nf;
+      else if (lane < 32) lds.t.nv[nbuf][key] = nf;
+      else lds.t.gm[nbuf][key] = nf;
     }
     if constexpr (KPROD) {
       // sketch bit set: +1 (0x3C00), clear: -1 (0xBC00), coordinate order
@@ -544,7 +547,7 @@ __global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(Prefil
   auto softmax = [&](int j) __attribute__((always_inline)) {
     const bool ok0 = page_ok(page_id(2 * j)), ok1 = page_ok(page_id(2 * j + 1));
     const bool full = ok0 && ok1 && kStepKeys * (j + 1) <= first_pos + 1;
-    const int nbuf = j & 1;
+    const int nbuf = KPROD ? j % 3 : j & 1;
     float4 nkr[2], nvr[2], gmr[KPROD ? 2 : 1];
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
@@ -635,15 +638,25 @@ __global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(Prefil
   if (nsteps > 0) {
     // Phases 0 .. 2 nsteps + 1, one barrier after each; each group runs its own loop (the two execute the
     // same sequence of barriers). Group 0: M_0, V_0, M_1, .., V_{nsteps-1}, M_nsteps, then one idle phase;
-    // group 1: one idle phase, then the same sequence. Codes are loaded one matrix phase ahead of their lookup.
+    // group 1 one phase later. The table lookups go where the phases balance: into the matrix phase, or with a
+    // sketched K (whose matrix phase is bound by its three LDS operand tiles) into the vector phase. Codes are
+    // loaded one phase pair ahead of their lookup. Either way each tile is written in the phase pair before the
+    // first matrix phase that reads it, after the last read of its buffer's previous content.
+    constexpr bool kLookupsInMatrix = !KPROD;
     if (grp == 0) {
       load_v(0);
       __syncthreads();  // step 0's K tile and norms
       for (int j = 0; j < nsteps; ++j) {
         mphase(j);
-        store_v(j & 1);
-        if (j + 1 < nsteps) load_v(j + 1);
+        if constexpr (kLookupsInMatrix) {  // V tile j, read from M_{j+1} on
+          store_v(j & 1);
+          if (j + 1 < nsteps) load_v(j + 1);
+        }
         __syncthreads();
+        if constexpr (!kLookupsInMatrix) {
+          store_v(j & 1);
+          if (j + 1 < nsteps) load_v(j + 1);
+        }
         softmax(j);
         __syncthreads();
       }
@@ -655,12 +668,22 @@ __global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(Prefil
       store_k(0);
       if (nsteps > 1) load_k(1);
       __syncthreads();
+      if constexpr (!kLookupsInMatrix) {  // K tile 1 in group 1's first (idle) phase
+        if (nsteps > 1) store_k(1);
+        if (nsteps > 2) load_k(2);
+      }
       __syncthreads();
       for (int j = 0; j < nsteps; ++j) {
         mphase(j);
-        if (j + 1 < nsteps) store_k((j + 1) & 1);
-        if (j + 2 < nsteps) load_k(j + 2);
+        if constexpr (kLookupsInMatrix) {  // K tile j + 1, read from group 0's M_{j+1} on
+          if (j + 1 < nsteps) store_k(j + 1);
+          if (j + 2 < nsteps) load_k(j + 2);
+        }
         __syncthreads();
+        if constexpr (!kLookupsInMatrix) {  // K tile j + 2
+          if (j + 2 < nsteps) store_k(j + 2);
+          if (j + 3 < nsteps) load_k(j + 3);
+        }
         softmax(j);
         __syncthreads();
       }
