@@ -355,6 +355,8 @@ __global__ __launch_bounds__(kThreadsP, kBlocksPerCU) void prefill_kernel(Prefil
   // wavefront issues MFMAs and table lookups while the other runs the softmax, and a barrier between phases keeps
   // the offset. In M_j group 0 builds the V tile of step j, group 1 the K tile and the norms of step j + 1; tile j
   // (K, V, norms) lives in buffer j & 1, which is rewritten only after both groups have read its previous content.
+  // With a sketched K the lookups move to the vector phases (group 0: V tile j in V_j; group 1: K tile j + 2 in
+  // V_j) and the norms to buffer j % 3 (the loops below).
   const int grp = wave >> 2;
   const int lw = wave & 3;
   const int t = tid & 255;
