@@ -394,6 +394,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   constexpr int NB = D / 16;    // 16-coordinate blocks of the value contraction
   constexpr int QF = 16 * D;    // floats in one [16][D] block
   constexpr bool LUT = KB == 4 && VB == 2 && D == 128 && !KPROD;
+  constexpr bool LUT1 = KB == 1 && KPROD && D == 128;  // 1-bit K with its sketch: one table for both operands
   using F = Frag<D, KB, KPROD, VB>;
 
   // Every argument the prologue needs, fetched from the argument segment in one round trip (left to
@@ -432,8 +433,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   // copy l % 32 (K) or l % 16 (V), so the 32 lanes of a 4-byte read or the 16 lanes of an 8-byte read fall in
   // distinct banks. The row address is the code byte itself shifted up by 8 bits, so one v_perm of the code word
   // and the lane's copy offset forms each address.
-  __shared__ __align__(16) uint32_t s_lut[LUT ? 256 * 64 : 4];
+  // LUT1 (1-bit K with the QJL sketch, head_dim 128): row x holds, for the sign bits of four K codes (bits 0..3
+  // of x) and of the same four coordinates' sketch (bits 4..7), their four fp16 K levels (a set bit: the positive
+  // level) and four fp16 sketch values (+1 / -1), 16 bytes, 16 times: lane l reads copy l % 16, so the 16 lanes of
+  // a 16-byte read fall in distinct banks.
+  __shared__ __align__(16) uint32_t s_lut[(LUT || LUT1) ? 256 * 64 : 4];
   auto lut_read = [&](uint32_t byte_addr) { return *(const uint32_t *)((const unsigned char *)s_lut + byte_addr); };
+  auto lut_read4 = [&](uint32_t byte_addr) { return *(const uint4 *)((const unsigned char *)s_lut + byte_addr); };
   auto lut_read2 = [&](uint32_t byte_addr) { return *(const uint2 *)((const unsigned char *)s_lut + byte_addr); };
   __shared__ float s_newnorm[2];
   float(*s_q)[QS] = (float(*)[QS])arena;              // rotated queries / d
@@ -610,6 +616,20 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) row[(i + lane) & 7] = val;
   }
+  if constexpr (LUT1) {
+    // thread pair (2x, 2x + 1) writes row x, eight 16-byte copies each, starting at a copy that rotates with the lane
+    const int x = tid >> 1;
+    uint32_t d[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      d[i] = (uint32_t)s_lutk[(x >> (2 * i)) & 1] | ((uint32_t)s_lutk[(x >> (2 * i + 1)) & 1] << 16);
+      d[2 + i] = (((x >> (4 + 2 * i)) & 1) ? 0x3C00u : 0xBC00u) | ((((x >> (5 + 2 * i)) & 1) ? 0x3C00u : 0xBC00u) << 16);
+    }
+    const uint4 val = {d[0], d[1], d[2], d[3]};
+    uint4 *row = (uint4 *)&s_lut[x * 64 + (tid & 1) * 32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) row[(i + lane) & 7] = val;
+  }
   const int full_end = min(p_end, seq_mem / TQ_PAGE_TOKENS);
   const int n_full = (all_ok && full_end > p_begin) ? (full_end - p_begin) / 2 : 0;
   if constexpr (KPROD) {
@@ -684,7 +704,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   Tab tk{0, 0, 0, 0}, tv{0, 0, 0, 0};
   // LUT: byte 0 of these words is the lane's copy offset inside a table row (K: bytes 0..127, V: 128..255)
   const uint32_t lut_kb = (uint32_t)(lane & 31) * 4u, lut_vb = 128u + (uint32_t)(lane & 15) * 8u;
-  if constexpr (LUT) __syncthreads();  // the table is complete
+  const uint32_t lut1_off = (uint32_t)(lane & 15) * 16u;  // LUT1: the lane's copy inside a row
+  if constexpr (LUT || LUT1) __syncthreads();  // the table is complete
   if constexpr (KB == 4 && !LUT) tk = make_tab_k4(s_lutk);
   if constexpr (KB == 3) tk = make_tab_k3(s_lutk);
   if constexpr (VB == 2 && !LUT) tv = make_tab_v2(s_lutv);
@@ -847,10 +868,25 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         }
       }
       floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+      floatx4_t acc2 = {0.f, 0.f, 0.f, 0.f};  // sketched K: <q_s, z>
+      // LUT1: byte b of t (u) is the table row of coordinates 8b..8b+3 (8b+4..8b+7): K sign nibble low, sketch high
+      uint32_t l1t = 0, l1u = 0;
+      if constexpr (LUT1) {
+        const uint32_t kwd = cur.kw[q2][0], zw = cur.zb[q2];
+        l1t = (kwd & 0x0F0F0F0Fu) | ((zw << 4) & 0xF0F0F0F0u);
+        l1u = ((kwd >> 4) & 0x0F0F0F0Fu) | (zw & 0xF0F0F0F0u);
+      }
 #pragma unroll
       for (int kb = 0; kb < KBLK; ++kb) {
         half8_t A;
-        if constexpr (LUT) {
+        if constexpr (LUT1) {
+          const uint4 lo = lut_read4(perm(l1t, lut1_off, 0x0C0C0400u + ((uint32_t)kb << 8)));
+          const uint4 hi = lut_read4(perm(l1u, lut1_off, 0x0C0C0400u + ((uint32_t)kb << 8)));
+          A = from_dwords(lo.x, lo.y, hi.x, hi.y);
+          const half8_t Z = from_dwords(lo.z, lo.w, hi.z, hi.w);
+          acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Z, shi[kb], acc2, 0, 0, 0);
+          if constexpr (!PK) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Z, slo[kb], acc2, 0, 0, 0);
+        } else if constexpr (LUT) {
           // dword j of the operand: the levels of coordinates 2j, 2j + 1 (code byte j) from table row byte j
           const uint32_t w = cur.kw[q2][kb];
           A = from_dwords(lut_read(perm(w, lut_kb, 0x0C0C0400u)), lut_read(perm(w, lut_kb, 0x0C0C0500u)),
@@ -872,12 +908,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       }
       float raw[4] = {acc[0], acc[1], acc[2], acc[3]};
       if constexpr (KPROD) {
-        floatx4_t acc2 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (!LUT1) {
 #pragma unroll
-        for (int kb = 0; kb < KBLK; ++kb) {
-          const half8_t A = signs_to_half8(cur.zb[q2], 8 * kb, 0x3CBCu, 0u);  // -1 (0xBC00); a set bit: +1 (0x3C00)
-          acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, shi[kb], acc2, 0, 0, 0);
-          if constexpr (!PK) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, slo[kb], acc2, 0, 0, 0);
+          for (int kb = 0; kb < KBLK; ++kb) {
+            const half8_t A = signs_to_half8(cur.zb[q2], 8 * kb, 0x3CBCu, 0u);  // -1 (0xBC00); a set bit: +1 (0x3C00)
+            acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, shi[kb], acc2, 0, 0, 0);
+            if constexpr (!PK) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, slo[kb], acc2, 0, 0, 0);
+          }
         }
         float gam[4];
         unpack4(cur.gm[q2], gam);
