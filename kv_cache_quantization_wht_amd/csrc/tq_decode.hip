@@ -395,6 +395,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   constexpr int QF = 16 * D;    // floats in one [16][D] block
   constexpr bool LUT = KB == 4 && VB == 2 && D == 128 && !KPROD;
   constexpr bool LUT1 = KB == 1 && KPROD && D == 128;  // 1-bit K with its sketch: one table for both operands
+  constexpr bool LUT3 = KB == 3 && VB == 3 && D == 128 && !KPROD;  // 3-bit K and V: a table of code pairs
   using F = Frag<D, KB, KPROD, VB>;
 
   // Every argument the prologue needs, fetched from the argument segment in one round trip (left to
@@ -437,7 +438,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   // of x) and of the same four coordinates' sketch (bits 4..7), their four fp16 K levels (a set bit: the positive
   // level) and four fp16 sketch values (+1 / -1), 16 bytes, 16 times: lane l reads copy l % 16, so the 16 lanes of
   // a 16-byte read fall in distinct banks.
-  __shared__ __align__(16) uint32_t s_lut[(LUT || LUT1) ? 256 * 64 : 4];
+  // LUT3 (3-bit K and V, head_dim 128): row x (256 bytes, 64 rows) holds, for the code pair x (first code in bits
+  // 0..2, second in 3..5), the K entry (their two fp16 levels, one dword) 32 times in bytes 0..127 and the V entry
+  // 32 times in bytes 128..255; lane l reads copy l % 32.
+  __shared__ __align__(16) uint32_t s_lut[(LUT || LUT1) ? 256 * 64 : (LUT3 ? 64 * 64 : 4)];
   auto lut_read = [&](uint32_t byte_addr) { return *(const uint32_t *)((const unsigned char *)s_lut + byte_addr); };
   auto lut_read4 = [&](uint32_t byte_addr) { return *(const uint4 *)((const unsigned char *)s_lut + byte_addr); };
   auto lut_read2 = [&](uint32_t byte_addr) { return *(const uint2 *)((const unsigned char *)s_lut + byte_addr); };
@@ -616,6 +620,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) row[(i + lane) & 7] = val;
   }
+  if constexpr (LUT3) {
+    // eight threads per row x: threads 0..3 the K copies, 4..7 the V copies, two 16-byte chunks each
+    const int x = tid >> 3, q = tid & 7;
+    const uint16_t *lv = q < 4 ? s_lutk : s_lutv;
+    const uint32_t e = (uint32_t)lv[x & 7] | ((uint32_t)lv[x >> 3] << 16);
+    uint4 *row = (uint4 *)&s_lut[x * 64];
+    row[2 * q] = uint4{e, e, e, e};
+    row[2 * q + 1] = uint4{e, e, e, e};
+  }
   if constexpr (LUT1) {
     // thread pair (2x, 2x + 1) writes row x, eight 16-byte copies each, starting at a copy that rotates with the lane
     const int x = tid >> 1;
@@ -672,7 +685,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       const float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
-        const float x = real ? v[LUT ? p : k_order<KB>(p)] * sig : 0.f;
+        const float x = real ? v[(LUT || LUT3) ? p : k_order<KB>(p)] * sig : 0.f;
         _Float16 h, l;
         split_hi_lo(x, h, l);
         if constexpr (PK) {
@@ -705,11 +718,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   // LUT: byte 0 of these words is the lane's copy offset inside a table row (K: bytes 0..127, V: 128..255)
   const uint32_t lut_kb = (uint32_t)(lane & 31) * 4u, lut_vb = 128u + (uint32_t)(lane & 15) * 8u;
   const uint32_t lut1_off = (uint32_t)(lane & 15) * 16u;  // LUT1: the lane's copy inside a row
-  if constexpr (LUT || LUT1) __syncthreads();  // the table is complete
+  const uint32_t lut3_vb = 128u + (uint32_t)(lane & 31) * 4u;  // LUT3: the lane's V copy (K: lut_kb)
+  // LUT3: the table address of code pair k (bits 6k..6k+5) of a 24-bit group of eight codes
+  auto lut3_addr = [&](uint32_t g, int k, uint32_t off) { return (__builtin_amdgcn_ubfe(g, 6 * k, 6) << 8) | off; };
+  if constexpr (LUT || LUT1 || LUT3) __syncthreads();  // the table is complete
   if constexpr (KB == 4 && !LUT) tk = make_tab_k4(s_lutk);
-  if constexpr (KB == 3) tk = make_tab_k3(s_lutk);
+  if constexpr (KB == 3 && !LUT3) tk = make_tab_k3(s_lutk);
   if constexpr (VB == 2 && !LUT) tv = make_tab_v2(s_lutv);
-  if constexpr (VB == 3 && D == 128) tv = make_tab_k3(s_lutv);
+  if constexpr (VB == 3 && D == 128 && !LUT3) tv = make_tab_k3(s_lutv);
   // 1-bit levels: the high byte of the negative and the positive level, and the low byte in all four bytes
   uint32_t lev1_hitab = 0, lev1_lo4 = 0;
   if constexpr (KB == 1) {
@@ -791,6 +807,30 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) Bop[nb] = from_dwords(pairs[nb][0], pairs[nb][1], pairs[nb][2], pairs[nb][3]);
+    } else if constexpr (LUT3) {
+      // per code pair k: the four tokens' entries of each page (levels of coordinates 2k and 2k + 1), then paired
+      // into the two coordinates' operands (low halves: coordinate 2k, high halves: 2k + 1)
+      uint32_t g[2][4];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) g[q2][j] = k3_field(cur.vw[q2], j);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          uint32_t d[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) d[j] = lut_read(lut3_addr(g[q2][j], k, lut3_vb));
+          lo[2 * q2] = perm(d[1], d[0], 0x05040100u);
+          hi[2 * q2] = perm(d[1], d[0], 0x07060302u);
+          lo[2 * q2 + 1] = perm(d[3], d[2], 0x05040100u);
+          hi[2 * q2 + 1] = perm(d[3], d[2], 0x07060302u);
+        }
+        Bop[2 * k] = from_dwords(lo[0], lo[1], lo[2], lo[3]);
+        Bop[2 * k + 1] = from_dwords(hi[0], hi[1], hi[2], hi[3]);
+      }
     } else if constexpr (VB == 3 && D == 128) {
       // each token's 24-bit group (code nb = coordinate nb of the lane's group) spread one code pair per byte;
       // then per byte k and page, the four tokens' pair k gathered into one dword
@@ -893,6 +933,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
                           lut_read(perm(w, lut_kb, 0x0C0C0600u)), lut_read(perm(w, lut_kb, 0x0C0C0700u)));
         } else if constexpr (KB == 4) {
           A = lut_k4(cur.kw[q2][kb], tk);
+        } else if constexpr (LUT3) {
+          // dword k of the operand: the levels of coordinates 2k, 2k + 1 (code pair k), natural order
+          const uint32_t g = k3_field(cur.kw[q2], kb);
+          A = from_dwords(lut_read(lut3_addr(g, 0, lut_kb)), lut_read(lut3_addr(g, 1, lut_kb)),
+                          lut_read(lut3_addr(g, 2, lut_kb)), lut_read(lut3_addr(g, 3, lut_kb)));
         } else if constexpr (KB == 3) {
           A = lut_k3(k3_field(cur.kw[q2], kb), tk);
         } else if constexpr (KB == 1) {
