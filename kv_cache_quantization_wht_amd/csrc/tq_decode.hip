@@ -411,7 +411,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   const int g4 = lane >> 4;  // 8-deep slice of the contraction held by this lane
   const int hc = PK ? (c & 7) : c;                // query head (inside the KV head's group) of column c
   const bool lo_part = PK && c >= 8;              // PK: column c carries the low fp16 parts
-  const float lo_neg = lo_part ? -1.f : 0.f;
+  float neg_one = -1.0f;  // opaque to the compiler, so that x - (float)h stays one mixed-precision FMA
+  asm volatile("" : "+s"(neg_one));
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = a.G;
   const int head0 = kvh * G;
@@ -767,7 +768,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         const float x = s_newnorm[0] * raw * a.scale_log2;
         m_run = x + kHeadroom;
         const float p = fast_exp2(-kHeadroom);
-        l_part = g4 == 0 ? p : 0.f;
+        l_part = (g4 == 0 && !lo_part) ? p : 0.f;  // PK: the low lanes' sums are added at the merge
         const float pv = lo_part ? 0.f : p * s_newnorm[1];  // PK: the value enters once, in the high column
         wmax = p * s_newnorm[1];
 #pragma unroll
@@ -892,18 +893,21 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   };
 
   // FULL: every token of the pair is a cached token of a valid page (no masking needed)
+  // PK: the lanes of a head's high column (c < 8) and low column (c ^ 8) hold the same scores once the two partial
+  // scores are summed; they then split the softmax by page: the high lane takes page 0 of the pair and the low lane
+  // page 1 (its own page), and the two exchange the weights the value MFMA needs at the end. Their reference
+  // m_run - ev is the same (every update of it reduces over both lanes), and their softmax sums add up at the merge.
+  constexpr int NPG = PK ? 1 : 2;  // pages whose softmax a lane computes
   auto process = [&](const F &cur, int pi, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int pp = p_begin + 2 * pi;
-    float s[2][4];
-    half4_t nv[2];
+    float rawp[2][4];
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
       if constexpr (!FULL) {
-        if (q2 == 1 && !cur.ok[1]) {  // a run's odd last page: no second page to score
+        if (q2 == 1 && !cur.ok[1]) {  // a run's odd last page: no second page to score (masked below)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) s[1][j] = -3.0e38f;
-          nv[1] = half4_t{0, 0, 0, 0};
+          for (int j = 0; j < 4; ++j) rawp[1][j] = 0.f;
           continue;
         }
       }
@@ -951,7 +955,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qhi[kb], acc, 0, 0, 0);
         if constexpr (!PK) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qlo[kb], acc, 0, 0, 0);
       }
-      float raw[4] = {acc[0], acc[1], acc[2], acc[3]};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rawp[q2][j] = acc[j];
       if constexpr (KPROD) {
         if constexpr (!LUT1) {
 #pragma unroll
@@ -964,47 +969,70 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         float gam[4];
         unpack4(cur.gm[q2], gam);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) raw[j] = fmaf(gam[j] * skratio, acc2[j], raw[j]);
+        for (int j = 0; j < 4; ++j) rawp[q2][j] = fmaf(gam[j] * skratio, acc2[j], rawp[q2][j]);
       }
-      if constexpr (PK) {
-        // the partial scores of the high (column c) and low (column c ^ 8) query parts: both lanes get the sum
+    }
+
+    // scores of the lane's page(s), in units of softmax scale * log2 e: the fp16 norms enter mixed-precision FMAs
+    // directly (fma with a zero addend, not folded to a multiply since signed zeros are kept)
+    float s[NPG][4];
+    half4_t nv[NPG];
+    bool okp[NPG];
+    int tpg[NPG];  // first token (sequence position) of the lane's page
+    if constexpr (PK) {
+      // the partial scores of the high (column c) and low (column c ^ 8) query parts of both pages: both lanes get
+      // the sums, each keeps its own page's
 #pragma unroll
-        for (int j = 0; j < 4; ++j) raw[j] += xor_lane<8>(raw[j]);
+      for (int j = 0; j < 4; ++j) {
+        const float t0 = rawp[0][j] + xor_lane<8>(rawp[0][j]);
+        const float t1 = rawp[1][j] + xor_lane<8>(rawp[1][j]);
+        rawp[0][j] = lo_part ? t1 : t0;
       }
-      // the fp16 norms enter mixed-precision FMAs directly (fma with a zero addend, not folded to a
-      // multiply since signed zeros are kept)
-      const half4_t nk = as_half4(cur.nk[q2]);
-      nv[q2] = as_half4(cur.nv[q2]);
+      const half4_t nk = as_half4(lo_part ? cur.nk[1] : cur.nk[0]);
+      nv[0] = as_half4(lo_part ? cur.nv[1] : cur.nv[0]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s[q2][j] = fmaf((float)nk[j], raw[j], 0.f);  // score / (softmax scale * log2 e)
+      for (int j = 0; j < 4; ++j) s[0][j] = fmaf((float)nk[j], rawp[0][j], 0.f);
+      okp[0] = lo_part ? cur.ok[1] : cur.ok[0];
+      tpg[0] = (pp + (lo_part ? 1 : 0)) * TQ_PAGE_TOKENS;
+    } else {
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const half4_t nk = as_half4(cur.nk[q2]);
+        nv[q2] = as_half4(cur.nv[q2]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[q2][j] = fmaf((float)nk[j], rawp[q2][j], 0.f);
+        okp[q2] = cur.ok[q2];
+        tpg[q2] = (pp + q2) * TQ_PAGE_TOKENS;
+      }
     }
 
     // tokens past the sequence end or in an invalid page: weight 0 (their bytes are not read as numbers).
     // A masked score is a finite, very negative value so that a zero softmax scale never meets an infinity.
-    bool okm[2][4];
+    bool okm[NPG][4];
     if constexpr (!FULL) {
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
+      for (int q2 = 0; q2 < NPG; ++q2)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int t = (pp + q2) * TQ_PAGE_TOKENS + 4 * g4 + j;
-          okm[q2][j] = cur.ok[q2] && t < seq_mem;
+          okm[q2][j] = okp[q2] && tpg[q2] + 4 * g4 + j < seq_mem;
           s[q2][j] = okm[q2][j] ? s[q2][j] : -3.0e38f;
           nv[q2][j] = okm[q2][j] ? nv[q2][j] : (_Float16)0.f;
         }
     }
 
     // online softmax in base 2 (m_run is in units of scale * log2 e); this lane holds head column c,
-    // tokens 4*g4 .. 4*g4+3 of both pages
-    const float mxl = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                            fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    // tokens 4*g4 .. 4*g4+3 of its page(s)
+    float mxl = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+    if constexpr (NPG == 2) mxl = fmaxf(mxl, fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     // m_run bounds the scores seen so far. When a score passes it, the new reference is set kHeadroom above
     // the new maximum, so the rescale (which any reference allows: it cancels between the sums and the
     // weights) runs only on real jumps of the maximum. The test is taken on the lane's own scores; the
-    // column's maximum (over its four lanes) only when some lane passes.
+    // column's maximum (over its four lanes, and PK: the other page's lanes) only when some lane passes.
     if (__any(colscale * mxl > m_run)) {
       // O holds head column c in this lane, as do m_run and l_part: the rescale stays in the lane
-      const float m_new = colscale * max_xor32(max_xor16(mxl));
+      float mc = max_xor32(max_xor16(mxl));
+      if constexpr (PK) mc = fmaxf(mc, xor_lane<8>(mc));
+      const float m_new = colscale * mc;
       const bool up = m_new > m_run;
       const float m_ref = up ? m_new + kHeadroom : m_run;
       const float alpha = up ? ((m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_ref)) : 1.f;
@@ -1016,9 +1044,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     }
     // weights against the effective reference m_run - ev: p <= 2^ev, value weights P' = p ||v||
     const float m_eff = m_run - ev;
-    float pv[2][4];
+    float pv[NPG][4];
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
+    for (int q2 = 0; q2 < NPG; ++q2) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float p = fast_exp2(fmaf(s[q2][j], colscale, -m_eff));
@@ -1027,34 +1055,54 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         pv[q2][j] = fmaf((float)nv[q2][j], p, 0.f);
       }
     }
-    const float pvl = fmaxf(fmaxf(fmaxf(pv[0][0], pv[0][1]), fmaxf(pv[0][2], pv[0][3])),
-                            fmaxf(fmaxf(pv[1][0], pv[1][1]), fmaxf(pv[1][2], pv[1][3])));
+    float pvl = fmaxf(fmaxf(pv[0][0], pv[0][1]), fmaxf(pv[0][2], pv[0][3]));
+    if constexpr (NPG == 2) pvl = fmaxf(pvl, fmaxf(fmaxf(pv[1][0], pv[1][1]), fmaxf(pv[1][2], pv[1][3])));
     wmax = fmaxf(wmax, pvl);
     if (__any(pvl > kWeightHigh || (wmax < kWeightLow && pvl > 0.f))) {
-      const float f = weight_shift(max_xor32(max_xor16(wmax)), ev, wmax);
+      float wc = max_xor32(max_xor16(wmax));
+      if constexpr (PK) wc = fmaxf(wc, xor_lane<8>(wc));
+      const float f = weight_shift(wc, ev, wmax);
       l_part *= f;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) O[nb] *= f;
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
+      for (int q2 = 0; q2 < NPG; ++q2)
 #pragma unroll
         for (int j = 0; j < 4; ++j) pv[q2][j] *= f;
     }
     half8_t phi, plo;
-#pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
+    if constexpr (PK) {
+      // the lane's four weights as fp16 hi + lo; the high column takes the high parts of both pages, the low column
+      // the low parts: each lane keeps one of its own and receives the other page's from lane c ^ 8 (a row rotation
+      // by 8 written only to the lanes of one half-row: bank mask 0x3 = lanes 0..7 of each 16-lane row, 0xC = 8..15)
+      uint32_t hw[2], lw[2];
 #pragma unroll
       for (int j = 0; j < 4; j += 2) {
-        const float2_t pw = {pv[q2][j], pv[q2][j + 1]};
+        const float2_t pw = {pv[0][j], pv[0][j + 1]};
         const half2_t h = __builtin_convertvector(pw, half2_t);
-        if constexpr (PK) {
-          // high column: P' rounded to fp16; low column: what that rounding left out
-          const float2_t hf = __builtin_convertvector(h, float2_t);
-          const float2_t t = {fmaf(lo_neg, hf[0], pw[0]), fmaf(lo_neg, hf[1], pw[1])};
-          const half2_t u = __builtin_convertvector(t, half2_t);
-          phi[4 * q2 + j] = u[0];
-          phi[4 * q2 + j + 1] = u[1];
-        } else {
+        const float2_t hf = __builtin_convertvector(h, float2_t);
+        // pw - hi as one mixed-precision FMA per element (the fp16 high part read directly)
+        const float2_t t = {fmaf(neg_one, hf[0], pw[0]), fmaf(neg_one, hf[1], pw[1])};
+        const half2_t l = __builtin_convertvector(t, half2_t);
+        hw[j / 2] = __builtin_bit_cast(uint32_t, h);
+        lw[j / 2] = __builtin_bit_cast(uint32_t, l);
+      }
+      uint32_t d[4];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        // page 0 part: high lanes keep their own high part, low lanes take the low part of lane c - 8
+        d[k] = (uint32_t)__builtin_amdgcn_update_dpp((int)hw[k], (int)lw[k], 0x128, 0xF, 0xC, false);
+        // page 1 part: low lanes keep their own low part, high lanes take the high part of lane c + 8
+        d[2 + k] = (uint32_t)__builtin_amdgcn_update_dpp((int)lw[k], (int)hw[k], 0x128, 0xF, 0x3, false);
+      }
+      phi = from_dwords(d[0], d[1], d[2], d[3]);
+    } else {
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+          const float2_t pw = {pv[q2][j], pv[q2][j + 1]};
+          const half2_t h = __builtin_convertvector(pw, half2_t);
           const half2_t l = __builtin_convertvector(pw - __builtin_convertvector(h, float2_t), half2_t);
           phi[4 * q2 + j] = h[0];
           phi[4 * q2 + j + 1] = h[1];
@@ -1101,7 +1149,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   // the sums are in units of the effective reference m_run - ev
   const float m_eff = m_run - ev;
   {
-    const float l_tot = sum_xor16_32(l_part);
+    // PK: the high and low lanes of a column summed the weights of different pages
+    const float l_tot = sum_xor16_32(PK ? l_part + xor_lane<8>(l_part) : l_part);
     if (g4 == 0) {
       s_m[wave][c] = m_eff;
       s_l[wave][c] = l_tot;
