@@ -269,12 +269,36 @@ __device__ __forceinline__ void load_pages(const DecodeArgs &a, const LaneOffset
   }
 }
 
-// The pair starting at run page pp, page ids from the run's table in LDS (pid[0] = page p_begin).
+// Both pages of one pair given as byte offsets into the pool (po.xy: the first page, po.zw: the second; bit 63
+// set marks an invalid page, whose loads get a zero-size buffer as in load_pages).
 template <int D, int KB, bool KPROD, int VB>
-__device__ __forceinline__ void load_pair(const DecodeArgs &a, const int *pid, const LaneOffsets &lo, int pp,
-                                          int p_begin, int p_end, Frag<D, KB, KPROD, VB> &f) {
-  load_pages<D, KB, KPROD, VB>(a, lo, pp < p_end ? pid[pp - p_begin] : -1, pp + 1 < p_end ? pid[pp + 1 - p_begin] : -1,
-                               f);
+__device__ __forceinline__ void load_pages_off(const DecodeArgs &a, const LaneOffsets &lo, uint4 po,
+                                               Frag<D, KB, KPROD, VB> &f) {
+  using F = Frag<D, KB, KPROD, VB>;
+#pragma unroll
+  for (int q2 = 0; q2 < 2; ++q2) {
+    const uint32_t olo = __builtin_amdgcn_readfirstlane(q2 ? po.z : po.x);
+    const uint32_t ohi = __builtin_amdgcn_readfirstlane(q2 ? po.w : po.y);
+    const bool ok = (int32_t)ohi >= 0;
+    f.ok[q2] = ok;
+    const uint64_t off = ((uint64_t)(ohi & 0x7FFFFFFFu) << 32) | olo;  // 0 for an invalid page
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)(a.pages + off), (short)0,
+                                                                       ok ? (int)a.page_bytes : 0, 0x00020000);
+    buf_bytes<F::KCH>(r, lo.k, f.kw[q2]);
+    uint32_t t[2];
+    buf_bytes<8>(r, lo.nk, t);
+    f.nk[q2] = uint2{t[0], t[1]};
+    buf_bytes<8>(r, lo.nv, t);
+    f.nv[q2] = uint2{t[0], t[1]};
+    buf_bytes<F::VCH>(r, lo.v, f.vw[q2]);
+    if constexpr (KPROD) {
+      uint32_t z[1];
+      buf_bytes<D / 32>(r, lo.z, z);
+      f.zb[q2] = z[0];
+      buf_bytes<8>(r, lo.gm, t);
+      f.gm[q2] = uint2{t[0], t[1]};
+    }
+  }
 }
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
@@ -422,7 +446,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   constexpr int QS = D + 4;
   static_assert(2 * 16 * QS <= 4 * QF, "query rows fit in the arena");
   __shared__ __align__(16) float arena[4 * QF];
-  __shared__ int s_pid[kPidCap];
   __shared__ float s_sig[16][2];
   __shared__ uint16_t s_lutk[1 << KB];
   __shared__ uint16_t s_lutv[1 << VB];
@@ -474,6 +497,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   // page ids of this wavefront's first pairs through the scalar cache: the head of the longest chain
   // (page id -> page data)
   constexpr int R = (KB >= 8 || VB >= 8) ? 2 : 3;  // fragments in the ring (wide codes leave room for fewer)
+  // The run's pages as byte offsets into the pool (an invalid page id: bit 63 set, offset 0), followed by invalid
+  // entries for the ring's loads past the run, so a load takes its two offsets with one LDS read and no test.
+  constexpr int PID_PAD = 4 * (R - 1) * kWaves + 4;
+  __shared__ __align__(16) uint2 s_poff[kPidCap + PID_PAD];
   int first_ids[R - 1][2];
   {
     const const_i32 ptab = (const_i32)(a.page_table) + (int64_t)b * a.max_pages;
@@ -542,10 +569,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   for (int u = 0; u < PID_PER_THREAD; ++u) {
     const int j = tid + u * NT;
     if (j < p_end - p_begin) {
-      s_pid[j] = pgv[u];
-      pids_ok &= (pgv[u] >= 0 && pgv[u] < a.num_pages32) ? 1 : 0;
+      const bool ok = pgv[u] >= 0 && pgv[u] < a.num_pages32;
+      const uint64_t off = ok ? (uint64_t)pgv[u] * (uint64_t)a.page_bytes : 0x8000000000000000ull;
+      s_poff[j] = uint2{(uint32_t)off, (uint32_t)(off >> 32)};
+      pids_ok &= ok ? 1 : 0;
     }
   }
+  if (tid < PID_PAD) s_poff[max(p_end - p_begin, 0) + tid] = uint2{0u, 0x80000000u};
   if (tid < (1 << KB)) s_lutk[tid] = lk;
   if (tid < (1 << VB)) s_lutv[tid] = lv;
 
@@ -1130,7 +1160,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     for (int r = 0; r < R; ++r) {
       const int ii = i + r * kWaves;
       const int nx = ii + (R - 1) * kWaves;
-      load_pair<D, KB, KPROD, VB>(a, s_pid, lo, p_begin + 2 * nx, p_begin, p_end, f[(r + R - 1) % R]);
+      const uint4 po = *(const uint4 *)&s_poff[2 * nx];  // pages p_begin + 2 nx and the next
+      load_pages_off<D, KB, KPROD, VB>(a, lo, po, f[(r + R - 1) % R]);
       if (ii < n_full) process(f[r], ii, std::true_type{});
       else if (ii < npairs) process(f[r], ii, std::false_type{});
     }
