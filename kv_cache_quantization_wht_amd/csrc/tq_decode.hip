@@ -269,19 +269,19 @@ __device__ __forceinline__ void load_pages(const DecodeArgs &a, const LaneOffset
   }
 }
 
-// Both pages of one pair given as byte offsets into the pool (po.xy: the first page, po.zw: the second; bit 63
-// set marks an invalid page, whose loads get a zero-size buffer as in load_pages).
+// Both pages of one pair given as checked page ids (pg.x, pg.y; -1 for an invalid page, whose loads get a zero-size
+// buffer as in load_pages). A page is smaller than 2^31 bytes (its buffer size is 32-bit), so the byte offset is one
+// 32 x 32 -> 64-bit unsigned product.
 template <int D, int KB, bool KPROD, int VB>
-__device__ __forceinline__ void load_pages_off(const DecodeArgs &a, const LaneOffsets &lo, uint4 po,
-                                               Frag<D, KB, KPROD, VB> &f) {
+__device__ __forceinline__ void load_pages_id(const DecodeArgs &a, const LaneOffsets &lo, int2 pg,
+                                              Frag<D, KB, KPROD, VB> &f) {
   using F = Frag<D, KB, KPROD, VB>;
 #pragma unroll
   for (int q2 = 0; q2 < 2; ++q2) {
-    const uint32_t olo = __builtin_amdgcn_readfirstlane(q2 ? po.z : po.x);
-    const uint32_t ohi = __builtin_amdgcn_readfirstlane(q2 ? po.w : po.y);
-    const bool ok = (int32_t)ohi >= 0;
+    const int id = __builtin_amdgcn_readfirstlane(q2 ? pg.y : pg.x);
+    const bool ok = id >= 0;
     f.ok[q2] = ok;
-    const uint64_t off = ((uint64_t)(ohi & 0x7FFFFFFFu) << 32) | olo;  // 0 for an invalid page
+    const uint64_t off = (uint64_t)(uint32_t)id * (uint32_t)a.page_bytes;  // unused (size 0) for an invalid page
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)(a.pages + off), (short)0,
                                                                        ok ? (int)a.page_bytes : 0, 0x00020000);
     buf_bytes<F::KCH>(r, lo.k, f.kw[q2]);
@@ -497,10 +497,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   // page ids of this wavefront's first pairs through the scalar cache: the head of the longest chain
   // (page id -> page data)
   constexpr int R = (KB >= 8 || VB >= 8) ? 2 : 3;  // fragments in the ring (wide codes leave room for fewer)
-  // The run's pages as byte offsets into the pool (an invalid page id: bit 63 set, offset 0), followed by invalid
-  // entries for the ring's loads past the run, so a load takes its two offsets with one LDS read and no test.
+  // The run's page ids (an invalid id replaced by -1), followed by -1 entries for the ring's loads past the run,
+  // so a load takes its two ids with one LDS read and no bounds test.
   constexpr int PID_PAD = 4 * (R - 1) * kWaves + 4;
-  __shared__ __align__(16) uint2 s_poff[kPidCap + PID_PAD];
+  __shared__ __align__(8) int s_pid[kPidCap + PID_PAD];
   int first_ids[R - 1][2];
   {
     const const_i32 ptab = (const_i32)(a.page_table) + (int64_t)b * a.max_pages;
@@ -570,12 +570,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     const int j = tid + u * NT;
     if (j < p_end - p_begin) {
       const bool ok = pgv[u] >= 0 && pgv[u] < a.num_pages32;
-      const uint64_t off = ok ? (uint64_t)pgv[u] * (uint64_t)a.page_bytes : 0x8000000000000000ull;
-      s_poff[j] = uint2{(uint32_t)off, (uint32_t)(off >> 32)};
+      s_pid[j] = ok ? pgv[u] : -1;
       pids_ok &= ok ? 1 : 0;
     }
   }
-  if (tid < PID_PAD) s_poff[max(p_end - p_begin, 0) + tid] = uint2{0u, 0x80000000u};
+  if (tid < PID_PAD) s_pid[max(p_end - p_begin, 0) + tid] = -1;
   if (tid < (1 << KB)) s_lutk[tid] = lk;
   if (tid < (1 << VB)) s_lutv[tid] = lv;
 
@@ -1160,8 +1159,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     for (int r = 0; r < R; ++r) {
       const int ii = i + r * kWaves;
       const int nx = ii + (R - 1) * kWaves;
-      const uint4 po = *(const uint4 *)&s_poff[2 * nx];  // pages p_begin + 2 nx and the next
-      load_pages_off<D, KB, KPROD, VB>(a, lo, po, f[(r + R - 1) % R]);
+      const int2 pg = *(const int2 *)&s_pid[2 * nx];  // pages p_begin + 2 nx and the next
+      load_pages_id<D, KB, KPROD, VB>(a, lo, pg, f[(r + R - 1) % R]);
       if (ii < n_full) process(f[r], ii, std::true_type{});
       else if (ii < npairs) process(f[r], ii, std::false_type{});
     }
