@@ -275,3 +275,19 @@ def test_decode_step_equals_append_then_attention(case):
     for b, L in enumerate(lens):
         if L == 0:
             assert np.all(ob[b] == 0)
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 2), (8, 8)], ids=["k4v2", "k8v8"])
+def test_longest_single_run(kb, vb):
+    """One sequence of 4095 pages read as a single run, the longest one work-group holds (a run is at most 4096
+    pages): its page ids fill the work-group's id table, the run ends on a half pair, and the ring's loads past the
+    end read the table's padding. Eight query heads per KV head (packed columns)."""
+    H, d, Hq, T = 1, 128, 8, 4095 * 16
+    print(f"longest single run K{kb}/V{vb}, {T} tokens", flush=True)
+    c = build(H, d, Hq, 1, [T], kb, 0, vb, 0, seed=61 + kb)
+    scale = 1 / math.sqrt(d)
+    out = run_gpu(c, scale, pps=4096)
+    ref = run_ref(c, scale)
+    err = parity.attention_error(out, ref)
+    print(f"longest single run K{kb}/V{vb}: max rel err {err:.3e}")
+    assert err <= parity.ATTN_TOL
