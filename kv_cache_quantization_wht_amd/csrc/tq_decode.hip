@@ -458,10 +458,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   // copy l % 32 (K) or l % 16 (V), so the 32 lanes of a 4-byte read or the 16 lanes of an 8-byte read fall in
   // distinct banks. The row address is the code byte itself shifted up by 8 bits, so one v_perm of the code word
   // and the lane's copy offset forms each address.
-  // LUT1 (1-bit K with the QJL sketch, head_dim 128): row x holds, for the sign bits of four K codes (bits 0..3
-  // of x) and of the same four coordinates' sketch (bits 4..7), their four fp16 K levels (a set bit: the positive
-  // level) and four fp16 sketch values (+1 / -1), 16 bytes, 16 times: lane l reads copy l % 16, so the 16 lanes of
-  // a 16-byte read fall in distinct banks.
+  // LUT1 (1-bit K with the QJL sketch, head_dim 128): row x holds the eight fp16 values +1 / -1 of the bits of x
+  // (bit i: value i; a set bit: +1), 16 bytes, 16 times: lane l reads copy l % 16, so the 16 lanes of a 16-byte read
+  // fall in distinct banks. A byte of sketch bits looks up its eight sketch values, and a byte of 1-bit K codes the
+  // signs of its eight levels: the Lloyd-Max levels of one bit are -L and +L, and L multiplies the query operand.
   // LUT3 (3-bit K and V, head_dim 128): row x (256 bytes, 64 rows) holds, for the code pair x (first code in bits
   // 0..2, second in 3..5), the K entry (their two fp16 levels, one dword) 32 times in bytes 0..127 and the V entry
   // 32 times in bytes 128..255; lane l reads copy l % 32.
@@ -664,10 +664,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     const int x = tid >> 1;
     uint32_t d[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      d[i] = (uint32_t)s_lutk[(x >> (2 * i)) & 1] | ((uint32_t)s_lutk[(x >> (2 * i + 1)) & 1] << 16);
-      d[2 + i] = (((x >> (4 + 2 * i)) & 1) ? 0x3C00u : 0xBC00u) | ((((x >> (5 + 2 * i)) & 1) ? 0x3C00u : 0xBC00u) << 16);
-    }
+    for (int i = 0; i < 4; ++i)
+      d[i] = (((x >> (2 * i)) & 1) ? 0x3C00u : 0xBC00u) | ((((x >> (2 * i + 1)) & 1) ? 0x3C00u : 0xBC00u) << 16);
     const uint4 val = {d[0], d[1], d[2], d[3]};
     uint4 *row = (uint4 *)&s_lut[x * 64 + (tid & 1) * 32];
 #pragma unroll
@@ -707,6 +705,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     const float sig = s_sig[r][0], sig2 = KPROD ? s_sig[r][1] : 1.f;
     colscale = real ? a.scale_log2 / sig : 0.f;
     skratio = sig / sig2;
+    // LUT1: the K operand holds the signs of the levels (+1 / -1), the query operand the level L = level of code 1
+    const float kq = LUT1 ? half_bits_to_float(s_lutk[1]) * sig : sig;
 #pragma unroll
     for (int kb = 0; kb < KBLK; ++kb) {
       // the lane's 8 consecutive coordinates as two 16-byte LDS reads
@@ -715,7 +715,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       const float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
-        const float x = real ? v[(LUT || LUT3) ? p : k_order<KB>(p)] * sig : 0.f;
+        const float x = real ? v[(LUT || LUT3) ? p : k_order<KB>(p)] * kq : 0.f;
         _Float16 h, l;
         split_hi_lo(x, h, l);
         if constexpr (PK) {
@@ -942,21 +942,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       }
       floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
       floatx4_t acc2 = {0.f, 0.f, 0.f, 0.f};  // sketched K: <q_s, z>
-      // LUT1: byte b of t (u) is the table row of coordinates 8b..8b+3 (8b+4..8b+7): K sign nibble low, sketch high
-      uint32_t l1t = 0, l1u = 0;
-      if constexpr (LUT1) {
-        const uint32_t kwd = cur.kw[q2][0], zw = cur.zb[q2];
-        l1t = (kwd & 0x0F0F0F0Fu) | ((zw << 4) & 0xF0F0F0F0u);
-        l1u = ((kwd >> 4) & 0x0F0F0F0Fu) | (zw & 0xF0F0F0F0u);
-      }
 #pragma unroll
       for (int kb = 0; kb < KBLK; ++kb) {
         half8_t A;
         if constexpr (LUT1) {
-          const uint4 lo = lut_read4(perm(l1t, lut1_off, 0x0C0C0400u + ((uint32_t)kb << 8)));
-          const uint4 hi = lut_read4(perm(l1u, lut1_off, 0x0C0C0400u + ((uint32_t)kb << 8)));
-          A = from_dwords(lo.x, lo.y, hi.x, hi.y);
-          const half8_t Z = from_dwords(lo.z, lo.w, hi.z, hi.w);
+          // byte kb of the code word and of the sketch word: coordinates 8 kb .. 8 kb + 7, one table row each
+          const uint4 ks = lut_read4(perm(cur.kw[q2][0], lut1_off, 0x0C0C0400u + ((uint32_t)kb << 8)));
+          const uint4 zs = lut_read4(perm(cur.zb[q2], lut1_off, 0x0C0C0400u + ((uint32_t)kb << 8)));
+          A = from_dwords(ks.x, ks.y, ks.z, ks.w);
+          const half8_t Z = from_dwords(zs.x, zs.y, zs.z, zs.w);
           acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Z, shi[kb], acc2, 0, 0, 0);
           if constexpr (!PK) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Z, slo[kb], acc2, 0, 0, 0);
         } else if constexpr (LUT) {
