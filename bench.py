@@ -44,10 +44,13 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the decode kernel's sources and of the build recipe (its compile flags)."""
     h = hashlib.sha256()
     for f in ("tq_decode.hip", "tq_common.h", "tq_quant_common.h", "tq_lanes.h", "tq_operands.h"):
         with open(os.path.join(ROOT, "kv_cache_quantization_wht_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    with open(os.path.join(ROOT, "kv_cache_quantization_wht_amd", "build.py"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 

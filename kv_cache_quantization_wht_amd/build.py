@@ -29,7 +29,9 @@ COMMON = [
 # (source, object, extra flags). The decode source is compiled in four parts (head_dim 128 / 64, each
 # with packed or one-per-head query columns) so its kernel instantiations build in parallel. No NaN reaches
 # a max or compare on the decode path (masked scores are finite), so the NaN-quieting copies in front of
-# every max are dropped there.
+# every max are dropped there. The head_dim 128 packed-column part (the kernels of every benchmarked
+# workload) uses the instruction-level-parallelism scheduling strategy: measured 1-2% faster on the
+# Llama-70B K4/V2 scan, neutral on the other workloads, no spills in the kernels they run.
 SOURCES = [
     ("tq_capi.cpp", "tq_capi.o", []),
     ("tq_quantize.hip", "tq_quantize.o", []),
@@ -38,7 +40,8 @@ SOURCES = [
     ("tq_stream.hip", "tq_stream.o", []),
     ("tq_qr.cpp", "tq_qr.o", []),
     ("tq_prefill.hip", "tq_prefill.o", ["-fno-honor-nans"]),
-    ("tq_decode.hip", "tq_decode_d128_pk.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=1"]),
+    ("tq_decode.hip", "tq_decode_d128_pk.o",
+     ["-fno-honor-nans", "-DTQ_DECODE_PART=1", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]),
     ("tq_decode.hip", "tq_decode_d128.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=2"]),
     ("tq_decode.hip", "tq_decode_d64_pk.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=3"]),
     ("tq_decode.hip", "tq_decode_d64.o", ["-fno-honor-nans", "-DTQ_DECODE_PART=4"]),
