@@ -60,6 +60,9 @@ CASES = [
     ("gqa2", 4, 128, 8, 1, [129], 3, 0, 3, 0, "bf16", 1.0),
     ("gqa8", 2, 128, 16, 2, [300, 47], 4, 0, 2, 0, "bf16", 1.0),
     ("gqa16", 1, 128, 16, 1, [250], 4, 0, 2, 0, "f16", 1.0),
+    ("gqa3", 2, 128, 6, 2, [333, 31], 4, 0, 2, 0, "bf16", 1.0),
+    ("gqa6-prod-k2v2", 2, 128, 12, 2, [210, 95], 2, 1, 2, 0, "bf16", 1.0),
+    ("gqa5-k3v3", 1, 128, 5, 1, [477], 3, 0, 3, 0, "bf16", 2.0),
     ("k8v8", 2, 128, 8, 2, [90, 161], 8, 0, 8, 0, "bf16", 1.0),
     ("k1v4", 2, 128, 8, 1, [150], 1, 0, 4, 0, "bf16", 1.0),
     ("k3v3-d64", 2, 64, 8, 2, [77, 130], 3, 0, 3, 0, "bf16", 1.0),
