@@ -22,8 +22,8 @@ Readings adopted where the pages are silent:
     (the 1/sqrt(d) factor is applied in arithmetic), and the decision thresholds are
     the exact midpoints of those stored levels;
   * the Lloyd-Max index of coordinate i is the number of thresholds t_j with y'_i >= t_j,
-    where y' = sqrt(d) * R u is the rotated unit vector in N(0,1) units rounded to fp32
-    (ties go to the upper cell);
+    where y' = sqrt(d) * R u is the rotated unit vector in N(0,1) units, taken exactly
+    (fp64, no rounding to a narrower type; ties go to the upper cell);
   * the stored b-bit code is the sign-magnitude form of that index (the codebook is symmetric):
     the top bit is set for the non-negative half, the low b-1 bits count the level's rank away
     from zero (index L/2 + r -> code L/2 + r; index L/2 - 1 - r -> code r, L = 2^b);
