@@ -49,7 +49,11 @@ struct QuantArgs {
 };
 
 constexpr int kProdChunk = 1024;  // tokens per work-group of the prod kernel (S is loaded once per work-group)
-constexpr int kQuantPasses = 2;   // vectors per lane group of one MSE work-group
+// vectors per lane group of one MSE work-group: two for codes of 1 to 4 bits; eight for 8-bit codes, whose
+// work-group first builds its bucket table (below), so that the build is spread over more tokens
+constexpr int kQuantPasses = 2;
+constexpr int kQuantPassesWide = 8;
+constexpr int quant_passes(int bits) { return bits == 8 ? kQuantPassesWide : kQuantPasses; }
 
 // 8-bit codes: a bucket table over the bit patterns of |y| (non-negative floats order like their patterns). Bucket
 // b covers the patterns [(z0 + b) << kBucketShift, (z0 + b + 1) << kBucketShift); its entry holds the pattern of the
@@ -349,7 +353,7 @@ __device__ __forceinline__ void lane_sign_words(const unsigned char *signs, int 
   }
 }
 
-// A work-group holds kQuantPasses * VPB consecutive tokens of one head (K or V, MSE mode): in each pass one
+// A work-group holds quant_passes(BT) * VPB consecutive tokens of one head (K or V, MSE mode): in each pass one
 // vector per D / 32 lanes, the next pass's input rows already in flight (bf16 inputs).
 template <int D, int BT>
 __device__ __forceinline__ void quantize_tokens(const QuantArgs &a, int which, float *s_th) {
@@ -363,7 +367,8 @@ __device__ __forceinline__ void quantize_tokens(const QuantArgs &a, int which, f
   const int lane = threadIdx.x % LANES;
   const int vl = threadIdx.x / LANES;
   const int h = blockIdx.x % a.H;
-  const int64_t t0 = (int64_t)(blockIdx.x / a.H) * (VPB * kQuantPasses);  // first token of the work-group
+  constexpr int NP = quant_passes(BT);
+  const int64_t t0 = (int64_t)(blockIdx.x / a.H) * (VPB * NP);  // first token of the work-group
 
   uint32_t sword, W;
   lane_sign_words<D>(cb + bo.signs, lane, sword, W);
@@ -400,10 +405,10 @@ __device__ __forceinline__ void quantize_tokens(const QuantArgs &a, int which, f
     int64_t slot[2];
     fetch(t0 + vl, d[0], slot[0]);
 #pragma unroll
-    for (int v = 0; v < kQuantPasses; ++v) {
+    for (int v = 0; v < NP; ++v) {
       const int64_t tp = t0 + (int64_t)v * VPB;  // first token of the pass
       if (tp >= a.n_tok) break;
-      if (v + 1 < kQuantPasses && tp + VPB < a.n_tok) fetch(tp + VPB + vl, d[(v + 1) & 1], slot[(v + 1) & 1]);
+      if (v + 1 < NP && tp + VPB < a.n_tok) fetch(tp + VPB + vl, d[(v + 1) & 1], slot[(v + 1) & 1]);
       float x[32];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -415,7 +420,7 @@ __device__ __forceinline__ void quantize_tokens(const QuantArgs &a, int which, f
     }
   } else {
 #pragma unroll 1
-    for (int v = 0; v < kQuantPasses; ++v) {
+    for (int v = 0; v < NP; ++v) {
       const int64_t tp = t0 + (int64_t)v * VPB;
       if (tp >= a.n_tok) break;
       const int64_t t = tp + vl;
@@ -429,6 +434,8 @@ __device__ __forceinline__ void quantize_tokens(const QuantArgs &a, int which, f
   }
 }
 
+// MSE codes of 1 to 4 bits. The 8-bit codes have a kernel of their own: their longer work-groups need more
+// registers, and in one kernel that allocation would cost the narrow widths a wavefront per SIMD.
 template <int D>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   __shared__ float s_th[256];
@@ -437,9 +444,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     case 1: quantize_tokens<D, 1>(a, which, s_th); break;
     case 2: quantize_tokens<D, 2>(a, which, s_th); break;
     case 3: quantize_tokens<D, 3>(a, which, s_th); break;
-    case 4: quantize_tokens<D, 4>(a, which, s_th); break;
-    default: quantize_tokens<D, 8>(a, which, s_th); break;  // MSE widths are 1, 2, 3, 4 or 8
+    default: quantize_tokens<D, 4>(a, which, s_th); break;  // the launch holds widths 1..4 only
   }
+}
+
+// MSE codes of 8 bits.
+template <int D>
+__global__ __launch_bounds__(256) void quantize_wide_kernel(QuantArgs a) {
+  __shared__ float s_th[256];
+  quantize_tokens<D, 8>(a, a.which_of_y[blockIdx.y], s_th);
 }
 
 // Dense random (QR) rotation ahead of the MSE steps ("What the Paper Doesn't Tell You", Finding 4), fused:
@@ -843,16 +856,25 @@ int launch_quantize(const PageGeom &g, void *pages, int64_t num_pages, const voi
     if (a.mode[w] == TQ_PROD) prod_of[n_prod++] = w;
     else mse_of[n_mse++] = w;
   }
-  if (n_mse) {
+  // one launch for both MSE tensors when both codes are 8-bit or both narrower, else one launch each
+  const bool both = n_mse == 2 && (a.bits[mse_of[0]] == 8) == (a.bits[mse_of[1]] == 8);
+  for (int i = 0; i < n_mse; i += both ? 2 : 1) {
     QuantArgs m = a;
-    m.which_of_y[0] = mse_of[0];
-    m.which_of_y[1] = mse_of[1];
-    const int vpb = 256 / (g.head_dim / 32) * kQuantPasses;  // vectors per work-group
+    m.which_of_y[0] = mse_of[i];
+    m.which_of_y[1] = both ? mse_of[1] : mse_of[i];
+    const int bits = a.bits[mse_of[i]];
+    const int vpb = 256 / (g.head_dim / 32) * quant_passes(bits);  // vectors per work-group
     const int64_t blocks = (n_tok + vpb - 1) / vpb * g.num_kv_heads;
     if (blocks > 0x7FFFFFFF) return TQ_EINVAL;
-    const dim3 grid((unsigned)blocks, n_mse);
-    if (g.head_dim == 128) hipLaunchKernelGGL(quantize_kernel<128>, grid, dim3(256), 0, stream, m);
-    else hipLaunchKernelGGL(quantize_kernel<64>, grid, dim3(256), 0, stream, m);
+    const dim3 grid((unsigned)blocks, both ? 2 : 1);
+    const bool d128 = g.head_dim == 128;
+    if (bits == 8) {
+      if (d128) hipLaunchKernelGGL(quantize_wide_kernel<128>, grid, dim3(256), 0, stream, m);
+      else hipLaunchKernelGGL(quantize_wide_kernel<64>, grid, dim3(256), 0, stream, m);
+    } else {
+      if (d128) hipLaunchKernelGGL(quantize_kernel<128>, grid, dim3(256), 0, stream, m);
+      else hipLaunchKernelGGL(quantize_kernel<64>, grid, dim3(256), 0, stream, m);
+    }
     if (hipGetLastError() != hipSuccess) return TQ_EHIP;
   }
   for (int i = 0; i < n_prod; ++i) {  // one launch per prod tensor, its code width fixed at compile time

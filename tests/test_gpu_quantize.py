@@ -19,17 +19,22 @@ CASES = [
     (2, 64, 3, 1, 1, 0, "f32"),
     (2, 64, 8, 0, 3, 0, "bf16"),
     (2, 128, 4, 1, 2, 1, "f32"),
+    # 8-bit work-groups hold 8 passes of tokens, the others 2: several work-groups per head with ragged tails, and
+    # a layer whose K and V widths take separate launches
+    (2, 128, 8, 0, 8, 0, "bf16", 1301),
+    (3, 128, 8, 0, 2, 0, "bf16", 1301),
+    (2, 64, 4, 0, 8, 0, "f16", 2333),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "H{}d{}-K{}{}-V{}{}-{}".format(
-    c[0], c[1], c[2], "p" if c[3] else "m", c[4], "p" if c[5] else "m", c[6]))
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "H{}d{}-K{}{}-V{}{}-{}{}".format(
+    c[0], c[1], c[2], "p" if c[3] else "m", c[4], "p" if c[5] else "m", c[6], f"-T{c[7]}" if len(c) > 7 else ""))
 def test_quantize_matches_oracle(case):
-    H, d, kb, km, vb, vm, dt = case
+    H, d, kb, km, vb, vm, dt = case[:7]
     print(f"quantize case {case}", flush=True)
     layout, Lo = parity.make_layout(H, d, kb, km, vb, vm)
-    n_tok = 301
-    num_pages = 24
+    n_tok = case[7] if len(case) > 7 else 301
+    num_pages = (n_tok * 5 // 4 + 15) // 16  # a quarter of the slots left free (24 pages for 301 tokens)
     k, v = parity.seeded_kv(n_tok, H, d, seed=H * 1000 + d + 10 * kb + vb, dtype=dt)
     rng = np.random.Generator(np.random.Philox(5))
     slots = rng.permutation(num_pages * 16)[:n_tok].astype(np.int64)
