@@ -641,7 +641,8 @@ def run_workload(args, wi):
                                     "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": bytes_io,
                                     "traffic": load_traffic("quantize_traffic.json", quantize_source_hash(),
                                                             key=f"hbm_bytes_per_launch_{f.replace('/', '')}"),
-                                    "kernel": "quantize_kernel (tq_quantize_kv)",
+                                    "kernel": ("quantize_wide_kernel" if x["bits"].k_bits == 8 else "quantize_kernel")
+                                              + " (tq_quantize_kv)",
                                     "bytes": "bf16 K and V in (2 x 256 B per token and KV head) + their records out"}}
         log(f"prefill quantize {f} (layer {l}, {n_vec} vectors): {t * 1e6:.0f} us -> {n_vec / t / 1e9:.2f} G vectors/s, "
             f"{gbs:.0f} GB/s in + out ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak)")
