@@ -35,6 +35,7 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
+QREPS = 4                  # prefill quantize launches timed back to back per format
 WORKLOAD_INDEX = 4         # the headline workload: the largest one that fits one GPU (Llama-70B shape)
 SINGLE_LAYER_INDEX = 1     # the Llama-3.1-8B single layer (secondary line)
 
@@ -607,23 +608,25 @@ def run_workload(args, wi):
         return f"K{b0.k_bits}{'qjl' if b0.k_mode else ''}/V{b0.v_bits}{'qjl' if b0.v_mode else ''}"
 
     # ---- prefill every layer (all sequences of a layer in one launch). The first layer of each format is timed
-    #      (median of 3 launches, HIP events on the launch stream): the quantize-on-write rate and its bytes
+    #      (4 more launches back to back, HIP events between them on the launch stream, the median launch): the
+    #      quantize-on-write rate and its bytes
     prefill_t = {}
     for l, x in enumerate(layers):
         k, v = kvsynth.make_kv(wl, wi, l, B * T, device=dev)
         sl_all = torch.from_numpy(np.concatenate([kvsynth.slots_for(x["pt"], b, 0, T) for b in range(B)])).to(dev)
         f = fmt_of(x)
-        reps = 3 if f not in prefill_t else 1
-        times = []
-        for _ in range(reps):
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            ev[0].record()
-            tq.quantize_kv(x["layout"], x["pages"], k, v, sl_all, x["kcb"], x["vcb"])
-            ev[1].record()
-            torch.cuda.synchronize()
-            times.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+        tq.quantize_kv(x["layout"], x["pages"], k, v, sl_all, x["kcb"], x["vcb"])
         if f not in prefill_t:
-            prefill_t[f] = (l, float(np.median(times)))
+            # the same launch QREPS more times back to back (it writes the same bytes again), an event between each
+            # two: the median of the launch intervals
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(QREPS + 1)]
+            ev[0].record()
+            for i in range(QREPS):
+                tq.quantize_kv(x["layout"], x["pages"], k, v, sl_all, x["kcb"], x["vcb"])
+                ev[i + 1].record()
+            torch.cuda.synchronize()
+            prefill_t[f] = (l, float(np.median([ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(QREPS)])))
         del k, v, sl_all
         if l % 16 == 15:
             log(f"  prefilled {l + 1} layers")
