@@ -178,16 +178,16 @@ def single_layer(args, K, W, cpu=True):
     # ---- prefill: quantize T tokens into every copy (timed on copy 0 for the quantize rate)
     k_pre, v_pre = kvsynth.make_kv(wl, SINGLE_LAYER_INDEX, 0, T, device=dev)
     slots0 = torch.arange(T, dtype=torch.int64, device=dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    qtimes = []
-    for rep in range(6):
-        ev[0].record()
+    # one launch, then 8 more back to back with an event between each two: the median launch interval
+    tq.quantize_kv(layout, pages, k_pre, v_pre, slots0, kcb, vcb)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(9)]
+    ev[0].record()
+    for rep in range(8):
         tq.quantize_kv(layout, pages, k_pre, v_pre, slots0, kcb, vcb)
-        ev[1].record()
-        torch.cuda.synchronize()
-        if rep:
-            qtimes.append(ev[0].elapsed_time(ev[1]) * 1e-3)
-    q_time = float(np.median(qtimes))
+        ev[rep + 1].record()
+    torch.cuda.synchronize()
+    q_time = float(np.median([ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(8)]))
     n_vec = T * H * 2
     quant_vps = n_vec / q_time
     for c in range(1, C):
